@@ -1,0 +1,216 @@
+/*
+ * moe.h - C ABI of the quantized routed-expert MoE layer for AMD MI355X (gfx950).
+ *
+ * One layer of a sparse Mixture-of-Experts model: a router picks k of E
+ * routed experts per token (the pages' model uses 10 of 512, plus one shared
+ * expert that always runs: Strata write-up, "The 30-Second Overview" table;
+ * explainer video, transcript at 2:01). Each selected expert is a SwiGLU FFN
+ * whose weights are block-quantised (the pages run 2-3.5 bit experts: write-up
+ * section 1 "Low-Bit Quantization"); the outputs of a token's experts are
+ * summed into one result (video, transcript at 3:36). The router, gate and
+ * FFN formulas are not on the pages; this library computes:
+ *
+ *   l_e  = sum_h W_r[e,h] x[h] + b_e                 (fp64 accumulation)
+ *   S    = k largest l_e, ordered by (l_e desc, e asc)
+ *   g_i  = softmax over all E, renormalised over S   (= softmax of l_S)
+ *   y    = sum_i g_i * D_{S_i}( SiLU(G_{S_i} x) * (U_{S_i} x) )
+ *          + D_s( SiLU(G_s x) * (U_s x) )            (shared expert, weight 1)
+ *
+ * with w = fp16_scale * signed_code for quantised weights (blocks of 32
+ * consecutive elements along the input dimension).
+ *
+ * CONVENTIONS
+ *  - Every pointer passed to a compute entry point is DEVICE memory owned by
+ *    the caller. The library never allocates device memory, never holds state
+ *    between calls (except the counters of the optional kernel timer) and
+ *    never synchronises the stream: calls enqueue work on `stream` and
+ *    return. Calls are graph-capturable (no memset nodes, no host syncs).
+ *  - Arguments are validated on the host before anything is enqueued. A
+ *    failing call returns a non-zero moe_status and enqueues nothing. A HIP
+ *    launch failure returns MOE_ERR_HIP; moe_last_error() describes it.
+ *  - Device pointers must be 16-byte aligned.
+ *  - Activations are bf16 (uint16 bit patterns) in and out, row-major [T][H].
+ *  - Two calls that share one workspace must be ordered on one stream.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_NULL = 1,      /* a required pointer is NULL */
+  MOE_ERR_SHAPE = 2,     /* a size is out of range or not a multiple it must be */
+  MOE_ERR_ALIGN = 3,     /* a device pointer is not 16-byte aligned */
+  MOE_ERR_DTYPE = 4,     /* unsupported weight type or combination */
+  MOE_ERR_WORKSPACE = 5, /* workspace too small */
+  MOE_ERR_HIP = 6,       /* a HIP runtime call failed */
+  MOE_ERR_VALUE = 7      /* host packing: a code is outside its type's range */
+} moe_status;
+
+/* Weight storage types. */
+typedef enum {
+  MOE_W_F32 = 0,   /* fp32 values */
+  MOE_W_BF16 = 1,  /* bf16 values */
+  MOE_W_Q4 = 2,    /* signed 4-bit codes in [-8,7], one fp16 scale per 32-element block */
+  MOE_W_Q3 = 3,    /* signed 3-bit codes in [-4,3], one fp16 scale per 32-element block */
+  MOE_W_NONE = -1  /* no shared expert */
+} moe_wtype;
+
+/*
+ * PACKED WEIGHT LAYOUT (the library's own; produce it with moe_pack_matrix)
+ *
+ * A weight matrix W[R][K] (R output rows, K input elements, K % 32 == 0) is
+ * stored "chunk-major": the K axis is cut into chunks, and chunk c of every
+ * row is stored before chunk c+1 of any row:
+ *
+ *     value bytes : [K / kc][R][cb]      scales : [K / 32][R]  (fp16)
+ *
+ *   F32 : kc = 4 elements,  cb = 16 bytes (4 x fp32)
+ *   BF16: kc = 8 elements,  cb = 16 bytes (8 x bf16)
+ *   Q4  : kc = 32 elements, cb = 16 bytes = four little-endian 32-bit words
+ *         w0..w3; word j holds elements 8j..8j+7 as unsigned (code + 8):
+ *         element 8j+2s   at bits [4s, 4s+4),
+ *         element 8j+2s+1 at bits [16+4s, 16+4s+4),   s = 0..3
+ *   Q3  : kc = 32 elements, cb = 12 bytes = words L0, L1, HB holding the
+ *         unsigned (code + 4) in [0,7]:
+ *         low two bits: element 2i (i=0..7) at L0 bits [2i, 2i+2) and
+ *         element 2i+1 at L0 bits [16+2i, 16+2i+2); elements 16..31 the
+ *         same in L1 with i-8;
+ *         bit two: element 2i at HB bit i, element 2i+1 at HB bit 16+i
+ *         (i = 0..15).
+ *   F32 and BF16 matrices have no scales.
+ *
+ * An expert's gate and up projections (each [I][H]) are fused into one
+ * matrix GU[2I][H] whose rows come in groups of 32: rows 32q..32q+15 are
+ * gate rows 16q..16q+15 and rows 32q+16..32q+31 are up rows 16q..16q+15
+ * (I % 16 == 0). The down projection is D[H][I].
+ *
+ * Routed experts are stored back to back: expert e's fused gate/up values
+ * start at byte e * moe_matrix_bytes(wt, 2I, H) of gate_up, its scales at
+ * element e * moe_matrix_scales(wt, 2I, H) of gate_up_scales; likewise for
+ * down with (H, I).
+ */
+typedef struct {
+  int32_t hidden;          /* H: multiple of 32, 32..8192 */
+  int32_t inter;           /* I: multiple of 32, 32..4096 */
+  int32_t n_experts;       /* E: 1..1024 */
+  int32_t top_k;           /* k: 1..min(16, E) */
+  const float *router_w;   /* [E][H] fp32 row-major */
+  const float *router_bias;/* [E] fp32, or NULL for no bias */
+  int32_t expert_wtype;    /* moe_wtype of the routed experts: F32, BF16, Q4 or Q3 */
+  const void *gate_up;     /* packed [E] x GU[2I][H] */
+  const uint16_t *gate_up_scales; /* fp16, NULL for F32/BF16 */
+  const void *down;        /* packed [E] x D[H][I] */
+  const uint16_t *down_scales;    /* fp16, NULL for F32/BF16 */
+  int32_t shared_wtype;    /* F32, BF16 or MOE_W_NONE */
+  const void *shared_gate_up;     /* packed GU[2I][H] of the shared expert */
+  const void *shared_down;        /* packed D[H][I] of the shared expert */
+} moe_layer;
+
+/* ------------------------------------------------------------------------ */
+/* Sizes and workspace                                                      */
+/* ------------------------------------------------------------------------ */
+
+/* Bytes of packed values of one R x K matrix of type wt (0 on bad input). */
+size_t moe_matrix_bytes(int32_t wt, int32_t rows, int32_t K);
+/* Number of fp16 scales of one R x K matrix (0 for F32/BF16). */
+size_t moe_matrix_scales(int32_t wt, int32_t rows, int32_t K);
+
+/* Workspace bytes needed by moe_route / moe_forward_decode (mode 0, up to
+ * max_tokens <= MOE_DECODE_MAX_TOKENS tokens per call) or
+ * moe_forward_prefill (mode 1, up to max_tokens tokens per call). Returns 0
+ * when the layer or sizes are invalid. */
+size_t moe_workspace_bytes(const moe_layer *layer, int32_t max_tokens, int32_t mode);
+#define MOE_DECODE_MAX_TOKENS 8
+
+/* The workspace needs no initialisation and keeps no state between calls. */
+
+/* ------------------------------------------------------------------------ */
+/* Compute entry points                                                     */
+/* ------------------------------------------------------------------------ */
+
+/* Routing only (router GEMV/GEMM, softmax, ordered top-k, renormalised
+ * gates) for T >= 1 tokens x[T][H] (bf16).
+ *   topk_idx   [T][k] int32   experts in (logit desc, index asc) order
+ *   topk_gate  [T][k] fp32    renormalised gates, same order
+ *   expert_counts [E] int32 or NULL: number of tokens routed to each expert
+ * Workspace: moe_workspace_bytes(layer, T, 1). */
+moe_status moe_route(const moe_layer *layer, const void *x, int32_t T,
+                     int32_t *topk_idx, float *topk_gate, int32_t *expert_counts,
+                     void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* Decode: B in 1..MOE_DECODE_MAX_TOKENS tokens x[B][H] -> y[B][H] (bf16).
+ * (B * H * 2 bytes of activations are staged in LDS: B * H must not exceed
+ * 8 * 2048; larger requests return MOE_ERR_SHAPE.)
+ * Batch-1 decode is bound by the bytes of the selected experts' weights: a
+ * fused dequantise-GEMV streams each selected expert once per call (experts
+ * chosen by several tokens of the batch are read once). topk_idx/topk_gate
+ * ([B][k]) are optional outputs (NULL to skip).
+ * Workspace: moe_workspace_bytes(layer, B, 0). */
+moe_status moe_forward_decode(const moe_layer *layer, const void *x, int32_t B, void *y,
+                              int32_t *topk_idx, float *topk_gate,
+                              void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* Prefill: T >= 1 tokens x[T][H] -> y[T][H] (bf16). Tokens are grouped by
+ * expert (histogram, exclusive scan, stable permutation) and each expert's
+ * tokens go through an MFMA grouped GEMM with the expert's weights
+ * dequantised to bf16 in LDS; a gather combine adds the gated expert
+ * outputs in slot order and the shared expert. topk_idx/topk_gate ([T][k])
+ * are optional outputs. Workspace: moe_workspace_bytes(layer, T, 1). */
+moe_status moe_forward_prefill(const moe_layer *layer, const void *x, int32_t T, void *y,
+                               int32_t *topk_idx, float *topk_gate,
+                               void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* Between stacked layers (pre-norm residual stream):
+ *   moe_rmsnorm:      z = h / sqrt(mean(h^2) + eps), unit gain, fp32 math
+ *   moe_residual_add: h = bf16(h + y)
+ * h, z, y: bf16 [T][H]. */
+moe_status moe_rmsnorm(const void *h, void *z, int32_t T, int32_t H, float eps, hipStream_t stream);
+moe_status moe_residual_add(void *h, const void *y, int32_t T, int32_t H, hipStream_t stream);
+
+/* ------------------------------------------------------------------------ */
+/* Host-side packing (no device work; host pointers)                        */
+/* ------------------------------------------------------------------------ */
+
+/* Pack one matrix W[R][K] (row-major source) into the chunk-major layout.
+ *   Q4/Q3: src = int8 codes [R][K] (range-checked), src_scales = fp16 [R][K/32]
+ *   F32  : src = float [R][K];  BF16: src = uint16 bf16 [R][K]; src_scales NULL
+ * out: moe_matrix_bytes(wt,R,K) bytes; out_scales: moe_matrix_scales(wt,R,K)
+ * elements (may be NULL for F32/BF16). */
+moe_status moe_pack_matrix(int32_t wt, int32_t rows, int32_t K, const void *src,
+                           const uint16_t *src_scales, void *out, uint16_t *out_scales);
+
+/* Pack gate [I][H] and up [I][H] into the fused GU[2I][H] described above. */
+moe_status moe_pack_gate_up(int32_t wt, int32_t I, int32_t H, const void *gate,
+                            const uint16_t *gate_scales, const void *up,
+                            const uint16_t *up_scales, void *out, uint16_t *out_scales);
+
+/* ------------------------------------------------------------------------ */
+/* Diagnostics                                                              */
+/* ------------------------------------------------------------------------ */
+
+const char *moe_status_string(int32_t status);
+/* Description of the last failure on this thread ("" if none). */
+const char *moe_last_error(void);
+
+/* Optional per-kernel timer: when enabled, every kernel the library
+ * launches is bracketed by HIP events on its stream. moe_timer_read
+ * waits for the recorded events and returns, for kernel class `id`, the
+ * number of launches and their summed duration since the last reset. */
+int32_t moe_kernel_class_count(void);
+const char *moe_kernel_class_name(int32_t id);
+moe_status moe_timer_enable(int32_t on);
+moe_status moe_timer_reset(void);
+moe_status moe_timer_read(int32_t id, int64_t *launches, double *total_ms);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_H */

@@ -97,6 +97,9 @@ def expert_weights(layer, e: int) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
     if layer.wtype == "f32":
         return (layer.gate_f[e].astype(np.float64), layer.up_f[e].astype(np.float64),
                 layer.down_f[e].astype(np.float64))
+    if layer.wtype == "bf16":
+        return (bf16_bits_to_f64(layer.gate_f[e]), bf16_bits_to_f64(layer.up_f[e]),
+                bf16_bits_to_f64(layer.down_f[e]))
     return (dequant_blocks(layer.gate_q[e], layer.gate_s[e]),
             dequant_blocks(layer.up_q[e], layer.up_s[e]),
             dequant_blocks(layer.down_q[e], layer.down_s[e]))

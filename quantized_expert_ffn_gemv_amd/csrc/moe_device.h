@@ -1,0 +1,132 @@
+// Device-side helpers shared by the MoE kernels (gfx950, wave64).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "moe.h"
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef float floatx4_t __attribute__((ext_vector_type(4)));
+
+#define MOE_WAVE 64
+
+namespace moe {
+
+// ---------------------------------------------------------------------------
+// Number formats
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float bf16_lo(uint32_t pair) { return __uint_as_float(pair << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t pair) { return __uint_as_float(pair & 0xFFFF0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// Two floats -> packed bf16 pair (round to nearest even; v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  bf16x2_t r;
+  r[0] = (__bf16)lo;
+  r[1] = (__bf16)hi;
+  return __builtin_bit_cast(uint32_t, r);
+}
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  return (uint16_t)(pack_bf16x2(f, 0.0f) & 0xFFFFu);
+}
+__device__ __forceinline__ float f16_to_f32(uint16_t h) {
+  return (float)__builtin_bit_cast(_Float16, h);
+}
+
+// dot2 of bf16 pairs with fp32 accumulate: c + a.lo*b.lo + a.hi*b.hi
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                         __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
+// ---------------------------------------------------------------------------
+// Code extraction. A "pair" is a 32-bit register holding two 16-bit floats
+// built with a magic exponent: with MAGIC = 0x4300 (bf16 128.0) the halves
+// are bf16(128 + code); with MAGIC = 0x6400 (fp16 1024.0) they are
+// fp16(1024 + code). Codes are the unsigned stored values (signed + 8 for
+// Q4, signed + 4 for Q3). Pair i holds chunk elements 2i (low) and 2i+1.
+// ---------------------------------------------------------------------------
+template <uint32_t MAGIC2>
+__device__ __forceinline__ void q4_pairs(const uint4 w, uint32_t (&p)[16]) {
+  const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+  for (int j = 0; j < 4; j++) {
+#pragma unroll
+    for (int s = 0; s < 4; s++) p[4 * j + s] = ((wd[j] >> (4 * s)) & 0x000F000Fu) | MAGIC2;
+  }
+}
+
+// Pairs 4g..4g+3 of a Q4 chunk, from its word g alone.
+template <uint32_t MAGIC2>
+__device__ __forceinline__ void q4_word_pairs(uint32_t wd, uint32_t (&p)[4]) {
+#pragma unroll
+  for (int s = 0; s < 4; s++) p[s] = ((wd >> (4 * s)) & 0x000F000Fu) | MAGIC2;
+}
+
+template <uint32_t MAGIC2>
+__device__ __forceinline__ uint32_t q3_pair(uint32_t lw, uint32_t hb, int i) {
+  // i in 0..15 (compile-time after unrolling); lw is L0 for i<8, L1 otherwise
+  const int s = i & 7;
+  uint32_t p = ((lw >> (2 * s)) & 0x00030003u) | MAGIC2;
+  uint32_t h = (i >= 2) ? (hb >> (i - 2)) : (hb << (2 - i));
+  return p | (h & 0x00040004u);
+}
+
+template <uint32_t MAGIC2>
+__device__ __forceinline__ void q3_pairs(uint32_t l0, uint32_t l1, uint32_t hb, uint32_t (&p)[16]) {
+#pragma unroll
+  for (int i = 0; i < 16; i++) p[i] = q3_pair<MAGIC2>(i < 8 ? l0 : l1, hb, i);
+}
+
+// Pairs 4g..4g+3 of a Q3 chunk (elements 8g..8g+7).
+template <uint32_t MAGIC2>
+__device__ __forceinline__ void q3_group_pairs(uint32_t l0, uint32_t l1, uint32_t hb, int g,
+                                               uint32_t (&p)[4]) {
+  const uint32_t lw = (g < 2) ? l0 : l1;
+  const uint32_t lsh = lw >> (8 * (g & 1));           // pairs 4(g&1)..: bits 8*(g&1)
+  // high bits of pairs 4g+s sit at HB bits 4g+s (low half) and 16+4g+s
+  const uint32_t hsh = hb >> (4 * g);
+#pragma unroll
+  for (int s = 0; s < 4; s++) {
+    uint32_t v = ((lsh >> (2 * s)) & 0x00030003u) | MAGIC2;
+    uint32_t h = (s >= 2) ? (hsh >> (s - 2)) : (hsh << (2 - s));
+    p[s] = v | (h & 0x00040004u);
+  }
+}
+
+static constexpr uint32_t BF16_MAGIC2 = 0x43004300u;  // bf16(128) in both halves
+static constexpr uint32_t F16_MAGIC2 = 0x64006400u;   // fp16(1024) in both halves
+
+// Offset of stored codes: stored = signed + OFF
+template <int WT> struct QOff;
+template <> struct QOff<MOE_W_Q4> { static constexpr int v = 8; };
+template <> struct QOff<MOE_W_Q3> { static constexpr int v = 4; };
+
+// One fp16-magic pair -> two fp32 weights scale * (code - OFF), exact:
+// fma(1024 + code, s, -(1024 + OFF) * s) rounds the exact value once, and
+// the exact value needs at most 15 significant bits.
+__device__ __forceinline__ void f16pair_dequant(uint32_t pair, float s, float negbase,
+                                                float& lo, float& hi) {
+  half2_t h = __builtin_bit_cast(half2_t, pair);
+  lo = __builtin_fmaf((float)h[0], s, negbase);
+  hi = __builtin_fmaf((float)h[1], s, negbase);
+}
+
+// ---------------------------------------------------------------------------
+// Wave reductions
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ double wave_sum_f64(double v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, MOE_WAVE);
+  return v;
+}
+__device__ __forceinline__ float group_sum_f32(float v, int width) {
+  for (int o = width >> 1; o >= 1; o >>= 1) v += __shfl_xor(v, o, MOE_WAVE);
+  return v;
+}
+
+__device__ __forceinline__ float silu_f32(float a) { return a / (1.0f + __expf(-a)); }
+
+}  // namespace moe

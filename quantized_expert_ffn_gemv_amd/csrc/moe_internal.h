@@ -1,0 +1,102 @@
+// Host/device shared parameter blocks and launch declarations (internal).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "moe.h"
+
+namespace moe {
+
+// Kernel classes for the optional timer.
+enum KernelClass {
+  KC_DEC_ROUTER_SHARED = 0,
+  KC_DEC_GATE_UP,
+  KC_DEC_DOWN,
+  KC_PF_ROUTER,
+  KC_PF_TOPK,
+  KC_PF_COUNT,
+  KC_PF_SCAN,
+  KC_PF_SCATTER,
+  KC_PF_GATE_UP,
+  KC_PF_DOWN,
+  KC_PF_SHARED_GATE_UP,
+  KC_PF_SHARED_DOWN,
+  KC_PF_COMBINE,
+  KC_NORM,
+  KC_RESIDUAL,
+  KC_FILL,
+  KC_COUNT
+};
+
+struct LayerDev {
+  int32_t H, I, E, k;
+  const float* router_w;
+  const float* router_b;
+  int32_t wt;
+  const uint8_t* gu;
+  const uint16_t* gu_s;
+  const uint8_t* dn;
+  const uint16_t* dn_s;
+  int32_t swt;
+  const uint8_t* sgu;
+  const uint8_t* sdn;
+  size_t gu_stride;    // bytes per expert (fused gate/up values)
+  size_t gu_s_stride;  // scales per expert
+  size_t dn_stride;
+  size_t dn_s_stride;
+};
+
+// Decode workspace (all device pointers inside the caller's workspace).
+struct DecodeWs {
+  double* logits;    // [B][E]
+  int32_t* idx;      // [B][k]
+  float* gates;      // [B][k]
+  uint16_t* h;       // [B][k][I] bf16
+  uint16_t* hs;      // [B][I] bf16
+  float* hpart;      // [B][k][I/DEC_NP] sums of DEC_NP consecutive bf16 h values
+  int32_t* uniq;     // [1 + B*k]: count, then unique experts
+  uint32_t* tokmask; // [B*k]
+};
+
+// Prefill workspace.
+struct PrefillWs {
+  double* logits;     // [T][E]
+  int32_t* idx;       // [T][k]
+  float* gates;       // [T][k]
+  int32_t* blk_counts;// [nblk][E]
+  int32_t* blk_base;  // [nblk][E]
+  int32_t* counts;    // [E]
+  int32_t* offsets;   // [E+1]
+  int32_t* tile_start;// [E+1] routed GEMM M-tiles per expert, prefix summed
+  int32_t* perm;      // [T*k] sorted position -> slot
+  int32_t* inv;       // [T*k] slot -> sorted position
+  uint16_t* h;        // [T*k][I] bf16, sorted order
+  uint16_t* hs;       // [T][I] bf16, shared expert
+  uint16_t* Y;        // [T*k][H] bf16, sorted order, un-gated expert outputs
+  uint16_t* Ys;       // [T][H] bf16, shared expert output
+};
+
+// Launch wrappers (return hipError_t of the launch).
+hipError_t launch_decode(const LayerDev& L, const uint16_t* x, int B, uint16_t* y, int32_t* idx_out,
+                         float* gate_out, const DecodeWs& ws, hipStream_t st);
+hipError_t launch_route(const LayerDev& L, const uint16_t* x, int T, int32_t* idx_out, float* gate_out,
+                        int32_t* counts_out, const PrefillWs& ws, hipStream_t st);
+hipError_t launch_prefill(const LayerDev& L, const uint16_t* x, int T, uint16_t* y, int32_t* idx_out,
+                          float* gate_out, const PrefillWs& ws, hipStream_t st);
+hipError_t launch_rmsnorm(const uint16_t* h, uint16_t* z, int T, int H, float eps, hipStream_t st);
+hipError_t launch_residual(uint16_t* h, const uint16_t* y, int T, int H, hipStream_t st);
+hipError_t launch_fill(void* p, size_t bytes, hipStream_t st);
+
+// Decode: gate/up rows handled per workgroup come in DEC_NP (gate, up) pairs.
+constexpr int DEC_NP = 8;
+
+// Prefill tiling constants shared by host sizing and kernels.
+constexpr int PF_BM = 128;          // max rows (tokens) per grouped-GEMM tile
+constexpr int PF_TOK_PER_BLK = 256; // tokens per histogram block
+
+// Timer hooks (api.cpp).
+void timer_begin(int kc, hipStream_t st);
+void timer_end(int kc, hipStream_t st);
+
+}  // namespace moe

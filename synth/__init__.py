@@ -167,7 +167,7 @@ class HostLayer:
     I: int
     E: int
     k: int
-    wtype: str                      # "f32" | "q4" | "q3"
+    wtype: str                      # "f32" | "bf16" | "q4" | "q3"
     router_w: np.ndarray            # f32 [E, H]
     router_b: Optional[np.ndarray]  # f32 [E] or None
     # quantized experts: codes int8 and fp16 scale bits, blocks of 32 along K
@@ -177,7 +177,7 @@ class HostLayer:
     up_s: Optional[np.ndarray] = None
     down_q: Optional[np.ndarray] = None   # [E, H, I]
     down_s: Optional[np.ndarray] = None   # [E, H, I/32]
-    # fp32 experts
+    # fp32 experts (float32), or bf16 experts (uint16 bit patterns)
     gate_f: Optional[np.ndarray] = None   # [E, I, H]
     up_f: Optional[np.ndarray] = None
     down_f: Optional[np.ndarray] = None   # [E, H, I]
@@ -272,10 +272,12 @@ def random_layer(E: int, k: int, H: int, I: int, wtype: str, shared: Optional[st
     rb = zipf_bias(seed, wid, 0, E) if zipf else None
     L = HostLayer(H=H, I=I, E=E, k=k, wtype=wtype, router_w=rw, router_b=rb,
                   meta=dict(workload="random", seed=seed))
-    if wtype == "f32":
-        L.gate_f = np.stack([normal_f32(key(seed, wid, 0, T_GATE_F, e), (I, H), expert_sd) for e in range(E)])
-        L.up_f = np.stack([normal_f32(key(seed, wid, 0, T_UP_F, e), (I, H), expert_sd) for e in range(E)])
-        L.down_f = np.stack([normal_f32(key(seed, wid, 0, T_DOWN_F, e), (H, I), expert_sd) for e in range(E)])
+    if wtype in ("f32", "bf16"):
+        # fp32 values, or bf16 bit patterns for bf16 experts
+        mk = normal_f32 if wtype == "f32" else normal_bf16
+        L.gate_f = np.stack([mk(key(seed, wid, 0, T_GATE_F, e), (I, H), expert_sd) for e in range(E)])
+        L.up_f = np.stack([mk(key(seed, wid, 0, T_UP_F, e), (I, H), expert_sd) for e in range(E)])
+        L.down_f = np.stack([mk(key(seed, wid, 0, T_DOWN_F, e), (H, I), expert_sd) for e in range(E)])
     else:
         bits = 4 if wtype == "q4" else 3
         parts = [expert_codes(seed, wid, 0, e, H, I, bits) for e in range(E)]

@@ -1,0 +1,213 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Routing is compared bit-exactly (indices in order), gates and outputs within
+the tolerances of tests/moe_testlib.py. Full-size workloads are checked on
+sampled tokens of the same launch configuration the benchmark times.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from moe_testlib import check_gates, check_routing, check_y, from_dev_bits, log, to_dev
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def moe():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from quantized_expert_ffn_gemv_amd import moe as m
+    m.lib()
+    return m
+
+
+def _decode_calls(m, L, x_bits, B, ws=None):
+    """Run consecutive decode calls of B tokens; returns y bits, idx, gates."""
+    T, H = x_bits.shape
+    xd = to_dev(x_bits)
+    y = torch.empty((T, H), dtype=torch.int16, device="cuda")
+    idx = torch.empty((T, L.k), dtype=torch.int32, device="cuda")
+    g = torch.empty((T, L.k), dtype=torch.float32, device="cuda")
+    if ws is None:
+        ws = m.make_workspace(L, B, 0)
+    for t0 in range(0, T, B):
+        t1 = min(T, t0 + B)
+        m.moe_forward_decode(L, xd[t0:t1], y[t0:t1], ws, topk_idx=idx[t0:t1], topk_gate=g[t0:t1])
+    torch.cuda.synchronize()
+    return from_dev_bits(y), idx.cpu().numpy(), g.cpu().numpy()
+
+
+def _prefill(m, L, x_bits):
+    T, H = x_bits.shape
+    xd = to_dev(x_bits)
+    ws = m.make_workspace(L, T, 1)
+    y = torch.empty((T, H), dtype=torch.int16, device="cuda")
+    idx = torch.empty((T, L.k), dtype=torch.int32, device="cuda")
+    g = torch.empty((T, L.k), dtype=torch.float32, device="cuda")
+    m.moe_forward_prefill(L, xd, y, ws, topk_idx=idx, topk_gate=g)
+    torch.cuda.synchronize()
+    return from_dev_bits(y), idx.cpu().numpy(), g.cpu().numpy()
+
+
+def _check_all(host, x, y, idx, g, what):
+    y_ref, idx_ref, g_ref = oracle.moe_forward(host, x)
+    _, _, logits = oracle.route(host, x)
+    check_routing(idx, idx_ref, logits, what)
+    check_gates(g, g_ref, what)
+    check_y(y, y_ref, what)
+
+
+# ----------------------------------------------------------------------------- tiny
+
+def test_tiny_decode_b1_and_b8_and_prefill(moe):
+    log("tiny layer: decode B=1, decode B=8, prefill T=16")
+    host = synth.make_layer("tiny")
+    x = synth.make_tokens("tiny")
+    L = moe.DeviceLayer(host)
+    for B in (1, 8):
+        y, idx, g = _decode_calls(moe, L, x, B)
+        _check_all(host, x, y, idx, g, "tiny decode B=%d" % B)
+    y, idx, g = _prefill(moe, L, x)
+    _check_all(host, x, y, idx, g, "tiny prefill")
+
+
+@pytest.mark.parametrize("wtype,shared", [("q4", "bf16"), ("q3", None), ("f32", "f32"), ("bf16", "bf16")])
+def test_ragged_shapes(moe, wtype, shared):
+    # H/32 = 3 blocks (not a power of two), 37 experts, prefill tail of 300 tokens
+    log("ragged layer E=37 k=5 H=96 I=64 %s shared=%s" % (wtype, shared))
+    host = synth.random_layer(37, 5, 96, 64, wtype, shared, seed=11, router_sd=0.2)
+    x = synth.normal_bf16(synth.key(11, 1, 1, 1, 1), (300, 96), 1.0)
+    L = moe.DeviceLayer(host)
+    y, idx, g = _prefill(moe, L, x)
+    _check_all(host, x, y, idx, g, "ragged prefill %s" % wtype)
+    xs = x[:24]
+    for B in (1, 3, 8):
+        y, idx, g = _decode_calls(moe, L, xs, B)
+        _check_all(host, xs, y, idx, g, "ragged decode B=%d %s" % (B, wtype))
+
+
+@pytest.mark.parametrize("E,k", [(1, 1), (4, 4), (64, 16), (1024, 16)])
+def test_edge_expert_counts(moe, E, k):
+    log("edge E=%d k=%d" % (E, k))
+    host = synth.random_layer(E, k, 64, 32, "q4", "bf16", seed=5, router_sd=0.3)
+    x = synth.normal_bf16(synth.key(5, 2, 2, 2, 2), (20, 64), 1.0)
+    L = moe.DeviceLayer(host)
+    y, idx, g = _prefill(moe, L, x)
+    _check_all(host, x, y, idx, g, "edge prefill E=%d k=%d" % (E, k))
+    y, idx, g = _decode_calls(moe, L, x[:8], 1)
+    _check_all(host, x[:8], y, idx, g, "edge decode E=%d k=%d" % (E, k))
+
+
+def test_single_token_prefill_and_zero_input(moe):
+    host = synth.random_layer(16, 4, 64, 32, "q4", "bf16", seed=6)
+    L = moe.DeviceLayer(host)
+    x = np.zeros((1, 64), np.uint16)
+    y, idx, g = _prefill(moe, L, x)
+    assert np.all(oracle.bf16_bits_to_f64(y) == 0.0)
+    assert idx[0].tolist() == [0, 1, 2, 3] and np.allclose(g, 0.25)
+    y, idx, g = _decode_calls(moe, L, x, 1)
+    assert np.all(oracle.bf16_bits_to_f64(y) == 0.0) and idx[0].tolist() == [0, 1, 2, 3]
+
+
+# ----------------------------------------------------------------------------- full-size workloads
+
+@pytest.fixture(scope="module")
+def decode_q4(moe):
+    host = synth.make_layer("decode_q4")
+    return host, moe.DeviceLayer(host), synth.make_tokens("decode_q4")
+
+
+def test_decode_q4_sequence_sampled(moe, decode_q4):
+    # the benchmark's launch configuration: 256 consecutive batch-1 calls
+    host, L, x = decode_q4
+    log("decode_q4: 256 sequential B=1 calls, 24 sampled tokens checked")
+    y, idx, g = _decode_calls(moe, L, x, 1)
+    sample = np.arange(0, 256, 11)
+    _check_all(host, x[sample], y[sample], idx[sample], g[sample], "decode_q4 B=1")
+
+
+@pytest.fixture(scope="module")
+def decode_q3(moe):
+    host = synth.make_layer("decode_q3_zipf")
+    return host, moe.DeviceLayer(host), synth.make_tokens("decode_q3_zipf")
+
+
+def test_decode_q3_zipf_b1_sampled(moe, decode_q3):
+    host, L, x = decode_q3
+    log("decode_q3_zipf: B=1 on 20 sampled tokens")
+    sample = np.arange(3, 256, 13)
+    y, idx, g = _decode_calls(moe, L, x[sample], 1)
+    _check_all(host, x[sample], y, idx, g, "decode_q3 B=1")
+
+
+def test_decode_q3_zipf_b8(moe, decode_q3):
+    host, L, x = decode_q3
+    log("decode_q3_zipf: B=8, 32 calls, 4 calls checked")
+    y, idx, g = _decode_calls(moe, L, x, 8)
+    sample = np.concatenate([np.arange(0, 8), np.arange(64, 72), np.arange(128, 136), np.arange(248, 256)])
+    _check_all(host, x[sample], y[sample], idx[sample], g[sample], "decode_q3 B=8")
+
+
+@pytest.fixture(scope="module")
+def prefill_q4(moe):
+    host = synth.make_layer("prefill_q4")
+    return host, moe.DeviceLayer(host), synth.make_tokens("prefill_q4")
+
+
+def test_prefill_q4_full_routing_sampled_outputs(moe, prefill_q4):
+    host, L, x = prefill_q4
+    log("prefill_q4: T=4096, all routing checked, 48 sampled token outputs")
+    y, idx, g = _prefill(moe, L, x)
+    idx_ref, g_ref, logits = oracle.route(host, x)
+    n = check_routing(idx, idx_ref, logits, "prefill_q4")
+    check_gates(g, g_ref, "prefill_q4")
+    log("  routing: %d tokens differ (ties only)" % n)
+    sample = np.arange(5, 4096, 85)
+    y_ref, _, _ = oracle.moe_forward(host, x[sample])
+    check_y(y[sample], y_ref, "prefill_q4")
+
+
+def test_route_entry_counts(moe, prefill_q4):
+    host, L, x = prefill_q4
+    T = x.shape[0]
+    ws = moe.make_workspace(L, T, 1)
+    idx = torch.empty((T, L.k), dtype=torch.int32, device="cuda")
+    g = torch.empty((T, L.k), dtype=torch.float32, device="cuda")
+    counts = torch.empty((L.E,), dtype=torch.int32, device="cuda")
+    moe.moe_route(L, to_dev(x), idx, g, ws, expert_counts=counts)
+    torch.cuda.synchronize()
+    idx_ref, g_ref, logits = oracle.route(host, x)
+    check_routing(idx.cpu().numpy(), idx_ref, logits, "moe_route")
+    assert np.array_equal(counts.cpu().numpy(), np.bincount(idx.cpu().numpy().ravel(), minlength=L.E))
+
+
+def test_prefill_matches_decode(moe, decode_q4):
+    host, L, x = decode_q4
+    xs = x[:32]
+    yd, idd, _ = _decode_calls(moe, L, xs, 1)
+    yp, idp, _ = _prefill(moe, L, xs)
+    assert np.array_equal(idd, idp)
+    check_y(yp, oracle.bf16_bits_to_f64(yd), "prefill vs decode")
+
+
+# ----------------------------------------------------------------------------- between layers
+
+def test_rmsnorm_and_residual(moe):
+    T, H = 37, 2048
+    h = synth.normal_bf16(synth.key(8, 8, 8, 8, 8), (T, H), 3.0)
+    yv = synth.normal_bf16(synth.key(8, 8, 8, 8, 9), (T, H), 0.5)
+    hd, yd = to_dev(h), to_dev(yv)
+    z = torch.empty_like(hd)
+    moe.moe_rmsnorm(hd, z, 1e-6)
+    moe.moe_residual_add(hd, yd)
+    torch.cuda.synchronize()
+    z_ref = oracle.rmsnorm(oracle.bf16_bits_to_f64(h), 1e-6)
+    zf = oracle.bf16_bits_to_f64(from_dev_bits(z))
+    assert np.abs(zf - z_ref).max() <= 2 ** -8 * np.abs(z_ref).max()
+    r_ref = oracle.bf16_bits_to_f64(h) + oracle.bf16_bits_to_f64(yv)
+    rf = oracle.bf16_bits_to_f64(from_dev_bits(hd))
+    assert np.all(np.abs(rf - r_ref) <= 2 ** -8 * np.abs(r_ref) + 1e-30)

@@ -168,7 +168,7 @@ def test_silu_matches_scipy_expit():
     assert np.allclose(oracle.moe.silu(z), z * scipy.special.expit(z), rtol=1e-14, atol=1e-300)
 
 
-@pytest.mark.parametrize("wtype", ["q4", "q3", "f32"])
+@pytest.mark.parametrize("wtype", ["q4", "q3", "f32", "bf16"])
 def test_sparse_equals_dense_masked_mixture(wtype):
     # brute force: run every expert on every token, weight by gate (0 outside S)
     L = _tiny_q(E=6, k=2, H=64, I=32, wtype=wtype, shared="bf16", router_sd=0.2)
