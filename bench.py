@@ -157,17 +157,16 @@ def main():
     gu, dn, sgu, sdn = decode_expert_bytes(L)
     router_bytes = L.E * L.H * 4
     kbytes = {
-        "dec_router_shared": router_bytes + sgu,
-        "dec_gate_up": L.k * gu,
-        "dec_down": L.k * dn + sdn,
+        "dec_router_shared": router_bytes + sgu + sdn,
+        "dec_routed": L.k * (gu + dn),
     }
     dom = max(kbytes, key=lambda k: kt.get(k, (0, 0))[1])
     n_l, avg_ms = kt[dom]
     achieved = kbytes[dom] / (avg_ms * 1e-3) / 1e9
     per_token_bytes = L.k * (gu + dn) + sgu + sdn
-    kernels = {k: dict(launches=v[0], avg_us=round(v[1] * 1e3, 3),
-                       algo_bytes=kbytes.get(k), gbs=round(kbytes[k] / (v[1] * 1e-3) / 1e9, 1))
-               for k, v in kt.items() if k in kbytes}
+    kernels = {k: dict(launches=v[0], avg_us=round(v[1] * 1e3, 3), algo_bytes=kbytes.get(k),
+                       gbs=round(kbytes[k] / (v[1] * 1e-3) / 1e9, 1) if k in kbytes else None)
+               for k, v in kt.items()}
     log("kernels:", json.dumps(kernels))
 
     result = {

@@ -101,13 +101,7 @@ size_t carve_decode(const moe_layer* L, int B, uint8_t* base, moe::DecodeWs* ws)
   };
   moe::DecodeWs w{};
   w.logits = reinterpret_cast<double*>(take((size_t)B * E * 8));
-  w.idx = reinterpret_cast<int32_t*>(take((size_t)B * k * 4));
-  w.gates = reinterpret_cast<float*>(take((size_t)B * k * 4));
-  w.h = reinterpret_cast<uint16_t*>(take((size_t)B * k * I * 2));
-  w.hs = reinterpret_cast<uint16_t*>(take((size_t)B * I * 2));
-  w.hpart = reinterpret_cast<float*>(take((size_t)B * k * (I / moe::DEC_NP) * 4));
-  w.uniq = reinterpret_cast<int32_t*>(take((1 + (size_t)B * k) * 4));
-  w.tokmask = reinterpret_cast<uint32_t*>(take((size_t)B * k * 4));
+  w.part = reinterpret_cast<float*>(take((size_t)B * (k * (I / 16) + I / 4) * L->hidden * 4));
   if (ws) *ws = w;
   return off;
 }
@@ -187,7 +181,7 @@ void drain_locked() {
 }
 
 const char* const kKernelNames[moe::KC_COUNT] = {
-    "dec_router_shared", "dec_gate_up", "dec_down",         "pf_router",         "pf_topk",
+    "dec_router_shared", "dec_routed", "dec_reduce",         "pf_router",         "pf_topk",
     "pf_count",          "pf_scan",     "pf_scatter",       "pf_gate_up",        "pf_down",
     "pf_shared_gate_up", "pf_shared_down", "pf_combine",    "rmsnorm",           "residual_add",
     "fill"};
@@ -264,6 +258,9 @@ moe_status moe_forward_decode(const moe_layer* layer, const void* x, int32_t B, 
   if (B < 1 || B > MOE_DECODE_MAX_TOKENS) return fail(MOE_ERR_SHAPE, "B=%d not in [1, %d]", B, MOE_DECODE_MAX_TOKENS);
   if ((int64_t)B * layer->hidden > 8 * 2048)
     return fail(MOE_ERR_SHAPE, "B*H=%d exceeds the decode staging limit %d", B * layer->hidden, 8 * 2048);
+  if (moe::decode_lds_b(layer->expert_wtype, B, layer->hidden, layer->n_experts, layer->top_k) > 65536)
+    return fail(MOE_ERR_SHAPE, "B=%d with H=%d, E=%d, k=%d needs more than 64 KiB of LDS", B, layer->hidden,
+                layer->n_experts, layer->top_k);
   if (!aligned16(x) || !aligned16(y) || !aligned16(ws)) return fail(MOE_ERR_ALIGN, "x, y and ws must be 16-byte aligned");
   const size_t need = carve_decode(layer, B, nullptr, nullptr);
   if (ws_bytes < need) return fail(MOE_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);

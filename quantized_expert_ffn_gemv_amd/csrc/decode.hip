@@ -1,118 +1,113 @@
-// Decode path: batch-1 (and small-batch) MoE layer as three kernels.
+// Decode path: one MoE layer for B <= 8 tokens as three kernels.
 //
-//   A  k_dec_router_shared : router logits in fp64 (one wave per expert row)
-//                            and the shared expert's gate/up GEMV + SwiGLU.
-//   B  k_dec_gate_up       : ordered top-k + renormalised gates (every
-//                            workgroup recomputes it from the logits), the
-//                            unique-expert list of the batch, then the fused
-//                            dequantise-GEMV of each selected expert's gate
-//                            and up rows with the SwiGLU epilogue.
-//   C  k_dec_down          : down GEMV of every selected expert and the
-//                            shared expert, gate-weighted and summed per
-//                            output row in a fixed order (no atomics).
+//   A  k_dec_a : router logits in fp64 (one wave per expert row; an fp32
+//                weight times a bf16 activation is exact in fp64), and the
+//                whole shared expert: each workgroup owns 4 intermediate
+//                columns, computes them (gate/up GEMV + SwiGLU) and their
+//                contribution to every output row (a partial down product).
+//   B  k_dec_b : ordered top-k and renormalised gates (every workgroup
+//                derives them from the logits), the batch's unique-expert
+//                list, then per (selected expert, 16 intermediate columns):
+//                fused dequantise-GEMV of the 32 gate/up rows, SwiGLU, and
+//                the gated partial down product over those 16 columns. The
+//                down weights are loaded together with the gate/up weights,
+//                so the down projection adds no memory round trip.
+//   C  k_dec_c : y = sum of the partial products, in a fixed order.
 //
-// Weights are chunk-major (see moe.h), so the lanes of a wave that work on
-// consecutive rows of one chunk read consecutive 16-byte pieces.
+// No float atomics: every partial lands in its own fp32 slot and the sum
+// order is fixed, so results are bitwise reproducible. Threads issue all
+// of their weight loads before computing; lane partial sums reduce by DPP.
 #include "moe_device.h"
 #include "moe_internal.h"
 
 namespace moe {
 
-constexpr int DEC_THREADS = 256;
+constexpr int DA_THREADS = 512;  // kernel A: 8 waves
+constexpr int DB_THREADS = 512;  // kernel B: 8 waves
+constexpr int DC_THREADS = 256;  // kernel C
+constexpr int DC_ROWS = 16;      // output rows per kernel-C workgroup
+constexpr int DC_SPLIT = DC_THREADS / DC_ROWS;
 
-// ---------------------------------------------------------------------------
-// Shared helpers
-// ---------------------------------------------------------------------------
+template <int WT> constexpr int kchunk() { return WT == MOE_W_F32 ? 4 : (WT == MOE_W_BF16 ? 8 : 32); }
+template <int WT> constexpr bool is_q() { return WT == MOE_W_Q4 || WT == MOE_W_Q3; }
 
-// x[t][8c .. 8c+8) as four bf16 pairs from global memory.
-__device__ __forceinline__ uint4 ldg_x8(const uint16_t* x, size_t off) {
-  return *reinterpret_cast<const uint4*>(x + off);
-}
+struct Raw {
+  uint32_t w[4];
+};
 
-// Accumulate one chunk of a BF16 or F32 weight row against token activations
-// held as bf16 in LDS (xs: [nt][H]).
-template <int WT, int MAXB>
-__device__ __forceinline__ void acc_dense_chunk(const uint8_t* wrow_chunk, const uint16_t* xs, int H,
-                                                int c, int nt, float (&acc)[MAXB]) {
-  if constexpr (WT == MOE_W_BF16) {
-    const uint4 w = *reinterpret_cast<const uint4*>(wrow_chunk);
-#pragma unroll
-    for (int t = 0; t < MAXB; t++) {
-      if (t < nt) {
-        const uint4 xv = *reinterpret_cast<const uint4*>(xs + (size_t)t * H + 8 * c);
-        float a = acc[t];
-        a = dot2_bf16(w.x, xv.x, a);
-        a = dot2_bf16(w.y, xv.y, a);
-        a = dot2_bf16(w.z, xv.z, a);
-        a = dot2_bf16(w.w, xv.w, a);
-        acc[t] = a;
-      }
-    }
-  } else {  // F32, chunk = 4 elements
-    const float4 w = *reinterpret_cast<const float4*>(wrow_chunk);
-#pragma unroll
-    for (int t = 0; t < MAXB; t++) {
-      if (t < nt) {
-        const uint2 xv = *reinterpret_cast<const uint2*>(xs + (size_t)t * H + 4 * c);
-        float a = acc[t];
-        a = __builtin_fmaf(w.x, bf16_lo(xv.x), a);
-        a = __builtin_fmaf(w.y, bf16_hi(xv.x), a);
-        a = __builtin_fmaf(w.z, bf16_lo(xv.y), a);
-        a = __builtin_fmaf(w.w, bf16_hi(xv.y), a);
-        acc[t] = a;
-      }
-    }
+template <int WT>
+__device__ __forceinline__ Raw load_chunk(const uint8_t* base, size_t ci) {
+  Raw r;
+  if constexpr (WT == MOE_W_Q3) {
+    const uint32_t* p = reinterpret_cast<const uint32_t*>(base + ci * 12);
+    r.w[0] = p[0];
+    r.w[1] = p[1];
+    r.w[2] = p[2];
+    r.w[3] = 0;
+  } else {
+    const uint4 v = *reinterpret_cast<const uint4*>(base + ci * 16);
+    r.w[0] = v.x;
+    r.w[1] = v.y;
+    r.w[2] = v.z;
+    r.w[3] = v.w;
   }
+  return r;
 }
 
-// Accumulate one 32-element quantised chunk: acc[t] += s * sum_k (code_k - OFF) x_k.
-// xs: bf16 activations [nt][H] in LDS; xsum: [nt][H/32] block sums of x.
-template <int WT, int MAXB>
-__device__ __forceinline__ void acc_quant_chunk(const uint8_t* wchunk, float s, const uint16_t* xs,
-                                                const float* xsum, int H, int c, int nt,
-                                                float (&acc)[MAXB]) {
+// sum_k (code_k - OFF) * a_k over a 32-element chunk (`a`: 32 bf16 values in
+// LDS, asum their sum). Four independent dot2 chains. The caller scales.
+template <int WT>
+__device__ __forceinline__ float qdot32(const Raw& r, const uint16_t* a, float asum) {
   uint32_t p[16];
   if constexpr (WT == MOE_W_Q4) {
-    q4_pairs<BF16_MAGIC2>(*reinterpret_cast<const uint4*>(wchunk), p);
+    q4_pairs<BF16_MAGIC2>(make_uint4(r.w[0], r.w[1], r.w[2], r.w[3]), p);
   } else {
-    const uint32_t* w = reinterpret_cast<const uint32_t*>(wchunk);
-    q3_pairs<BF16_MAGIC2>(w[0], w[1], w[2], p);
+    q3_pairs<BF16_MAGIC2>(r.w[0], r.w[1], r.w[2], p);
   }
-  constexpr float base = 128.0f + (float)QOff<WT>::v;
-  const int nb = H >> 5;
+  const uint4* av = reinterpret_cast<const uint4*>(a);
+  float c0 = -(128.0f + (float)QOff<WT>::v) * asum, c1 = 0.0f, c2 = 0.0f, c3 = 0.0f;
 #pragma unroll
-  for (int t = 0; t < MAXB; t++) {
-    if (t < nt) {
-      const uint4* xv = reinterpret_cast<const uint4*>(xs + (size_t)t * H + 32 * c);
-      float a = -base * xsum[t * nb + c];
-#pragma unroll
-      for (int q = 0; q < 4; q++) {
-        const uint4 v = xv[q];
-        a = dot2_bf16(p[4 * q + 0], v.x, a);
-        a = dot2_bf16(p[4 * q + 1], v.y, a);
-        a = dot2_bf16(p[4 * q + 2], v.z, a);
-        a = dot2_bf16(p[4 * q + 3], v.w, a);
-      }
-      acc[t] = __builtin_fmaf(s, a, acc[t]);
-    }
+  for (int q = 0; q < 4; q++) {
+    const uint4 v = av[q];
+    c0 = dot2_bf16(p[4 * q + 0], v.x, c0);
+    c1 = dot2_bf16(p[4 * q + 1], v.y, c1);
+    c2 = dot2_bf16(p[4 * q + 2], v.z, c2);
+    c3 = dot2_bf16(p[4 * q + 3], v.w, c3);
+  }
+  return (c0 + c1) + (c2 + c3);
+}
+
+// Dot of one dense chunk (8 bf16 or 4 fp32 weights) with bf16 activations.
+template <int WT>
+__device__ __forceinline__ float ddot(const Raw& r, const uint16_t* a, float acc) {
+  if constexpr (WT == MOE_W_BF16) {
+    const uint4 v = *reinterpret_cast<const uint4*>(a);
+    float c1 = 0.0f;
+    acc = dot2_bf16(r.w[0], v.x, acc);
+    c1 = dot2_bf16(r.w[1], v.y, c1);
+    acc = dot2_bf16(r.w[2], v.z, acc);
+    c1 = dot2_bf16(r.w[3], v.w, c1);
+    return acc + c1;
+  } else {
+    const uint2 v = *reinterpret_cast<const uint2*>(a);
+    acc = __builtin_fmaf(__uint_as_float(r.w[0]), bf16_lo(v.x), acc);
+    acc = __builtin_fmaf(__uint_as_float(r.w[1]), bf16_hi(v.x), acc);
+    acc = __builtin_fmaf(__uint_as_float(r.w[2]), bf16_lo(v.y), acc);
+    acc = __builtin_fmaf(__uint_as_float(r.w[3]), bf16_hi(v.y), acc);
+    return acc;
   }
 }
 
-// Stage tokens tl[0..nt) of x into LDS (bf16) and, for quantised weights,
-// their 32-element block sums.
-__device__ __forceinline__ void stage_x(const uint16_t* x, const int* tl, int nt, int H, uint16_t* xs,
-                                        float* xsum, bool sums) {
-  const int n16 = H / 8;  // 16-byte pieces per token
-  for (int i = threadIdx.x; i < nt * n16; i += blockDim.x) {
-    const int ti = i / n16, c = i - ti * n16;
-    reinterpret_cast<uint4*>(xs + (size_t)ti * H)[c] = ldg_x8(x, (size_t)tl[ti] * H + 8 * c);
-  }
-  if (sums) {
+// Copy B tokens of x into LDS (bf16) and, if asked, their 32-element block sums.
+template <int NT>
+__device__ __forceinline__ void stage_tokens(const uint16_t* __restrict__ x, int B, int H, uint16_t* xs, float* xsum) {
+  const int n16 = H / 8;
+  for (int i = threadIdx.x; i < B * n16; i += NT) reinterpret_cast<uint4*>(xs)[i] = reinterpret_cast<const uint4*>(x)[i];
+  if (xsum) {
     __syncthreads();
     const int nb = H >> 5;
-    for (int i = threadIdx.x; i < nt * nb; i += blockDim.x) {
-      const int ti = i / nb, b = i - ti * nb;
-      const uint32_t* v = reinterpret_cast<const uint32_t*>(xs + (size_t)ti * H + 32 * b);
+    for (int i = threadIdx.x; i < B * nb; i += NT) {
+      const uint32_t* v = reinterpret_cast<const uint32_t*>(xs + (size_t)i * 32);
       float a = 0.0f;
 #pragma unroll
       for (int j = 0; j < 16; j++) a += bf16_lo(v[j]) + bf16_hi(v[j]);
@@ -121,498 +116,705 @@ __device__ __forceinline__ void stage_x(const uint16_t* x, const int* tl, int nt
   }
 }
 
-// Gate/up GEMV for NP (gate, up) row pairs of group q starting at pair j0,
-// for the staged tokens. Writes h (bf16) through out(t, j) pointers.
-// Thread map: rr = tid % (2*NP) (rows 0..NP-1 gate, NP..2NP-1 up),
-// kpart = tid / (2*NP).
-template <int WT, int MAXB, int NP>
-__device__ __forceinline__ void gate_up_rows(const uint8_t* gu, const uint16_t* gus, int H, int I, int q,
-                                             int j0, const uint16_t* xs, const float* xsum, int nt,
-                                             float* red, float (&acc)[MAXB]) {
-  constexpr int RW = 2 * NP;
-  constexpr int NK = DEC_THREADS / RW;
-  const int tid = threadIdx.x;
-  const int rr = tid % RW, kp = tid / RW;
-  const int R = 2 * I;
-  const int row = 32 * q + (rr < NP ? j0 + rr : 16 + j0 + (rr - NP));
+__device__ __forceinline__ float wave_total_f32(float v) {
+  v = sum16_f32(v);
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return (r0 + r1) + (r2 + r3);
+}
+
+// ---------------------------------------------------------------------------
+// Down-projection pieces: NCOL consecutive intermediate columns (16 for a
+// routed workgroup, 4 for a shared-expert workgroup) of one output row of a
+// chunk-major D[H][I], and their dot with NCOL bf16 h values (NCOL/2 pairs).
+// ---------------------------------------------------------------------------
+template <int WT, int NCOL>
+struct DownPiece {
+  static constexpr int NW = is_q<WT>() ? 2 : (WT == MOE_W_F32 ? NCOL : NCOL / 2);
+  uint32_t w[NW];
+  float s;
+};
+
+template <int WT, int NCOL>
+__device__ __forceinline__ void load_down_piece(const uint8_t* dn, const uint16_t* dns, int H, int row, int col0,
+                                                DownPiece<WT, NCOL>& d) {
+  if constexpr (is_q<WT>()) {
+    static_assert(NCOL == 16, "quantised down pieces are half chunks");
+    const int c = col0 >> 5, half = (col0 >> 4) & 1;
+    const uint8_t* base = dn + ((size_t)c * H + row) * (WT == MOE_W_Q4 ? 16 : 12);
+    if constexpr (WT == MOE_W_Q4) {
+      const uint2 v = *reinterpret_cast<const uint2*>(base + 8 * half);  // words 2h, 2h+1
+      d.w[0] = v.x;
+      d.w[1] = v.y;
+    } else {
+      const uint32_t* p = reinterpret_cast<const uint32_t*>(base);
+      d.w[0] = p[half];  // L0 or L1
+      d.w[1] = p[2];     // HB
+    }
+    d.s = f16_to_f32(dns[(size_t)c * H + row]);
+  } else {
+    constexpr int KC = kchunk<WT>();
+    constexpr int ES = (WT == MOE_W_F32) ? 4 : 2;
+    if constexpr (NCOL >= KC) {
+      constexpr int NCH = NCOL / KC;
 #pragma unroll
-  for (int t = 0; t < MAXB; t++) acc[t] = 0.0f;
-  if constexpr (WT == MOE_W_Q4 || WT == MOE_W_Q3) {
-    constexpr int CB = (WT == MOE_W_Q4) ? 16 : 12;
-    const int nc = H >> 5;
-    for (int c = kp; c < nc; c += NK) {
-      const float s = f16_to_f32(gus[(size_t)c * R + row]);
-      acc_quant_chunk<WT, MAXB>(gu + ((size_t)c * R + row) * CB, s, xs, xsum, H, c, nt, acc);
+      for (int i = 0; i < NCH; i++) {
+        const uint4 v = *reinterpret_cast<const uint4*>(dn + ((size_t)(col0 / KC + i) * H + row) * 16);
+        d.w[4 * i] = v.x;
+        d.w[4 * i + 1] = v.y;
+        d.w[4 * i + 2] = v.z;
+        d.w[4 * i + 3] = v.w;
+      }
+    } else {  // part of one chunk: NCOL * ES bytes (8 for 4 bf16 columns)
+      static_assert(NCOL * ES == 8, "sub-chunk pieces are 8 bytes");
+      const uint2 v = *reinterpret_cast<const uint2*>(dn + ((size_t)(col0 / KC) * H + row) * 16 + (col0 % KC) * ES);
+      d.w[0] = v.x;
+      d.w[1] = v.y;
+    }
+    d.s = 1.0f;
+  }
+}
+
+template <int WT, int NCOL>
+__device__ __forceinline__ float down_piece_dot(const DownPiece<WT, NCOL>& d, int half, const uint32_t* hp, float hs) {
+  if constexpr (is_q<WT>()) {
+    uint32_t p[8];
+    if constexpr (WT == MOE_W_Q4) {
+#pragma unroll
+      for (int w = 0; w < 2; w++)
+#pragma unroll
+        for (int s = 0; s < 4; s++) p[4 * w + s] = ((d.w[w] >> (4 * s)) & 0x000F000Fu) | BF16_MAGIC2;
+    } else {
+      // pairs 8*half + i: low bits from L(half) bits 2i, high bits from HB bits 8*half + i (+16)
+      const uint32_t hsh = d.w[1] >> (8 * half);
+#pragma unroll
+      for (int i = 0; i < 8; i++) {
+        const uint32_t v = ((d.w[0] >> (2 * i)) & 0x00030003u) | BF16_MAGIC2;
+        const uint32_t h = (i >= 2) ? (hsh >> (i - 2)) : (hsh << (2 - i));
+        p[i] = v | (h & 0x00040004u);
+      }
+    }
+    float c0 = -(128.0f + (float)QOff<WT>::v) * hs, c1 = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; i += 2) {
+      c0 = dot2_bf16(p[i], hp[i], c0);
+      c1 = dot2_bf16(p[i + 1], hp[i + 1], c1);
+    }
+    return d.s * (c0 + c1);
+  } else if constexpr (WT == MOE_W_BF16) {
+    float c0 = 0.0f, c1 = 0.0f;
+#pragma unroll
+    for (int i = 0; i < NCOL / 2; i += 2) {
+      c0 = dot2_bf16(d.w[i], hp[i], c0);
+      c1 = dot2_bf16(d.w[i + 1], hp[i + 1], c1);
+    }
+    return c0 + c1;
+  } else {
+    float c0 = 0.0f, c1 = 0.0f;
+#pragma unroll
+    for (int i = 0; i < NCOL / 2; i++) {
+      c0 = __builtin_fmaf(__uint_as_float(d.w[2 * i]), bf16_lo(hp[i]), c0);
+      c1 = __builtin_fmaf(__uint_as_float(d.w[2 * i + 1]), bf16_hi(hp[i]), c1);
+    }
+    return c0 + c1;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Top-k of one token in one wave. Lane holds the logits of experts
+// lane + 64 i (i < 16).
+//   1. lane best (value, index);
+//   2. radix select, by ballots, of tau = the k-th largest of the 64 lane
+//      bests' 32-bit sortable keys (sign, exponent, top mantissa bits of the
+//      fp64 logit, so key order never contradicts value order);
+//   3. candidates = all values whose key is >= tau. Every true top-k value is
+//      one: a value below tau is beaten by k lane bests. Compacted to LDS;
+//   4. exact rank of each candidate among the candidates (fp64 value, then
+//      index) picks and orders the k winners.
+// If ties of the truncated keys leave more than TOPK_CMAX candidates (only
+// for massively equal logits), k rounds of a wave arg-max decide instead.
+// Order: larger logit first, lower expert index on ties. Lane r < k ends
+// with expert r and its renormalised gate.
+// ---------------------------------------------------------------------------
+constexpr int TOPK_CMAX = 256;
+constexpr size_t TOPK_SCRATCH = (size_t)TOPK_CMAX * 12 + 16 * 12;  // per wave
+
+__device__ __forceinline__ uint32_t sort_key_hi(double v) {
+  const uint64_t b = (uint64_t)__double_as_longlong(v);
+  const uint64_t k = (b >> 63) ? ~b : (b | 0x8000000000000000ull);
+  return (uint32_t)(k >> 32);
+}
+
+__device__ __forceinline__ void wave_topk(const double (&v)[16], int E, int k, int lane, uint8_t* scratch, int& my_idx,
+                                          float& my_gate) {
+  double* S_cv = reinterpret_cast<double*>(scratch);
+  double* S_ov = S_cv + TOPK_CMAX;
+  int* S_ci = reinterpret_cast<int*>(S_ov + 16);
+  int* S_oi = S_ci + TOPK_CMAX;
+  // 1. lane best
+  double bv = -__builtin_inf();
+#pragma unroll
+  for (int i = 0; i < 16; i++)
+    if (lane + 64 * i < E) bv = (v[i] > bv) ? v[i] : bv;
+  const uint32_t kh = sort_key_hi(bv);
+  // 2. radix select of tau over the 64 lane keys
+  uint32_t prefix = 0;
+  int need = k;
+#pragma unroll
+  for (int b = 31; b >= 0; b--) {
+    const bool match = (b == 31) ? true : (((kh ^ prefix) >> (b + 1)) == 0u);
+    const uint64_t m = __ballot(match & ((kh >> b) & 1u));
+    const int c = __popcll(m);
+    if (c >= need) prefix |= (1u << b);
+    else need -= c;
+  }
+  const uint32_t tau = prefix;
+  // 3. candidates, compacted in lane order
+  int base = 0;
+#pragma unroll
+  for (int i = 0; i < 16; i++) {
+    const int e = lane + 64 * i;
+    const bool cand = (e < E) & (sort_key_hi(v[i]) >= tau);
+    const uint64_t bal = __ballot(cand);
+    if (cand) {
+      const int pos = base + __popcll(bal & ((1ull << lane) - 1ull));
+      if (pos < TOPK_CMAX) {
+        S_cv[pos] = v[i];
+        S_ci[pos] = e;
+      }
+    }
+    base += __popcll(bal);
+  }
+  const int nc = base;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  if (nc <= TOPK_CMAX) {
+    // 4. exact ranks among the candidates
+    for (int c = lane; c < nc; c += 64) {
+      const double cvv = S_cv[c];
+      const int cii = S_ci[c];
+      int r0 = 0, r1 = 0;
+      int j = 0;
+      for (; j + 1 < nc; j += 2) {
+        r0 += topk_before(S_cv[j], S_ci[j], cvv, cii);
+        r1 += topk_before(S_cv[j + 1], S_ci[j + 1], cvv, cii);
+      }
+      if (j < nc) r0 += topk_before(S_cv[j], S_ci[j], cvv, cii);
+      const int rk = r0 + r1;
+      if (rk < k) {
+        S_ov[rk] = cvv;
+        S_oi[rk] = cii;
+      }
     }
   } else {
-    constexpr int KC = (WT == MOE_W_BF16) ? 8 : 4;
-    const int nc = H / KC;
-    for (int c = kp; c < nc; c += NK)
-      acc_dense_chunk<WT, MAXB>(gu + ((size_t)c * R + row) * 16, xs, H, c, nt, acc);
-  }
-  // partials -> LDS red[kp][t][rr]
+    // massively tied keys: k rounds of a wave arg-max over all values
+    double w[16];
 #pragma unroll
-  for (int t = 0; t < MAXB; t++)
-    if (t < nt) red[(kp * MAXB + t) * RW + rr] = acc[t];
-  __syncthreads();
-}
-
-// Sum the K-parts for (t, j) and apply SwiGLU.
-template <int MAXB, int NP>
-__device__ __forceinline__ float swiglu_from_red(const float* red, int t, int j) {
-  constexpr int RW = 2 * NP;
-  constexpr int NK = DEC_THREADS / RW;
-  float g = 0.0f, u = 0.0f;
-  for (int kp = 0; kp < NK; kp++) {
-    g += red[(kp * MAXB + t) * RW + j];
-    u += red[(kp * MAXB + t) * RW + NP + j];
+    for (int i = 0; i < 16; i++) w[i] = v[i];
+    for (int r = 0; r < k; r++) {
+      double best = -__builtin_inf();
+      int bi = 0x7FFFFFFF;
+#pragma unroll
+      for (int i = 0; i < 16; i++) {
+        const int e = lane + 64 * i;
+        const bool take = (e < E) & (w[i] > best);
+        best = take ? w[i] : best;
+        bi = take ? e : bi;
+      }
+      wave_argmax(best, bi);
+#pragma unroll
+      for (int i = 0; i < 16; i++)
+        if (lane + 64 * i == bi) w[i] = -__builtin_inf();
+      if (lane == 0) {
+        S_ov[r] = best;
+        S_oi[r] = bi;
+      }
+    }
   }
-  return silu_f32(g) * u;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  // gates: softmax over the selected logits (equal to the renormalised softmax over all E)
+  const double mv = S_ov[0];
+  const double ev = (lane < k) ? exp(S_ov[lane < k ? lane : 0] - mv) : 0.0;
+  const double z = wave_total_f64(ev);
+  my_idx = (lane < k) ? S_oi[lane] : 0;
+  my_gate = (float)(ev / z);
 }
 
 // ---------------------------------------------------------------------------
-// Kernel A: router logits + shared expert gate/up
+// Kernel A: router rows (blocks < nRB) and shared-expert column groups
 // ---------------------------------------------------------------------------
-template <int SWT, int MAXB, int NP>
-__global__ __launch_bounds__(DEC_THREADS) void k_dec_router_shared(LayerDev L, const uint16_t* __restrict__ x,
-                                                                   int B, DecodeWs ws, int nRB) {
-  const int H = L.H, E = L.E;
+constexpr int A_CPR = 8;  // router float4 chunks per lane and batch
+constexpr int A_CPS = 4;  // shared gate/up chunks per lane and batch
+constexpr int A_RPT = 4;  // shared down rows per thread and batch
+
+template <int SWT, int MAXB>
+__global__ __launch_bounds__(DA_THREADS) void k_dec_a(LayerDev L, const uint16_t* __restrict__ x, int B, DecodeWs ws,
+                                                      int nRB) {
+  extern __shared__ __align__(16) uint8_t smem[];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int H = L.H, E = L.E, I = L.I;
+  uint16_t* xs = reinterpret_cast<uint16_t*>(smem);
   if ((int)blockIdx.x < nRB) {
-    // one router row per wave, all tokens; fp32 x bf16 products are exact in fp64
-    const int e = blockIdx.x * (DEC_THREADS / 64) + wave;
-    if (e >= E) return;
+    const int e = blockIdx.x * 8 + wave;
+    const bool valid = e < E;
+    const int n4 = H >> 2;
+    const float4* wr = reinterpret_cast<const float4*>(L.router_w + (size_t)(valid ? e : 0) * H);
+    const double bias = (valid && L.router_b) ? (double)L.router_b[e] : 0.0;
     double acc[MAXB];
 #pragma unroll
     for (int t = 0; t < MAXB; t++) acc[t] = 0.0;
-    const float4* wr = reinterpret_cast<const float4*>(L.router_w + (size_t)e * H);
-    const int n4 = H >> 2;
-    for (int c = lane; c < n4; c += 64) {
-      const float4 w = wr[c];
+    for (int c0 = 0; c0 < n4; c0 += 64 * A_CPR) {
+      float4 w[A_CPR];
+#pragma unroll
+      for (int i = 0; i < A_CPR; i++) {
+        const int c = c0 + lane + 64 * i;
+        w[i] = (valid && c < n4) ? wr[c] : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+      if (c0 == 0) {
+        stage_tokens<DA_THREADS>(x, B, H, xs, nullptr);
+        __syncthreads();
+      }
 #pragma unroll
       for (int t = 0; t < MAXB; t++) {
         if (t < B) {
-          const uint2 xv = *reinterpret_cast<const uint2*>(x + (size_t)t * H + 4 * c);
-          double a = acc[t];
-          a = __builtin_fma((double)w.x, (double)bf16_lo(xv.x), a);
-          a = __builtin_fma((double)w.y, (double)bf16_hi(xv.x), a);
-          a = __builtin_fma((double)w.z, (double)bf16_lo(xv.y), a);
-          a = __builtin_fma((double)w.w, (double)bf16_hi(xv.y), a);
-          acc[t] = a;
+#pragma unroll
+          for (int i = 0; i < A_CPR; i++) {
+            const int c = c0 + lane + 64 * i;
+            if (c < n4) {
+              const uint2 xv = *reinterpret_cast<const uint2*>(xs + (size_t)t * H + 4 * c);
+              acc[t] = __builtin_fma((double)w[i].x, (double)bf16_lo(xv.x), acc[t]);
+              acc[t] = __builtin_fma((double)w[i].y, (double)bf16_hi(xv.x), acc[t]);
+              acc[t] = __builtin_fma((double)w[i].z, (double)bf16_lo(xv.y), acc[t]);
+              acc[t] = __builtin_fma((double)w[i].w, (double)bf16_hi(xv.y), acc[t]);
+            }
+          }
         }
       }
     }
-    const double b = L.router_b ? (double)L.router_b[e] : 0.0;
 #pragma unroll
     for (int t = 0; t < MAXB; t++) {
       if (t < B) {
-        const double v = wave_sum_f64(acc[t]);
-        if (lane == 0) ws.logits[(size_t)t * E + e] = v + b;
+        const double tot = wave_total_f64(acc[t]);
+        if (valid && lane == 0) ws.logits[(size_t)t * E + e] = tot + bias;
       }
     }
     return;
   }
-  // shared expert gate/up for NP pairs
-  extern __shared__ __align__(16) uint8_t smem[];
-  const int I = L.I;
-  const int bpq = 16 / NP;
-  const int b = blockIdx.x - nRB;
-  const int q = b / bpq, j0 = (b % bpq) * NP;
-  uint16_t* xs = reinterpret_cast<uint16_t*>(smem);
-  float* red = reinterpret_cast<float*>(smem + (size_t)B * H * 2);
-  int tl[MAXB];
+  // ---- shared expert: intermediate columns 4p .. 4p+3 (p = workgroup index)
+  constexpr int KC = kchunk<SWT>();
+  const int R = 2 * I;
+  const int p = blockIdx.x - nRB;
+  const int q = p >> 2, j0 = (p & 3) * 4;
+  // lane -> (row r = lane / 8: 0..3 gate rows j0.., 4..7 up rows; kpart = lane % 8 + 8 wave)
+  const int r = lane >> 3;
+  const int row = 32 * q + (r < 4 ? j0 + r : 16 + j0 + (r - 4));
+  const int kp = (lane & 7) + 8 * wave;
+  const int nc = H / KC;
+  float* s_gu = reinterpret_cast<float*>(smem + (size_t)B * H * 2);  // [8 waves][MAXB][8 rows]
+  uint32_t* s_hp = reinterpret_cast<uint32_t*>(s_gu + 8 * MAXB * 8);  // [MAXB][2] bf16 pairs
+  float* s_hs = reinterpret_cast<float*>(s_hp + MAXB * 2);            // [MAXB]
+  const int col0 = 4 * p;
+  // first batch of down pieces is issued together with the gate/up loads
+  DownPiece<SWT, 4> dp[A_RPT];
 #pragma unroll
-  for (int t = 0; t < MAXB; t++) tl[t] = t;
-  stage_x(x, tl, B, H, xs, nullptr, false);
-  __syncthreads();
+  for (int i = 0; i < A_RPT; i++) {
+    const int rw = threadIdx.x + DA_THREADS * i;
+    if (rw < H) load_down_piece<SWT, 4>(L.sdn, nullptr, H, rw, col0, dp[i]);
+  }
   float acc[MAXB];
-  gate_up_rows<SWT, MAXB, NP>(L.sgu, nullptr, H, I, q, j0, xs, nullptr, B, red, acc);
-  for (int i = threadIdx.x; i < B * NP; i += DEC_THREADS) {
-    const int t = i / NP, j = i - t * NP;
-    const float hv = swiglu_from_red<MAXB, NP>(red, t, j);
-    ws.hs[(size_t)t * I + 16 * q + j0 + j] = f32_to_bf16(hv);
+#pragma unroll
+  for (int t = 0; t < MAXB; t++) acc[t] = 0.0f;
+  for (int c0 = 0; c0 < nc; c0 += 64 * A_CPS) {
+    Raw raw[A_CPS];
+#pragma unroll
+    for (int i = 0; i < A_CPS; i++) {
+      const int c = c0 + kp + 64 * i;
+      if (c < nc) raw[i] = load_chunk<SWT>(L.sgu, (size_t)c * R + row);
+    }
+    if (c0 == 0) {
+      stage_tokens<DA_THREADS>(x, B, H, xs, nullptr);
+      __syncthreads();
+    }
+#pragma unroll
+    for (int t = 0; t < MAXB; t++) {
+      if (t < B) {
+#pragma unroll
+        for (int i = 0; i < A_CPS; i++) {
+          const int c = c0 + kp + 64 * i;
+          if (c < nc) acc[t] = ddot<SWT>(raw[i], xs + (size_t)t * H + (size_t)c * KC, acc[t]);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < MAXB; t++) {
+    if (t < B) {
+      const float v = sum8_f32(acc[t]);
+      if ((lane & 7) == 0) s_gu[(wave * MAXB + t) * 8 + r] = v;
+    }
+  }
+  __syncthreads();
+  if ((int)threadIdx.x < B * 4) {
+    const int t = threadIdx.x >> 2, j = threadIdx.x & 3;
+    float g = 0.0f, u = 0.0f;
+#pragma unroll
+    for (int wv = 0; wv < 8; wv++) {
+      g += s_gu[(wv * MAXB + t) * 8 + j];
+      u += s_gu[(wv * MAXB + t) * 8 + 4 + j];
+    }
+    reinterpret_cast<uint16_t*>(s_hp)[t * 4 + j] = f32_to_bf16(silu_f32(g) * u);
+  }
+  __syncthreads();
+  if ((int)threadIdx.x < B) {
+    const uint16_t* hh = reinterpret_cast<const uint16_t*>(s_hp) + threadIdx.x * 4;
+    s_hs[threadIdx.x] = (bf16_to_f32(hh[0]) + bf16_to_f32(hh[1])) + (bf16_to_f32(hh[2]) + bf16_to_f32(hh[3]));
+  }
+  __syncthreads();
+  const size_t pbase = (size_t)B * L.k * (I >> 4);  // shared partials follow the routed ones
+  for (int r0 = 0; r0 < H; r0 += DA_THREADS * A_RPT) {
+    if (r0 > 0) {
+#pragma unroll
+      for (int i = 0; i < A_RPT; i++) {
+        const int rw = r0 + threadIdx.x + DA_THREADS * i;
+        if (rw < H) load_down_piece<SWT, 4>(L.sdn, nullptr, H, rw, col0, dp[i]);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < A_RPT; i++) {
+      const int rw = r0 + threadIdx.x + DA_THREADS * i;
+      if (rw < H) {
+#pragma unroll
+        for (int t = 0; t < MAXB; t++) {
+          if (t < B) {
+            const float v = down_piece_dot<SWT, 4>(dp[i], 0, s_hp + 2 * t, s_hs[t]);
+            ws.part[(pbase + (size_t)t * (I >> 2) + p) * H + rw] = v;
+          }
+        }
+      }
+    }
   }
 }
 
 // ---------------------------------------------------------------------------
-// Routing inside a workgroup: ordered top-k + gates for tokens 0..B-1,
-// results in LDS (s_idx [B][k], s_gate [B][k]).
+// Kernel B: routing + routed experts, one (unique expert, 16 columns) each
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ void wave_topk(const double* __restrict__ logits, int E, int k, int lane,
-                                          int* s_idx, float* s_gate) {
-  double v[16];
-#pragma unroll
-  for (int i = 0; i < 16; i++) {
-    const int e = lane + 64 * i;
-    v[i] = (e < E) ? logits[e] : -__builtin_inf();
-  }
-  double m = 0.0, myv = -__builtin_inf();
-  int myi = 0;
-  for (int r = 0; r < k; r++) {
-    double best = -__builtin_inf();
-    int bi = 0x7FFFFFFF;
-    // within a lane, experts lane + 64 i rise with i: strict > keeps the lower index on ties
-#pragma unroll
-    for (int i = 0; i < 16; i++) {
-      const int e = lane + 64 * i;
-      if (e < E && v[i] > best) { best = v[i]; bi = e; }
-    }
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-      const double ov = __shfl_xor(best, o, 64);
-      const int oi = __shfl_xor(bi, o, 64);
-      if (ov > best || (ov == best && oi < bi)) { best = ov; bi = oi; }
-    }
-#pragma unroll
-    for (int i = 0; i < 16; i++)
-      if (lane + 64 * i == bi) v[i] = -__builtin_inf();
-    if (r == 0) m = best;
-    if (lane == r) { myv = best; myi = bi; }
-  }
-  // gates: softmax over the selected logits (equal to the renormalised softmax over all E)
-  const double ev = (lane < k) ? exp(myv - m) : 0.0;
-  const double z = wave_sum_f64(ev);
-  if (lane < k) {
-    s_idx[lane] = myi;
-    s_gate[lane] = (float)(ev / z);
-  }
-}
+constexpr int B_CPT = 4;  // gate/up chunks per lane and batch
+constexpr int B_RPT = 4;  // down rows per thread and batch
 
-// ---------------------------------------------------------------------------
-// Kernel B: routing + routed gate/up
-// ---------------------------------------------------------------------------
-template <int WT, int MAXB, int NP>
-__global__ __launch_bounds__(DEC_THREADS) void k_dec_gate_up(LayerDev L, const uint16_t* __restrict__ x, int B,
-                                                             DecodeWs ws, int32_t* idx_out, float* gate_out) {
+template <int WT, int MAXB>
+__global__ __launch_bounds__(DB_THREADS) void k_dec_b(LayerDev L, const uint16_t* __restrict__ x, int B, DecodeWs ws,
+                                                      int32_t* idx_out, float* gate_out) {
   const int H = L.H, I = L.I, E = L.E, k = L.k;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   __shared__ int s_idx[MAXB * 16];
   __shared__ float s_gate[MAXB * 16];
   __shared__ int s_uniq[MAXB * 16];
   __shared__ uint32_t s_mask[MAXB * 16];
+  __shared__ int s_uid[MAXB * 16];
+  __shared__ int s_wcnt[DB_THREADS / 64];
   __shared__ int s_nu;
-  __shared__ int s_tl[MAXB];
+  __shared__ float s_gu[MAXB * 32];
+  __shared__ uint32_t s_hp[MAXB * 8];
+  __shared__ float s_hs[MAXB];
   extern __shared__ __align__(16) uint8_t smem[];
+  constexpr bool QT = is_q<WT>();
+  uint16_t* xs = reinterpret_cast<uint16_t*>(smem);
+  float* xsum = reinterpret_cast<float*>(smem + (size_t)B * H * 2);
+  uint8_t* tks = reinterpret_cast<uint8_t*>(xsum + (QT ? ((B * (H >> 5) + 1) & ~1) : 0));
+  int* mark = reinterpret_cast<int*>(tks);  // reuses the top-k scratch after the top-k
 
-  for (int t = wave; t < B; t += DEC_THREADS / 64)
-    wave_topk(ws.logits + (size_t)t * E, E, k, lane, s_idx + t * k, s_gate + t * k);
+  // 1. logits of this wave's token (issued first), the activations, then the top-k
+  double lv[16];
+  const int tw = wave;  // B <= 8 = waves: one token per wave
+#pragma unroll
+  for (int i = 0; i < 16; i++) {
+    const int e = lane + 64 * i;
+    lv[i] = (tw < B && e < E) ? ws.logits[(size_t)tw * E + e] : -__builtin_inf();
+  }
+  stage_tokens<DB_THREADS>(x, B, H, xs, QT ? xsum : nullptr);
+  if (tw < B) {
+    int mi;
+    float mg;
+    wave_topk(lv, E, k, lane, tks + (size_t)tw * TOPK_SCRATCH, mi, mg);
+    if (lane < k) {
+      s_idx[tw * k + lane] = mi;
+      s_gate[tw * k + lane] = mg;
+    }
+  }
   __syncthreads();
   const int nslot = B * k;
-  if (MAXB == 1) {
-    if (threadIdx.x < k) { s_uniq[threadIdx.x] = s_idx[threadIdx.x]; s_mask[threadIdx.x] = 1u; }
+  if constexpr (MAXB == 1) {
+    if ((int)threadIdx.x < k) {
+      s_uniq[threadIdx.x] = s_idx[threadIdx.x];
+      s_mask[threadIdx.x] = 1u;
+    }
     if (threadIdx.x == 0) s_nu = k;
-    __syncthreads();
   } else {
-    // unique experts in first-occurrence (slot) order, with the tokens using each
-    int* mark = reinterpret_cast<int*>(smem);  // [E], reuses the dynamic LDS before staging
-    for (int e = threadIdx.x; e < E; e += DEC_THREADS) mark[e] = 0x7FFFFFFF;
+    // unique experts in first-occurrence (slot) order and the tokens using each
+    for (int e = threadIdx.x; e < E; e += DB_THREADS) mark[e] = 0x7FFFFFFF;
     __syncthreads();
     if ((int)threadIdx.x < nslot) atomicMin(&mark[s_idx[threadIdx.x]], (int)threadIdx.x);
     __syncthreads();
-    // first occurrences, ranked by slot order (nslot <= 256 = one pass)
     const bool first = (int)threadIdx.x < nslot && mark[s_idx[threadIdx.x]] == (int)threadIdx.x;
-    __shared__ int s_wcnt[DEC_THREADS / 64];
-    __shared__ int s_uid[MAXB * 16];
     const uint64_t bal = __ballot(first);
     if (lane == 0) s_wcnt[wave] = __popcll(bal);
     __syncthreads();
     int base = 0;
-    for (int w = 0; w < wave; w++) base += s_wcnt[w];
+    for (int wv = 0; wv < wave; wv++) base += s_wcnt[wv];
     const int rank = base + __popcll(bal & ((1ull << lane) - 1ull));
-    if (first) { s_uniq[rank] = s_idx[threadIdx.x]; s_mask[rank] = 0u; s_uid[threadIdx.x] = rank; }
+    if (first) {
+      s_uniq[rank] = s_idx[threadIdx.x];
+      s_mask[rank] = 0u;
+      s_uid[threadIdx.x] = rank;
+    }
     if (threadIdx.x == 0) {
       int n = 0;
-      for (int w = 0; w < DEC_THREADS / 64; w++) n += s_wcnt[w];
+      for (int wv = 0; wv < DB_THREADS / 64; wv++) n += s_wcnt[wv];
       s_nu = n;
     }
     __syncthreads();
-    if ((int)threadIdx.x < nslot) {
-      const int u = s_uid[mark[s_idx[threadIdx.x]]];
-      atomicOr(&s_mask[u], 1u << (threadIdx.x / k));
-    }
-    __syncthreads();
+    if ((int)threadIdx.x < nslot) atomicOr(&s_mask[s_uid[mark[s_idx[threadIdx.x]]]], 1u << (threadIdx.x / k));
   }
+  __syncthreads();
+  const int nu = s_nu;
   if (blockIdx.x == 0) {
-    for (int i = threadIdx.x; i < nslot; i += DEC_THREADS) {
-      ws.idx[i] = s_idx[i];
-      ws.gates[i] = s_gate[i];
+    for (int i = threadIdx.x; i < nslot; i += DB_THREADS) {
       if (idx_out) idx_out[i] = s_idx[i];
       if (gate_out) gate_out[i] = s_gate[i];
     }
-    for (int i = threadIdx.x; i < s_nu; i += DEC_THREADS) {
-      ws.uniq[1 + i] = s_uniq[i];
-      ws.tokmask[i] = s_mask[i];
-    }
-    if (threadIdx.x == 0) ws.uniq[0] = s_nu;
   }
-  // this workgroup's (unique expert, row pairs)
-  const int bpq = 16 / NP;
-  const int gpe = (I / 16) * bpq;  // workgroups per expert
+  const int gpe = I >> 4;  // 16-column groups per expert
   const int u = blockIdx.x / gpe;
-  if (u >= s_nu) return;
-  const int r = blockIdx.x - u * gpe;
-  const int q = r / bpq, j0 = (r % bpq) * NP;
+  if (u >= nu) return;
+  const int q = blockIdx.x - u * gpe;
   const int e = s_uniq[u];
   const uint32_t mask = s_mask[u];
-  if (threadIdx.x == 0) {
-    int n = 0;
-    for (int t = 0; t < B; t++)
-      if (mask & (1u << t)) s_tl[n++] = t;
-  }
-  __syncthreads();
-  const int nt = __popc(mask);
-  uint16_t* xs = reinterpret_cast<uint16_t*>(smem);
-  float* xsum = reinterpret_cast<float*>(smem + (size_t)nt * H * 2);
-  float* red = xsum + (size_t)nt * (H >> 5);
-  constexpr bool quant = (WT == MOE_W_Q4 || WT == MOE_W_Q3);
-  stage_x(x, s_tl, nt, H, xs, xsum, quant);
-  __syncthreads();
-  float acc[MAXB];
-  gate_up_rows<WT, MAXB, NP>(L.gu + (size_t)e * L.gu_stride, quant ? L.gu_s + (size_t)e * L.gu_s_stride : nullptr,
-                             H, I, q, j0, xs, xsum, nt, red, acc);
-  // SwiGLU, bf16 h, and the sum of this workgroup's NP bf16 h values per token
-  float* hv_lds = red + (DEC_THREADS / (2 * NP)) * MAXB * 2 * NP;  // [nt][NP]
-  __syncthreads();
-  for (int i = threadIdx.x; i < nt * NP; i += DEC_THREADS) {
-    const int ti = i / NP, j = i - ti * NP;
-    const int t = s_tl[ti];
-    int slot = 0;
-    for (int jj = 0; jj < k; jj++)
-      if (s_idx[t * k + jj] == e) slot = jj;
-    const uint16_t hb = f32_to_bf16(swiglu_from_red<MAXB, NP>(red, ti, j));
-    ws.h[((size_t)t * k + slot) * I + 16 * q + j0 + j] = hb;
-    hv_lds[ti * NP + j] = bf16_to_f32(hb);
-  }
-  __syncthreads();
-  if ((int)threadIdx.x < nt) {
-    const int ti = threadIdx.x, t = s_tl[ti];
-    int slot = 0;
-    for (int jj = 0; jj < k; jj++)
-      if (s_idx[t * k + jj] == e) slot = jj;
-    float a = 0.0f;
-    for (int j = 0; j < NP; j++) a += hv_lds[ti * NP + j];
-    ws.hpart[((size_t)t * k + slot) * (I / NP) + (16 * q + j0) / NP] = a;
-  }
-}
 
-// ---------------------------------------------------------------------------
-// Kernel C: down GEMV of selected + shared experts, gated sum per row
-// ---------------------------------------------------------------------------
-constexpr int DC_ROWS = 8;
-constexpr int DC_THREADS = 128;
-constexpr int DC_KP = DC_THREADS / DC_ROWS;  // 16 K-parts
-
-// One down chunk of expert weights against one h row (bf16 pairs in hrow):
-// returns sum over the chunk of w * h (scale applied for quantised weights).
-template <int WT>
-__device__ __forceinline__ float down_chunk(const uint8_t* dn, const uint16_t* dns, int H, int row, int c,
-                                            const uint16_t* hrow, float hsum_c) {
-  if constexpr (WT == MOE_W_Q4 || WT == MOE_W_Q3) {
-    constexpr int CB = (WT == MOE_W_Q4) ? 16 : 12;
-    uint32_t p[16];
-    if constexpr (WT == MOE_W_Q4) {
-      q4_pairs<BF16_MAGIC2>(*reinterpret_cast<const uint4*>(dn + ((size_t)c * H + row) * CB), p);
-    } else {
-      const uint32_t* w = reinterpret_cast<const uint32_t*>(dn + ((size_t)c * H + row) * CB);
-      q3_pairs<BF16_MAGIC2>(w[0], w[1], w[2], p);
-    }
-    constexpr float base = 128.0f + (float)QOff<WT>::v;
-    const uint4* hv = reinterpret_cast<const uint4*>(hrow + 32 * c);
-    float a = -base * hsum_c;
+  // 2. loads: 32 gate/up rows (wave w: rows 4w..4w+3 of group q; lane -> row 4w + lane/16,
+  //    kpart lane%16) and the 16-column down piece of rows tid + 512 i
+  constexpr int KC = kchunk<WT>();
+  const int R = 2 * I;
+  const int rr = 4 * wave + (lane >> 4);
+  const int row = 32 * q + rr;
+  const int kp = lane & 15;
+  const int nc = H / KC;
+  const uint8_t* wgu = L.gu + (size_t)e * L.gu_stride;
+  const uint16_t* wgs = QT ? L.gu_s + (size_t)e * L.gu_s_stride : nullptr;
+  const uint8_t* wdn = L.dn + (size_t)e * L.dn_stride;
+  const uint16_t* wds = QT ? L.dn_s + (size_t)e * L.dn_s_stride : nullptr;
+  const int col0 = 16 * q;
+  DownPiece<WT, 16> dp[B_RPT];
 #pragma unroll
-    for (int qq = 0; qq < 4; qq++) {
-      const uint4 v = hv[qq];
-      a = dot2_bf16(p[4 * qq + 0], v.x, a);
-      a = dot2_bf16(p[4 * qq + 1], v.y, a);
-      a = dot2_bf16(p[4 * qq + 2], v.z, a);
-      a = dot2_bf16(p[4 * qq + 3], v.w, a);
-    }
-    return f16_to_f32(dns[(size_t)c * H + row]) * a;
-  } else {
-    float one[1] = {0.0f};
-    acc_dense_chunk<WT, 1>(dn + ((size_t)c * H + row) * 16, hrow, 0, c, 1, one);
-    return one[0];
+  for (int i = 0; i < B_RPT; i++) {
+    const int rw = threadIdx.x + DB_THREADS * i;
+    if (rw < H) load_down_piece<WT, 16>(wdn, wds, H, rw, col0, dp[i]);
   }
-}
-
-template <int WT, int SWT, int MAXB>
-__global__ __launch_bounds__(DC_THREADS) void k_dec_down(LayerDev L, int B, DecodeWs ws, uint16_t* __restrict__ y,
-                                                         int stage_lds) {
-  const int H = L.H, I = L.I, k = L.k;
-  const int tid = threadIdx.x;
-  const int rr = tid % DC_ROWS, kp = tid / DC_ROWS;
-  const int row = blockIdx.x * DC_ROWS + rr;
-  extern __shared__ __align__(16) uint8_t smem[];
-  constexpr bool quant = (WT == MOE_W_Q4 || WT == MOE_W_Q3);
-  const int nslot = B * k;
-  const bool has_shared = (SWT != MOE_W_NONE);
-  const int nrow = nslot + (has_shared ? B : 0);
-  const int nb = I >> 5;
-  const int hp = I / DEC_NP;  // h partial sums per slot
-  // LDS: red [MAXB][KP][ROWS] f32 | slot-of(u,t) [MAXB*16] | hsum [nslot][nb] | (staged h)
-  float* red = reinterpret_cast<float*>(smem);
-  int* s_slot = reinterpret_cast<int*>(red + MAXB * DC_KP * DC_ROWS);
-  float* hsum = reinterpret_cast<float*>(s_slot + MAXB * 16);
-  uint16_t* hst = reinterpret_cast<uint16_t*>(hsum + nslot * nb);
-  if (stage_lds) {
-    const int n16 = I / 8;
-    for (int i = tid; i < nrow * n16; i += DC_THREADS) {
-      const int s = i / n16, c = i - s * n16;
-      const uint16_t* src = (s < nslot) ? ws.h + (size_t)s * I : ws.hs + (size_t)(s - nslot) * I;
-      reinterpret_cast<uint4*>(hst + (size_t)s * I)[c] = reinterpret_cast<const uint4*>(src)[c];
-    }
-  }
-  if (quant) {
-    for (int i = tid; i < nslot * nb; i += DC_THREADS) {
-      const int s = i / nb, c = i - s * nb;
-      const float* hpp = ws.hpart + (size_t)s * hp + c * (32 / DEC_NP);
-      float a = 0.0f;
-      for (int j = 0; j < 32 / DEC_NP; j++) a += hpp[j];
-      hsum[i] = a;
-    }
-  }
-  const int nu = ws.uniq[0];
-  // slot index of (unique expert u, token t): s_slot[u*MAXB + t] = t*k + j
-  for (int i = tid; i < nu * B; i += DC_THREADS) {
-    const int u = i / B, t = i - u * B;
-    const int e = ws.uniq[1 + u];
-    int slot = -1;
-    for (int j = 0; j < k; j++)
-      if (ws.idx[t * k + j] == e) slot = t * k + j;
-    if (u < 16) s_slot[u * MAXB + t] = slot;
-  }
-  __syncthreads();
+  const int nb = H >> 5;
   float acc[MAXB];
 #pragma unroll
   for (int t = 0; t < MAXB; t++) acc[t] = 0.0f;
-  const uint16_t* hbase = stage_lds ? hst : ws.h;
-  if (row < H) {
-    for (int u = 0; u < nu; u++) {
-      const int e = ws.uniq[1 + u];
-      const uint8_t* dn = L.dn + (size_t)e * L.dn_stride;
-      const uint16_t* dns = quant ? L.dn_s + (size_t)e * L.dn_s_stride : nullptr;
-      constexpr int KC = quant ? 32 : (WT == MOE_W_BF16 ? 8 : 4);
-      const int nc = I / KC;
+  for (int c0 = 0; c0 < nc; c0 += 16 * B_CPT) {
+    Raw raw[B_CPT];
+    float sc[B_CPT];
 #pragma unroll
-      for (int t = 0; t < MAXB; t++) {
-        if (t < B) {
-          int sr;
-          if (MAXB == 1) {
-            sr = u;
-          } else if (u < 16) {
-            sr = s_slot[u * MAXB + t];
-          } else {
-            sr = -1;
-            for (int j = 0; j < k; j++)
-              if (ws.idx[t * k + j] == e) sr = t * k + j;
-          }
-          if (sr >= 0) {
-            const float g = ws.gates[sr];
-            const uint16_t* hrow = hbase + (size_t)sr * I;
-            float a = 0.0f;
-            for (int c = kp; c < nc; c += DC_KP)
-              a += down_chunk<WT>(dn, dns, H, row, c, hrow, quant ? hsum[sr * nb + (c * KC >> 5)] : 0.0f);
-            acc[t] = __builtin_fmaf(g, a, acc[t]);
+    for (int i = 0; i < B_CPT; i++) {
+      const int c = c0 + kp + 16 * i;
+      if (c < nc) {
+        raw[i] = load_chunk<WT>(wgu, (size_t)c * R + row);
+        if constexpr (QT) sc[i] = f16_to_f32(wgs[(size_t)c * R + row]);
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < MAXB; t++) {
+      if (t < B && (mask >> t & 1u)) {
+#pragma unroll
+        for (int i = 0; i < B_CPT; i++) {
+          const int c = c0 + kp + 16 * i;
+          if (c < nc) {
+            if constexpr (QT)
+              acc[t] = __builtin_fmaf(sc[i], qdot32<WT>(raw[i], xs + (size_t)t * H + 32 * c, xsum[t * nb + c]), acc[t]);
+            else
+              acc[t] = ddot<WT>(raw[i], xs + (size_t)t * H + (size_t)c * KC, acc[t]);
           }
         }
       }
     }
-    if (has_shared) {
-      constexpr int SKC = (SWT == MOE_W_BF16) ? 8 : 4;
-      const int nc = I / SKC;
-      const uint16_t* hsb = stage_lds ? hst + (size_t)nslot * I : ws.hs;
-      for (int c = kp; c < nc; c += DC_KP) acc_dense_chunk<SWT, MAXB>(L.sdn + ((size_t)c * H + row) * 16, hsb, I, c, B, acc);
+  }
+#pragma unroll
+  for (int t = 0; t < MAXB; t++) {
+    if (t < B && (mask >> t & 1u)) {
+      const float v = sum16_f32(acc[t]);
+      if (kp == 0) s_gu[t * 32 + rr] = v;
     }
   }
-  // reduce over the 16 K-parts: lanes rr + 8*kp; kp spans both waves
-#pragma unroll
-  for (int t = 0; t < MAXB; t++)
-    if (t < B) red[(t * DC_KP + kp) * DC_ROWS + rr] = acc[t];
   __syncthreads();
-  for (int i = tid; i < B * DC_ROWS; i += DC_THREADS) {
-    const int t = i / DC_ROWS, r2 = i - t * DC_ROWS;
-    const int orow = blockIdx.x * DC_ROWS + r2;
+  // 3. SwiGLU (bf16 h) and the sum of the 16 bf16 h values; thread = 16 t + j
+  {
+    const int t = threadIdx.x >> 4, j = threadIdx.x & 15;
+    const bool act = t < B && (mask >> t & 1u);
+    float hv = 0.0f;
+    if (act) {
+      const uint16_t hb = f32_to_bf16(silu_f32(s_gu[t * 32 + j]) * s_gu[t * 32 + 16 + j]);
+      reinterpret_cast<uint16_t*>(s_hp)[t * 16 + j] = hb;
+      hv = bf16_to_f32(hb);
+    }
+    hv = sum16_f32(hv);
+    if (act && j == 0) s_hs[t] = hv;
+  }
+  __syncthreads();
+  // 4. gated partial down products of this expert's tokens
+  int slot[MAXB];
+  float gt[MAXB];
+#pragma unroll
+  for (int t = 0; t < MAXB; t++) {
+    slot[t] = -1;
+    gt[t] = 0.0f;
+    if (t < B && (mask >> t & 1u)) {
+      for (int j = 0; j < k; j++)
+        if (s_idx[t * k + j] == e) {
+          slot[t] = t * k + j;
+          gt[t] = s_gate[t * k + j];
+        }
+    }
+  }
+  for (int r0 = 0; r0 < H; r0 += DB_THREADS * B_RPT) {
+    if (r0 > 0) {
+#pragma unroll
+      for (int i = 0; i < B_RPT; i++) {
+        const int rw = r0 + threadIdx.x + DB_THREADS * i;
+        if (rw < H) load_down_piece<WT, 16>(wdn, wds, H, rw, col0, dp[i]);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < B_RPT; i++) {
+      const int rw = r0 + threadIdx.x + DB_THREADS * i;
+      if (rw < H) {
+#pragma unroll
+        for (int t = 0; t < MAXB; t++) {
+          if (slot[t] >= 0) {
+            const float v = down_piece_dot<WT, 16>(dp[i], q & 1, s_hp + 8 * t, s_hs[t]);
+            ws.part[((size_t)slot[t] * gpe + q) * H + rw] = gt[t] * v;
+          }
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Kernel C: y[t][r] = sum over token t's partials (routed slots in order,
+// 16-column groups in order, then the shared expert's 4-column groups)
+// ---------------------------------------------------------------------------
+constexpr int DC_BATCH = 24;  // partial loads in flight per thread
+
+__global__ __launch_bounds__(DC_THREADS) void k_dec_c(const float* __restrict__ part, int H, int k, int I, int B,
+                                                      uint16_t* __restrict__ y, int has_shared) {
+  __shared__ float red[DC_SPLIT][DC_ROWS];
+  const int t = blockIdx.y;
+  const int rr = threadIdx.x % DC_ROWS, sp = threadIdx.x / DC_ROWS;
+  const int r = blockIdx.x * DC_ROWS + rr;
+  const int nr = k * (I >> 4);  // routed partials of this token, then its shared-expert partials
+  const int ns = has_shared ? (I >> 2) : 0;
+  const size_t rbase = (size_t)t * nr;
+  const size_t sbase = (size_t)B * nr + (size_t)t * ns;
+  const int n = nr + ns;
+  float acc = 0.0f;
+  if (r < H) {
+    // this thread's partials: i = sp, sp + SPLIT, ... (all loads of a batch issued together)
+    for (int i0 = sp; i0 < n; i0 += DC_SPLIT * DC_BATCH) {
+      float v[DC_BATCH];
+#pragma unroll
+      for (int j = 0; j < DC_BATCH; j++) {
+        const int i = i0 + DC_SPLIT * j;
+        const size_t pi = (i < nr) ? rbase + i : sbase + (i - nr);
+        v[j] = (i < n) ? part[pi * H + r] : 0.0f;
+      }
+#pragma unroll
+      for (int j = 0; j < DC_BATCH; j++) acc += v[j];
+    }
+  }
+  red[sp][rr] = acc;
+  __syncthreads();
+  if (sp == 0 && r < H) {
     float sum = 0.0f;
-    for (int p = 0; p < DC_KP; p++) sum += red[(t * DC_KP + p) * DC_ROWS + r2];
-    if (orow < H) y[(size_t)t * H + orow] = f32_to_bf16(sum);
+#pragma unroll
+    for (int j = 0; j < DC_SPLIT; j++) sum += red[j][rr];
+    y[(size_t)t * H + r] = f32_to_bf16(sum);
   }
 }
 
 // ---------------------------------------------------------------------------
 // Host launch
 // ---------------------------------------------------------------------------
+size_t decode_lds_b(int wt, int B, int H, int E, int k) {
+  const bool q = (wt == MOE_W_Q4 || wt == MOE_W_Q3);
+  const size_t xsb = q ? (size_t)((B * (H / 32) + 1) & ~1) * 4 : 0;
+  const size_t tk = (size_t)B * TOPK_SCRATCH;
+  const size_t mk = (B > 1) ? (size_t)E * 4 : 0;
+  return (size_t)B * H * 2 + xsb + (tk > mk ? tk : mk);
+}
+
 template <int WT, int SWT, int MAXB>
-static hipError_t launch_decode_t(const LayerDev& L, const uint16_t* x, int B, uint16_t* y, int32_t* idx_out,
-                                  float* gate_out, const DecodeWs& ws, hipStream_t st) {
-  constexpr int NP = DEC_NP;
+static hipError_t launch_t(const LayerDev& L, const uint16_t* x, int B, uint16_t* y, int32_t* idx_out, float* gate_out,
+                           const DecodeWs& ws, hipStream_t st) {
   const int H = L.H, I = L.I, E = L.E, k = L.k;
-  // A
-  const int nRB = (E + 3) / 4;
-  const int nSB = (SWT != MOE_W_NONE) ? (I / 16) * (16 / NP) : 0;
+  constexpr int SW = (SWT == MOE_W_F32) ? MOE_W_F32 : MOE_W_BF16;
   {
-    constexpr int SW = (SWT == MOE_W_NONE) ? MOE_W_BF16 : SWT;
-    const size_t lds = (size_t)B * H * 2 + (size_t)(DEC_THREADS / (2 * NP)) * MAXB * 2 * NP * 4;
+    const int nRB = (E + 7) / 8;
+    const int nSB = (SWT == MOE_W_NONE) ? 0 : I / 4;
+    const size_t lds = (size_t)B * H * 2 + (size_t)(8 * MAXB * 8 + MAXB * 2 + MAXB) * 4;
     timer_begin(KC_DEC_ROUTER_SHARED, st);
-    hipLaunchKernelGGL((k_dec_router_shared<SW, MAXB, NP>), dim3(nRB + nSB), dim3(DEC_THREADS), lds, st, L, x, B,
-                       ws, nRB);
+    hipLaunchKernelGGL((k_dec_a<SW, MAXB>), dim3(nRB + nSB), dim3(DA_THREADS), lds, st, L, x, B, ws, nRB);
     timer_end(KC_DEC_ROUTER_SHARED, st);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
-  // B
   {
     const int maxU = (B * k < E) ? B * k : E;
-    const int gpe = (I / 16) * (16 / NP);
-    const size_t stage = (size_t)B * H * 2 + (size_t)B * (H / 32) * 4 +
-                         (size_t)(DEC_THREADS / (2 * NP)) * MAXB * 2 * NP * 4 + (size_t)MAXB * NP * 4;
-    const size_t lds = (stage > (size_t)E * 4) ? stage : (size_t)E * 4;
+    const size_t lds = decode_lds_b(WT, B, H, E, k);
     timer_begin(KC_DEC_GATE_UP, st);
-    hipLaunchKernelGGL((k_dec_gate_up<WT, MAXB, NP>), dim3(maxU * gpe), dim3(DEC_THREADS), lds, st, L, x, B, ws,
-                       idx_out, gate_out);
+    hipLaunchKernelGGL((k_dec_b<WT, MAXB>), dim3(maxU * (I / 16)), dim3(DB_THREADS), lds, st, L, x, B, ws, idx_out,
+                       gate_out);
     timer_end(KC_DEC_GATE_UP, st);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
-  // C
-  {
-    const int nslot = B * k;
-    const int nrow = nslot + (SWT != MOE_W_NONE ? B : 0);
-    const size_t fixed = (size_t)MAXB * DC_KP * DC_ROWS * 4 + (size_t)MAXB * 16 * 4 + (size_t)nslot * (I / 32) * 4;
-    const size_t hbytes = (size_t)nrow * I * 2;
-    const int stage = (fixed + hbytes <= 48 * 1024) ? 1 : 0;
-    const size_t lds = fixed + (stage ? hbytes : 0);
-    timer_begin(KC_DEC_DOWN, st);
-    hipLaunchKernelGGL((k_dec_down<WT, SWT, MAXB>), dim3((H + DC_ROWS - 1) / DC_ROWS), dim3(DC_THREADS), lds, st,
-                       L, B, ws, y, stage);
-    timer_end(KC_DEC_DOWN, st);
-    return hipGetLastError();
-  }
+  timer_begin(KC_DEC_DOWN, st);
+  hipLaunchKernelGGL(k_dec_c, dim3((H + DC_ROWS - 1) / DC_ROWS, B), dim3(DC_THREADS), 0, st, ws.part, H, k, I, B, y,
+                     SWT == MOE_W_NONE ? 0 : 1);
+  timer_end(KC_DEC_DOWN, st);
+  return hipGetLastError();
 }
 
 template <int WT, int SWT>
-static hipError_t launch_decode_b(const LayerDev& L, const uint16_t* x, int B, uint16_t* y, int32_t* io, float* go,
-                                  const DecodeWs& ws, hipStream_t st) {
-  if (B == 1) return launch_decode_t<WT, SWT, 1>(L, x, B, y, io, go, ws, st);
-  return launch_decode_t<WT, SWT, 16>(L, x, B, y, io, go, ws, st);
+static hipError_t launch_b(const LayerDev& L, const uint16_t* x, int B, uint16_t* y, int32_t* io, float* go,
+                           const DecodeWs& ws, hipStream_t st) {
+  if (B == 1) return launch_t<WT, SWT, 1>(L, x, B, y, io, go, ws, st);
+  return launch_t<WT, SWT, 8>(L, x, B, y, io, go, ws, st);
 }
 
 template <int WT>
-static hipError_t launch_decode_s(const LayerDev& L, const uint16_t* x, int B, uint16_t* y, int32_t* io, float* go,
-                                  const DecodeWs& ws, hipStream_t st) {
+static hipError_t launch_s(const LayerDev& L, const uint16_t* x, int B, uint16_t* y, int32_t* io, float* go,
+                           const DecodeWs& ws, hipStream_t st) {
   switch (L.swt) {
-    case MOE_W_BF16: return launch_decode_b<WT, MOE_W_BF16>(L, x, B, y, io, go, ws, st);
-    case MOE_W_F32: return launch_decode_b<WT, MOE_W_F32>(L, x, B, y, io, go, ws, st);
-    default: return launch_decode_b<WT, MOE_W_NONE>(L, x, B, y, io, go, ws, st);
+    case MOE_W_BF16: return launch_b<WT, MOE_W_BF16>(L, x, B, y, io, go, ws, st);
+    case MOE_W_F32: return launch_b<WT, MOE_W_F32>(L, x, B, y, io, go, ws, st);
+    default: return launch_b<WT, MOE_W_NONE>(L, x, B, y, io, go, ws, st);
   }
 }
 
 hipError_t launch_decode(const LayerDev& L, const uint16_t* x, int B, uint16_t* y, int32_t* idx_out, float* gate_out,
                          const DecodeWs& ws, hipStream_t st) {
   switch (L.wt) {
-    case MOE_W_Q4: return launch_decode_s<MOE_W_Q4>(L, x, B, y, idx_out, gate_out, ws, st);
-    case MOE_W_Q3: return launch_decode_s<MOE_W_Q3>(L, x, B, y, idx_out, gate_out, ws, st);
-    case MOE_W_BF16: return launch_decode_s<MOE_W_BF16>(L, x, B, y, idx_out, gate_out, ws, st);
-    default: return launch_decode_s<MOE_W_F32>(L, x, B, y, idx_out, gate_out, ws, st);
+    case MOE_W_Q4: return launch_s<MOE_W_Q4>(L, x, B, y, idx_out, gate_out, ws, st);
+    case MOE_W_Q3: return launch_s<MOE_W_Q3>(L, x, B, y, idx_out, gate_out, ws, st);
+    case MOE_W_BF16: return launch_s<MOE_W_BF16>(L, x, B, y, idx_out, gate_out, ws, st);
+    default: return launch_s<MOE_W_F32>(L, x, B, y, idx_out, gate_out, ws, st);
   }
 }
 

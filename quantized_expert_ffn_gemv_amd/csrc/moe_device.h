@@ -130,3 +130,86 @@ __device__ __forceinline__ float group_sum_f32(float v, int width) {
 __device__ __forceinline__ float silu_f32(float a) { return a / (1.0f + __expf(-a)); }
 
 }  // namespace moe
+
+namespace moe {
+// ---------------------------------------------------------------------------
+// DPP cross-lane helpers (no LDS traffic). Controls: quad_perm(1,0,3,2) = xor 1,
+// quad_perm(2,3,0,1) = xor 2, row_half_mirror (i <-> 7-i in 8 lanes),
+// row_mirror (i <-> 15-i in 16 lanes).
+// ---------------------------------------------------------------------------
+constexpr int DPP_XOR1 = 0xB1, DPP_XOR2 = 0x4E, DPP_HALF_MIRROR = 0x141, DPP_MIRROR = 0x140;
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+template <int CTRL>
+__device__ __forceinline__ int dpp_i32(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double v) {
+  const uint64_t u = __double_as_longlong(v);
+  const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)u, CTRL, 0xF, 0xF, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(u >> 32), CTRL, 0xF, 0xF, false);
+  return __longlong_as_double((long long)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo));
+}
+// Sum over aligned groups of 8 / 16 lanes; every lane of the group gets the sum.
+__device__ __forceinline__ float sum8_f32(float v) {
+  v += dpp_f32<DPP_XOR1>(v);
+  v += dpp_f32<DPP_XOR2>(v);
+  v += dpp_f32<DPP_HALF_MIRROR>(v);
+  return v;
+}
+__device__ __forceinline__ float sum16_f32(float v) {
+  v = sum8_f32(v);
+  v += dpp_f32<DPP_MIRROR>(v);
+  return v;
+}
+__device__ __forceinline__ double sum16_f64(double v) {
+  v += dpp_f64<DPP_XOR1>(v);
+  v += dpp_f64<DPP_XOR2>(v);
+  v += dpp_f64<DPP_HALF_MIRROR>(v);
+  v += dpp_f64<DPP_MIRROR>(v);
+  return v;
+}
+__device__ __forceinline__ double readlane_f64(double v, int lane) {
+  const uint64_t u = __double_as_longlong(v);
+  const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)u, lane);
+  const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), lane);
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+// Whole-wave fp64 sum, fixed association ((r0 + r1) + (r2 + r3)) over 16-lane rows; uniform result.
+__device__ __forceinline__ double wave_total_f64(double v) {
+  v = sum16_f64(v);
+  return (readlane_f64(v, 0) + readlane_f64(v, 16)) + (readlane_f64(v, 32) + readlane_f64(v, 48));
+}
+
+// (value, index) ordering used by top-k: larger value first, lower index on ties.
+__device__ __forceinline__ bool topk_before(double va, int ia, double vb, int ib) {
+  return (va > vb) | ((va == vb) & (ia < ib));  // bitwise: no branches
+}
+template <int CTRL>
+__device__ __forceinline__ void argmax_step(double& v, int& i) {
+  const double ov = dpp_f64<CTRL>(v);
+  const int oi = dpp_i32<CTRL>(i);
+  if (topk_before(ov, oi, v, i)) { v = ov; i = oi; }
+}
+// Wave-wide best (value, index); uniform result.
+__device__ __forceinline__ void wave_argmax(double& v, int& i) {
+  argmax_step<DPP_XOR1>(v, i);
+  argmax_step<DPP_XOR2>(v, i);
+  argmax_step<DPP_HALF_MIRROR>(v, i);
+  argmax_step<DPP_MIRROR>(v, i);
+  double bv = readlane_f64(v, 0);
+  int bi = __builtin_amdgcn_readlane(i, 0);
+#pragma unroll
+  for (int r = 1; r < 4; r++) {
+    const double rv = readlane_f64(v, 16 * r);
+    const int ri = __builtin_amdgcn_readlane(i, 16 * r);
+    if (topk_before(rv, ri, bv, bi)) { bv = rv; bi = ri; }
+  }
+  v = bv;
+  i = bi;
+}
+}  // namespace moe

@@ -10,9 +10,9 @@ namespace moe {
 
 // Kernel classes for the optional timer.
 enum KernelClass {
-  KC_DEC_ROUTER_SHARED = 0,
-  KC_DEC_GATE_UP,
-  KC_DEC_DOWN,
+  KC_DEC_ROUTER_SHARED = 0,  // router logits + the whole shared expert
+  KC_DEC_GATE_UP,            // top-k + routed experts (gate/up, SwiGLU, partial down)
+  KC_DEC_DOWN,               // sum of the partial down products
   KC_PF_ROUTER,
   KC_PF_TOPK,
   KC_PF_COUNT,
@@ -49,14 +49,8 @@ struct LayerDev {
 
 // Decode workspace (all device pointers inside the caller's workspace).
 struct DecodeWs {
-  double* logits;    // [B][E]
-  int32_t* idx;      // [B][k]
-  float* gates;      // [B][k]
-  uint16_t* h;       // [B][k][I] bf16
-  uint16_t* hs;      // [B][I] bf16
-  float* hpart;      // [B][k][I/DEC_NP] sums of DEC_NP consecutive bf16 h values
-  int32_t* uniq;     // [1 + B*k]: count, then unique experts
-  uint32_t* tokmask; // [B*k]
+  double* logits;  // [B][E]
+  float* part;     // [B*k*(I/16) + B*(I/4)][H] partial down products (routed, then shared)
 };
 
 // Prefill workspace.
@@ -78,6 +72,7 @@ struct PrefillWs {
 };
 
 // Launch wrappers (return hipError_t of the launch).
+size_t decode_lds_b(int wt, int B, int H, int E, int k);  // LDS bytes of the routed-expert kernel
 hipError_t launch_decode(const LayerDev& L, const uint16_t* x, int B, uint16_t* y, int32_t* idx_out,
                          float* gate_out, const DecodeWs& ws, hipStream_t st);
 hipError_t launch_route(const LayerDev& L, const uint16_t* x, int T, int32_t* idx_out, float* gate_out,
@@ -87,9 +82,6 @@ hipError_t launch_prefill(const LayerDev& L, const uint16_t* x, int T, uint16_t*
 hipError_t launch_rmsnorm(const uint16_t* h, uint16_t* z, int T, int H, float eps, hipStream_t st);
 hipError_t launch_residual(uint16_t* h, const uint16_t* y, int T, int H, hipStream_t st);
 hipError_t launch_fill(void* p, size_t bytes, hipStream_t st);
-
-// Decode: gate/up rows handled per workgroup come in DEC_NP (gate, up) pairs.
-constexpr int DEC_NP = 8;
 
 // Prefill tiling constants shared by host sizing and kernels.
 constexpr int PF_BM = 128;          // max rows (tokens) per grouped-GEMM tile
