@@ -14,6 +14,9 @@ of the dominant decode kernel (HIP events on the launch stream), and the CPU
 oracle timed on a bounded sample of the headline workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-prefill] [--no-cpu]
+       python bench.py --profile-sample   (short eager run for hardware-counter passes:
+                                           a 256 MiB elementwise copy, then 32 decode
+                                           tokens and one 4096-token prefill)
 """
 import argparse
 import json
@@ -116,6 +119,41 @@ def cpu_baseline(host, x_bits, budget_s=12.0, max_tokens=256):
                        "%.1f s" % (n, el))
 
 
+COPY_BYTES = 256 << 20
+
+
+def profile_sample(moe, torch, synth):
+    """Eager launches for counter collection: the copy kernel of known size
+    calibrates FETCH_SIZE / WRITE_SIZE, then the decode and prefill kernels."""
+    dev = torch.device("cuda")
+    a = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+    b = torch.empty_like(a)
+    for _ in range(3):
+        torch.neg(a, out=b)          # reads COPY_BYTES, writes COPY_BYTES
+    torch.cuda.synchronize()
+    del a, b
+    host = synth.make_layer("decode_q4")
+    x = synth.make_tokens("decode_q4")
+    L = moe.DeviceLayer(host)
+    xd = torch.from_numpy(x.view(np.int16)).to(dev)
+    yd = torch.empty_like(xd)
+    ws = moe.make_workspace(L, 1, 0)
+    for t in range(32):
+        moe.moe_forward_decode(L, xd[t:t + 1], yd[t:t + 1], ws)
+    torch.cuda.synchronize()
+    log("profile sample: copy %d B x3, 32 decode tokens done" % COPY_BYTES)
+    del L
+    hp = synth.make_layer("prefill_q4")
+    xp = synth.make_tokens("prefill_q4")
+    Lp = moe.DeviceLayer(hp)
+    xpd = torch.from_numpy(xp.view(np.int16)).to(dev)
+    ypd = torch.empty_like(xpd)
+    wsp = moe.make_workspace(Lp, xp.shape[0], 1)
+    moe.moe_forward_prefill(Lp, xpd, ypd, wsp)
+    torch.cuda.synchronize()
+    log("profile sample: prefill %d tokens done" % xp.shape[0])
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -123,6 +161,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--profile-sample", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (use --gpus 1)", file=sys.stderr)
@@ -132,6 +171,9 @@ def main():
     import synth
     from quantized_expert_ffn_gemv_amd import moe
     moe.lib()
+    if args.profile_sample:
+        profile_sample(moe, torch, synth)
+        return
 
     # ---------------------------------------------------------------- headline: decode Q4 batch 1
     log("generating the 512-expert Q4 layer ...")
@@ -157,6 +199,7 @@ def main():
     gu, dn, sgu, sdn = decode_expert_bytes(L)
     router_bytes = L.E * L.H * 4
     kbytes = {
+        "dec_fused": router_bytes + sgu + sdn + L.k * (gu + dn),   # the one batch-1 kernel: all weight bytes
         "dec_router_shared": router_bytes + sgu + sdn,
         "dec_routed": L.k * (gu + dn),
     }

@@ -51,7 +51,8 @@ typedef enum {
   MOE_ERR_DTYPE = 4,     /* unsupported weight type or combination */
   MOE_ERR_WORKSPACE = 5, /* workspace too small */
   MOE_ERR_HIP = 6,       /* a HIP runtime call failed */
-  MOE_ERR_VALUE = 7      /* host packing: a code is outside its type's range */
+  MOE_ERR_VALUE = 7,     /* host packing: a code is outside its type's range */
+  MOE_ERR_DEVICE = 8     /* a device-side wait ran out (reported by moe_workspace_check) */
 } moe_status;
 
 /* Weight storage types. */
@@ -130,7 +131,23 @@ size_t moe_matrix_scales(int32_t wt, int32_t rows, int32_t K);
 size_t moe_workspace_bytes(const moe_layer *layer, int32_t max_tokens, int32_t mode);
 #define MOE_DECODE_MAX_TOKENS 8
 
-/* The workspace needs no initialisation and keeps no state between calls. */
+/* Workspace contract. The first 4096 bytes of a decode workspace hold the
+ * counters through which the workgroups of the batch-1 decode kernel hand
+ * data to each other; they must be zero before the first decode call
+ * (moe_workspace_init, or any zero fill) and every call leaves them zero
+ * again, so the workspace can be reused call after call and inside captured
+ * HIP graphs. Calls that share one workspace must be ordered (one stream);
+ * concurrent calls on one workspace race. Prefill workspaces need no
+ * initialisation. */
+moe_status moe_workspace_init(void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* Synchronises `stream`, then reports whether a device-side wait of a
+ * decode call on this workspace ran out of time since the last check
+ * (MOE_ERR_DEVICE: results of those calls are invalid) and clears the
+ * report. A wait only runs out when the workgroups it waits for never ran,
+ * which the launch order rules out; the bound exists so that a kernel can
+ * never hang. */
+moe_status moe_workspace_check(void *ws, size_t ws_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------ */
 /* Compute entry points                                                     */
@@ -151,9 +168,12 @@ moe_status moe_route(const moe_layer *layer, const void *x, int32_t T,
  * 8 * 2048; larger requests return MOE_ERR_SHAPE.)
  * Batch-1 decode is bound by the bytes of the selected experts' weights: a
  * fused dequantise-GEMV streams each selected expert once per call (experts
- * chosen by several tokens of the batch are read once). topk_idx/topk_gate
- * ([B][k]) are optional outputs (NULL to skip).
- * Workspace: moe_workspace_bytes(layer, B, 0). */
+ * chosen by several tokens of the batch are read once). B = 1 runs as one
+ * kernel (router, top-k, gate/up, SwiGLU, down and combine) when
+ * I <= 1024 and its LDS need fits 64 KiB; otherwise, and for B > 1, as
+ * three kernels. topk_idx/topk_gate ([B][k]) are optional outputs (NULL to
+ * skip). Workspace: moe_workspace_bytes(layer, B, 0), initialised once as
+ * described above. */
 moe_status moe_forward_decode(const moe_layer *layer, const void *x, int32_t B, void *y,
                               int32_t *topk_idx, float *topk_gate,
                               void *ws, size_t ws_bytes, hipStream_t stream);
@@ -201,9 +221,11 @@ const char *moe_status_string(int32_t status);
 const char *moe_last_error(void);
 
 /* Optional per-kernel timer: when enabled, every kernel the library
- * launches is bracketed by HIP events on its stream. moe_timer_read
- * waits for the recorded events and returns, for kernel class `id`, the
- * number of launches and their summed duration since the last reset. */
+ * launches carries a start and a stop HIP event in its own dispatch on its
+ * stream (hipExtLaunchKernel), so each interval is that kernel's execution.
+ * moe_timer_read waits for the recorded events and returns, for kernel
+ * class `id`, the number of launches and their summed duration since the
+ * last reset. Not for use under graph capture. */
 int32_t moe_kernel_class_count(void);
 const char *moe_kernel_class_name(int32_t id);
 moe_status moe_timer_enable(int32_t on);

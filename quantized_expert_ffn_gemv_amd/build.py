@@ -13,7 +13,7 @@ INCLUDE = os.path.join(ROOT, "include")
 OUT_DIR = os.path.join(PKG, "_lib")
 LIB = os.path.join(OUT_DIR, "libmoe.so")
 
-SOURCES = ["api.cpp", "decode.hip", "prefill.hip", "norm.hip"]
+SOURCES = ["api.cpp", "decode.hip", "decode1.hip", "prefill.hip", "norm.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # Packed fp32 instructions are left out on purpose: the compiler must not
 # form v_pk_{add,mul,fma}_f32 from ordinary float code on this target.

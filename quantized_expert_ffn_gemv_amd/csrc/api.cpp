@@ -90,6 +90,8 @@ moe::LayerDev to_dev(const moe_layer* L) {
   return d;
 }
 
+constexpr size_t DECODE_SYNC_BYTES = 4096;  // counters at the start of a decode workspace (word 0: error bits)
+
 // Workspace carving. ptr == nullptr only sizes.
 size_t carve_decode(const moe_layer* L, int B, uint8_t* base, moe::DecodeWs* ws) {
   const size_t E = L->n_experts, k = L->top_k, I = L->inter;
@@ -100,8 +102,13 @@ size_t carve_decode(const moe_layer* L, int B, uint8_t* base, moe::DecodeWs* ws)
     return p;
   };
   moe::DecodeWs w{};
-  w.logits = reinterpret_cast<double*>(take((size_t)B * E * 8));
-  w.part = reinterpret_cast<float*>(take((size_t)B * (k * (I / 16) + I / 4) * L->hidden * 4));
+  w.sync = reinterpret_cast<uint32_t*>(take(DECODE_SYNC_BYTES));
+  // logits: [B][E] fp64 (three kernels) or 4 rotating slots of [E] x 16 B tagged words (one kernel)
+  w.logits = reinterpret_cast<double*>(take((size_t)E * 64));
+  // h: 4 rotating slots of (k+1)*I/2 tagged 8-byte words
+  w.h = reinterpret_cast<uint16_t*>(take(16 * (k + 1) * I));
+  const bool one_kernel = B == 1 && moe::decode1_fits(L->n_experts, L->hidden, L->inter, L->top_k, L->shared_wtype != MOE_W_NONE);
+  w.part = one_kernel ? nullptr : reinterpret_cast<float*>(take((size_t)B * (k * (I / 16) + I / 4) * L->hidden * 4));
   if (ws) *ws = w;
   return off;
 }
@@ -152,7 +159,6 @@ std::mutex g_tmu;
 bool g_timer_on = false;
 std::vector<Pending> g_pending;
 std::vector<hipEvent_t> g_pool;
-hipEvent_t g_open[moe::KC_COUNT];
 int64_t g_launches[moe::KC_COUNT];
 double g_ms[moe::KC_COUNT];
 
@@ -181,7 +187,7 @@ void drain_locked() {
 }
 
 const char* const kKernelNames[moe::KC_COUNT] = {
-    "dec_router_shared", "dec_routed", "dec_reduce",         "pf_router",         "pf_topk",
+    "dec_fused",         "dec_router_shared", "dec_routed", "dec_reduce",         "pf_router",         "pf_topk",
     "pf_count",          "pf_scan",     "pf_scatter",       "pf_gate_up",        "pf_down",
     "pf_shared_gate_up", "pf_shared_down", "pf_combine",    "rmsnorm",           "residual_add",
     "fill"};
@@ -189,23 +195,24 @@ const char* const kKernelNames[moe::KC_COUNT] = {
 }  // namespace
 
 namespace moe {
-void timer_begin(int kc, hipStream_t st) {
-  if (!g_timer_on) return;
+bool timer_events(int kc, hipEvent_t* start, hipEvent_t* stop) {
+  if (!g_timer_on) return false;
   std::lock_guard<std::mutex> lk(g_tmu);
-  hipEvent_t e = get_event();
-  if (e && hipEventRecord(e, st) == hipSuccess) g_open[kc] = e;
-  else g_open[kc] = nullptr;
-}
-void timer_end(int kc, hipStream_t st) {
-  if (!g_timer_on) return;
-  std::lock_guard<std::mutex> lk(g_tmu);
-  if (!g_open[kc]) return;
-  hipEvent_t e = get_event();
-  if (e && hipEventRecord(e, st) == hipSuccess) {
-    g_pending.push_back({kc, g_open[kc], e});
-    if (g_pending.size() > 4096) drain_locked();
+  (void)kc;
+  hipEvent_t a = get_event(), b = get_event();
+  if (!a || !b) {
+    if (a) g_pool.push_back(a);
+    if (b) g_pool.push_back(b);
+    return false;
   }
-  g_open[kc] = nullptr;
+  *start = a;
+  *stop = b;
+  return true;
+}
+void timer_commit(int kc, hipEvent_t start, hipEvent_t stop) {
+  std::lock_guard<std::mutex> lk(g_tmu);
+  g_pending.push_back({kc, start, stop});
+  if (g_pending.size() > 4096) drain_locked();
 }
 }  // namespace moe
 
@@ -225,7 +232,12 @@ size_t moe_workspace_bytes(const moe_layer* layer, int32_t max_tokens, int32_t m
   if (check_shape(layer) != MOE_OK) return 0;
   if (mode == 0) {
     if (max_tokens < 1 || max_tokens > MOE_DECODE_MAX_TOKENS) return 0;
-    return carve_decode(layer, max_tokens, nullptr, nullptr);
+    size_t m = 0;
+    for (int b = 1; b <= max_tokens; b++) {
+      const size_t n = carve_decode(layer, b, nullptr, nullptr);
+      m = n > m ? n : m;
+    }
+    return m;
   }
   if (mode == 1) {
     if (max_tokens < 1 || max_tokens > PREFILL_MAX_TOKENS) return 0;
@@ -258,7 +270,9 @@ moe_status moe_forward_decode(const moe_layer* layer, const void* x, int32_t B, 
   if (B < 1 || B > MOE_DECODE_MAX_TOKENS) return fail(MOE_ERR_SHAPE, "B=%d not in [1, %d]", B, MOE_DECODE_MAX_TOKENS);
   if ((int64_t)B * layer->hidden > 8 * 2048)
     return fail(MOE_ERR_SHAPE, "B*H=%d exceeds the decode staging limit %d", B * layer->hidden, 8 * 2048);
-  if (moe::decode_lds_b(layer->expert_wtype, B, layer->hidden, layer->n_experts, layer->top_k) > 65536)
+  const bool one_kernel =
+      B == 1 && moe::decode1_fits(layer->n_experts, layer->hidden, layer->inter, layer->top_k, layer->shared_wtype != MOE_W_NONE);
+  if (!one_kernel && moe::decode_lds_b(layer->expert_wtype, B, layer->hidden, layer->n_experts, layer->top_k) > 65536)
     return fail(MOE_ERR_SHAPE, "B=%d with H=%d, E=%d, k=%d needs more than 64 KiB of LDS", B, layer->hidden,
                 layer->n_experts, layer->top_k);
   if (!aligned16(x) || !aligned16(y) || !aligned16(ws)) return fail(MOE_ERR_ALIGN, "x, y and ws must be 16-byte aligned");
@@ -285,6 +299,28 @@ moe_status moe_forward_prefill(const moe_layer* layer, const void* x, int32_t T,
   return hip_status(moe::launch_prefill(to_dev(layer), static_cast<const uint16_t*>(x), T, static_cast<uint16_t*>(y),
                                         topk_idx, topk_gate, w, stream),
                     "moe_forward_prefill launch");
+}
+
+moe_status moe_workspace_init(void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!ws) return fail(MOE_ERR_NULL, "ws is required");
+  if (!aligned16(ws)) return fail(MOE_ERR_ALIGN, "ws must be 16-byte aligned");
+  if (ws_bytes < DECODE_SYNC_BYTES) return fail(MOE_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, DECODE_SYNC_BYTES);
+  return hip_status(moe::launch_fill(ws, DECODE_SYNC_BYTES, stream), "moe_workspace_init launch");
+}
+
+moe_status moe_workspace_check(void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!ws) return fail(MOE_ERR_NULL, "ws is required");
+  if (ws_bytes < DECODE_SYNC_BYTES) return fail(MOE_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, DECODE_SYNC_BYTES);
+  hipError_t e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return hip_status(e, "moe_workspace_check sync");
+  uint32_t flags = 0;
+  e = hipMemcpy(&flags, ws, sizeof flags, hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return hip_status(e, "moe_workspace_check read");
+  if (flags == 0) return ok();
+  const uint32_t zero = 0;
+  e = hipMemcpy(ws, &zero, sizeof zero, hipMemcpyHostToDevice);
+  if (e != hipSuccess) return hip_status(e, "moe_workspace_check clear");
+  return fail(MOE_ERR_DEVICE, "a device-side wait ran out (flags 0x%x); results since the last check are invalid", flags);
 }
 
 moe_status moe_rmsnorm(const void* h, void* z, int32_t T, int32_t H, float eps, hipStream_t stream) {
@@ -407,6 +443,7 @@ const char* moe_status_string(int32_t status) {
     case MOE_ERR_WORKSPACE: return "workspace too small";
     case MOE_ERR_HIP: return "HIP error";
     case MOE_ERR_VALUE: return "value out of range";
+    case MOE_ERR_DEVICE: return "device-side wait ran out";
     default: return "unknown status";
   }
 }

@@ -1,0 +1,269 @@
+// Device helpers of the decode kernels: weight chunks, dot products against
+// LDS-staged bf16 vectors, and the ordered top-k of one token's logits.
+#pragma once
+#include "moe_device.h"
+
+namespace moe {
+
+template <int WT> constexpr int kchunk() { return WT == MOE_W_F32 ? 4 : (WT == MOE_W_BF16 ? 8 : 32); }
+template <int WT> constexpr bool is_q() { return WT == MOE_W_Q4 || WT == MOE_W_Q3; }
+
+struct Raw {
+  uint32_t w[4];
+};
+
+template <int WT>
+__device__ __forceinline__ Raw load_chunk(const uint8_t* base, size_t ci) {
+  Raw r;
+  if constexpr (WT == MOE_W_Q3) {
+    const uint32_t* p = reinterpret_cast<const uint32_t*>(base + ci * 12);
+    r.w[0] = p[0];
+    r.w[1] = p[1];
+    r.w[2] = p[2];
+    r.w[3] = 0;
+  } else {
+    const uint4 v = *reinterpret_cast<const uint4*>(base + ci * 16);
+    r.w[0] = v.x;
+    r.w[1] = v.y;
+    r.w[2] = v.z;
+    r.w[3] = v.w;
+  }
+  return r;
+}
+
+// sum_k (code_k - OFF) * a_k over a 32-element chunk (`a`: 32 bf16 values in
+// LDS, asum their sum). Four independent dot2 chains. The caller scales.
+template <int WT>
+__device__ __forceinline__ float qdot32(const Raw& r, const uint16_t* a, float asum) {
+  uint32_t p[16];
+  if constexpr (WT == MOE_W_Q4) {
+    q4_pairs<BF16_MAGIC2>(make_uint4(r.w[0], r.w[1], r.w[2], r.w[3]), p);
+  } else {
+    q3_pairs<BF16_MAGIC2>(r.w[0], r.w[1], r.w[2], p);
+  }
+  const uint4* av = reinterpret_cast<const uint4*>(a);
+  float c0 = -(128.0f + (float)QOff<WT>::v) * asum, c1 = 0.0f, c2 = 0.0f, c3 = 0.0f;
+#pragma unroll
+  for (int q = 0; q < 4; q++) {
+    const uint4 v = av[q];
+    c0 = dot2_bf16(p[4 * q + 0], v.x, c0);
+    c1 = dot2_bf16(p[4 * q + 1], v.y, c1);
+    c2 = dot2_bf16(p[4 * q + 2], v.z, c2);
+    c3 = dot2_bf16(p[4 * q + 3], v.w, c3);
+  }
+  return (c0 + c1) + (c2 + c3);
+}
+
+// Dot of one dense chunk (8 bf16 or 4 fp32 weights) with bf16 activations.
+template <int WT>
+__device__ __forceinline__ float ddot(const Raw& r, const uint16_t* a, float acc) {
+  if constexpr (WT == MOE_W_BF16) {
+    const uint4 v = *reinterpret_cast<const uint4*>(a);
+    float c1 = 0.0f;
+    acc = dot2_bf16(r.w[0], v.x, acc);
+    c1 = dot2_bf16(r.w[1], v.y, c1);
+    acc = dot2_bf16(r.w[2], v.z, acc);
+    c1 = dot2_bf16(r.w[3], v.w, c1);
+    return acc + c1;
+  } else {
+    const uint2 v = *reinterpret_cast<const uint2*>(a);
+    acc = __builtin_fmaf(__uint_as_float(r.w[0]), bf16_lo(v.x), acc);
+    acc = __builtin_fmaf(__uint_as_float(r.w[1]), bf16_hi(v.x), acc);
+    acc = __builtin_fmaf(__uint_as_float(r.w[2]), bf16_lo(v.y), acc);
+    acc = __builtin_fmaf(__uint_as_float(r.w[3]), bf16_hi(v.y), acc);
+    return acc;
+  }
+}
+
+// Copy B tokens of x into LDS (bf16) and, if asked, their 32-element block sums.
+template <int NT>
+__device__ __forceinline__ void stage_tokens(const uint16_t* __restrict__ x, int B, int H, uint16_t* xs, float* xsum) {
+  const int n16 = H / 8;
+  for (int i = threadIdx.x; i < B * n16; i += NT) reinterpret_cast<uint4*>(xs)[i] = reinterpret_cast<const uint4*>(x)[i];
+  if (xsum) {
+    __syncthreads();
+    const int nb = H >> 5;
+    for (int i = threadIdx.x; i < B * nb; i += NT) {
+      const uint32_t* v = reinterpret_cast<const uint32_t*>(xs + (size_t)i * 32);
+      float a = 0.0f;
+#pragma unroll
+      for (int j = 0; j < 16; j++) a += bf16_lo(v[j]) + bf16_hi(v[j]);
+      xsum[i] = a;
+    }
+  }
+}
+
+__device__ __forceinline__ float wave_total_f32(float v) {
+  v = sum16_f32(v);
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return (r0 + r1) + (r2 + r3);
+}
+
+// ---------------------------------------------------------------------------
+// Ordered top-k of one token's logits in one wave (lane holds the logits of
+// experts lane + 64 i, i < NV, so E <= 64 NV; invalid entries are -inf).
+//   1. each lane's best value; its 32-bit sortable key (sign, exponent and
+//      leading mantissa bits of the fp64 logit) with the low 6 bits replaced
+//      by 63 - lane, so the 64 keys are distinct and never contradict value
+//      order at the 26 bits they keep;
+//   2. rank of every lane key by counting (keys exchanged through LDS); tau
+//      = the key of rank k-1, and tv = the smallest fp64 value whose key
+//      truncates to tau's. Any value below tv is beaten by k lane bests, so
+//      it cannot be in the top-k;
+//   3. candidates = values >= tv, compacted to LDS without branches (a
+//      non-candidate writes to its lane's scratch slot);
+//   4. exact rank of each candidate among the candidates (fp64 value, then
+//      index) picks and orders the k winners.
+// Only massively tied logits (more than TOPK_CMAX candidates) take the slow
+// path: k rounds of a wave arg-max. Order: larger logit first, lower expert
+// index on ties. Lane r < k ends with expert r and its renormalised gate,
+// the softmax of the k selected logits (equal to p_S / sum of p over S):
+// exp in fp32 of the fp64 difference to the largest, summed in fp64.
+// ---------------------------------------------------------------------------
+constexpr int TOPK_CMAX = 128;
+// bytes per wave: 64 keys, (TOPK_CMAX + 64) candidate slots, 16 outputs; slots are 16 B (value, index)
+constexpr size_t TOPK_SCRATCH = 64 * 4 + (size_t)(TOPK_CMAX + 64) * 16 + 16 * 16;
+
+__device__ __forceinline__ uint32_t sort_key_hi(double v) {
+  const uint64_t b = (uint64_t)__double_as_longlong(v);
+  const uint64_t k = (b >> 63) ? ~b : (b | 0x8000000000000000ull);
+  return (uint32_t)(k >> 32);
+}
+
+// Smallest fp64 value whose sortable key has high word `hi` (low word 0).
+__device__ __forceinline__ double key_floor_value(uint32_t hi) {
+  const uint64_t k = (uint64_t)hi << 32;
+  const uint64_t b = (k >> 63) ? (k & 0x7FFFFFFFFFFFFFFFull) : ~k;
+  const double v = __longlong_as_double((long long)b);
+  return (v == v) ? v : -__builtin_inf();  // a NaN pattern (keys of -inf or below) admits every value
+}
+
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+struct TopkSlot {  // 16 bytes in LDS
+  double v;
+  int i;
+  int pad;
+};
+
+template <int NV>
+__device__ __forceinline__ void wave_topk(const double (&v)[NV], int E, int k, int lane, uint8_t* scratch, int& my_idx,
+                                          float& my_gate) {
+  uint32_t* S_key = reinterpret_cast<uint32_t*>(scratch);
+  TopkSlot* S_c = reinterpret_cast<TopkSlot*>(scratch + 256);  // [TOPK_CMAX] candidates + [64] per-lane scratch
+  TopkSlot* S_o = S_c + TOPK_CMAX + 64;                          // [16] ordered winners
+  const int nv = (E + 63) >> 6;  // value slots in use (uniform)
+  // 1. lane best and its distinct key
+  double bv = -__builtin_inf();
+#pragma unroll
+  for (int i = 0; i < NV; i++)
+    if (i < nv) bv = (v[i] > bv) ? v[i] : bv;
+  const uint32_t key = (sort_key_hi(bv) & ~63u) | (uint32_t)(63 - lane);
+  S_key[lane] = key;
+  wave_lds_sync();
+  // 2. rank of this lane's key among the 64, and the threshold
+  int r0 = 0, r1 = 0, r2 = 0, r3 = 0;
+  const uint4* kv = reinterpret_cast<const uint4*>(S_key);
+#pragma unroll
+  for (int j = 0; j < 16; j++) {
+    const uint4 q = kv[j];
+    r0 += q.x > key;
+    r1 += q.y > key;
+    r2 += q.z > key;
+    r3 += q.w > key;
+  }
+  const int rank = (r0 + r1) + (r2 + r3);
+  const uint64_t sel = __ballot(rank == k - 1);
+  const uint32_t tau = (uint32_t)__builtin_amdgcn_readlane((int)key, __ffsll((long long)sel) - 1) & ~63u;
+  const double tv = key_floor_value(tau);
+  // 3. candidates, compacted in (slot, lane) order
+  int base = 0;
+#pragma unroll
+  for (int i = 0; i < NV; i++) {
+    if (i < nv) {
+      const int e = lane + 64 * i;
+      const bool cand = (e < E) & (v[i] >= tv);
+      const uint64_t bal = __ballot(cand);
+      const int pos = base + __popcll(bal & ((1ull << lane) - 1ull));
+      const int slot = (cand & (pos < TOPK_CMAX)) ? pos : TOPK_CMAX + lane;
+      S_c[slot].v = v[i];
+      S_c[slot].i = e;
+      base += __popcll(bal);
+    }
+  }
+  const int nc = base;
+  wave_lds_sync();
+  if (nc <= 64) {
+    // 4. exact ranks: one candidate per lane against all (LDS broadcast reads)
+    const double cvv = (lane < nc) ? S_c[lane].v : -__builtin_inf();
+    const int cii = (lane < nc) ? S_c[lane].i : 0x7FFFFFFF;
+    int q0 = 0, q1 = 0, q2 = 0, q3 = 0;
+    for (int j = 0; j < nc; j += 4) {  // slots past nc hold scratch; masked
+      const TopkSlot a0 = S_c[j], a1 = S_c[j + 1], a2 = S_c[j + 2], a3 = S_c[j + 3];
+      q0 += topk_before(a0.v, a0.i, cvv, cii);
+      q1 += (j + 1 < nc) & topk_before(a1.v, a1.i, cvv, cii);
+      q2 += (j + 2 < nc) & topk_before(a2.v, a2.i, cvv, cii);
+      q3 += (j + 3 < nc) & topk_before(a3.v, a3.i, cvv, cii);
+    }
+    const int rk = (q0 + q1) + (q2 + q3);
+    if (lane < nc && rk < k) {
+      S_o[rk].v = cvv;
+      S_o[rk].i = cii;
+    }
+  } else if (nc <= TOPK_CMAX) {
+    // 4'. many candidates: each lane ranks several
+    for (int c = lane; c < nc; c += 64) {
+      const double cvv = S_c[c].v;
+      const int cii = S_c[c].i;
+      int q0 = 0;
+      for (int j = 0; j < nc; j++) q0 += topk_before(S_c[j].v, S_c[j].i, cvv, cii);
+      if (q0 < k) {
+        S_o[q0].v = cvv;
+        S_o[q0].i = cii;
+      }
+    }
+  } else {
+    // massively tied keys: k rounds of a wave arg-max over all values
+    double w[NV];
+#pragma unroll
+    for (int i = 0; i < NV; i++) w[i] = v[i];
+    for (int r = 0; r < k; r++) {
+      double best = -__builtin_inf();
+      int bi = 0x7FFFFFFF;
+#pragma unroll
+      for (int i = 0; i < NV; i++) {
+        const int e = lane + 64 * i;
+        const bool take = (e < E) & (w[i] > best);
+        best = take ? w[i] : best;
+        bi = take ? e : bi;
+      }
+      wave_argmax(best, bi);
+#pragma unroll
+      for (int i = 0; i < NV; i++)
+        if (lane + 64 * i == bi) w[i] = -__builtin_inf();
+      if (lane == 0) {
+        S_o[r].v = best;
+        S_o[r].i = bi;
+      }
+    }
+  }
+  wave_lds_sync();
+  // gates (k <= 16: the winners sit in lanes 0..15, one DPP row)
+  const TopkSlot o = S_o[lane < k ? lane : 0];
+  const double mv = S_o[0].v;
+  const float ef = (lane < k) ? expf((float)(o.v - mv)) : 0.0f;
+  const double z = sum16_f64((double)ef);
+  int ix = (lane < k) ? o.i : 0;
+  ix = ix < 0 ? 0 : (ix >= E ? E - 1 : ix);  // in range whatever the logits held
+  my_idx = ix;
+  my_gate = (lane < k) ? (float)((double)ef / z) : 0.0f;
+}
+
+}  // namespace moe

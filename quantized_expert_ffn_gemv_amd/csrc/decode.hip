@@ -1,4 +1,5 @@
-// Decode path: one MoE layer for B <= 8 tokens as three kernels.
+// Decode path: one MoE layer for B <= 8 tokens as three kernels. (Batch 1
+// takes the one-kernel path of decode1.hip whenever its shape fits there.)
 //
 //   A  k_dec_a : router logits in fp64 (one wave per expert row; an fp32
 //                weight times a bf16 activation is exact in fp64), and the
@@ -19,6 +20,7 @@
 // of their weight loads before computing; lane partial sums reduce by DPP.
 #include "moe_device.h"
 #include "moe_internal.h"
+#include "dec_common.h"
 
 namespace moe {
 
@@ -27,103 +29,6 @@ constexpr int DB_THREADS = 512;  // kernel B: 8 waves
 constexpr int DC_THREADS = 256;  // kernel C
 constexpr int DC_ROWS = 16;      // output rows per kernel-C workgroup
 constexpr int DC_SPLIT = DC_THREADS / DC_ROWS;
-
-template <int WT> constexpr int kchunk() { return WT == MOE_W_F32 ? 4 : (WT == MOE_W_BF16 ? 8 : 32); }
-template <int WT> constexpr bool is_q() { return WT == MOE_W_Q4 || WT == MOE_W_Q3; }
-
-struct Raw {
-  uint32_t w[4];
-};
-
-template <int WT>
-__device__ __forceinline__ Raw load_chunk(const uint8_t* base, size_t ci) {
-  Raw r;
-  if constexpr (WT == MOE_W_Q3) {
-    const uint32_t* p = reinterpret_cast<const uint32_t*>(base + ci * 12);
-    r.w[0] = p[0];
-    r.w[1] = p[1];
-    r.w[2] = p[2];
-    r.w[3] = 0;
-  } else {
-    const uint4 v = *reinterpret_cast<const uint4*>(base + ci * 16);
-    r.w[0] = v.x;
-    r.w[1] = v.y;
-    r.w[2] = v.z;
-    r.w[3] = v.w;
-  }
-  return r;
-}
-
-// sum_k (code_k - OFF) * a_k over a 32-element chunk (`a`: 32 bf16 values in
-// LDS, asum their sum). Four independent dot2 chains. The caller scales.
-template <int WT>
-__device__ __forceinline__ float qdot32(const Raw& r, const uint16_t* a, float asum) {
-  uint32_t p[16];
-  if constexpr (WT == MOE_W_Q4) {
-    q4_pairs<BF16_MAGIC2>(make_uint4(r.w[0], r.w[1], r.w[2], r.w[3]), p);
-  } else {
-    q3_pairs<BF16_MAGIC2>(r.w[0], r.w[1], r.w[2], p);
-  }
-  const uint4* av = reinterpret_cast<const uint4*>(a);
-  float c0 = -(128.0f + (float)QOff<WT>::v) * asum, c1 = 0.0f, c2 = 0.0f, c3 = 0.0f;
-#pragma unroll
-  for (int q = 0; q < 4; q++) {
-    const uint4 v = av[q];
-    c0 = dot2_bf16(p[4 * q + 0], v.x, c0);
-    c1 = dot2_bf16(p[4 * q + 1], v.y, c1);
-    c2 = dot2_bf16(p[4 * q + 2], v.z, c2);
-    c3 = dot2_bf16(p[4 * q + 3], v.w, c3);
-  }
-  return (c0 + c1) + (c2 + c3);
-}
-
-// Dot of one dense chunk (8 bf16 or 4 fp32 weights) with bf16 activations.
-template <int WT>
-__device__ __forceinline__ float ddot(const Raw& r, const uint16_t* a, float acc) {
-  if constexpr (WT == MOE_W_BF16) {
-    const uint4 v = *reinterpret_cast<const uint4*>(a);
-    float c1 = 0.0f;
-    acc = dot2_bf16(r.w[0], v.x, acc);
-    c1 = dot2_bf16(r.w[1], v.y, c1);
-    acc = dot2_bf16(r.w[2], v.z, acc);
-    c1 = dot2_bf16(r.w[3], v.w, c1);
-    return acc + c1;
-  } else {
-    const uint2 v = *reinterpret_cast<const uint2*>(a);
-    acc = __builtin_fmaf(__uint_as_float(r.w[0]), bf16_lo(v.x), acc);
-    acc = __builtin_fmaf(__uint_as_float(r.w[1]), bf16_hi(v.x), acc);
-    acc = __builtin_fmaf(__uint_as_float(r.w[2]), bf16_lo(v.y), acc);
-    acc = __builtin_fmaf(__uint_as_float(r.w[3]), bf16_hi(v.y), acc);
-    return acc;
-  }
-}
-
-// Copy B tokens of x into LDS (bf16) and, if asked, their 32-element block sums.
-template <int NT>
-__device__ __forceinline__ void stage_tokens(const uint16_t* __restrict__ x, int B, int H, uint16_t* xs, float* xsum) {
-  const int n16 = H / 8;
-  for (int i = threadIdx.x; i < B * n16; i += NT) reinterpret_cast<uint4*>(xs)[i] = reinterpret_cast<const uint4*>(x)[i];
-  if (xsum) {
-    __syncthreads();
-    const int nb = H >> 5;
-    for (int i = threadIdx.x; i < B * nb; i += NT) {
-      const uint32_t* v = reinterpret_cast<const uint32_t*>(xs + (size_t)i * 32);
-      float a = 0.0f;
-#pragma unroll
-      for (int j = 0; j < 16; j++) a += bf16_lo(v[j]) + bf16_hi(v[j]);
-      xsum[i] = a;
-    }
-  }
-}
-
-__device__ __forceinline__ float wave_total_f32(float v) {
-  v = sum16_f32(v);
-  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
-  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
-  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
-  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
-  return (r0 + r1) + (r2 + r3);
-}
 
 // ---------------------------------------------------------------------------
 // Down-projection pieces: NCOL consecutive intermediate columns (16 for a
@@ -220,129 +125,6 @@ __device__ __forceinline__ float down_piece_dot(const DownPiece<WT, NCOL>& d, in
     }
     return c0 + c1;
   }
-}
-
-// ---------------------------------------------------------------------------
-// Top-k of one token in one wave. Lane holds the logits of experts
-// lane + 64 i (i < 16).
-//   1. lane best (value, index);
-//   2. radix select, by ballots, of tau = the k-th largest of the 64 lane
-//      bests' 32-bit sortable keys (sign, exponent, top mantissa bits of the
-//      fp64 logit, so key order never contradicts value order);
-//   3. candidates = all values whose key is >= tau. Every true top-k value is
-//      one: a value below tau is beaten by k lane bests. Compacted to LDS;
-//   4. exact rank of each candidate among the candidates (fp64 value, then
-//      index) picks and orders the k winners.
-// If ties of the truncated keys leave more than TOPK_CMAX candidates (only
-// for massively equal logits), k rounds of a wave arg-max decide instead.
-// Order: larger logit first, lower expert index on ties. Lane r < k ends
-// with expert r and its renormalised gate.
-// ---------------------------------------------------------------------------
-constexpr int TOPK_CMAX = 256;
-constexpr size_t TOPK_SCRATCH = (size_t)TOPK_CMAX * 12 + 16 * 12;  // per wave
-
-__device__ __forceinline__ uint32_t sort_key_hi(double v) {
-  const uint64_t b = (uint64_t)__double_as_longlong(v);
-  const uint64_t k = (b >> 63) ? ~b : (b | 0x8000000000000000ull);
-  return (uint32_t)(k >> 32);
-}
-
-__device__ __forceinline__ void wave_topk(const double (&v)[16], int E, int k, int lane, uint8_t* scratch, int& my_idx,
-                                          float& my_gate) {
-  double* S_cv = reinterpret_cast<double*>(scratch);
-  double* S_ov = S_cv + TOPK_CMAX;
-  int* S_ci = reinterpret_cast<int*>(S_ov + 16);
-  int* S_oi = S_ci + TOPK_CMAX;
-  // 1. lane best
-  double bv = -__builtin_inf();
-#pragma unroll
-  for (int i = 0; i < 16; i++)
-    if (lane + 64 * i < E) bv = (v[i] > bv) ? v[i] : bv;
-  const uint32_t kh = sort_key_hi(bv);
-  // 2. radix select of tau over the 64 lane keys
-  uint32_t prefix = 0;
-  int need = k;
-#pragma unroll
-  for (int b = 31; b >= 0; b--) {
-    const bool match = (b == 31) ? true : (((kh ^ prefix) >> (b + 1)) == 0u);
-    const uint64_t m = __ballot(match & ((kh >> b) & 1u));
-    const int c = __popcll(m);
-    if (c >= need) prefix |= (1u << b);
-    else need -= c;
-  }
-  const uint32_t tau = prefix;
-  // 3. candidates, compacted in lane order
-  int base = 0;
-#pragma unroll
-  for (int i = 0; i < 16; i++) {
-    const int e = lane + 64 * i;
-    const bool cand = (e < E) & (sort_key_hi(v[i]) >= tau);
-    const uint64_t bal = __ballot(cand);
-    if (cand) {
-      const int pos = base + __popcll(bal & ((1ull << lane) - 1ull));
-      if (pos < TOPK_CMAX) {
-        S_cv[pos] = v[i];
-        S_ci[pos] = e;
-      }
-    }
-    base += __popcll(bal);
-  }
-  const int nc = base;
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  if (nc <= TOPK_CMAX) {
-    // 4. exact ranks among the candidates
-    for (int c = lane; c < nc; c += 64) {
-      const double cvv = S_cv[c];
-      const int cii = S_ci[c];
-      int r0 = 0, r1 = 0;
-      int j = 0;
-      for (; j + 1 < nc; j += 2) {
-        r0 += topk_before(S_cv[j], S_ci[j], cvv, cii);
-        r1 += topk_before(S_cv[j + 1], S_ci[j + 1], cvv, cii);
-      }
-      if (j < nc) r0 += topk_before(S_cv[j], S_ci[j], cvv, cii);
-      const int rk = r0 + r1;
-      if (rk < k) {
-        S_ov[rk] = cvv;
-        S_oi[rk] = cii;
-      }
-    }
-  } else {
-    // massively tied keys: k rounds of a wave arg-max over all values
-    double w[16];
-#pragma unroll
-    for (int i = 0; i < 16; i++) w[i] = v[i];
-    for (int r = 0; r < k; r++) {
-      double best = -__builtin_inf();
-      int bi = 0x7FFFFFFF;
-#pragma unroll
-      for (int i = 0; i < 16; i++) {
-        const int e = lane + 64 * i;
-        const bool take = (e < E) & (w[i] > best);
-        best = take ? w[i] : best;
-        bi = take ? e : bi;
-      }
-      wave_argmax(best, bi);
-#pragma unroll
-      for (int i = 0; i < 16; i++)
-        if (lane + 64 * i == bi) w[i] = -__builtin_inf();
-      if (lane == 0) {
-        S_ov[r] = best;
-        S_oi[r] = bi;
-      }
-    }
-  }
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  // gates: softmax over the selected logits (equal to the renormalised softmax over all E)
-  const double mv = S_ov[0];
-  const double ev = (lane < k) ? exp(S_ov[lane < k ? lane : 0] - mv) : 0.0;
-  const double z = wave_total_f64(ev);
-  my_idx = (lane < k) ? S_oi[lane] : 0;
-  my_gate = (float)(ev / z);
 }
 
 // ---------------------------------------------------------------------------
@@ -768,26 +550,20 @@ static hipError_t launch_t(const LayerDev& L, const uint16_t* x, int B, uint16_t
     const int nRB = (E + 7) / 8;
     const int nSB = (SWT == MOE_W_NONE) ? 0 : I / 4;
     const size_t lds = (size_t)B * H * 2 + (size_t)(8 * MAXB * 8 + MAXB * 2 + MAXB) * 4;
-    timer_begin(KC_DEC_ROUTER_SHARED, st);
-    hipLaunchKernelGGL((k_dec_a<SW, MAXB>), dim3(nRB + nSB), dim3(DA_THREADS), lds, st, L, x, B, ws, nRB);
-    timer_end(KC_DEC_ROUTER_SHARED, st);
+    (void)launch_k(KC_DEC_ROUTER_SHARED, (k_dec_a<SW, MAXB>), dim3(nRB + nSB), dim3(DA_THREADS), lds, st, L, x, B, ws, nRB);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
   {
     const int maxU = (B * k < E) ? B * k : E;
     const size_t lds = decode_lds_b(WT, B, H, E, k);
-    timer_begin(KC_DEC_GATE_UP, st);
-    hipLaunchKernelGGL((k_dec_b<WT, MAXB>), dim3(maxU * (I / 16)), dim3(DB_THREADS), lds, st, L, x, B, ws, idx_out,
+    (void)launch_k(KC_DEC_GATE_UP, (k_dec_b<WT, MAXB>), dim3(maxU * (I / 16)), dim3(DB_THREADS), lds, st, L, x, B, ws, idx_out,
                        gate_out);
-    timer_end(KC_DEC_GATE_UP, st);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
-  timer_begin(KC_DEC_DOWN, st);
-  hipLaunchKernelGGL(k_dec_c, dim3((H + DC_ROWS - 1) / DC_ROWS, B), dim3(DC_THREADS), 0, st, ws.part, H, k, I, B, y,
+  (void)launch_k(KC_DEC_DOWN, k_dec_c, dim3((H + DC_ROWS - 1) / DC_ROWS, B), dim3(DC_THREADS), 0, st, ws.part, H, k, I, B, y,
                      SWT == MOE_W_NONE ? 0 : 1);
-  timer_end(KC_DEC_DOWN, st);
   return hipGetLastError();
 }
 
@@ -810,6 +586,8 @@ static hipError_t launch_s(const LayerDev& L, const uint16_t* x, int B, uint16_t
 
 hipError_t launch_decode(const LayerDev& L, const uint16_t* x, int B, uint16_t* y, int32_t* idx_out, float* gate_out,
                          const DecodeWs& ws, hipStream_t st) {
+  if (B == 1 && decode1_fits(L.E, L.H, L.I, L.k, L.swt != MOE_W_NONE))
+    return launch_decode_fused(L, x, y, idx_out, gate_out, ws, st);
   switch (L.wt) {
     case MOE_W_Q4: return launch_s<MOE_W_Q4>(L, x, B, y, idx_out, gate_out, ws, st);
     case MOE_W_Q3: return launch_s<MOE_W_Q3>(L, x, B, y, idx_out, gate_out, ws, st);

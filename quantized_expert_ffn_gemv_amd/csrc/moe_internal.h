@@ -1,5 +1,6 @@
 // Host/device shared parameter blocks and launch declarations (internal).
 #pragma once
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -10,7 +11,8 @@ namespace moe {
 
 // Kernel classes for the optional timer.
 enum KernelClass {
-  KC_DEC_ROUTER_SHARED = 0,  // router logits + the whole shared expert
+  KC_DEC_FUSED = 0,          // batch-1 decode, one kernel
+  KC_DEC_ROUTER_SHARED,      // router logits + the whole shared expert
   KC_DEC_GATE_UP,            // top-k + routed experts (gate/up, SwiGLU, partial down)
   KC_DEC_DOWN,               // sum of the partial down products
   KC_PF_ROUTER,
@@ -49,8 +51,10 @@ struct LayerDev {
 
 // Decode workspace (all device pointers inside the caller's workspace).
 struct DecodeWs {
-  double* logits;  // [B][E]
-  float* part;     // [B*k*(I/16) + B*(I/4)][H] partial down products (routed, then shared)
+  uint32_t* sync;  // counters and epoch of the one-kernel path (counters zero between calls)
+  double* logits;  // three-kernel path: [B][E] fp64; one-kernel path: [E][2] tagged 64-bit words
+  uint16_t* h;     // one-kernel path: [(k+1) * I / 2] tagged words, two bf16 SwiGLU outputs each
+  float* part;     // [B*k*(I/16) + B*(I/4)][H] partial down products of the three-kernel path
 };
 
 // Prefill workspace.
@@ -73,6 +77,10 @@ struct PrefillWs {
 
 // Launch wrappers (return hipError_t of the launch).
 size_t decode_lds_b(int wt, int B, int H, int E, int k);  // LDS bytes of the routed-expert kernel
+size_t decode1_lds(int H, int I, int k, bool has_shared);  // LDS bytes of the one-kernel batch-1 path
+bool decode1_fits(int E, int H, int I, int k, bool has_shared);  // shape handled by the one-kernel path
+hipError_t launch_decode_fused(const LayerDev& L, const uint16_t* x, uint16_t* y, int32_t* idx_out,
+                               float* gate_out, const DecodeWs& ws, hipStream_t st);
 hipError_t launch_decode(const LayerDev& L, const uint16_t* x, int B, uint16_t* y, int32_t* idx_out,
                          float* gate_out, const DecodeWs& ws, hipStream_t st);
 hipError_t launch_route(const LayerDev& L, const uint16_t* x, int T, int32_t* idx_out, float* gate_out,
@@ -87,8 +95,22 @@ hipError_t launch_fill(void* p, size_t bytes, hipStream_t st);
 constexpr int PF_BM = 128;          // max rows (tokens) per grouped-GEMM tile
 constexpr int PF_TOK_PER_BLK = 256; // tokens per histogram block
 
-// Timer hooks (api.cpp).
-void timer_begin(int kc, hipStream_t st);
-void timer_end(int kc, hipStream_t st);
+// Timer hooks (api.cpp). When the timer is on, a launch carries a start and
+// a stop event in its own dispatch packet, so the measured interval is the
+// kernel's execution, not the gap between host-side records.
+bool timer_events(int kc, hipEvent_t* start, hipEvent_t* stop);
+void timer_commit(int kc, hipEvent_t start, hipEvent_t stop);
+
+template <typename F, typename... Args>
+hipError_t launch_k(int kc, F kernel, dim3 grid, dim3 block, size_t lds, hipStream_t st, Args... args) {
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  if (timer_events(kc, &e0, &e1)) {
+    hipExtLaunchKernelGGL(kernel, grid, block, (uint32_t)lds, st, e0, e1, 0u, args...);
+    timer_commit(kc, e0, e1);
+  } else {
+    kernel<<<grid, block, lds, st>>>(args...);
+  }
+  return hipPeekAtLastError();  // sticky: the caller's hipGetLastError() reports it
+}
 
 }  // namespace moe

@@ -56,17 +56,13 @@ __global__ __launch_bounds__(256) void k_fill(uint32_t* __restrict__ p, size_t n
 }
 
 hipError_t launch_rmsnorm(const uint16_t* h, uint16_t* z, int T, int H, float eps, hipStream_t st) {
-  timer_begin(KC_NORM, st);
-  hipLaunchKernelGGL(k_rmsnorm, dim3(T), dim3(256), 0, st, h, z, H, eps);
-  timer_end(KC_NORM, st);
+  (void)launch_k(KC_NORM, k_rmsnorm, dim3(T), dim3(256), 0, st, h, z, H, eps);
   return hipGetLastError();
 }
 
 hipError_t launch_residual(uint16_t* h, const uint16_t* y, int T, int H, hipStream_t st) {
   const size_t n8 = (size_t)T * H / 8;
-  timer_begin(KC_RESIDUAL, st);
-  hipLaunchKernelGGL(k_residual, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, st, h, y, n8);
-  timer_end(KC_RESIDUAL, st);
+  (void)launch_k(KC_RESIDUAL, k_residual, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, st, h, y, n8);
   return hipGetLastError();
 }
 
@@ -75,9 +71,7 @@ hipError_t launch_fill(void* p, size_t bytes, hipStream_t st) {
   size_t blocks = (n4 + 255) / 256;
   if (blocks > 4096) blocks = 4096;
   if (blocks == 0) return hipSuccess;
-  timer_begin(KC_FILL, st);
-  hipLaunchKernelGGL(k_fill, dim3((unsigned)blocks), dim3(256), 0, st, reinterpret_cast<uint32_t*>(p), n4);
-  timer_end(KC_FILL, st);
+  (void)launch_k(KC_FILL, k_fill, dim3((unsigned)blocks), dim3(256), 0, st, reinterpret_cast<uint32_t*>(p), n4);
   return hipGetLastError();
 }
 

@@ -485,28 +485,18 @@ __global__ __launch_bounds__(256) void k_pf_combine(const uint16_t* __restrict__
 static hipError_t route_steps(const LayerDev& L, const uint16_t* x, int T, int32_t* idx_out, float* gate_out,
                               int32_t* counts_out, const PrefillWs& ws, hipStream_t st, bool permute) {
   const int E = L.E, k = L.k, H = L.H;
-  timer_begin(KC_PF_ROUTER, st);
-  hipLaunchKernelGGL(k_pf_router, dim3((T + RT_M - 1) / RT_M, (E + RT_N - 1) / RT_N), dim3(256), 0, st, L.router_w,
+  (void)launch_k(KC_PF_ROUTER, k_pf_router, dim3((T + RT_M - 1) / RT_M, (E + RT_N - 1) / RT_N), dim3(256), 0, st, L.router_w,
                      L.router_b, x, T, E, H, ws.logits);
-  timer_end(KC_PF_ROUTER, st);
-  timer_begin(KC_PF_TOPK, st);
-  hipLaunchKernelGGL(k_pf_topk, dim3((T + 3) / 4), dim3(256), 0, st, ws.logits, T, E, k, ws.idx, ws.gates, idx_out,
+  (void)launch_k(KC_PF_TOPK, k_pf_topk, dim3((T + 3) / 4), dim3(256), 0, st, ws.logits, T, E, k, ws.idx, ws.gates, idx_out,
                      gate_out);
-  timer_end(KC_PF_TOPK, st);
   if (!permute && !counts_out) return hipGetLastError();
   const int nblk = (T + PF_TOK_PER_BLK - 1) / PF_TOK_PER_BLK;
-  timer_begin(KC_PF_COUNT, st);
-  hipLaunchKernelGGL(k_pf_count, dim3(nblk), dim3(256), E * sizeof(int), st, ws.idx, T, E, k, ws.blk_counts);
-  timer_end(KC_PF_COUNT, st);
-  timer_begin(KC_PF_SCAN, st);
-  hipLaunchKernelGGL(k_pf_scan, dim3(1), dim3(1024), 0, st, ws.blk_counts, nblk, E, ws.blk_base, ws.counts,
+  (void)launch_k(KC_PF_COUNT, k_pf_count, dim3(nblk), dim3(256), E * sizeof(int), st, ws.idx, T, E, k, ws.blk_counts);
+  (void)launch_k(KC_PF_SCAN, k_pf_scan, dim3(1), dim3(1024), 0, st, ws.blk_counts, nblk, E, ws.blk_base, ws.counts,
                      ws.offsets, ws.tile_start, counts_out);
-  timer_end(KC_PF_SCAN, st);
   if (!permute) return hipGetLastError();
-  timer_begin(KC_PF_SCATTER, st);
-  hipLaunchKernelGGL(k_pf_scatter, dim3(nblk), dim3(256), E * sizeof(int), st, ws.idx, T, E, k, ws.blk_base, ws.perm,
+  (void)launch_k(KC_PF_SCATTER, k_pf_scatter, dim3(nblk), dim3(256), E * sizeof(int), st, ws.idx, T, E, k, ws.blk_base, ws.perm,
                      ws.inv);
-  timer_end(KC_PF_SCATTER, st);
   return hipGetLastError();
 }
 
@@ -516,17 +506,17 @@ hipError_t launch_route(const LayerDev& L, const uint16_t* x, int T, int32_t* id
 }
 
 template <int WT, int KIND>
-static void gemm_launch(const GemmArgs& g, int tiles_x, hipStream_t st) {
-  hipLaunchKernelGGL((k_pf_gemm<WT, KIND>), dim3(tiles_x, (g.N + G_BN - 1) / G_BN), dim3(G_THREADS), 0, st, g);
+static void gemm_launch(int kc, const GemmArgs& g, int tiles_x, hipStream_t st) {
+  (void)launch_k(kc, k_pf_gemm<WT, KIND>, dim3(tiles_x, (g.N + G_BN - 1) / G_BN), dim3(G_THREADS), 0, st, g);
 }
 
 template <int KIND>
-static void gemm_dispatch(int wt, const GemmArgs& g, int tiles_x, hipStream_t st) {
+static void gemm_dispatch(int kc, int wt, const GemmArgs& g, int tiles_x, hipStream_t st) {
   switch (wt) {
-    case MOE_W_Q4: gemm_launch<MOE_W_Q4, KIND>(g, tiles_x, st); break;
-    case MOE_W_Q3: gemm_launch<MOE_W_Q3, KIND>(g, tiles_x, st); break;
-    case MOE_W_BF16: gemm_launch<MOE_W_BF16, KIND>(g, tiles_x, st); break;
-    default: gemm_launch<MOE_W_F32, KIND>(g, tiles_x, st); break;
+    case MOE_W_Q4: gemm_launch<MOE_W_Q4, KIND>(kc, g, tiles_x, st); break;
+    case MOE_W_Q3: gemm_launch<MOE_W_Q3, KIND>(kc, g, tiles_x, st); break;
+    case MOE_W_BF16: gemm_launch<MOE_W_BF16, KIND>(kc, g, tiles_x, st); break;
+    default: gemm_launch<MOE_W_F32, KIND>(kc, g, tiles_x, st); break;
   }
 }
 
@@ -543,18 +533,14 @@ hipError_t launch_prefill(const LayerDev& L, const uint16_t* x, int T, uint16_t*
     g.w = L.gu; g.ws = quant ? L.gu_s : nullptr; g.w_stride = L.gu_stride; g.ws_stride = L.gu_s_stride;
     g.N = 2 * I; g.K = H; g.a = x; g.perm = ws.perm; g.k = k;
     g.offsets = ws.offsets; g.tile_start = ws.tile_start; g.E = E; g.out = ws.h;
-    timer_begin(KC_PF_GATE_UP, st);
-    gemm_dispatch<GK_GATE_UP>(L.wt, g, max_tiles, st);
-    timer_end(KC_PF_GATE_UP, st);
+    gemm_dispatch<GK_GATE_UP>(KC_PF_GATE_UP, L.wt, g, max_tiles, st);
   }
   // shared gate/up
   if (L.swt != MOE_W_NONE) {
     GemmArgs g{};
     g.w = L.sgu; g.N = 2 * I; g.K = H; g.a = x; g.perm = nullptr; g.k = k;
     g.offsets = nullptr; g.M_total = T; g.out = ws.hs;
-    timer_begin(KC_PF_SHARED_GATE_UP, st);
-    gemm_dispatch<GK_GATE_UP>(L.swt, g, (T + PF_BM - 1) / PF_BM, st);
-    timer_end(KC_PF_SHARED_GATE_UP, st);
+    gemm_dispatch<GK_GATE_UP>(KC_PF_SHARED_GATE_UP, L.swt, g, (T + PF_BM - 1) / PF_BM, st);
   }
   // routed down
   {
@@ -562,22 +548,16 @@ hipError_t launch_prefill(const LayerDev& L, const uint16_t* x, int T, uint16_t*
     g.w = L.dn; g.ws = quant ? L.dn_s : nullptr; g.w_stride = L.dn_stride; g.ws_stride = L.dn_s_stride;
     g.N = H; g.K = I; g.a = ws.h; g.perm = nullptr; g.k = k;
     g.offsets = ws.offsets; g.tile_start = ws.tile_start; g.E = E; g.out = ws.Y;
-    timer_begin(KC_PF_DOWN, st);
-    gemm_dispatch<GK_DOWN>(L.wt, g, max_tiles, st);
-    timer_end(KC_PF_DOWN, st);
+    gemm_dispatch<GK_DOWN>(KC_PF_DOWN, L.wt, g, max_tiles, st);
   }
   if (L.swt != MOE_W_NONE) {
     GemmArgs g{};
     g.w = L.sdn; g.N = H; g.K = I; g.a = ws.hs; g.perm = nullptr; g.k = k;
     g.offsets = nullptr; g.M_total = T; g.out = ws.Ys;
-    timer_begin(KC_PF_SHARED_DOWN, st);
-    gemm_dispatch<GK_DOWN>(L.swt, g, (T + PF_BM - 1) / PF_BM, st);
-    timer_end(KC_PF_SHARED_DOWN, st);
+    gemm_dispatch<GK_DOWN>(KC_PF_SHARED_DOWN, L.swt, g, (T + PF_BM - 1) / PF_BM, st);
   }
-  timer_begin(KC_PF_COMBINE, st);
-  hipLaunchKernelGGL(k_pf_combine, dim3(T), dim3(256), 0, st, ws.Y, (L.swt != MOE_W_NONE) ? ws.Ys : nullptr, ws.inv,
+  (void)launch_k(KC_PF_COMBINE, k_pf_combine, dim3(T), dim3(256), 0, st, ws.Y, (L.swt != MOE_W_NONE) ? ws.Ys : nullptr, ws.inv,
                      ws.gates, T, H, k, y);
-  timer_end(KC_PF_COMBINE, st);
   return hipGetLastError();
 }
 

@@ -16,7 +16,8 @@ import numpy as np
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "_lib", "libmoe.so")
 
-MOE_OK, MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_ALIGN, MOE_ERR_DTYPE, MOE_ERR_WORKSPACE, MOE_ERR_HIP, MOE_ERR_VALUE = range(8)
+MOE_OK, MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_ALIGN, MOE_ERR_DTYPE, MOE_ERR_WORKSPACE, MOE_ERR_HIP, MOE_ERR_VALUE, \
+    MOE_ERR_DEVICE = range(9)
 W_F32, W_BF16, W_Q4, W_Q3, W_NONE = 0, 1, 2, 3, -1
 WTYPES = {"f32": W_F32, "bf16": W_BF16, "q4": W_Q4, "q3": W_Q3, None: W_NONE}
 DECODE_MAX_TOKENS = 8
@@ -26,7 +27,7 @@ EXPORTS = [
     "moe_matrix_bytes", "moe_matrix_scales", "moe_workspace_bytes", "moe_route", "moe_forward_decode",
     "moe_forward_prefill", "moe_rmsnorm", "moe_residual_add", "moe_pack_matrix", "moe_pack_gate_up",
     "moe_status_string", "moe_last_error", "moe_kernel_class_count", "moe_kernel_class_name",
-    "moe_timer_enable", "moe_timer_reset", "moe_timer_read",
+    "moe_timer_enable", "moe_timer_reset", "moe_timer_read", "moe_workspace_init", "moe_workspace_check",
 ]
 
 
@@ -77,6 +78,8 @@ def lib():
         L.moe_last_error.restype = ctypes.c_char_p; L.moe_last_error.argtypes = []
         L.moe_kernel_class_count.restype = i32; L.moe_kernel_class_count.argtypes = []
         L.moe_kernel_class_name.restype = ctypes.c_char_p; L.moe_kernel_class_name.argtypes = [i32]
+        L.moe_workspace_init.restype = i32; L.moe_workspace_init.argtypes = [vp, sz, vp]
+        L.moe_workspace_check.restype = i32; L.moe_workspace_check.argtypes = [vp, sz, vp]
         L.moe_timer_enable.restype = i32; L.moe_timer_enable.argtypes = [i32]
         L.moe_timer_reset.restype = i32; L.moe_timer_reset.argtypes = []
         L.moe_timer_read.restype = i32
@@ -223,9 +226,22 @@ def moe_workspace_bytes(layer: DeviceLayer, max_tokens: int, mode: int) -> int:
     return n
 
 
-def make_workspace(layer: DeviceLayer, max_tokens: int, mode: int, device="cuda"):
+def make_workspace(layer: DeviceLayer, max_tokens: int, mode: int, device="cuda", stream=None):
+    """Workspace tensor; a decode workspace (mode 0) comes initialised (see moe_workspace_init)."""
     import torch
-    return torch.empty(moe_workspace_bytes(layer, max_tokens, mode), dtype=torch.uint8, device=device)
+    ws = torch.empty(moe_workspace_bytes(layer, max_tokens, mode), dtype=torch.uint8, device=device)
+    if mode == 0:
+        moe_workspace_init(ws, stream)
+    return ws
+
+
+def moe_workspace_init(ws, stream=None):
+    _check(lib().moe_workspace_init(_tptr(ws), ws.numel(), _stream(stream)), "moe_workspace_init")
+
+
+def moe_workspace_check(ws, stream=None):
+    """Raises MoeError(MOE_ERR_DEVICE) if a device-side wait of a decode call ran out."""
+    _check(lib().moe_workspace_check(_tptr(ws), ws.numel(), _stream(stream)), "moe_workspace_check")
 
 
 def moe_route(layer, x, topk_idx, topk_gate, ws, expert_counts=None, stream=None):

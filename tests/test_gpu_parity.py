@@ -38,6 +38,7 @@ def _decode_calls(m, L, x_bits, B, ws=None):
         t1 = min(T, t0 + B)
         m.moe_forward_decode(L, xd[t0:t1], y[t0:t1], ws, topk_idx=idx[t0:t1], topk_gate=g[t0:t1])
     torch.cuda.synchronize()
+    m.moe_workspace_check(ws)  # no device-side wait ran out
     return from_dev_bits(y), idx.cpu().numpy(), g.cpu().numpy()
 
 
@@ -100,6 +101,47 @@ def test_edge_expert_counts(moe, E, k):
     _check_all(host, x, y, idx, g, "edge prefill E=%d k=%d" % (E, k))
     y, idx, g = _decode_calls(moe, L, x[:8], 1)
     _check_all(host, x[:8], y, idx, g, "edge decode E=%d k=%d" % (E, k))
+
+
+def test_decode_b1_three_kernel_shape(moe):
+    # I = 2048 is beyond the one-kernel batch-1 path: batch 1 runs as three kernels
+    log("decode B=1 with I=2048 (three-kernel path)")
+    host = synth.random_layer(8, 2, 64, 2048, "q4", "bf16", seed=12, router_sd=0.3)
+    x = synth.normal_bf16(synth.key(12, 3, 3, 3, 3), (6, 64), 1.0)
+    L = moe.DeviceLayer(host)
+    y, idx, g = _decode_calls(moe, L, x, 1)
+    _check_all(host, x, y, idx, g, "decode B=1 I=2048")
+
+
+def test_decode_graph_replay(moe):
+    # the one-kernel path resets its counters itself: replays of a captured
+    # sequence match the eager results bit for bit, with eager work between
+    log("decode B=1 captured in a HIP graph, 3 replays against eager")
+    host = synth.random_layer(64, 6, 256, 128, "q4", "bf16", seed=13, router_sd=0.3)
+    x = synth.normal_bf16(synth.key(13, 4, 4, 4, 4), (12, 256), 1.0)
+    L = moe.DeviceLayer(host)
+    y_eager, idx_eager, _ = _decode_calls(moe, L, x, 1)
+    xd = to_dev(x)
+    yd = torch.zeros((12, 256), dtype=torch.int16, device="cuda")
+    ws = moe.make_workspace(L, 1, 0)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for t in range(12):
+            moe.moe_forward_decode(L, xd[t:t + 1], yd[t:t + 1], ws)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    gr = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gr):
+        for t in range(12):
+            moe.moe_forward_decode(L, xd[t:t + 1], yd[t:t + 1], ws)
+    for rep in range(3):
+        yd.zero_()
+        _decode_calls(moe, L, x[:2], 1)  # eager work between replays
+        gr.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(from_dev_bits(yd), y_eager), "replay %d differs from eager" % rep
+    moe.moe_workspace_check(ws)
 
 
 def test_single_token_prefill_and_zero_input(moe):
