@@ -92,7 +92,7 @@ hipError_t launch_residual(uint16_t* h, const uint16_t* y, int T, int H, hipStre
 hipError_t launch_fill(void* p, size_t bytes, hipStream_t st);
 
 // Prefill tiling constants shared by host sizing and kernels.
-constexpr int PF_BM = 128;          // max rows (tokens) per grouped-GEMM tile
+constexpr int PF_BM = 96;           // max rows (tokens) per grouped-GEMM tile
 constexpr int PF_TOK_PER_BLK = 256; // tokens per histogram block
 
 // Timer hooks (api.cpp). When the timer is on, a launch carries a start and

@@ -220,11 +220,9 @@ __global__ __launch_bounds__(256) void k_pf_scatter(const int32_t* __restrict__ 
 // ---------------------------------------------------------------------------
 // Grouped GEMM (MFMA 16x16x32 bf16, fp32 accumulate)
 // ---------------------------------------------------------------------------
-constexpr int G_THREADS = 256;
-constexpr int G_BN = 256;       // weight rows (output columns) per tile
-constexpr int G_BK = 32;        // one quantisation block per K-step
-constexpr int G_LDA = 40;       // LDS row stride in bf16 (80 B: 16-byte aligned, bank-spread)
-constexpr int G_MSUB = PF_BM / 16;
+constexpr int G_THREADS = 256;     // 4 waves; wave w owns columns [16 NSW w, 16 NSW (w + 1)) of the tile
+constexpr int G_BK = 128;          // K per pipeline stage (4 MFMA K-steps of 32)
+constexpr int G_MSUB = PF_BM / 16; // 16-row subtiles per tile
 
 enum GemmKind { GK_GATE_UP = 0, GK_DOWN = 1 };
 
@@ -246,171 +244,274 @@ struct GemmArgs {
   uint16_t* out;          // gate/up: h [rows][N/2]; down: Y [rows][N]
 };
 
-// Raw bytes of one 32-element K-step of weight row n (and its scale).
+// ---------------------------------------------------------------------------
+// Weight fragments straight from HBM to registers. In one stage (K = 128,
+// four 32-element blocks) lane l of a wave serves weight row n = l % 16 of a
+// 16-column subtile and K block j = l / 16: it loads the whole block (one
+// quantised chunk: 16 B Q4, 12 B Q3, plus its fp16 scale; 64 B bf16; 128 B
+// fp32) and feeds MFMA step t = 0..3 with elements 8t .. 8t+7 of it. The
+// MFMA therefore sees, for its k-group j, the actual K positions
+// 32 j + 8 t + 0..7; the A fragments use the same positions, so the sum over
+// K is unchanged. Lanes of consecutive rows read consecutive chunks of one
+// chunk column (16 rows x 16 B = 256 contiguous bytes).
+// ---------------------------------------------------------------------------
+template <int WT> struct BRaw;
+template <> struct BRaw<MOE_W_Q4> { uint4 w; uint32_t s; };          // s: fp16 scale bits, 0 when out of range
+template <> struct BRaw<MOE_W_Q3> { uint32_t l0, l1, hb, s; };
+template <> struct BRaw<MOE_W_BF16> { uint4 w[4]; uint32_t ok; };
+template <> struct BRaw<MOE_W_F32> { uint4 w[8]; uint32_t ok; };
+
+// Loads are unconditional (indices clamped into the matrix) so that no branch
+// forces the compiler to wait for them; out-of-range blocks are zeroed when
+// used (a zero scale for quantised types, a zero mask for dense ones).
+// `cell` = (block, row) index blk * N + n of this lane's 32-element block,
+// clamped into the matrix; `ok` = whether the unclamped block exists.
 template <int WT>
-__device__ __forceinline__ void load_b_chunk(const GemmArgs& g, const uint8_t* w, const uint16_t* ws, int n, int s,
-                                             uint32_t (&raw)[32], float& scale) {
+__device__ __forceinline__ void load_b(const uint8_t* __restrict__ w, const uint16_t* __restrict__ ws, uint32_t N,
+                                       uint32_t cell, bool ok, BRaw<WT>& r) {
   if constexpr (WT == MOE_W_Q4) {
-    const uint4 v = *reinterpret_cast<const uint4*>(w + ((size_t)s * g.N + n) * 16);
-    raw[0] = v.x; raw[1] = v.y; raw[2] = v.z; raw[3] = v.w;
-    scale = f16_to_f32(ws[(size_t)s * g.N + n]);
+    r.w = *reinterpret_cast<const uint4*>(w + cell * 16u);
+    r.s = ws[cell] & (ok ? 0xFFFFu : 0u);
   } else if constexpr (WT == MOE_W_Q3) {
-    const uint32_t* p = reinterpret_cast<const uint32_t*>(w + ((size_t)s * g.N + n) * 12);
-    raw[0] = p[0]; raw[1] = p[1]; raw[2] = p[2];
-    scale = f16_to_f32(ws[(size_t)s * g.N + n]);
+    const uint32_t* p = reinterpret_cast<const uint32_t*>(w + cell * 12u);
+    r.l0 = p[0];
+    r.l1 = p[1];
+    r.hb = p[2];
+    r.s = ws[cell] & (ok ? 0xFFFFu : 0u);
   } else {
-    constexpr int NCH = (WT == MOE_W_BF16) ? 4 : 8;  // 16-byte chunks per K-step
+    // dense: the block is NCH consecutive 16-byte chunks of chunk columns NCH*blk .. ; cell -> (blk, n)
+    constexpr uint32_t NCH = (WT == MOE_W_BF16) ? 4 : 8;
+    const uint32_t blk = cell / N, n = cell - blk * N;
 #pragma unroll
-    for (int c = 0; c < NCH; c++) {
-      const uint4 v = *reinterpret_cast<const uint4*>(w + ((size_t)(NCH * s + c) * g.N + n) * 16);
-      raw[4 * c] = v.x; raw[4 * c + 1] = v.y; raw[4 * c + 2] = v.z; raw[4 * c + 3] = v.w;
-    }
-    scale = 0.0f;
+    for (uint32_t c = 0; c < NCH; c++) r.w[c] = *reinterpret_cast<const uint4*>(w + ((NCH * blk + c) * N + n) * 16u);
+    r.ok = ok ? 0xFFFFFFFFu : 0u;
   }
 }
 
-// Raw K-step -> 16 bf16 pairs (elements 2i, 2i+1 in pair i).
+// Elements 8t .. 8t+7 of the block as 4 bf16 pairs (the MFMA B fragment).
+// Quantised: fp16(1024 + code) by a magic exponent, then s * (code - off)
+// exactly in fp32 (one fma), rounded once to bf16.
 template <int WT>
-__device__ __forceinline__ void dequant_b_chunk(const uint32_t (&raw)[32], float scale, uint32_t (&out)[16]) {
+__device__ __forceinline__ bf16x8_t frag_b(const BRaw<WT>& r, int t) {
+  uint32_t o[4];
   if constexpr (WT == MOE_W_Q4 || WT == MOE_W_Q3) {
-    uint32_t p[16];
+    uint32_t p[4];
     if constexpr (WT == MOE_W_Q4) {
-      q4_pairs<F16_MAGIC2>(make_uint4(raw[0], raw[1], raw[2], raw[3]), p);
+      const uint32_t wd = (t == 0) ? r.w.x : (t == 1) ? r.w.y : (t == 2) ? r.w.z : r.w.w;
+      q4_word_pairs<F16_MAGIC2>(wd, p);
     } else {
-      q3_pairs<F16_MAGIC2>(raw[0], raw[1], raw[2], p);
+      q3_group_pairs<F16_MAGIC2>(r.l0, r.l1, r.hb, t, p);
     }
-    const float negbase = -(1024.0f + (float)QOff<WT>::v) * scale;
+    const float sc = f16_to_f32((uint16_t)r.s);
+    const float negbase = -(1024.0f + (float)QOff<WT>::v) * sc;
 #pragma unroll
-    for (int i = 0; i < 16; i++) {
+    for (int i = 0; i < 4; i++) {
       float lo, hi;
-      f16pair_dequant(p[i], scale, negbase, lo, hi);
-      out[i] = pack_bf16x2(lo, hi);
+      f16pair_dequant(p[i], sc, negbase, lo, hi);
+      o[i] = pack_bf16x2(lo, hi);
     }
   } else if constexpr (WT == MOE_W_BF16) {
-#pragma unroll
-    for (int i = 0; i < 16; i++) out[i] = raw[i];
+    const uint4 v = r.w[t];
+    o[0] = v.x & r.ok; o[1] = v.y & r.ok; o[2] = v.z & r.ok; o[3] = v.w & r.ok;
   } else {
-#pragma unroll
-    for (int i = 0; i < 16; i++) out[i] = pack_bf16x2(__uint_as_float(raw[2 * i]), __uint_as_float(raw[2 * i + 1]));
+    const uint4 v0 = r.w[2 * t], v1 = r.w[2 * t + 1];
+    o[0] = pack_bf16x2(__uint_as_float(v0.x), __uint_as_float(v0.y)) & r.ok;
+    o[1] = pack_bf16x2(__uint_as_float(v0.z), __uint_as_float(v0.w)) & r.ok;
+    o[2] = pack_bf16x2(__uint_as_float(v1.x), __uint_as_float(v1.y)) & r.ok;
+    o[3] = pack_bf16x2(__uint_as_float(v1.z), __uint_as_float(v1.w)) & r.ok;
   }
+  return __builtin_bit_cast(bf16x8_t, make_uint4(o[0], o[1], o[2], o[3]));
+}
+
+// ---------------------------------------------------------------------------
+// Grouped GEMM. Tile = (M tile of one expert's rows, 256 weight rows).
+// Workgroups go round-robin over the 8 XCDs; a contiguous range of logical
+// tiles runs on each XCD. Routed: the tiles of one expert are consecutive
+// (N tile outer, M tile inner), so the expert's weights and gathered rows
+// stay in that XCD's L2 while they run. Shared expert: N tile outer.
+//
+// Pipeline, per 128-wide K stage: A (bf16 rows, gathered) goes straight from
+// memory to LDS (global_load_lds, 16 B per lane) into a 2-slot ring; the
+// weights go to registers one stage at a time; two waves per SIMD overlap one
+// wave's loads and dequantisation with the other's MFMAs. One barrier per
+// stage. The ring slots are separate LDS arrays and the loop is unrolled by
+// 2, so each LDS read names its slot and the compiler need not wait for loads
+// still in flight into the other slot.
+// A rows in LDS: 16 chunks of 16 B per row, chunk c at position c ^ (row & 15)
+// (conflict-free fragment reads without padding).
+// ---------------------------------------------------------------------------
+typedef __attribute__((address_space(3))) void* lds_void_t;
+typedef __attribute__((address_space(1))) const void* gbl_void_t;
+
+constexpr int G_AROWS = PF_BM;                       // rows per A slot
+constexpr int G_ALOADS = G_AROWS * 16 / G_THREADS;   // 16-byte DMA loads per lane per stage
+constexpr int G_SLOT_U4 = G_AROWS * 16;              // uint4 per A slot
+
+// 16-column weight subtiles per wave: 4 for quantised weights (16 B + a scale per
+// lane and stage), 2 for dense ones (64 or 128 B per lane and stage)
+template <int WT> constexpr int g_nsw() { return (WT == MOE_W_Q4 || WT == MOE_W_Q3) ? 4 : 2; }
+template <int WT> constexpr int g_bn() { return 64 * g_nsw<WT>(); }
+// vm operations per lane and stage for the weights (loads of all subtiles)
+template <int WT> constexpr int b_vm_per_stage() {
+  return g_nsw<WT>() * ((WT == MOE_W_Q4) ? 2 : (WT == MOE_W_Q3) ? 4 : (WT == MOE_W_BF16) ? 4 : 8);
 }
 
 template <int WT, int KIND>
-__global__ __launch_bounds__(G_THREADS) void k_pf_gemm(GemmArgs g) {
-  __shared__ __align__(16) uint16_t sA[PF_BM * G_LDA];
-  __shared__ __align__(16) uint16_t sB[G_BN * G_LDA];
+__global__ __launch_bounds__(G_THREADS, 2) void k_pf_gemm(GemmArgs g) {
+  __shared__ __align__(16) uint4 sA0[G_SLOT_U4];
+  __shared__ __align__(16) uint4 sA1[G_SLOT_U4];
   __shared__ int s_row[PF_BM];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: wave-derived offsets live in SGPRs
+  constexpr int NSW = g_nsw<WT>();
+  constexpr int BN = g_bn<WT>();
 
-  // ---- which expert / rows
-  int e = 0, m0 = 0, M = 0, pos0 = 0;
+  // ---- tile
+  const int NT = (g.N + BN - 1) / BN;
+  const int mt_total = g.offsets ? g.tile_start[g.E] : (g.M_total + PF_BM - 1) / PF_BM;
+  const int total = mt_total * NT;
+  const int per = (total + 7) >> 3;
+  const int ix = blockIdx.x >> 3;
+  const int logical = (blockIdx.x & 7) * per + ix;
+  if (ix >= per || logical >= total) return;
+
+  int e = 0, m0 = 0, M = 0, pos0 = 0, nt = 0;
   if (g.offsets) {
-    const int tile = blockIdx.x;
-    if (tile >= g.tile_start[g.E]) return;
-    int lo = 0, hi = g.E - 1;  // largest e with tile_start[e] <= tile
+    const int q = logical / NT;
+    int lo = 0, hi = g.E - 1;  // largest e with tile_start[e] <= q (a non-empty expert)
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
-      if (g.tile_start[mid] <= tile) lo = mid; else hi = mid - 1;
+      if (g.tile_start[mid] <= q) lo = mid; else hi = mid - 1;
     }
     e = lo;
-    m0 = (tile - g.tile_start[e]) * PF_BM;
+    const int ntiles = g.tile_start[e + 1] - g.tile_start[e];
+    const int pos = logical - NT * g.tile_start[e];
+    nt = pos / ntiles;
+    m0 = (pos - nt * ntiles) * PF_BM;
     const int cnt = g.offsets[e + 1] - g.offsets[e];
     M = min(PF_BM, cnt - m0);
     pos0 = g.offsets[e] + m0;
   } else {
-    m0 = blockIdx.x * PF_BM;
-    if (m0 >= g.M_total) return;
+    nt = logical / mt_total;
+    m0 = (logical - nt * mt_total) * PF_BM;
     M = min(PF_BM, g.M_total - m0);
     pos0 = m0;
   }
-  const int n0 = blockIdx.y * G_BN;
+  const int n0 = nt * BN;
   const uint8_t* w = g.w + (size_t)e * g.w_stride;
   const uint16_t* wsc = g.ws ? g.ws + (size_t)e * g.ws_stride : nullptr;
-  // A row index (into g.a) for each tile row
   if (tid < PF_BM) {
-    int r = -1;
+    int r = 0;  // rows past M read row 0 of the matrix (finite values; their outputs are dropped)
     if (tid < M) {
       const int pos = pos0 + tid;
-      if (KIND == GK_GATE_UP && g.perm) r = g.perm[pos] / g.k;
-      else r = pos;
+      r = (KIND == GK_GATE_UP && g.perm) ? g.perm[pos] / g.k : pos;
     }
     s_row[tid] = r;
   }
   __syncthreads();
 
-  const int nsub = (M + 15) >> 4;  // active 16-row subtiles (wave-uniform)
-  floatx4_t acc[G_MSUB][4];
+  const int nsub = (M + 15) >> 4;  // active 16-row subtiles (uniform)
+  floatx4_t acc[G_MSUB][NSW];
 #pragma unroll
   for (int i = 0; i < G_MSUB; i++)
 #pragma unroll
-    for (int j = 0; j < 4; j++) acc[i][j] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < NSW; j++) acc[i][j] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 
-  // loaders: A: thread -> (row tid/2, 16 elements at 16*(tid&1)); B: thread -> weight row n0 + tid
-  const int arow = tid >> 1, ahalf = tid & 1;
-  const int asrc = s_row[arow];
-  const int bn = n0 + tid;
-  const int nsteps = g.K / G_BK;
-  uint4 ra0 = make_uint4(0, 0, 0, 0), ra1 = make_uint4(0, 0, 0, 0);
-  uint32_t rb[32];
-  float rs = 0.0f;
-  auto load_step = [&](int s) {
-    if (asrc >= 0) {
-      const uint4* src = reinterpret_cast<const uint4*>(g.a + (size_t)asrc * g.K + s * G_BK + 16 * ahalf);
-      ra0 = src[0];
-      ra1 = src[1];
+  const int nst = (g.K + G_BK - 1) / G_BK;
+  // A DMA: wave w, load i covers slot rows 4 (G_ALOADS w + i) .. +3; lane -> row + lane / 16, position
+  // lane % 16 holding chunk (lane % 16) ^ (row % 16)
+  // The issue helpers derive their per-lane offsets from an opaque copy of the
+  // lane index, so the compiler recomputes them (a few integer ops) at each
+  // stage instead of keeping dozens of loop invariants live across the loop.
+  auto issue_a = [&](int s, uint4* slot) {
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+#pragma unroll
+    for (int i = 0; i < G_ALOADS; i++) {
+      const int row = 4 * (G_ALOADS * wave + i) + (ln >> 4);
+      const int k = s * G_BK + 8 * ((ln & 15) ^ (row & 15));
+      const uint16_t* src = g.a + (size_t)s_row[row] * g.K + (k < g.K ? k : 0);  // past K: a finite element (weight 0)
+      __builtin_amdgcn_global_load_lds((gbl_void_t)src, (lds_void_t)(slot + 64 * (G_ALOADS * wave + i)), 16, 0, 0);
     }
-    if (bn < g.N) load_b_chunk<WT>(g, w, wsc, bn, s, rb, rs);
   };
-  load_step(0);
-  for (int s = 0; s < nsteps; s++) {
-    // stage step s into LDS
-    {
-      uint4* da = reinterpret_cast<uint4*>(sA + arow * G_LDA + 16 * ahalf);
-      da[0] = ra0;
-      da[1] = ra1;
-      uint32_t bq[16];
-      if (bn < g.N) {
-        dequant_b_chunk<WT>(rb, rs, bq);
-      } else {
+  // B: lane -> (row n = lane % 16 of each of the wave's 4 subtiles, K block j = lane / 16)
+  const int bj = lane >> 4;
+  const int nblk = g.K >> 5;
+  BRaw<WT> rb0[NSW];
+  // lane's block of stage s: 4 s + bj; rows past N read row N - 1, blocks past K the stage's first block
+  auto issue_b = [&](int s, BRaw<WT> (&r)[NSW]) {
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const int j = ln >> 4;
+    const bool okb = 4 * s + j < nblk;
+    const uint32_t blk = (uint32_t)(okb ? 4 * s + j : 4 * s);
 #pragma unroll
-        for (int i = 0; i < 16; i++) bq[i] = 0;
+    for (int sub = 0; sub < NSW; sub++) {
+      const int n = n0 + 16 * NSW * wave + (ln & 15) + 16 * sub;
+      const bool ok = okb && n < g.N;
+      const uint32_t cell = blk * (uint32_t)g.N + (uint32_t)(n < g.N ? n : g.N - 1);
+      load_b<WT>(w, wsc, (uint32_t)g.N, cell, ok, r[sub]);
+    }
+  };
+  // All G_MSUB row subtiles are computed (rows past M hold finite or stale
+  // values whose results are never stored): no branch interrupts the MFMA
+  // stream, and the A fragments of a step are read from LDS together.
+  auto compute = [&](const uint4* A, const BRaw<WT> (&r)[NSW]) {
+    const int m = lane & 15;
+#pragma unroll
+    for (int t = 0; t < 4; t++) {
+      bf16x8_t bfrag[NSW];
+#pragma unroll
+      for (int sub = 0; sub < NSW; sub++) bfrag[sub] = frag_b<WT>(r[sub], t);
+#pragma unroll
+      for (int h = 0; h < G_MSUB; h += G_MSUB / 2) {  // row subtiles in two halves: fewer live fragments
+        bf16x8_t afrag[G_MSUB / 2];
+#pragma unroll
+        for (int i = 0; i < G_MSUB / 2; i++)
+          afrag[i] = __builtin_bit_cast(bf16x8_t, A[(16 * (h + i) + m) * 16 + ((4 * bj + t) ^ m)]);
+#pragma unroll
+        for (int i = 0; i < G_MSUB / 2; i++)
+#pragma unroll
+          for (int sub = 0; sub < NSW; sub++)
+            acc[h + i][sub] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afrag[i], bfrag[sub], acc[h + i][sub], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
       }
-      uint4* db = reinterpret_cast<uint4*>(sB + tid * G_LDA);
-#pragma unroll
-      for (int i = 0; i < 4; i++) db[i] = make_uint4(bq[4 * i], bq[4 * i + 1], bq[4 * i + 2], bq[4 * i + 3]);
     }
-    __syncthreads();
-    if (s + 1 < nsteps) load_step(s + 1);
-    // MFMA: wave owns weight-row subtiles 4*wave .. 4*wave+3
-    bf16x8_t bfrag[4];
-#pragma unroll
-    for (int j = 0; j < 4; j++) {
-      const int col = (4 * wave + j) * 16 + (lane & 15);
-      bfrag[j] = *reinterpret_cast<const bf16x8_t*>(sB + col * G_LDA + 8 * (lane >> 4));
-    }
-#pragma unroll
-    for (int i = 0; i < G_MSUB; i++) {
-      if (i < nsub) {
-        const int row = 16 * i + (lane & 15);
-        const bf16x8_t afrag = *reinterpret_cast<const bf16x8_t*>(sA + row * G_LDA + 8 * (lane >> 4));
-#pragma unroll
-        for (int j = 0; j < 4; j++)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afrag, bfrag[j], acc[i][j], 0, 0, 0);
-      }
-    }
-    __syncthreads();
+  };
+  // A: two-slot LDS ring; stage s + 1 is issued once every wave has passed
+  // stage s's barrier (its slot, last read by stage s - 1, is then free) and
+  // lands while stage s computes. Weights: one register stage, reloaded as
+  // soon as a stage's MFMAs are issued; the second wave on each SIMD (another
+  // workgroup) computes while this one waits for it.
+  auto wait_stage = [&]() {
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this lane's loads of the stage have landed
+    __builtin_amdgcn_s_barrier();        // ... and every other lane's
+  };
+  issue_a(0, sA0);
+  issue_b(0, rb0);
+  for (int s = 0; s < nst; s += 2) {
+    wait_stage();
+    if (s + 1 < nst) issue_a(s + 1, sA1);
+    compute(sA0, rb0);
+    if (s + 1 >= nst) break;
+    issue_b(s + 1, rb0);
+    wait_stage();
+    if (s + 2 < nst) issue_a(s + 2, sA0);
+    compute(sA1, rb0);
+    if (s + 2 < nst) issue_b(s + 2, rb0);
   }
-  // ---- epilogue. acc[i][j] lane l: weight row (4*wave + j)*16 + (l & 15) of the tile,
+
+  // ---- epilogue. acc[i][j] lane l: weight row n0 + 16 NSW wave + 16 j + (l & 15),
   //      token rows 16 i + 4 (l >> 4) + r
   if (KIND == GK_GATE_UP) {
-    // subtiles (4w, 4w+1) = gate/up rows of group 2w of the tile, (4w+2, 4w+3) = group 2w+1
+    // subtiles (2 gg, 2 gg + 1) = gate/up rows of interleave group n0/32 + (NSW/2) wave + gg
     const int I = g.N / 2;
 #pragma unroll
     for (int i = 0; i < G_MSUB; i++) {
       if (i < nsub) {
 #pragma unroll
-        for (int gg = 0; gg < 2; gg++) {
-          const int col = (n0 / 32 + 2 * wave + gg) * 16 + (lane & 15);
+        for (int gg = 0; gg < NSW / 2; gg++) {
+          const int col = (n0 / 32 + (NSW / 2) * wave + gg) * 16 + (lane & 15);
 #pragma unroll
           for (int r = 0; r < 4; r++) {
             const int m = 16 * i + 4 * (lane >> 4) + r;
@@ -427,8 +528,8 @@ __global__ __launch_bounds__(G_THREADS) void k_pf_gemm(GemmArgs g) {
     for (int i = 0; i < G_MSUB; i++) {
       if (i < nsub) {
 #pragma unroll
-        for (int j = 0; j < 4; j++) {
-          const int col = n0 + (4 * wave + j) * 16 + (lane & 15);
+        for (int j = 0; j < NSW; j++) {
+          const int col = n0 + 16 * NSW * wave + 16 * j + (lane & 15);
 #pragma unroll
           for (int r = 0; r < 4; r++) {
             const int m = 16 * i + 4 * (lane >> 4) + r;
@@ -507,7 +608,11 @@ hipError_t launch_route(const LayerDev& L, const uint16_t* x, int T, int32_t* id
 
 template <int WT, int KIND>
 static void gemm_launch(int kc, const GemmArgs& g, int tiles_x, hipStream_t st) {
-  (void)launch_k(kc, k_pf_gemm<WT, KIND>, dim3(tiles_x, (g.N + G_BN - 1) / G_BN), dim3(G_THREADS), 0, st, g);
+  // tiles_x: an upper bound on the M tiles; the kernel reads the real count and
+  // maps workgroups XCD-major, so the grid is a multiple of 8
+  const int nt = (g.N + g_bn<WT>() - 1) / g_bn<WT>();
+  const int total = tiles_x * nt;
+  (void)launch_k(kc, k_pf_gemm<WT, KIND>, dim3(8 * ((total + 7) / 8)), dim3(G_THREADS), 0, st, g);
 }
 
 template <int KIND>
