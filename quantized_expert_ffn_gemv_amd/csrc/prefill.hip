@@ -1,6 +1,6 @@
 // Prefill path: T tokens through one MoE layer.
 //
-//   k_pf_router      router logits, fp64 accumulation (LDS-tiled)
+//   k_pf_router      router logits, fp64 MFMA (exact products, fp64 sums)
 //   k_pf_topk        ordered top-k and renormalised gates, one wave per token
 //   k_pf_count       per-block expert histograms (LDS atomics: order-free)
 //   k_pf_scan        exclusive scans: expert offsets, per-block bases, GEMM tiles
@@ -21,55 +21,97 @@ namespace moe {
 // ---------------------------------------------------------------------------
 // Router: logits[t][e] = sum_h W[e][h] x[t][h] + b[e] in fp64
 // ---------------------------------------------------------------------------
-constexpr int RT_M = 64, RT_N = 64, RT_K = 16;
+// fp64 MFMA (v_mfma_f64_16x16x4f64): an fp32 weight times a bf16 activation
+// is exact in fp64 and the sum accumulates in fp64, as the definition has it.
+// Operand layout of the instruction: A[m][k] in lane 16k + m, B[k][n] in lane
+// 16k + n, D[m][n] in lane 16 (m % 4) + n, element m / 4. In each 16-wide
+// hidden step lane (k, .) supplies hidden positions 4k .. 4k+3, one per MFMA
+// step j (the same permutation on both operands), so it loads 4 consecutive
+// weights (16 B) and 4 consecutive activations (8 B) per step.
+// Tile: workgroup 64 tokens x 128 experts, wave 32 tokens x 64 experts.
+constexpr int RT_TM = 64, RT_TN = 128;
+
+typedef double double4_t __attribute__((ext_vector_type(4)));
 
 __global__ __launch_bounds__(256) void k_pf_router(const float* __restrict__ W, const float* __restrict__ bias,
                                                     const uint16_t* __restrict__ x, int T, int E, int H,
                                                     double* __restrict__ logits) {
-  __shared__ double sa[RT_K][RT_M + 1];
-  __shared__ double sb[RT_K][RT_N + 1];
-  const int tid = threadIdx.x;
-  const int m0 = blockIdx.x * RT_M, n0 = blockIdx.y * RT_N;
-  const int tm = tid / 16, tn = tid % 16;  // 4x4 outputs each: rows tm + 16 i, cols tn + 16 j
-  double acc[4][4];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int t0 = blockIdx.x * RT_TM + 32 * (wave & 1);
+  const int e0 = blockIdx.y * RT_TN + 64 * (wave >> 1);
+  const int kq = lane >> 4, r16 = lane & 15;
+  // rows this lane loads (clamped into range; results for rows past T / E are not stored)
+  const uint16_t* xa[2];
+  const float* wb[4];
 #pragma unroll
-  for (int i = 0; i < 4; i++)
-#pragma unroll
-    for (int j = 0; j < 4; j++) acc[i][j] = 0.0;
-  for (int k0 = 0; k0 < H; k0 += RT_K) {
-    // 64 x 16 of each operand: 1024 values, 4 per thread
-#pragma unroll
-    for (int r = 0; r < 4; r++) {
-      const int i = tid + 256 * r;
-      const int row = i / RT_K, kk = i % RT_K;
-      const int t = m0 + row, e = n0 + row;
-      sa[kk][row] = (t < T) ? (double)bf16_to_f32(x[(size_t)t * H + k0 + kk]) : 0.0;
-      sb[kk][row] = (e < E) ? (double)W[(size_t)e * H + k0 + kk] : 0.0;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int kk = 0; kk < RT_K; kk++) {
-      double a[4], b[4];
-#pragma unroll
-      for (int i = 0; i < 4; i++) a[i] = sa[kk][tm + 16 * i];
-#pragma unroll
-      for (int j = 0; j < 4; j++) b[j] = sb[kk][tn + 16 * j];
-#pragma unroll
-      for (int i = 0; i < 4; i++)
-#pragma unroll
-        for (int j = 0; j < 4; j++) acc[i][j] = __builtin_fma(a[i], b[j], acc[i][j]);
-    }
-    __syncthreads();
+  for (int i = 0; i < 2; i++) {
+    const int t = t0 + 16 * i + r16;
+    xa[i] = x + (size_t)(t < T ? t : T - 1) * H + 4 * kq;
   }
 #pragma unroll
-  for (int i = 0; i < 4; i++) {
-    const int t = m0 + tm + 16 * i;
+  for (int j = 0; j < 4; j++) {
+    const int e = e0 + 16 * j + r16;
+    wb[j] = W + (size_t)(e < E ? e : E - 1) * H + 4 * kq;
+  }
+  double4_t acc[2][4];
+#pragma unroll
+  for (int i = 0; i < 2; i++)
+#pragma unroll
+    for (int j = 0; j < 4; j++) acc[i][j] = double4_t{0.0, 0.0, 0.0, 0.0};
+  uint2 ra[2][2];
+  float4 rb[2][4];
+  auto load = [&](int h0, int slot) {
+#pragma unroll
+    for (int i = 0; i < 2; i++) ra[slot][i] = *reinterpret_cast<const uint2*>(xa[i] + h0);
+#pragma unroll
+    for (int j = 0; j < 4; j++) rb[slot][j] = *reinterpret_cast<const float4*>(wb[j] + h0);
+  };
+  auto step = [&](int slot) {
+    double a[2][4], b[4][4];
+#pragma unroll
+    for (int i = 0; i < 2; i++) {
+      a[i][0] = (double)bf16_lo(ra[slot][i].x);
+      a[i][1] = (double)bf16_hi(ra[slot][i].x);
+      a[i][2] = (double)bf16_lo(ra[slot][i].y);
+      a[i][3] = (double)bf16_hi(ra[slot][i].y);
+    }
 #pragma unroll
     for (int j = 0; j < 4; j++) {
-      const int e = n0 + tn + 16 * j;
-      if (t < T && e < E) logits[(size_t)t * E + e] = acc[i][j] + (bias ? (double)bias[e] : 0.0);
+      b[j][0] = (double)rb[slot][j].x;
+      b[j][1] = (double)rb[slot][j].y;
+      b[j][2] = (double)rb[slot][j].z;
+      b[j][3] = (double)rb[slot][j].w;
     }
+#pragma unroll
+    for (int q = 0; q < 4; q++)
+#pragma unroll
+      for (int i = 0; i < 2; i++)
+#pragma unroll
+        for (int j = 0; j < 4; j++) acc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[i][q], b[j][q], acc[i][j], 0, 0, 0);
+  };
+  // two register stages: the loads of step s + 1 are in flight while step s computes
+  load(0, 0);
+  for (int h0 = 0; h0 < H; h0 += 32) {
+    if (h0 + 16 < H) load(h0 + 16, 1);
+    step(0);
+    if (h0 + 16 >= H) break;
+    if (h0 + 32 < H) load(h0 + 32, 0);
+    step(1);
   }
+  // D[m][n]: lane 16 (m % 4) + n, element m / 4
+#pragma unroll
+  for (int i = 0; i < 2; i++)
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      const int e = e0 + 16 * j + r16;
+      const double bv = (bias && e < E) ? (double)bias[e] : 0.0;
+#pragma unroll
+      for (int q = 0; q < 4; q++) {
+        const int t = t0 + 16 * i + 4 * q + kq;
+        if (t < T && e < E) logits[(size_t)t * E + e] = acc[i][j][q] + bv;
+      }
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -586,7 +628,7 @@ __global__ __launch_bounds__(256) void k_pf_combine(const uint16_t* __restrict__
 static hipError_t route_steps(const LayerDev& L, const uint16_t* x, int T, int32_t* idx_out, float* gate_out,
                               int32_t* counts_out, const PrefillWs& ws, hipStream_t st, bool permute) {
   const int E = L.E, k = L.k, H = L.H;
-  (void)launch_k(KC_PF_ROUTER, k_pf_router, dim3((T + RT_M - 1) / RT_M, (E + RT_N - 1) / RT_N), dim3(256), 0, st, L.router_w,
+  (void)launch_k(KC_PF_ROUTER, k_pf_router, dim3((T + RT_TM - 1) / RT_TM, (E + RT_TN - 1) / RT_TN), dim3(256), 0, st, L.router_w,
                      L.router_b, x, T, E, H, ws.logits);
   (void)launch_k(KC_PF_TOPK, k_pf_topk, dim3((T + 3) / 4), dim3(256), 0, st, ws.logits, T, E, k, ws.idx, ws.gates, idx_out,
                      gate_out);
