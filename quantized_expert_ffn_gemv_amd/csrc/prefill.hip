@@ -584,6 +584,273 @@ __global__ __launch_bounds__(G_THREADS, 2) void k_pf_gemm(GemmArgs g) {
 }
 
 // ---------------------------------------------------------------------------
+// Grouped GEMM over quantised weights (Q4, Q3). Same tiles, A ring and
+// fragment mapping as k_pf_gemm, but the weights also travel memory -> LDS by
+// DMA, into a two-slot ring of per-wave regions (lane-private: 16 B per lane
+// and subtile; Q3's three words in three 256-byte rows), so a whole stage of
+// weights and A rows is in flight while the previous stage computes, with no
+// weight registers held across it. LDS: 2 x 24 KB (A) + 2 x 16 KB (weights)
+// = 80 KB per workgroup, two workgroups per CU; the gathered row of each of a
+// lane's A loads is kept in a register instead of an LDS table.
+//
+// Q4 dequantisation, word t of a lane's block (elements 8t .. 8t+7: element
+// 8t + 2p at nibble p, 8t + 2p + 1 at nibble p + 4): pairs 0 and 2 are masked
+// to the low nibble of each half, fp16(1024 + code); pairs 1 and 3 keep their
+// nibble in bits 4..7, fp16(1024 + 16 code). Both are exact in one fma each:
+// s (code - 8) = fma(v, s, -1032 s) = fma(v, s / 16, -72 s) (every product
+// and sum fits fp32), then one rounding to bf16.
+// ---------------------------------------------------------------------------
+struct Q4Scale { float s, s16, nb_even, nb_odd; };
+__device__ __forceinline__ Q4Scale q4_scale(uint32_t sbits) {
+  const float sc = f16_to_f32((uint16_t)sbits);
+  return {sc, sc * 0.0625f, sc * -1032.0f, sc * -72.0f};
+}
+__device__ __forceinline__ bf16x8_t q4_frag(uint32_t wd, const Q4Scale& q, uint32_t magic) {
+  const uint32_t w8 = wd >> 8;
+  const uint32_t p[4] = {(wd & 0x000F000Fu) | magic, (wd & 0x00F000F0u) | magic,
+                         (w8 & 0x000F000Fu) | magic, (w8 & 0x00F000F0u) | magic};
+  uint32_t o[4];
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    float lo, hi;
+    if (i & 1) f16pair_dequant(p[i], q.s16, q.nb_odd, lo, hi);
+    else f16pair_dequant(p[i], q.s, q.nb_even, lo, hi);
+    o[i] = pack_bf16x2(lo, hi);
+  }
+  return __builtin_bit_cast(bf16x8_t, make_uint4(o[0], o[1], o[2], o[3]));
+}
+
+constexpr int GQ_NSW = 4;                       // 16-column subtiles per wave
+constexpr int GQ_BN = 64 * GQ_NSW;              // weight rows per tile
+constexpr int GQ_REGION = 64 * 16;              // bytes per (wave, subtile) weight region
+constexpr int GQ_BSLOT = (G_THREADS / 64) * GQ_NSW * GQ_REGION;  // 16 KB
+
+template <int WT, int KIND>
+__global__ __launch_bounds__(G_THREADS, 2) void k_pf_gemm_q(GemmArgs g) {
+  static_assert(WT == MOE_W_Q4 || WT == MOE_W_Q3, "quantised weights only");
+  __shared__ __align__(16) uint4 sA0[G_SLOT_U4];
+  __shared__ __align__(16) uint4 sA1[G_SLOT_U4];
+  __shared__ __align__(16) uint8_t sB0[GQ_BSLOT];
+  __shared__ __align__(16) uint8_t sB1[GQ_BSLOT];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  constexpr int NSW = GQ_NSW, BN = GQ_BN;
+
+  // ---- tile (as k_pf_gemm)
+  const int NT = (g.N + BN - 1) / BN;
+  const int mt_total = g.offsets ? g.tile_start[g.E] : (g.M_total + PF_BM - 1) / PF_BM;
+  const int total = mt_total * NT;
+  const int per = (total + 7) >> 3;
+  const int ix = blockIdx.x >> 3;
+  const int logical = (blockIdx.x & 7) * per + ix;
+  if (ix >= per || logical >= total) return;
+  int e = 0, m0 = 0, M = 0, pos0 = 0, nt = 0;
+  if (g.offsets) {
+    const int q = logical / NT;
+    int lo = 0, hi = g.E - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (g.tile_start[mid] <= q) lo = mid; else hi = mid - 1;
+    }
+    e = lo;
+    const int ntiles = g.tile_start[e + 1] - g.tile_start[e];
+    const int pos = logical - NT * g.tile_start[e];
+    nt = pos / ntiles;
+    m0 = (pos - nt * ntiles) * PF_BM;
+    M = min(PF_BM, g.offsets[e + 1] - g.offsets[e] - m0);
+    pos0 = g.offsets[e] + m0;
+  } else {
+    nt = logical / mt_total;
+    m0 = (logical - nt * mt_total) * PF_BM;
+    M = min(PF_BM, g.M_total - m0);
+    pos0 = m0;
+  }
+  const int n0 = nt * BN;
+  const uint8_t* w = g.w + (size_t)e * g.w_stride;
+  const uint16_t* wsc = g.ws + (size_t)e * g.ws_stride;
+
+  // A rows of this lane's loads: load i covers slot rows 4 (G_ALOADS wave + i) + lane / 16
+  // (rows past M read row 0 of the matrix: finite values whose results are dropped)
+  uint32_t arow[G_ALOADS];
+#pragma unroll
+  for (int i = 0; i < G_ALOADS; i++) {
+    const int row = 4 * (G_ALOADS * wave + i) + (lane >> 4);
+    int r = 0;
+    if (row < M) r = (KIND == GK_GATE_UP && g.perm) ? g.perm[pos0 + row] / g.k : pos0 + row;
+    arow[i] = (uint32_t)r;
+  }
+
+  floatx4_t acc[G_MSUB][NSW];
+#pragma unroll
+  for (int i = 0; i < G_MSUB; i++)
+#pragma unroll
+    for (int j = 0; j < NSW; j++) acc[i][j] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+
+  const int nst = (g.K + G_BK - 1) / G_BK;
+  const int nblk = g.K >> 5;
+  const int bj = lane >> 4;
+  // fp16 scale bits of the lane's blocks and, beside them, which blocks are in
+  // range (applied after the stage's wait: a use right after the load would
+  // wait for every load in flight)
+  uint32_t scl[2][NSW], okm[2];
+
+  // one stage's loads into ring slot (sa, sb, scales sc, in-range bits ok)
+  auto issue = [&](int s, uint4* sa, uint8_t* sb, uint32_t (&sc)[NSW], uint32_t& okbits) {
+    int ln = lane;
+    asm volatile("" : "+v"(ln));  // recompute lane offsets per stage rather than hold them
+#pragma unroll
+    for (int i = 0; i < G_ALOADS; i++) {
+      const int row = 4 * (G_ALOADS * wave + i) + (ln >> 4);
+      const int k = s * G_BK + 8 * ((ln & 15) ^ (row & 15));
+      const uint16_t* src = g.a + (size_t)arow[i] * g.K + (k < g.K ? k : 0);  // past K: finite (weight 0)
+      __builtin_amdgcn_global_load_lds((gbl_void_t)src, (lds_void_t)(sa + 64 * (G_ALOADS * wave + i)), 16, 0, 0);
+    }
+    const int j = ln >> 4;
+    const bool okb = 4 * s + j < nblk;  // blocks past K (also whole stages past the end): scale 0
+    const uint32_t blk = (uint32_t)min(4 * s + j, nblk - 1);
+    uint32_t bits = 0;
+#pragma unroll
+    for (int sub = 0; sub < NSW; sub++) {
+      const int n = n0 + 16 * NSW * wave + (ln & 15) + 16 * sub;
+      const bool ok = okb && n < g.N;
+      const uint32_t cell = blk * (uint32_t)g.N + (uint32_t)(n < g.N ? n : g.N - 1);
+      uint8_t* region = sb + (wave * NSW + sub) * GQ_REGION;
+      if constexpr (WT == MOE_W_Q4) {
+        __builtin_amdgcn_global_load_lds((gbl_void_t)(w + cell * 16u), (lds_void_t)region, 16, 0, 0);
+      } else {
+#pragma unroll
+        for (int q = 0; q < 3; q++)
+          __builtin_amdgcn_global_load_lds((gbl_void_t)(w + cell * 12u + 4u * q), (lds_void_t)(region + 256 * q), 4, 0, 0);
+      }
+      sc[sub] = wsc[cell];
+      bits |= ok ? (1u << sub) : 0u;
+    }
+    okbits = bits;
+  };
+
+  uint32_t magic = F16_MAGIC2;
+  asm volatile("" : "+v"(magic));  // held in a register: one and-or per pair
+  const int m = lane & 15;
+  auto compute = [&](const uint4* A, const uint8_t* sb, const uint32_t (&sc)[NSW], uint32_t okbits) {
+    if constexpr (WT == MOE_W_Q4) {
+      Q4Scale qs[NSW];
+#pragma unroll
+      for (int sub = 0; sub < NSW; sub++) qs[sub] = q4_scale(sc[sub] & ((okbits >> sub) & 1u ? 0xFFFFu : 0u));
+#pragma unroll
+      for (int t = 0; t < 4; t++) {
+        bf16x8_t bfrag[NSW];
+#pragma unroll
+        for (int sub = 0; sub < NSW; sub++) {
+          const uint32_t wd = reinterpret_cast<const uint32_t*>(sb + (wave * NSW + sub) * GQ_REGION)[4 * lane + t];
+          bfrag[sub] = q4_frag(wd, qs[sub], magic);
+        }
+#pragma unroll
+        for (int h = 0; h < G_MSUB; h += G_MSUB / 2) {
+          bf16x8_t afrag[G_MSUB / 2];
+#pragma unroll
+          for (int i = 0; i < G_MSUB / 2; i++)
+            afrag[i] = __builtin_bit_cast(bf16x8_t, A[(16 * (h + i) + m) * 16 + ((4 * bj + t) ^ m)]);
+#pragma unroll
+          for (int i = 0; i < G_MSUB / 2; i++)
+#pragma unroll
+            for (int sub = 0; sub < NSW; sub++)
+              acc[h + i][sub] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afrag[i], bfrag[sub], acc[h + i][sub], 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+    } else {
+      BRaw<WT> r[NSW];
+#pragma unroll
+      for (int sub = 0; sub < NSW; sub++) {
+        const uint32_t* p = reinterpret_cast<const uint32_t*>(sb + (wave * NSW + sub) * GQ_REGION) + lane;
+        r[sub].l0 = p[0];
+        r[sub].l1 = p[64];
+        r[sub].hb = p[128];
+        r[sub].s = sc[sub] & ((okbits >> sub) & 1u ? 0xFFFFu : 0u);
+      }
+#pragma unroll
+      for (int t = 0; t < 4; t++) {
+        bf16x8_t bfrag[NSW];
+#pragma unroll
+        for (int sub = 0; sub < NSW; sub++) bfrag[sub] = frag_b<WT>(r[sub], t);
+#pragma unroll
+        for (int h = 0; h < G_MSUB; h += G_MSUB / 2) {
+          bf16x8_t afrag[G_MSUB / 2];
+#pragma unroll
+          for (int i = 0; i < G_MSUB / 2; i++)
+            afrag[i] = __builtin_bit_cast(bf16x8_t, A[(16 * (h + i) + m) * 16 + ((4 * bj + t) ^ m)]);
+#pragma unroll
+          for (int i = 0; i < G_MSUB / 2; i++)
+#pragma unroll
+            for (int sub = 0; sub < NSW; sub++)
+              acc[h + i][sub] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afrag[i], bfrag[sub], acc[h + i][sub], 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+    }
+  };
+  auto wait_stage = [&]() {
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this lane's loads of the stage have landed
+    __builtin_amdgcn_s_barrier();        // ... and every other lane's
+  };
+  // Stage s + 1 is issued right after stage s's barrier: its A slot and this
+  // wave's weight region were last read in stage s - 1, which every wave has
+  // finished. The loop runs an even number of stages with no exit in between
+  // (one exit keeps the accumulators in place): stages past the end load
+  // in-range addresses with zero scales and add nothing; the wait after the
+  // loop drains the last issue.
+  const int nst2 = (nst + 1) & ~1;
+  issue(0, sA0, sB0, scl[0], okm[0]);
+  for (int s = 0; s < nst2; s += 2) {
+    wait_stage();
+    issue(s + 1, sA1, sB1, scl[1], okm[1]);
+    compute(sA0, sB0, scl[0], okm[0]);
+    wait_stage();
+    issue(s + 2, sA0, sB0, scl[0], okm[0]);
+    compute(sA1, sB1, scl[1], okm[1]);
+  }
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+
+  // ---- epilogue (as k_pf_gemm)
+  const int nsub = (M + 15) >> 4;
+  if (KIND == GK_GATE_UP) {
+    const int I = g.N / 2;
+#pragma unroll
+    for (int i = 0; i < G_MSUB; i++) {
+      if (i < nsub) {
+#pragma unroll
+        for (int gg = 0; gg < NSW / 2; gg++) {
+          const int col = (n0 / 32 + (NSW / 2) * wave + gg) * 16 + (lane & 15);
+#pragma unroll
+          for (int r = 0; r < 4; r++) {
+            const int mm = 16 * i + 4 * (lane >> 4) + r;
+            if (mm < M && col < I) {
+              const float gv = acc[i][2 * gg][r], uv = acc[i][2 * gg + 1][r];
+              g.out[(size_t)(pos0 + mm) * I + col] = f32_to_bf16(silu_f32(gv) * uv);
+            }
+          }
+        }
+      }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < G_MSUB; i++) {
+      if (i < nsub) {
+#pragma unroll
+        for (int j = 0; j < NSW; j++) {
+          const int col = n0 + 16 * NSW * wave + 16 * j + (lane & 15);
+#pragma unroll
+          for (int r = 0; r < 4; r++) {
+            const int mm = 16 * i + 4 * (lane >> 4) + r;
+            if (mm < M && col < g.N) g.out[(size_t)(pos0 + mm) * g.N + col] = f32_to_bf16(acc[i][j][r]);
+          }
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Combine: y[t] = sum_j g[t][j] Y[inv[t*k+j]] + Ys[t]
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_pf_combine(const uint16_t* __restrict__ Y, const uint16_t* __restrict__ Ys,
@@ -654,7 +921,12 @@ static void gemm_launch(int kc, const GemmArgs& g, int tiles_x, hipStream_t st) 
   // maps workgroups XCD-major, so the grid is a multiple of 8
   const int nt = (g.N + g_bn<WT>() - 1) / g_bn<WT>();
   const int total = tiles_x * nt;
-  (void)launch_k(kc, k_pf_gemm<WT, KIND>, dim3(8 * ((total + 7) / 8)), dim3(G_THREADS), 0, st, g);
+  if constexpr (WT == MOE_W_Q4 || WT == MOE_W_Q3) {
+    static_assert(GQ_BN == g_bn<WT>(), "tile width");
+    (void)launch_k(kc, k_pf_gemm_q<WT, KIND>, dim3(8 * ((total + 7) / 8)), dim3(G_THREADS), 0, st, g);
+  } else {
+    (void)launch_k(kc, k_pf_gemm<WT, KIND>, dim3(8 * ((total + 7) / 8)), dim3(G_THREADS), 0, st, g);
+  }
 }
 
 template <int KIND>
