@@ -273,6 +273,33 @@ def moe_residual_add(h, y, stream=None):
     _check(lib().moe_residual_add(_tptr(h), _tptr(y), T, H, _stream(stream)), "moe_residual_add")
 
 
+class StackBuffers:
+    """Per-call tensors of a layer stack over T tokens (z, y, routing)."""
+
+    def __init__(self, T: int, H: int, k: int, device="cuda"):
+        import torch
+        self.z = torch.empty((T, H), dtype=torch.int16, device=device)
+        self.y = torch.empty((T, H), dtype=torch.int16, device=device)
+        self.idx = torch.empty((T, k), dtype=torch.int32, device=device)
+        self.gate = torch.empty((T, k), dtype=torch.float32, device=device)
+
+
+def stack_forward(layers, h, ws, decode: bool, buf: "StackBuffers", eps: float = 1e-6, stream=None,
+                  each_layer=None):
+    """Pre-norm residual stack of MoE layers over h (bf16 [T, H], updated in
+    place): per layer z = RMSNorm(h), y = MoE(z), h = bf16(h + y). Every step
+    is a library call on the same stream; each_layer(l, buf), when given, runs
+    after layer l's MoE call and before its residual add."""
+    fwd = moe_forward_decode if decode else moe_forward_prefill
+    for l, layer in enumerate(layers):
+        moe_rmsnorm(h, buf.z, eps, stream)
+        fwd(layer, buf.z, buf.y, ws, buf.idx, buf.gate, stream)
+        if each_layer is not None:
+            each_layer(l, buf)
+        moe_residual_add(h, buf.y, stream)
+    return h
+
+
 # ---------------------------------------------------------------------------
 # kernel timer
 # ---------------------------------------------------------------------------

@@ -210,11 +210,12 @@ def expert_codes(seed: int, wid: int, layer: int, e: int, H: int, I: int, bits: 
     return g, gs, u, us, d, ds
 
 
-def make_layer(name: str, layer: int = 0, seed: int = 0, experts: bool = True) -> HostLayer:
+def make_layer(name: str, layer: int = 0, seed: int = 0, experts: bool = True, threads: int = 1) -> HostLayer:
     """Generate the weights of layer `layer` of workload `name`.
 
     experts=False skips the routed experts (for workloads where only a few
-    experts are regenerated on demand with expert_codes)."""
+    experts are regenerated on demand with expert_codes). threads > 1 makes
+    the experts on a thread pool (same values: each expert has its own keys)."""
     c = WORKLOADS[name]
     wid, E, k, H, I = c["id"], c["E"], c["k"], c["H"], c["I"]
     rw = normal_f32(key(seed, wid, layer, T_ROUTER_W, 0), (E, H), c["router_sd"])
@@ -233,9 +234,16 @@ def make_layer(name: str, layer: int = 0, seed: int = 0, experts: bool = True) -
             L.down_q = np.empty((E, H, I), np.int8)
             L.gate_s = np.empty((E, I, H // 32), np.uint16); L.up_s = np.empty((E, I, H // 32), np.uint16)
             L.down_s = np.empty((E, H, I // 32), np.uint16)
-            for e in range(E):
+            def one(e):
                 (L.gate_q[e], L.gate_s[e], L.up_q[e], L.up_s[e], L.down_q[e],
                  L.down_s[e]) = expert_codes(seed, wid, layer, e, H, I, bits)
+            if threads > 1:
+                from concurrent.futures import ThreadPoolExecutor
+                with ThreadPoolExecutor(max_workers=threads) as ex:
+                    list(ex.map(one, range(E)))
+            else:
+                for e in range(E):
+                    one(e)
     sh = c["shared"]
     if sh is not None:
         L.shared = sh
