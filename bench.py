@@ -13,7 +13,9 @@ the 4096-token prefill of a layer of the same shape, the per-kernel roofline
 of the dominant decode kernel (HIP events on the launch stream), and the CPU
 oracle timed on a bounded sample of the headline workload.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-prefill] [--no-cpu]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-prefill] [--no-cpu] [--stack]
+       (--stack adds the 48-layer stack: 512 batch-1 decode tokens and a 32768-token
+        prefill through 48 resident layers)
        python bench.py --profile-sample   (short eager run for hardware-counter passes:
                                            a 256 MiB elementwise copy, then 32 decode
                                            tokens and one 4096-token prefill)
@@ -192,6 +194,97 @@ def profile_sample(moe, torch, synth):
     log("profile sample: prefill %d tokens done" % xp.shape[0])
 
 
+def run_stack(moe, torch, synth, steps):
+    """The 48-layer stack (pre-norm RMSNorm, MoE layer, bf16 residual; 44 GB of
+    weights resident): 512 batch-1 decode tokens, each one HIP-graph replay of
+    the 48 layers, and the 32768-token prefill in one pass."""
+    name = "stack48_q4"
+    c = synth.WORKLOADS[name]
+    layers = []
+    t0 = time.perf_counter()
+    for l in range(c["layers"]):
+        layers.append(moe.DeviceLayer(synth.make_layer(name, layer=l, threads=16)))
+    log("stack: %d layers resident (%.1f GB) in %.0f s" % (len(layers), sum(L.weight_bytes() for L in layers) / 1e9,
+                                                          time.perf_counter() - t0))
+    dev = torch.device("cuda")
+    L0 = layers[0]
+    H, k = L0.H, L0.k
+    # decode: one graph = copy the token in, 48 layers, on a fixed buffer
+    x = synth.make_tokens(name)
+    T = x.shape[0]
+    xd = torch.from_numpy(x.view(np.int16)).to(dev)
+    out = torch.empty_like(xd)
+    stage = torch.empty((1, H), dtype=torch.int16, device=dev)
+    h = torch.empty((1, H), dtype=torch.int16, device=dev)
+    ws = moe.make_workspace(L0, 1, 0)
+    buf = moe.StackBuffers(1, H, k)
+
+    def one():
+        h.copy_(stage)
+        moe.stack_forward(layers, h, ws, True, buf)
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        one()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        one()
+
+    def tokens():
+        for t in range(T):
+            stage.copy_(xd[t:t + 1])
+            g.replay()
+            out[t:t + 1].copy_(h)
+
+    tokens()
+    torch.cuda.synchronize()
+    reps = max(1, steps // 10)
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        tokens()
+    torch.cuda.synchronize()
+    dec_s = (time.perf_counter() - t0) / (reps * T)
+    moe.moe_workspace_check(ws)
+    gu, dn, sgu, sdn = decode_expert_bytes(L0)
+    per_tok = len(layers) * (L0.k * (gu + dn) + sgu + sdn)
+    del g
+    # prefill: all tokens, one pass through the 48 layers
+    xp = synth.make_prefill_tokens(name)
+    Tp = xp.shape[0]
+    xpd = torch.from_numpy(xp.view(np.int16)).to(dev)
+    hp = torch.empty_like(xpd)
+    wsp = moe.make_workspace(L0, Tp, 1)
+    bufp = moe.StackBuffers(Tp, H, k)
+
+    def prefill():
+        hp.copy_(xpd)
+        moe.stack_forward(layers, hp, wsp, False, bufp)
+
+    prefill()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    prefill()
+    torch.cuda.synchronize()
+    pf_s = time.perf_counter() - t0
+    flops = len(layers) * Tp * 2.0 * (L0.k + 1) * 3 * H * L0.I
+    return {
+        "workload": "48-layer stack: each layer 512 experts top-10 + shared, hidden 2048, intermediate 512, Q4 "
+                    "experts, bf16 shared, fp32 router with its own Zipf bias; pre-norm RMSNorm, bf16 residual",
+        "decode_tokens": T,
+        "decode_us_per_token": round(dec_s * 1e6, 2),
+        "decode_tokens_per_s": round(1.0 / dec_s, 1),
+        "decode_expert_bytes_per_token": per_tok,
+        "decode_effective_expert_GBps": round(per_tok / dec_s / 1e9, 1),
+        "prefill_tokens": Tp,
+        "prefill_ms": round(pf_s * 1e3, 2),
+        "prefill_tokens_per_s": round(Tp / pf_s, 1),
+        "prefill_expert_TFLOPs": round(flops / pf_s / 1e12, 1),
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -200,6 +293,7 @@ def main():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--profile-sample", action="store_true")
+    ap.add_argument("--stack", action="store_true", help="also run the 48-layer stack (about a minute to build)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (use --gpus 1)", file=sys.stderr)
@@ -330,6 +424,13 @@ def main():
             "kernels_avg_us": {k: round(v[1] * 1e3, 2) for k, v in kp.items()},
         }
         log("prefill:", json.dumps(result["prefill"]))
+
+    # ---------------------------------------------------------------- 48-layer stack (opt-in)
+    if args.stack:
+        log("48-layer stack ...")
+        Lp = L = None  # release the single layers first
+        result["stack48"] = run_stack(moe, torch, synth, args.steps)
+        log("stack48:", json.dumps(result["stack48"]))
 
     # ---------------------------------------------------------------- CPU oracle
     if not args.no_cpu:
