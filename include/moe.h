@@ -131,12 +131,15 @@ size_t moe_matrix_scales(int32_t wt, int32_t rows, int32_t K);
 size_t moe_workspace_bytes(const moe_layer *layer, int32_t max_tokens, int32_t mode);
 #define MOE_DECODE_MAX_TOKENS 8
 
-/* Workspace contract. The first 4096 bytes of a decode workspace hold the
- * counters through which the workgroups of the batch-1 decode kernel hand
- * data to each other; they must be zero before the first decode call
- * (moe_workspace_init, or any zero fill) and every call leaves them zero
- * again, so the workspace can be reused call after call and inside captured
- * HIP graphs. Calls that share one workspace must be ordered (one stream);
+/* Workspace contract. A decode workspace must be all zero before its first
+ * decode call: moe_workspace_init zero-fills all ws_bytes (as would any zero
+ * fill). Its first 4096 bytes hold the counts and the call epoch of the
+ * batch-1 decode kernel; the rest holds the tagged words through which its
+ * workgroups hand data to each other (a word counts only when it carries the
+ * current call's tag, so memory left by an earlier owner must not be reused
+ * uninitialised). Every call leaves the counts zero and advances the epoch,
+ * so the workspace can be reused call after call and inside captured HIP
+ * graphs. Calls that share one workspace must be ordered (one stream);
  * concurrent calls on one workspace race. Prefill workspaces need no
  * initialisation. */
 moe_status moe_workspace_init(void *ws, size_t ws_bytes, hipStream_t stream);

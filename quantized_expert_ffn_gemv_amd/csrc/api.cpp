@@ -105,10 +105,14 @@ size_t carve_decode(const moe_layer* L, int B, uint8_t* base, moe::DecodeWs* ws)
   w.sync = reinterpret_cast<uint32_t*>(take(DECODE_SYNC_BYTES));
   // logits: [B][E] fp64 (three kernels) or 4 rotating slots of [E] x 16 B tagged words (one kernel)
   w.logits = reinterpret_cast<double*>(take((size_t)E * 64));
-  // h: 4 rotating slots of (k+1)*I/2 tagged 8-byte words
-  w.h = reinterpret_cast<uint16_t*>(take(16 * (k + 1) * I));
-  const bool one_kernel = B == 1 && moe::decode1_fits(L->n_experts, L->hidden, L->inter, L->top_k, L->shared_wtype != MOE_W_NONE);
-  w.part = one_kernel ? nullptr : reinterpret_cast<float*>(take((size_t)B * (k * (I / 16) + I / 4) * L->hidden * 4));
+  const bool has_s = L->shared_wtype != MOE_W_NONE;
+  const bool one_kernel = B == 1 && moe::decode1_fits(L->n_experts, L->hidden, L->inter, L->top_k, has_s);
+  if (one_kernel) {
+    w.flags = reinterpret_cast<uint64_t*>(take(8 * moe::decode1_flag_words(L->n_experts, L->inter, L->top_k, has_s)));
+    w.part_words = reinterpret_cast<uint64_t*>(take(8 * moe::decode1_part_words(L->hidden, L->inter, L->top_k, has_s)));
+  } else {
+    w.part = reinterpret_cast<float*>(take((size_t)B * (k * (I / 16) + I / 4) * L->hidden * 4));
+  }
   if (ws) *ws = w;
   return off;
 }
@@ -305,7 +309,9 @@ moe_status moe_workspace_init(void* ws, size_t ws_bytes, hipStream_t stream) {
   if (!ws) return fail(MOE_ERR_NULL, "ws is required");
   if (!aligned16(ws)) return fail(MOE_ERR_ALIGN, "ws must be 16-byte aligned");
   if (ws_bytes < DECODE_SYNC_BYTES) return fail(MOE_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, DECODE_SYNC_BYTES);
-  return hip_status(moe::launch_fill(ws, DECODE_SYNC_BYTES, stream), "moe_workspace_init launch");
+  // the whole workspace: counts and epoch, and the tagged hand-off words (a
+  // word left by an earlier owner of the memory must not carry a current tag)
+  return hip_status(moe::launch_fill(ws, ws_bytes & ~(size_t)3, stream), "moe_workspace_init launch");
 }
 
 moe_status moe_workspace_check(void* ws, size_t ws_bytes, hipStream_t stream) {

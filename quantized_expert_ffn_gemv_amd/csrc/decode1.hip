@@ -5,25 +5,33 @@
 //   [0, nR)        router: 8 expert rows each, fp64 logits (an fp32 weight
 //                  times a bf16 activation is exact in fp64).
 //   [nR, +nSG)     shared expert: 8 intermediates each (16 gate/up rows),
-//                  gate/up GEMV + SwiGLU -> h (bf16).        waits: logits
+//                  gate/up GEMV + SwiGLU -> h (bf16, in LDS), then those 8
+//                  columns of the shared down matrix times h: a partial y
+//                  over all H rows.                         waits: logits
 //                  (only so the router's bytes reach the chip first; the
 //                  shared bytes then fill the memory-idle top-k window)
-//   [.., +nRG)     routed experts: (slot, 16 intermediates) each; ordered
+//   [.., +nRG)     routed experts: (slot, 32 intermediates) each; ordered
 //                  top-k from the logits, then fused dequantise-GEMV of the
-//                  32 gate/up rows + SwiGLU -> h (bf16).    waits: logits
-//   down blocks    F_RD output rows each: top-k, then all down weights of
-//                  its rows (k routed experts and the shared one) are loaded
-//                  while the gate/up roles run; y = sum_i g_i D_i h_i +
-//                  D_s h_s in a fixed order.          waits: logits, then h
-//                  Block d runs on workgroup d once its router or shared
+//                  64 gate/up rows + SwiGLU -> h (bf16, in LDS), then the
+//                  matching 32-column block of the expert's down matrix
+//                  (loaded with the gate/up rows) times h, scaled by the
+//                  slot's gate: a partial y over all H rows. waits: logits
+//   reducers       F_RD output rows each: y = the sum of the partials of
+//                  all shared and routed workgroups in a fixed order.
+//                  Reducer d runs on workgroup d once its router or shared
 //                  role is done (extra workgroups after the routed ones take
-//                  blocks beyond nR + nSG), so the whole grid fits on the
-//                  chip at once.
+//                  reducers beyond nR + nSG), so the grid fits on the chip.
+//                                                waits: every partial
 //
-// Progress: the routed gate/up workgroups wait only on the router, which
-// never waits, so they always finish; a down block waits on them, and
-// can only hold a slot they need if nR + nSG workgroups filled every slot
-// on the chip, which 256 CUs rule out.
+// The down product is split along the intermediate dimension (split-K), so
+// h never leaves the workgroup that made it and the down weights stream
+// together with the gate/up weights; the only hand-off after the top-k is
+// the partials, read by the reducers.
+//
+// Progress: the routed and shared workgroups wait only on the router, which
+// never waits, so they always finish; a reducer waits on them, and can only
+// hold a slot they need if nR + nSG workgroups filled every slot on the
+// chip, which 256 CUs rule out.
 //
 // Hand-off without cache flushes. Every value one workgroup passes to
 // another (logits, h) travels in a 64-bit word whose high half is a tag
@@ -31,13 +39,17 @@
 // agent-scope relaxed atomics: each word is single-copy atomic and coherent
 // across the chip's L2 slices on its own, and a reader uses a word only once
 // its tag is current, so no release/acquire fence (an L2 write-back or
-// invalidate per workgroup) is needed. Per-role counters are hints that
-// keep polling traffic low: one thread per workgroup spins on the counter,
-// then the words are read and checked. Every spin is bounded; one that runs
-// out sets an error bit in the workspace and lets the workgroup finish, so
-// the kernel always ends. The last workgroup to finish resets the counters
-// and advances the epoch, so the workspace is ready for the next call (and
-// for graph replay) without a memset.
+// invalidate per workgroup) is needed. Each producer workgroup also writes
+// one tagged flag word once its values are issued; a consumer polls the
+// flags of its producers (one wave, a few words per lane) and then reads and
+// checks the values. Flags are plain stores, one per producer: a shared
+// counter bumped by hundreds of producers serialises its atomics at the
+// memory side and was measured to add microseconds. Every spin is bounded;
+// one that runs out sets an error bit in the workspace and lets the
+// workgroup finish, so the kernel always ends. The last workgroup to finish
+// (a per-XCD count, then a count of the XCD groups) resets the counts and
+// advances the epoch, so the workspace is ready for the next call (and for
+// graph replay) without a memset.
 //
 // No float atomics: each value has one writer and every sum has a fixed
 // order, so results are bitwise reproducible.
@@ -51,22 +63,22 @@ constexpr int F_THREADS = 512;
 constexpr int F_RCPL = 8;                       // router float4 chunks per lane and batch
 constexpr uint64_t F_WAIT_TICKS = 1ull << 25;   // ~0.34 s of the 100 MHz wall clock
 
-// Workspace sync area (uint32 words; every counter in its own 128-byte line).
-// The logits and h counters and the epoch have one replica per XCD, so the
-// pollers of one XCD share a line of their own; producers bump every replica.
+// Workspace sync area (uint32 words; every count in its own 128-byte line).
+// The epoch has one replica per XCD group (workgroups b with b % 8 == r), so
+// the readers of one group share a line; the finish counts are per group.
 constexpr int SY_LINE = 32;                                   // words per line
-constexpr int SY_NREP = 8;                                    // replicas (XCDs)
-constexpr int SY_LOGITS = 1 * SY_LINE;                        // + r * SY_LINE
-constexpr int SY_H = (1 + SY_NREP) * SY_LINE;                 // + r * SY_LINE
-constexpr int SY_EPOCH = (1 + 2 * SY_NREP) * SY_LINE;         // + r * SY_LINE
-constexpr int SY_DONE = (1 + 3 * SY_NREP) * SY_LINE;
+constexpr int SY_NREP = 8;                                    // replicas (XCD groups)
+constexpr int SY_EPOCH = 1 * SY_LINE;                         // + r * SY_LINE
+constexpr int SY_DONEX = (1 + SY_NREP) * SY_LINE;             // + r * SY_LINE
+constexpr int SY_DONE = (1 + 2 * SY_NREP) * SY_LINE;
 constexpr int SY_ERR = 0;
-constexpr int SY_WORDS = (2 + 3 * SY_NREP) * SY_LINE;         // 3328 bytes
-constexpr int F_SLOTS = 4;  // logits/h buffers rotate over this many calls
+constexpr int SY_WORDS = (2 + 2 * SY_NREP) * SY_LINE;         // 2304 bytes
+static_assert(SY_WORDS * 4 <= 4096, "sync area");
+constexpr int F_SLOTS = 4;  // logits and flag buffers rotate over this many calls
 
 struct FusedGeo {
-  int nR, nSG, nRG;  // router, shared gate/up, routed gate/up workgroups
-  int nD;            // down blocks: block d < nR + nSG runs on workgroup d after its first role,
+  int nR, nSG, nRG;  // router, shared, routed workgroups
+  int nD;            // reducers: reducer d < nR + nSG runs on workgroup d after its first role,
                      // the rest on extra workgroups after the routed ones
 };
 
@@ -87,31 +99,49 @@ __device__ __forceinline__ void flag_error(uint32_t* sync, uint32_t bit) {
 }
 __device__ __forceinline__ int my_rep() { return blockIdx.x & (SY_NREP - 1); }
 
-// Count the workgroup in on every replica once its tagged stores are issued.
-// The count may become visible before the stores do; readers check tags.
-__device__ __forceinline__ void count_in(uint32_t* sync, int which) {
+// The workgroup's flag: written by one thread once every thread's tagged
+// stores are issued (the flag may become visible before them; readers
+// check the values' tags).
+__device__ __forceinline__ void raise_flag(uint64_t* flag, uint32_t tag) {
   __syncthreads();
-  if (threadIdx.x < SY_NREP)
-    __hip_atomic_fetch_add(sync + which + SY_LINE * threadIdx.x, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (threadIdx.x == 0) st_word(flag, 0u, tag);
 }
 
-// Bounded wait until this XCD's replica of counter `which` reaches target;
-// the whole workgroup leaves together.
-__device__ __forceinline__ void wait_hint(uint32_t* sync, int which, uint32_t target) {
-  if (threadIdx.x == 0) {
-    const uint32_t* c = sync + which + SY_LINE * my_rep();
+// Bounded wait until at least `need` of flags[0 .. n) carry the current tag
+// (need <= n): wave 0 polls, eight flags per lane per pass; the whole
+// workgroup leaves together. Callers that pass need < n then read the
+// values with per-word tag checks (settle), so the loads of the last
+// producers' values overlap their arrival instead of following it.
+__device__ __forceinline__ void wait_flags(const uint64_t* flags, int n, int need, uint32_t tag, uint32_t* sync) {
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
     const uint64_t t0 = wall_clock64();
     int it = 0;
-    while (ld_u32(c) < target) {
-      __builtin_amdgcn_s_sleep(4);
+    while (true) {
+      int have = 0;
+      for (int base = 0; base < n; base += 64 * 8) {
+        uint64_t v[8];
+#pragma unroll
+        for (int j = 0; j < 8; j++) v[j] = ld_word_coherent(flags + min(base + lane + 64 * j, n - 1));
+#pragma unroll
+        for (int j = 0; j < 8; j++) {
+          const bool ok = (base + lane + 64 * j < n) && (uint32_t)(v[j] >> 32) == tag;
+          have += __popcll(__builtin_amdgcn_ballot_w64(ok));
+        }
+      }
+      if (have >= need) break;
+      __builtin_amdgcn_s_sleep(1);
       if ((++it & 15) == 0 && wall_clock64() - t0 > F_WAIT_TICKS) {
-        flag_error(sync, 1u);
+        if (lane == 0) flag_error(sync, 1u);
         break;
       }
     }
   }
   __syncthreads();
 }
+
+// how many producer flags a consumer waits for before it reads the values
+__device__ __forceinline__ int flags_needed(int n) { return n - n / 8; }
 
 // A word loaded once: if its tag is not current yet (the producer's store
 // is still on its way), reload it (bounded).
@@ -132,18 +162,28 @@ __device__ __forceinline__ uint64_t settle(const uint64_t* p, uint64_t w, uint32
   return w;
 }
 
+// Count the workgroup out: first in its XCD group, then the group's last
+// workgroup counts the group; the last group's last workgroup (every other
+// workgroup is past all of its waits) resets the counts and advances the
+// epoch for the next call.
 __device__ __forceinline__ void finish(uint32_t* sync) {
   __syncthreads();
   if (threadIdx.x == 0) {
-    const uint32_t old = __hip_atomic_fetch_add(sync + SY_DONE, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (old == gridDim.x - 1) {  // every other workgroup is past all of its waits
-      const uint32_t next = ld_u32(sync + SY_EPOCH) + 1u;
-      for (int r = 0; r < SY_NREP; r++) {
-        __hip_atomic_store(sync + SY_LOGITS + SY_LINE * r, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(sync + SY_H + SY_LINE * r, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(sync + SY_EPOCH + SY_LINE * r, next, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int r = my_rep();
+    const uint32_t in_group = (gridDim.x - r + SY_NREP - 1) / SY_NREP;
+    const uint32_t groups = gridDim.x < (unsigned)SY_NREP ? gridDim.x : (unsigned)SY_NREP;
+    const uint32_t old = __hip_atomic_fetch_add(sync + SY_DONEX + SY_LINE * r, 1u, __ATOMIC_RELAXED,
+                                                __HIP_MEMORY_SCOPE_AGENT);
+    if (old == in_group - 1) {
+      const uint32_t g = __hip_atomic_fetch_add(sync + SY_DONE, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (g == groups - 1) {
+        const uint32_t next = ld_u32(sync + SY_EPOCH) + 1u;
+        for (int q = 0; q < SY_NREP; q++) {
+          __hip_atomic_store(sync + SY_DONEX + SY_LINE * q, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          __hip_atomic_store(sync + SY_EPOCH + SY_LINE * q, next, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        __hip_atomic_store(sync + SY_DONE, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
-      __hip_atomic_store(sync + SY_DONE, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
 }
@@ -163,12 +203,21 @@ __device__ __forceinline__ void role_router(const LayerDev& L, const uint16_t* _
   for (int c0 = 0; c0 < n4; c0 += 64 * F_RCPL) {
     float4 w[F_RCPL];
     uint2 xx[F_RCPL];
+    // loads with clamped indices and no branch (a load inside a branch makes
+    // the compiler wait for every load in flight where the branch joins);
+    // elements past the row are masked after
 #pragma unroll
     for (int i = 0; i < F_RCPL; i++) {
-      const int c = c0 + lane + 64 * i;
-      const bool in = valid && c < n4;
-      w[i] = in ? wr[c] : make_float4(0.f, 0.f, 0.f, 0.f);
-      xx[i] = in ? xv[c] : make_uint2(0u, 0u);
+      const int c = min(c0 + lane + 64 * i, n4 - 1);
+      w[i] = wr[c];
+      xx[i] = xv[c];
+    }
+#pragma unroll
+    for (int i = 0; i < F_RCPL; i++) {
+      if (!(valid && c0 + lane + 64 * i < n4)) {
+        w[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+        xx[i] = make_uint2(0u, 0u);
+      }
     }
 #pragma unroll
     for (int i = 0; i < F_RCPL; i++) {
@@ -188,36 +237,39 @@ __device__ __forceinline__ void role_router(const LayerDev& L, const uint16_t* _
 }
 
 // ---------------------------------------------------------------------------
-// Gate/up rows of one expert: RPW rows per workgroup (32 = 16 gate + 16 up
-// rows of one interleave group; 16 = half a group), SwiGLU, h -> hout.
+// Gate/up rows of one expert -> SwiGLU -> h (bf16) in LDS.
+//   RPW = 64: rows 64q .. 64q+63, two interleave groups of 32 rows (16 gate
+//             rows, then their 16 up rows): intermediates 32q .. 32q+31;
+//   RPW = 16: half a group, rows 32q + 8hf + (0..7) (gate) and + 16 (up):
+//             intermediates 16q + 8hf .. +7.
 // Lane -> (row rr = lane % RPW, k-part kp); lanes with consecutive rows read
 // consecutive 16-byte chunks (rows are contiguous within a chunk column).
+// Threads j < RPW/2 end holding intermediate j's value (returned, 0 for
+// others), also stored to s_h[j].
 // ---------------------------------------------------------------------------
-template <int WT> constexpr int gu_batch() { return is_q<WT>() ? 4 : 8; }
+constexpr int F_GU_NB = 8;  // chunks per thread and batch
 
 template <int WT, int RPW>
-__device__ __forceinline__ void gate_up_rows(const uint8_t* __restrict__ gu, const uint16_t* __restrict__ gus, int H,
-                                             int R, int q, int hf, const uint16_t* xs, const float* xsum, float* s_red,
-                                             uint64_t* hout, uint32_t tag) {
+__device__ __forceinline__ float gate_up_h(const uint8_t* __restrict__ gu, const uint16_t* __restrict__ gus, int H, int R,
+                                           int q, int hf, const uint16_t* xs, const float* xsum, float* s_red,
+                                           uint16_t* s_h) {
   constexpr int KC = kchunk<WT>();
   constexpr int NKP = F_THREADS / RPW;  // k-parts
-  constexpr int NB = gu_batch<WT>();
+  constexpr int NB = F_GU_NB;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int rr = lane % RPW;
   const int kp = lane / RPW + (64 / RPW) * wave;
-  const int row = (RPW == 32) ? 32 * q + rr : 32 * q + 8 * hf + (rr & 7) + ((rr >> 3) << 4);
+  const int row = (RPW == 64) ? 64 * q + rr : 32 * q + 8 * hf + (rr & 7) + ((rr >> 3) << 4);
   const int nc = H / KC;
   float acc = 0.0f;
   for (int c0 = 0; c0 < nc; c0 += NKP * NB) {
     Raw raw[NB];
     float sc[NB];
 #pragma unroll
-    for (int i = 0; i < NB; i++) {
-      const int c = c0 + kp + NKP * i;
-      if (c < nc) {
-        raw[i] = load_chunk<WT>(gu, (size_t)c * R + row);
-        if constexpr (is_q<WT>()) sc[i] = f16_to_f32(gus[(size_t)c * R + row]);
-      }
+    for (int i = 0; i < NB; i++) {  // clamped, unconditional loads (see role_router)
+      const int c = min(c0 + kp + NKP * i, nc - 1);
+      raw[i] = load_chunk<WT>(gu, (size_t)c * R + row);
+      if constexpr (is_q<WT>()) sc[i] = f16_to_f32(gus[(size_t)c * R + row]);
     }
 #pragma unroll
     for (int i = 0; i < NB; i++) {
@@ -235,19 +287,23 @@ __device__ __forceinline__ void gate_up_rows(const uint8_t* __restrict__ gu, con
   if constexpr (RPW <= 32) acc += __shfl_xor(acc, 32, 64);
   if (lane < RPW) s_red[wave * RPW + rr] = acc;
   __syncthreads();
-  if ((int)threadIdx.x < RPW / 4) {  // two intermediates per thread, one tagged word
-    const int j = 2 * threadIdx.x;
-    float g0 = 0.0f, u0 = 0.0f, g1 = 0.0f, u1 = 0.0f;
+  float hv = 0.0f;
+  if ((int)threadIdx.x < RPW / 2) {
+    const int j = threadIdx.x;
+    const int gi = (RPW == 16) ? j : 32 * (j >> 4) + (j & 15);
+    const int ui = (RPW == 16) ? j + 8 : gi + 16;
+    float g = 0.0f, u = 0.0f;
 #pragma unroll
     for (int w = 0; w < F_THREADS / 64; w++) {
-      g0 += s_red[w * RPW + j];
-      u0 += s_red[w * RPW + RPW / 2 + j];
-      g1 += s_red[w * RPW + j + 1];
-      u1 += s_red[w * RPW + RPW / 2 + j + 1];
+      g += s_red[w * RPW + gi];
+      u += s_red[w * RPW + ui];
     }
-    st_word(hout + threadIdx.x, pack_bf16x2(silu_f32(g0) * u0, silu_f32(g1) * u1), tag);
+    const uint16_t hb = f32_to_bf16(silu_f32(g) * u);  // h is rounded to bf16, as in the other paths
+    s_h[j] = hb;
+    hv = bf16_to_f32(hb);
   }
   (void)NKP;
+  return hv;
 }
 
 // x -> LDS (bf16) and, for quantised weights, its 32-element block sums.
@@ -277,11 +333,11 @@ __device__ __forceinline__ void block_topk(const uint64_t* logits, int E, int k,
     uint64_t wl[F_NV], wh[F_NV];
 #pragma unroll
     for (int i = 0; i < F_NV; i++) {
-      const int e = lane + 64 * i;
-      if (e < E) {  // coherent loads: a line another call left in this XCD's L2 is never used
-        wl[i] = ld_word_coherent(logits + 2 * e);
-        wh[i] = ld_word_coherent(logits + 2 * e + 1);
-      }
+      // coherent loads (a line another call left in this XCD's L2 is never
+      // used), clamped and unconditional (see role_router)
+      const int e = min(lane + 64 * i, E - 1);
+      wl[i] = ld_word_coherent(logits + 2 * e);
+      wh[i] = ld_word_coherent(logits + 2 * e + 1);
     }
     double lv[F_NV];
 #pragma unroll
@@ -306,253 +362,247 @@ __device__ __forceinline__ void block_topk(const uint64_t* logits, int E, int k,
 }
 
 // ---------------------------------------------------------------------------
-// Down role: output rows r0 .. r0 + F_RD - 1.
-// Items: routed (j < k, block b < I/32, row rr) and shared (block b, row rr);
-// an item is 32 consecutive columns of one row: one quantised chunk + scale,
-// or 4 (bf16) / 8 (fp32) dense chunks.
+// Split-K down: one workgroup's columns of a down matrix times its h, for
+// all H output rows, as tagged partial words part[row] (fp32 bits). Rows go
+// to threads round-robin (lane-consecutive rows read consecutive chunks).
+// Routed: the 32-column block cb of the expert (one quantised chunk per row,
+// or 32 / kchunk dense chunks); shared: 8 columns (8 / kchunk chunks).
+// When a row's columns are one chunk (quantised routed, bf16 shared) the
+// chunks of all rows travel memory -> LDS by DMA while the gate/up rows
+// stream (16 bytes per row; Q3's three words in three 256-byte rows per wave)
+// and the scales go to registers; otherwise the rows are loaded once h is
+// ready.
 // ---------------------------------------------------------------------------
-template <int WT> constexpr int dn_batch() { return is_q<WT>() ? 6 : (WT == MOE_W_BF16 ? 2 : 1); }
-template <int WT> constexpr int item_chunks() { return is_q<WT>() ? 1 : 32 / kchunk<WT>(); }
+constexpr int F_RPT = 4;  // down rows per thread (H <= F_RPT * F_THREADS)
 
-template <int WT>
-struct Item {
-  Raw r[item_chunks<WT>()];
-  float s;
+typedef __attribute__((address_space(3))) void* lds_void_t;
+typedef __attribute__((address_space(1))) const void* gbl_void_t;
+
+template <int WT, int NCOL> struct DownPlan {
+  static constexpr int NCH = NCOL / kchunk<WT>() > 0 ? NCOL / kchunk<WT>() : 1;
+  static constexpr bool PRE = NCH == 1;  // chunks prefetched into LDS
 };
 
-template <int WT>
-__device__ __forceinline__ void load_item(const uint8_t* __restrict__ d, const uint16_t* __restrict__ ds, int H, int row,
-                                          int b, Item<WT>& it) {
-  constexpr int NCH = item_chunks<WT>();
+// issue the prefetch of this thread's rows (column block cb); `lds`: 16 bytes
+// per row slot, F_RPT * F_THREADS slots
+template <int WT, int NCOL>
+__device__ __forceinline__ void down_prefetch(const uint8_t* __restrict__ d, const uint16_t* __restrict__ ds, int H,
+                                              int cb, uint8_t* lds, float (&sc)[F_RPT]) {
+  if constexpr (DownPlan<WT, NCOL>::PRE) {
+    const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+    // every slot is filled, with no branch (a load inside a branch makes the
+    // compiler wait for all loads in flight where the branch joins); rows
+    // past H load row H - 1 and are not used
 #pragma unroll
-  for (int c = 0; c < NCH; c++) it.r[c] = load_chunk<WT>(d, (size_t)(b * NCH + c) * H + row);
-  if constexpr (is_q<WT>()) it.s = f16_to_f32(ds[(size_t)b * H + row]);
-}
-
-template <int WT>
-__device__ __forceinline__ float item_dot(const Item<WT>& it, const uint16_t* h32, float hsum) {
-  if constexpr (is_q<WT>()) {
-    return it.s * qdot32<WT>(it.r[0], h32, hsum);
-  } else {
-    constexpr int NCH = item_chunks<WT>();
-    constexpr int KC = kchunk<WT>();
-    float a = 0.0f;
+    for (int n = 0; n < F_RPT; n++) {
+      const int row = min((int)threadIdx.x + F_THREADS * n, H - 1);
+      uint8_t* dst = lds + (size_t)(n * F_THREADS + 64 * wave) * 16;
+      if constexpr (WT == MOE_W_Q3) {
 #pragma unroll
-    for (int c = 0; c < NCH; c++) a = ddot<WT>(it.r[c], h32 + KC * c, a);
-    return a;
-  }
-}
-
-constexpr int F_RD = 16;  // output rows per down block
-
-template <int WT, int SWT>
-__device__ __forceinline__ void role_down(const LayerDev& L, const FusedGeo& G, const DecodeWs& ws, uint16_t* __restrict__ y,
-                                          int d, uint8_t* smem, uint32_t tag, const uint64_t* tl, const uint64_t* th) {
-  const int H = L.H, I = L.I, E = L.E, k = L.k;
-  const int nB = I >> 5;
-  constexpr bool HAS_S = SWT != MOE_W_NONE;
-  constexpr int SW = (SWT == MOE_W_F32) ? MOE_W_F32 : MOE_W_BF16;
-  const int r0 = d * F_RD;
-  const int nj = k + (HAS_S ? 1 : 0);
-  // LDS: h [nj][I] bf16 | hsum [k][nB] | part [nj][nB][F_RD] | pj [nj][F_RD] | idx, gate [16] | top-k scratch
-  uint16_t* s_h = reinterpret_cast<uint16_t*>(smem);
-  float* s_hsum = reinterpret_cast<float*>(smem + (((size_t)nj * I * 2 + 15) & ~(size_t)15));
-  float* s_part = s_hsum + k * nB;
-  float* s_pj = s_part + (size_t)nj * nB * F_RD;
-  int* s_idx = reinterpret_cast<int*>(s_pj + nj * F_RD);
-  float* s_gate = reinterpret_cast<float*>(s_idx + 16);
-  uint8_t* s_tk = smem + ((reinterpret_cast<uint8_t*>(s_gate + 16) - smem + 15) & ~(ptrdiff_t)15);
-
-  wait_hint(ws.sync, SY_LOGITS, (uint32_t)G.nR);
-  // the top-k first: its logits loads must not queue behind weight loads
-  block_topk(tl, E, k, tag, ws.sync, s_tk, s_idx, s_gate);
-  // shared items
-  const int nsi = nB * F_RD;
-  Item<SW> si;
-  const int st = threadIdx.x;
-  if constexpr (HAS_S) {
-    if (st < nsi) {
-      const int row = r0 + st % F_RD;
-      if (row < H) load_item<SW>(L.sdn, nullptr, H, row, st / F_RD, si);
+        for (int q = 0; q < 3; q++)
+          __builtin_amdgcn_global_load_lds((gbl_void_t)(d + ((size_t)cb * H + row) * 12 + 4 * q),
+                                           (lds_void_t)(dst + 256 * q), 4, 0, 0);
+      } else {
+        __builtin_amdgcn_global_load_lds((gbl_void_t)(d + ((size_t)cb * H + row) * 16), (lds_void_t)dst, 16, 0, 0);
+      }
+      if constexpr (is_q<WT>()) sc[n] = f16_to_f32(ds[(size_t)cb * H + row]);
     }
   }
-  // routed items, first batch issued now
-  constexpr int NB = dn_batch<WT>();
-  const int nri = k * nB * F_RD;
-  Item<WT> it[NB];
-  auto issue = [&](int base) {
+}
+
+// partial[row] = scale * (its columns . h), stored as tagged words
+template <int WT, int NCOL>
+__device__ __forceinline__ void down_store(const uint8_t* __restrict__ d, const uint16_t* __restrict__ ds, int H, int cb,
+                                           const uint8_t* lds, const float (&sc)[F_RPT], const uint16_t* s_h, float hsum,
+                                           float scale, uint64_t* part, uint32_t tag) {
+  constexpr int NCH = DownPlan<WT, NCOL>::NCH;
+  constexpr int KC = kchunk<WT>();
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
-    for (int n = 0; n < NB; n++) {
-      const int i = base + (int)threadIdx.x + F_THREADS * n;
-      if (i < nri) {
-        const int rr = i % F_RD, b = (i / F_RD) % nB, j = i / (F_RD * nB);
-        const int row = r0 + rr;
-        const int e = s_idx[j];
-        if (row < H)
-          load_item<WT>(L.dn + (size_t)e * L.dn_stride, is_q<WT>() ? L.dn_s + (size_t)e * L.dn_s_stride : nullptr, H,
-                        row, b, it[n]);
-      }
-    }
-  };
-  issue(0);
-  wait_hint(ws.sync, SY_H, (uint32_t)(G.nSG + G.nRG));
-  // stage h (slot order, then shared) from its tagged words, and the routed block sums
-  {
-    const uint64_t* hw = th;
-    const int nw = (nj * I) >> 1;
-    constexpr int HB = 8;
-    for (int w0 = 0; w0 < nw; w0 += F_THREADS * HB) {
-      uint64_t v[HB];
-#pragma unroll
-      for (int n = 0; n < HB; n++) {
-        const int w = w0 + (int)threadIdx.x + F_THREADS * n;
-        if (w < nw) v[n] = ld_word_coherent(hw + w);
-      }
-#pragma unroll
-      for (int n = 0; n < HB; n++) {
-        const int w = w0 + (int)threadIdx.x + F_THREADS * n;
-        if (w < nw) reinterpret_cast<uint32_t*>(s_h)[w] = (uint32_t)settle(hw + w, v[n], tag, ws.sync);
-      }
-    }
-    __syncthreads();
-    if constexpr (is_q<WT>()) {
-      for (int i = threadIdx.x; i < k * nB; i += F_THREADS) {
-        const uint4* v = reinterpret_cast<const uint4*>(s_h + (size_t)i * 32);
-        float a = 0.0f;
-#pragma unroll
-        for (int c = 0; c < 4; c++) {
-          const uint4 q = v[c];
-          a += ((bf16_lo(q.x) + bf16_hi(q.x)) + (bf16_lo(q.y) + bf16_hi(q.y))) +
-               ((bf16_lo(q.z) + bf16_hi(q.z)) + (bf16_lo(q.w) + bf16_hi(q.w)));
+  for (int n = 0; n < F_RPT; n++) {
+    const int row = (int)threadIdx.x + F_THREADS * n;
+    if (row < H) {
+      float v = 0.0f;
+      if constexpr (DownPlan<WT, NCOL>::PRE) {
+        const uint8_t* src = lds + (size_t)(n * F_THREADS + 64 * wave) * 16;
+        Raw r;
+        if constexpr (WT == MOE_W_Q3) {
+          const uint32_t* w = reinterpret_cast<const uint32_t*>(src) + lane;
+          r.w[0] = w[0]; r.w[1] = w[64]; r.w[2] = w[128]; r.w[3] = 0;
+        } else {
+          const uint4 q = reinterpret_cast<const uint4*>(src)[lane];
+          r.w[0] = q.x; r.w[1] = q.y; r.w[2] = q.z; r.w[3] = q.w;
         }
-        s_hsum[i] = a;
-      }
-      __syncthreads();
-    }
-  }
-  // routed items
-  for (int base = 0; base < nri; base += F_THREADS * NB) {
-    if (base > 0) issue(base);
+        if constexpr (is_q<WT>()) v = sc[n] * qdot32<WT>(r, s_h, hsum);
+        else v = ddot<WT>(r, s_h, 0.0f);
+      } else {
 #pragma unroll
-    for (int n = 0; n < NB; n++) {
-      const int i = base + (int)threadIdx.x + F_THREADS * n;
-      if (i < nri) {
-        const int rr = i % F_RD, b = (i / F_RD) % nB, j = i / (F_RD * nB);
-        const float hs = is_q<WT>() ? s_hsum[j * nB + b] : 0.0f;
-        s_part[(size_t)(j * nB + b) * F_RD + rr] = (r0 + rr < H) ? item_dot<WT>(it[n], s_h + (size_t)j * I + 32 * b, hs) : 0.0f;
+        for (int c = 0; c < NCH; c++) v = ddot<WT>(load_chunk<WT>(d, (size_t)(cb * NCH + c) * H + row), s_h + KC * c, v);
+      }
+      st_word(part + row, __float_as_uint(v * scale), tag);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Reducer: output rows r0 .. r0 + F_RD - 1, y = sum over the nP partials in
+// producer order (shared workgroups, then routed), each thread summing a
+// fixed subset and the workgroup adding the subsets in a fixed order.
+// ---------------------------------------------------------------------------
+constexpr int F_RD = 16;                   // output rows per reducer
+constexpr int F_RG = F_THREADS / F_RD;     // producer groups per reducer (32)
+
+__device__ __forceinline__ void role_reduce(const uint64_t* part, int nP, int H, int r0, uint16_t* __restrict__ y,
+                                            float* s_red, uint32_t tag, uint32_t* sync) {
+  const int rr = threadIdx.x % F_RD, pg = threadIdx.x / F_RD;
+  const int row = r0 + rr;
+  float acc = 0.0f;
+  if (row < H) {
+    constexpr int NB = 8;
+    for (int p0 = pg; p0 < nP; p0 += F_RG * NB) {
+      uint64_t w[NB];
+#pragma unroll
+      for (int n = 0; n < NB; n++)  // clamped, unconditional loads (see role_router)
+        w[n] = ld_word_coherent(part + (size_t)min(p0 + F_RG * n, nP - 1) * H + row);
+#pragma unroll
+      for (int n = 0; n < NB; n++) {
+        const int p = p0 + F_RG * n;
+        if (p < nP) acc += __uint_as_float((uint32_t)settle(part + (size_t)p * H + row, w[n], tag, sync));
       }
     }
   }
-  if constexpr (HAS_S) {
-    if (st < nsi) {
-      const int rr = st % F_RD, b = st / F_RD;
-      s_part[(size_t)(k * nB + b) * F_RD + rr] = (r0 + rr < H) ? item_dot<SW>(si, s_h + (size_t)k * I + 32 * b, 0.0f) : 0.0f;
-    }
-  }
+  s_red[threadIdx.x] = acc;
   __syncthreads();
-  // per (expert, row): sum over blocks; then y = sum_j g_j s_j + s_shared
-  for (int t = threadIdx.x; t < nj * F_RD; t += F_THREADS) {
-    const int j = t / F_RD, rr = t % F_RD;
-    const float* p = s_part + (size_t)j * nB * F_RD + rr;
-    float a0 = 0.0f, a1 = 0.0f;
-    int b = 0;
-    for (; b + 1 < nB; b += 2) {
-      a0 += p[b * F_RD];
-      a1 += p[(b + 1) * F_RD];
-    }
-    if (b < nB) a0 += p[b * F_RD];
-    s_pj[t] = a0 + a1;
+  if ((int)threadIdx.x < F_RD && row < H) {
+    float a = 0.0f;
+#pragma unroll 8
+    for (int g = 0; g < F_RG; g++) a += s_red[g * F_RD + rr];
+    y[row] = f32_to_bf16(a);
   }
-  __syncthreads();
-  if ((int)threadIdx.x < F_RD) {
-    const int rr = threadIdx.x;
-    float acc = 0.0f;
-    for (int j = 0; j < k; j++) acc = __builtin_fmaf(s_gate[j], s_pj[j * F_RD + rr], acc);
-    if (HAS_S) acc += s_pj[k * F_RD + rr];
-    if (r0 + rr < H) y[r0 + rr] = f32_to_bf16(acc);
-  }
+}
+
+// ---------------------------------------------------------------------------
+// LDS of a producer: x (bf16) | x block sums | wave partials | top-k scratch
+// | prefetched down chunks (16 bytes per row slot, F_RPT * F_THREADS slots).
+// A reducer uses the first 2 KB.
+// ---------------------------------------------------------------------------
+__host__ __device__ constexpr size_t lds_down_off(int H) {
+  return (((size_t)H * 2 + (size_t)(H >> 5) * 4 + 15) & ~(size_t)15) + F_THREADS / 64 * 64 * 4 + TOPK_SCRATCH;
 }
 
 // ---------------------------------------------------------------------------
 // The kernel
 // ---------------------------------------------------------------------------
 template <int WT, int SWT>
-__global__ __launch_bounds__(F_THREADS) void k_decode1(LayerDev L, const uint16_t* __restrict__ x,
+__global__ __launch_bounds__(F_THREADS, 4) void k_decode1(LayerDev L, const uint16_t* __restrict__ x,
                                                        uint16_t* __restrict__ y, int32_t* idx_out, float* gate_out,
                                                        DecodeWs ws, FusedGeo G) {
   extern __shared__ __align__(16) uint8_t smem[];
   __shared__ int s_idx[16];
   __shared__ float s_gate[16];
+  __shared__ __align__(16) uint16_t s_h[32];
+  __shared__ float s_hsum;
   const int H = L.H, I = L.I;
+  const int nP = G.nSG + G.nRG;  // partial producers: shared workgroups, then routed
   // this call's tag: the epoch (stable until every workgroup is done) + 1
   const uint32_t tag = ld_u32(ws.sync + SY_EPOCH + SY_LINE * my_rep()) + 1u;
   uint64_t* tl = reinterpret_cast<uint64_t*>(ws.logits) + (size_t)(tag % F_SLOTS) * 2 * L.E;
-  uint64_t* th = reinterpret_cast<uint64_t*>(ws.h) + (size_t)(tag % F_SLOTS) * ((L.k + 1) * I / 2);
+  // flags: router workgroups [0, nR), then the partial producers
+  uint64_t* fl = ws.flags + (size_t)(tag % F_SLOTS) * (G.nR + nP);
+  uint64_t* part = ws.part_words;  // [nP][H]
   int b = blockIdx.x;
   if (b < G.nR) {
     role_router(L, x, tl, b, tag);
-    count_in(ws.sync, SY_LOGITS);
+    raise_flag(fl + b, tag);
   } else if ((b -= G.nR) < G.nSG) {
     // shared expert, intermediates 16q + 8hf .. +7
     constexpr int SW = (SWT == MOE_W_F32) ? MOE_W_F32 : MOE_W_BF16;
     uint16_t* xs = reinterpret_cast<uint16_t*>(smem);
     float* s_red = reinterpret_cast<float*>(smem + (size_t)H * 2);
-    stage_x(x, H, xs, nullptr);
-    wait_hint(ws.sync, SY_LOGITS, (uint32_t)G.nR);  // the router's bytes first; these fill the top-k window
     const int q = b >> 1, hf = b & 1;
-    gate_up_rows<SW, 16>(L.sgu, nullptr, H, 2 * I, q, hf, xs, nullptr, s_red,
-                         th + (((size_t)L.k * I + 16 * q + 8 * hf) >> 1), tag);
-    count_in(ws.sync, SY_H);
+    stage_x(x, H, xs, nullptr);
+    wait_flags(fl, G.nR, G.nR, tag, ws.sync);  // the router's bytes first; these fill the top-k window
+    uint8_t* s_dn = smem + lds_down_off(H);
+    float dsc[F_RPT];
+    down_prefetch<SW, 8>(L.sdn, nullptr, H, 2 * q + hf, s_dn, dsc);
+    gate_up_h<SW, 16>(L.sgu, nullptr, H, 2 * I, q, hf, xs, nullptr, s_red, s_h);
+    __syncthreads();
+    down_store<SW, 8>(L.sdn, nullptr, H, 2 * q + hf, s_dn, dsc, s_h, 0.0f, 1.0f, part + (size_t)b * H, tag);
+    raise_flag(fl + G.nR + b, tag);
   } else if ((b -= G.nSG) < G.nRG) {
-    // routed slot u, intermediates 16q .. 16q+15
+    // routed slot u, intermediates 32q .. 32q+31
     uint16_t* xs = reinterpret_cast<uint16_t*>(smem);
     float* xsum = reinterpret_cast<float*>(smem + (size_t)H * 2);
     float* s_red = reinterpret_cast<float*>(smem + (((size_t)H * 2 + (H >> 5) * 4 + 15) & ~(size_t)15));
-    uint8_t* s_tk = reinterpret_cast<uint8_t*>(s_red + 8 * 32);
+    uint8_t* s_tk = reinterpret_cast<uint8_t*>(s_red + F_THREADS / 64 * 64);
     stage_x(x, H, xs, is_q<WT>() ? xsum : nullptr);
-    wait_hint(ws.sync, SY_LOGITS, (uint32_t)G.nR);
+    wait_flags(fl, G.nR, flags_needed(G.nR), tag, ws.sync);
     block_topk(tl, L.E, L.k, tag, ws.sync, s_tk, s_idx, s_gate);
-    const int gpe = I >> 4;
+    const int gpe = I >> 5;
     const int u = b / gpe, q = b - u * gpe;
     if (b == 0 && (int)threadIdx.x < L.k) {
       if (idx_out) idx_out[threadIdx.x] = s_idx[threadIdx.x];
       if (gate_out) gate_out[threadIdx.x] = s_gate[threadIdx.x];
     }
     const int e = s_idx[u];
-    gate_up_rows<WT, 32>(L.gu + (size_t)e * L.gu_stride, is_q<WT>() ? L.gu_s + (size_t)e * L.gu_s_stride : nullptr, H,
-                         2 * I, q, 0, xs, xsum, s_red, th + (((size_t)u * I + 16 * q) >> 1), tag);
-    count_in(ws.sync, SY_H);
+    const uint8_t* dn = L.dn + (size_t)e * L.dn_stride;
+    const uint16_t* dns = is_q<WT>() ? L.dn_s + (size_t)e * L.dn_s_stride : nullptr;
+    uint8_t* s_dn = smem + lds_down_off(H);
+    float dsc[F_RPT];
+    down_prefetch<WT, 32>(dn, dns, H, q, s_dn, dsc);
+    const float hv = gate_up_h<WT, 64>(L.gu + (size_t)e * L.gu_stride,
+                                       is_q<WT>() ? L.gu_s + (size_t)e * L.gu_s_stride : nullptr, H, 2 * I, q, 0, xs, xsum,
+                                       s_red, s_h);
+    if constexpr (is_q<WT>()) {
+      // block sum of the 32 bf16 h values (threads 0..31 of wave 0), fixed order
+      float t = hv;
+      if (threadIdx.x < 64) {
+#pragma unroll
+        for (int o = 16; o >= 1; o >>= 1) t += __shfl_xor(t, o, 64);
+        if (threadIdx.x == 0) s_hsum = t;
+      }
+    }
+    __syncthreads();
+    down_store<WT, 32>(dn, dns, H, q, s_dn, dsc, s_h, is_q<WT>() ? s_hsum : 0.0f, s_gate[u],
+                       part + (size_t)(G.nSG + b) * H, tag);
+    raise_flag(fl + G.nR + G.nSG + b, tag);
   }
-  // down blocks
+  // reducers
   const int first = G.nR + G.nSG, extra0 = first + G.nRG;
   int d = -1;
   if ((int)blockIdx.x < first) d = blockIdx.x;
   else if ((int)blockIdx.x >= extra0) d = first + ((int)blockIdx.x - extra0);
-  if (d >= 0 && d < G.nD) role_down<WT, SWT>(L, G, ws, y, d, smem, tag, tl, th);
+  if (d >= 0 && d < G.nD) {
+    wait_flags(fl + G.nR, nP, flags_needed(nP), tag, ws.sync);
+    role_reduce(part, nP, H, d * F_RD, y, reinterpret_cast<float*>(smem), tag, ws.sync);
+  }
   finish(ws.sync);
 }
 
 // ---------------------------------------------------------------------------
 // Host side
 // ---------------------------------------------------------------------------
-static size_t lds_gate_up(int H) {
-  return (((size_t)H * 2 + (size_t)(H >> 5) * 4 + 15) & ~(size_t)15) + 8 * 32 * 4 + TOPK_SCRATCH;
-}
-static size_t lds_down(int I, int k, bool has_s) {
-  const size_t nj = k + (has_s ? 1 : 0), nB = I >> 5;
-  return (((size_t)nj * I * 2 + 15) & ~(size_t)15) + (((k * nB + nj * nB * F_RD + nj * F_RD + 32) * 4 + 15) & ~(size_t)15) +
-         TOPK_SCRATCH;
+size_t decode1_lds(int H, int I, int k, bool has_shared) {
+  (void)I; (void)k; (void)has_shared;
+  // the prefetch fills all F_RPT blocks of F_THREADS rows (rows past H take a slot each)
+  const size_t a = lds_down_off(H) + (size_t)F_RPT * F_THREADS * 16, r = F_THREADS * 4;
+  return a > r ? a : r;
 }
 
-size_t decode1_lds(int H, int I, int k, bool has_shared) {
-  const size_t a = lds_gate_up(H), d = lds_down(I, k, has_shared);
-  return a > d ? a : d;
+static int producers(int I, int k, bool has_shared) { return (has_shared ? I / 8 : 0) + k * (I / 32); }
+
+size_t decode1_flag_words(int E, int I, int k, bool has_shared) {
+  return (size_t)F_SLOTS * ((E + 7) / 8 + producers(I, k, has_shared));
+}
+
+size_t decode1_part_words(int H, int I, int k, bool has_shared) {
+  return (size_t)producers(I, k, has_shared) * H;
 }
 
 bool decode1_fits(int E, int H, int I, int k, bool has_shared) {
-  // F_NV logits per lane in the top-k, one shared-expert down item per thread
-  // (I/32 * F_RD <= F_THREADS) and a 64 KiB LDS budget
-  return E <= 64 * F_NV && I <= 1024 && decode1_lds(H, I, k, has_shared) <= 65536;
+  // F_NV logits per lane in the top-k, F_RPT down rows per thread, a 64 KiB
+  // LDS budget
+  return E <= 64 * F_NV && H <= F_RPT * F_THREADS && I <= 1024 && decode1_lds(H, I, k, has_shared) <= 65536;
 }
 
 template <int WT, int SWT>
@@ -561,7 +611,7 @@ static hipError_t launch_fused_t(const LayerDev& L, const uint16_t* x, uint16_t*
   FusedGeo G;
   G.nR = (L.E + 7) / 8;
   G.nSG = (SWT == MOE_W_NONE) ? 0 : L.I / 8;
-  G.nRG = L.k * (L.I / 16);
+  G.nRG = L.k * (L.I / 32);
   G.nD = (L.H + F_RD - 1) / F_RD;
   const size_t lds = decode1_lds(L.H, L.I, L.k, SWT != MOE_W_NONE);
   const int extra = G.nD > G.nR + G.nSG ? G.nD - (G.nR + G.nSG) : 0;

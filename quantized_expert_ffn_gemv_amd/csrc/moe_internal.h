@@ -51,10 +51,11 @@ struct LayerDev {
 
 // Decode workspace (all device pointers inside the caller's workspace).
 struct DecodeWs {
-  uint32_t* sync;  // counters and epoch of the one-kernel path (counters zero between calls)
-  double* logits;  // three-kernel path: [B][E] fp64; one-kernel path: [E][2] tagged 64-bit words
-  uint16_t* h;     // one-kernel path: [(k+1) * I / 2] tagged words, two bf16 SwiGLU outputs each
-  float* part;     // [B*k*(I/16) + B*(I/4)][H] partial down products of the three-kernel path
+  uint32_t* sync;  // counts and epoch of the one-kernel path (counts zero between calls)
+  double* logits;  // three-kernel path: [B][E] fp64; one-kernel path: rotating slots of [E][2] tagged words
+  float* part;     // three-kernel path: [B*k*(I/16) + B*(I/4)][H] partial down products
+  uint64_t* flags; // one-kernel path: per-producer tagged flag words, rotating slots
+  uint64_t* part_words;  // one-kernel path: [producers][H] tagged partial down products (fp32 bits)
 };
 
 // Prefill workspace.
@@ -78,6 +79,8 @@ struct PrefillWs {
 // Launch wrappers (return hipError_t of the launch).
 size_t decode_lds_b(int wt, int B, int H, int E, int k);  // LDS bytes of the routed-expert kernel
 size_t decode1_lds(int H, int I, int k, bool has_shared);  // LDS bytes of the one-kernel batch-1 path
+size_t decode1_flag_words(int E, int I, int k, bool has_shared);
+size_t decode1_part_words(int H, int I, int k, bool has_shared);
 bool decode1_fits(int E, int H, int I, int k, bool has_shared);  // shape handled by the one-kernel path
 hipError_t launch_decode_fused(const LayerDev& L, const uint16_t* x, uint16_t* y, int32_t* idx_out,
                                float* gate_out, const DecodeWs& ws, hipStream_t st);
