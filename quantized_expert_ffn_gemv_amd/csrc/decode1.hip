@@ -60,6 +60,8 @@
 namespace moe {
 
 constexpr int F_THREADS = 512;
+constexpr int F_RPT = 4;                        // down rows per thread (H <= F_RPT * F_THREADS)
+constexpr int F_HMAX = F_RPT * F_THREADS;       // largest H of this path (LDS arrays are sized for it)
 constexpr int F_RCPL = 8;                       // router float4 chunks per lane and batch
 constexpr uint64_t F_WAIT_TICKS = 1ull << 25;   // ~0.34 s of the 100 MHz wall clock
 
@@ -236,6 +238,33 @@ __device__ __forceinline__ void role_router(const LayerDev& L, const uint16_t* _
   }
 }
 
+// qdot32 with the magic exponent held in a register: each code pair is one
+// shift and one and-or (the constants then need no instruction of their own).
+template <int WT>
+__device__ __forceinline__ float qdot32_reg(const Raw& r, const uint16_t* a, float asum, uint32_t magic) {
+  if constexpr (WT == MOE_W_Q4) {
+    uint32_t p[16];
+#pragma unroll
+    for (int j = 0; j < 4; j++)
+#pragma unroll
+      for (int t = 0; t < 4; t++) p[4 * j + t] = ((r.w[j] >> (4 * t)) & 0x000F000Fu) | magic;
+    const uint4* av = reinterpret_cast<const uint4*>(a);
+    float c0 = -(128.0f + (float)QOff<WT>::v) * asum, c1 = 0.0f, c2 = 0.0f, c3 = 0.0f;
+#pragma unroll
+    for (int q = 0; q < 4; q++) {
+      const uint4 v = av[q];
+      c0 = dot2_bf16(p[4 * q + 0], v.x, c0);
+      c1 = dot2_bf16(p[4 * q + 1], v.y, c1);
+      c2 = dot2_bf16(p[4 * q + 2], v.z, c2);
+      c3 = dot2_bf16(p[4 * q + 3], v.w, c3);
+    }
+    return (c0 + c1) + (c2 + c3);
+  } else {
+    (void)magic;
+    return qdot32<WT>(r, a, asum);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Gate/up rows of one expert -> SwiGLU -> h (bf16) in LDS.
 //   RPW = 64: rows 64q .. 64q+63, two interleave groups of 32 rows (16 gate
@@ -261,24 +290,37 @@ __device__ __forceinline__ float gate_up_h(const uint8_t* __restrict__ gu, const
   const int kp = lane / RPW + (64 / RPW) * wave;
   const int row = (RPW == 64) ? 64 * q + rr : 32 * q + 8 * hf + (rr & 7) + ((rr >> 3) << 4);
   const int nc = H / KC;
+  uint32_t magic = BF16_MAGIC2;
+  asm volatile("" : "+v"(magic));  // a register operand: one and-or per code pair
+  // batches known at compile time (H <= F_HMAX): straight-line code, so no
+  // loop head makes the compiler wait for loads issued before it (the down
+  // prefetch)
+  constexpr int NBATCH = (F_HMAX / KC + NKP * NB - 1) / (NKP * NB);
   float acc = 0.0f;
-  for (int c0 = 0; c0 < nc; c0 += NKP * NB) {
+#pragma unroll
+  for (int bt = 0; bt < NBATCH; bt++) {
+    const int c0 = bt * NKP * NB;
     Raw raw[NB];
     float sc[NB];
 #pragma unroll
-    for (int i = 0; i < NB; i++) {  // clamped, unconditional loads (see role_router)
-      const int c = min(c0 + kp + NKP * i, nc - 1);
-      raw[i] = load_chunk<WT>(gu, (size_t)c * R + row);
-      if constexpr (is_q<WT>()) sc[i] = f16_to_f32(gus[(size_t)c * R + row]);
+    for (int i = 0; i < NB; i++)  // clamped, unconditional loads (see role_router)
+      raw[i] = load_chunk<WT>(gu, (size_t)min(c0 + kp + NKP * i, nc - 1) * R + row);
+    if constexpr (is_q<WT>()) {
+#pragma unroll
+      for (int i = 0; i < NB; i++) sc[i] = f16_to_f32(gus[(size_t)min(c0 + kp + NKP * i, nc - 1) * R + row]);
     }
+    __builtin_amdgcn_sched_barrier(0);  // every load of the batch is issued before the first wait
+    // every chunk is computed (no branch around the dot products): a chunk
+    // past the row reads a valid chunk and contributes zero
 #pragma unroll
     for (int i = 0; i < NB; i++) {
-      const int c = c0 + kp + NKP * i;
-      if (c < nc) {
-        if constexpr (is_q<WT>())
-          acc = __builtin_fmaf(sc[i], qdot32<WT>(raw[i], xs + 32 * c, xsum[c]), acc);
-        else
-          acc = ddot<WT>(raw[i], xs + (size_t)c * KC, acc);
+      const bool in = c0 + kp + NKP * i < nc;
+      const int c = min(c0 + kp + NKP * i, nc - 1);
+      if constexpr (is_q<WT>()) {
+        acc = __builtin_fmaf(in ? sc[i] : 0.0f, qdot32_reg<WT>(raw[i], xs + 32 * c, xsum[c], magic), acc);
+      } else {
+        const float t = ddot<WT>(raw[i], xs + (size_t)c * KC, 0.0f);
+        acc += in ? t : 0.0f;
       }
     }
   }
@@ -365,79 +407,62 @@ __device__ __forceinline__ void block_topk(const uint64_t* logits, int E, int k,
 // Split-K down: one workgroup's columns of a down matrix times its h, for
 // all H output rows, as tagged partial words part[row] (fp32 bits). Rows go
 // to threads round-robin (lane-consecutive rows read consecutive chunks).
-// Routed: the 32-column block cb of the expert (one quantised chunk per row,
-// or 32 / kchunk dense chunks); shared: 8 columns (8 / kchunk chunks).
-// When a row's columns are one chunk (quantised routed, bf16 shared) the
-// chunks of all rows travel memory -> LDS by DMA while the gate/up rows
-// stream (16 bytes per row; Q3's three words in three 256-byte rows per wave)
-// and the scales go to registers; otherwise the rows are loaded once h is
-// ready.
+// Columns c0 ..: routed 32 (one quantised chunk per row, or 32 / kchunk
+// dense chunks), shared 8 (8 / kchunk chunks). When a row's columns are one
+// chunk (quantised routed, bf16 shared) the chunks and scales of the
+// thread's rows go to registers while the gate/up rows stream; otherwise the
+// rows are loaded once h is ready.
 // ---------------------------------------------------------------------------
-constexpr int F_RPT = 4;  // down rows per thread (H <= F_RPT * F_THREADS)
-
-typedef __attribute__((address_space(3))) void* lds_void_t;
-typedef __attribute__((address_space(1))) const void* gbl_void_t;
-
 template <int WT, int NCOL> struct DownPlan {
-  static constexpr int NCH = NCOL / kchunk<WT>() > 0 ? NCOL / kchunk<WT>() : 1;
-  static constexpr bool PRE = NCH == 1;  // chunks prefetched into LDS
+  static constexpr int KC = kchunk<WT>();
+  static constexpr int NCH = NCOL / KC > 0 ? NCOL / KC : 1;  // chunks per row holding the columns
+  static constexpr bool PRE = NCH == 1;                      // chunks prefetched into registers
 };
 
-// issue the prefetch of this thread's rows (column block cb); `lds`: 16 bytes
-// per row slot, F_RPT * F_THREADS slots
+// this thread's prefetched rows: chunk and scale per row
+template <int WT>
+struct DownPre {
+  Raw r[F_RPT];
+  float s[F_RPT];
+};
+
+// issue the prefetch of this thread's rows (columns from c0) into registers;
+// every row slot is filled, with no branch (a load inside a branch makes the
+// compiler wait for all loads in flight where the branch joins); rows past H
+// load row H - 1 and are not used
 template <int WT, int NCOL>
 __device__ __forceinline__ void down_prefetch(const uint8_t* __restrict__ d, const uint16_t* __restrict__ ds, int H,
-                                              int cb, uint8_t* lds, float (&sc)[F_RPT]) {
+                                              int c0, DownPre<WT>& pre) {
   if constexpr (DownPlan<WT, NCOL>::PRE) {
-    const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
-    // every slot is filled, with no branch (a load inside a branch makes the
-    // compiler wait for all loads in flight where the branch joins); rows
-    // past H load row H - 1 and are not used
+    const int cb = c0 / DownPlan<WT, NCOL>::KC;  // the chunk column
 #pragma unroll
-    for (int n = 0; n < F_RPT; n++) {
-      const int row = min((int)threadIdx.x + F_THREADS * n, H - 1);
-      uint8_t* dst = lds + (size_t)(n * F_THREADS + 64 * wave) * 16;
-      if constexpr (WT == MOE_W_Q3) {
+    for (int n = 0; n < F_RPT; n++)
+      pre.r[n] = load_chunk<WT>(d, (size_t)cb * H + min((int)threadIdx.x + F_THREADS * n, H - 1));
+    if constexpr (is_q<WT>()) {
 #pragma unroll
-        for (int q = 0; q < 3; q++)
-          __builtin_amdgcn_global_load_lds((gbl_void_t)(d + ((size_t)cb * H + row) * 12 + 4 * q),
-                                           (lds_void_t)(dst + 256 * q), 4, 0, 0);
-      } else {
-        __builtin_amdgcn_global_load_lds((gbl_void_t)(d + ((size_t)cb * H + row) * 16), (lds_void_t)dst, 16, 0, 0);
-      }
-      if constexpr (is_q<WT>()) sc[n] = f16_to_f32(ds[(size_t)cb * H + row]);
+      for (int n = 0; n < F_RPT; n++)
+        pre.s[n] = f16_to_f32(ds[(size_t)cb * H + min((int)threadIdx.x + F_THREADS * n, H - 1)]);
     }
   }
 }
 
 // partial[row] = scale * (its columns . h), stored as tagged words
 template <int WT, int NCOL>
-__device__ __forceinline__ void down_store(const uint8_t* __restrict__ d, const uint16_t* __restrict__ ds, int H, int cb,
-                                           const uint8_t* lds, const float (&sc)[F_RPT], const uint16_t* s_h, float hsum,
-                                           float scale, uint64_t* part, uint32_t tag) {
+__device__ __forceinline__ void down_store(const uint8_t* __restrict__ d, int H, int c0, const DownPre<WT>& pre,
+                                           const uint16_t* s_h, float hsum, float scale, uint64_t* part, uint32_t tag) {
+  constexpr int KC = DownPlan<WT, NCOL>::KC;
   constexpr int NCH = DownPlan<WT, NCOL>::NCH;
-  constexpr int KC = kchunk<WT>();
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
   for (int n = 0; n < F_RPT; n++) {
     const int row = (int)threadIdx.x + F_THREADS * n;
     if (row < H) {
       float v = 0.0f;
       if constexpr (DownPlan<WT, NCOL>::PRE) {
-        const uint8_t* src = lds + (size_t)(n * F_THREADS + 64 * wave) * 16;
-        Raw r;
-        if constexpr (WT == MOE_W_Q3) {
-          const uint32_t* w = reinterpret_cast<const uint32_t*>(src) + lane;
-          r.w[0] = w[0]; r.w[1] = w[64]; r.w[2] = w[128]; r.w[3] = 0;
-        } else {
-          const uint4 q = reinterpret_cast<const uint4*>(src)[lane];
-          r.w[0] = q.x; r.w[1] = q.y; r.w[2] = q.z; r.w[3] = q.w;
-        }
-        if constexpr (is_q<WT>()) v = sc[n] * qdot32<WT>(r, s_h, hsum);
-        else v = ddot<WT>(r, s_h, 0.0f);
+        if constexpr (is_q<WT>()) v = pre.s[n] * qdot32<WT>(pre.r[n], s_h, hsum);
+        else v = ddot<WT>(pre.r[n], s_h, 0.0f);
       } else {
 #pragma unroll
-        for (int c = 0; c < NCH; c++) v = ddot<WT>(load_chunk<WT>(d, (size_t)(cb * NCH + c) * H + row), s_h + KC * c, v);
+        for (int c = 0; c < NCH; c++) v = ddot<WT>(load_chunk<WT>(d, (size_t)(c0 / KC + c) * H + row), s_h + KC * c, v);
       }
       st_word(part + row, __float_as_uint(v * scale), tag);
     }
@@ -482,14 +507,9 @@ __device__ __forceinline__ void role_reduce(const uint64_t* part, int nP, int H,
 }
 
 // ---------------------------------------------------------------------------
-// LDS of a producer: x (bf16) | x block sums | wave partials | top-k scratch
-// | prefetched down chunks (16 bytes per row slot, F_RPT * F_THREADS slots).
-// A reducer uses the first 2 KB.
+// LDS: static arrays (x, x block sums, wave partials, top-k scratch) sized
+// for H <= F_HMAX.
 // ---------------------------------------------------------------------------
-__host__ __device__ constexpr size_t lds_down_off(int H) {
-  return (((size_t)H * 2 + (size_t)(H >> 5) * 4 + 15) & ~(size_t)15) + F_THREADS / 64 * 64 * 4 + TOPK_SCRATCH;
-}
-
 // ---------------------------------------------------------------------------
 // The kernel
 // ---------------------------------------------------------------------------
@@ -497,7 +517,10 @@ template <int WT, int SWT>
 __global__ __launch_bounds__(F_THREADS, 4) void k_decode1(LayerDev L, const uint16_t* __restrict__ x,
                                                        uint16_t* __restrict__ y, int32_t* idx_out, float* gate_out,
                                                        DecodeWs ws, FusedGeo G) {
-  extern __shared__ __align__(16) uint8_t smem[];
+  __shared__ __align__(16) uint16_t s_x[F_HMAX];
+  __shared__ __align__(16) float s_xsum[F_HMAX / 32];
+  __shared__ __align__(16) float s_red[F_THREADS];
+  __shared__ __align__(16) uint8_t s_tk[TOPK_SCRATCH];
   __shared__ int s_idx[16];
   __shared__ float s_gate[16];
   __shared__ __align__(16) uint16_t s_h[32];
@@ -517,24 +540,20 @@ __global__ __launch_bounds__(F_THREADS, 4) void k_decode1(LayerDev L, const uint
   } else if ((b -= G.nR) < G.nSG) {
     // shared expert, intermediates 16q + 8hf .. +7
     constexpr int SW = (SWT == MOE_W_F32) ? MOE_W_F32 : MOE_W_BF16;
-    uint16_t* xs = reinterpret_cast<uint16_t*>(smem);
-    float* s_red = reinterpret_cast<float*>(smem + (size_t)H * 2);
+    uint16_t* xs = s_x;
     const int q = b >> 1, hf = b & 1;
     stage_x(x, H, xs, nullptr);
     wait_flags(fl, G.nR, G.nR, tag, ws.sync);  // the router's bytes first; these fill the top-k window
-    uint8_t* s_dn = smem + lds_down_off(H);
-    float dsc[F_RPT];
-    down_prefetch<SW, 8>(L.sdn, nullptr, H, 2 * q + hf, s_dn, dsc);
+    DownPre<SW> pre;
+    down_prefetch<SW, 8>(L.sdn, nullptr, H, 16 * q + 8 * hf, pre);
     gate_up_h<SW, 16>(L.sgu, nullptr, H, 2 * I, q, hf, xs, nullptr, s_red, s_h);
     __syncthreads();
-    down_store<SW, 8>(L.sdn, nullptr, H, 2 * q + hf, s_dn, dsc, s_h, 0.0f, 1.0f, part + (size_t)b * H, tag);
+    down_store<SW, 8>(L.sdn, H, 16 * q + 8 * hf, pre, s_h, 0.0f, 1.0f, part + (size_t)b * H, tag);
     raise_flag(fl + G.nR + b, tag);
   } else if ((b -= G.nSG) < G.nRG) {
     // routed slot u, intermediates 32q .. 32q+31
-    uint16_t* xs = reinterpret_cast<uint16_t*>(smem);
-    float* xsum = reinterpret_cast<float*>(smem + (size_t)H * 2);
-    float* s_red = reinterpret_cast<float*>(smem + (((size_t)H * 2 + (H >> 5) * 4 + 15) & ~(size_t)15));
-    uint8_t* s_tk = reinterpret_cast<uint8_t*>(s_red + F_THREADS / 64 * 64);
+    uint16_t* xs = s_x;
+    float* xsum = s_xsum;
     stage_x(x, H, xs, is_q<WT>() ? xsum : nullptr);
     wait_flags(fl, G.nR, flags_needed(G.nR), tag, ws.sync);
     block_topk(tl, L.E, L.k, tag, ws.sync, s_tk, s_idx, s_gate);
@@ -547,9 +566,8 @@ __global__ __launch_bounds__(F_THREADS, 4) void k_decode1(LayerDev L, const uint
     const int e = s_idx[u];
     const uint8_t* dn = L.dn + (size_t)e * L.dn_stride;
     const uint16_t* dns = is_q<WT>() ? L.dn_s + (size_t)e * L.dn_s_stride : nullptr;
-    uint8_t* s_dn = smem + lds_down_off(H);
-    float dsc[F_RPT];
-    down_prefetch<WT, 32>(dn, dns, H, q, s_dn, dsc);
+    DownPre<WT> pre;
+    down_prefetch<WT, 32>(dn, dns, H, 32 * q, pre);
     const float hv = gate_up_h<WT, 64>(L.gu + (size_t)e * L.gu_stride,
                                        is_q<WT>() ? L.gu_s + (size_t)e * L.gu_s_stride : nullptr, H, 2 * I, q, 0, xs, xsum,
                                        s_red, s_h);
@@ -563,7 +581,7 @@ __global__ __launch_bounds__(F_THREADS, 4) void k_decode1(LayerDev L, const uint
       }
     }
     __syncthreads();
-    down_store<WT, 32>(dn, dns, H, q, s_dn, dsc, s_h, is_q<WT>() ? s_hsum : 0.0f, s_gate[u],
+    down_store<WT, 32>(dn, H, 32 * q, pre, s_h, is_q<WT>() ? s_hsum : 0.0f, s_gate[u],
                        part + (size_t)(G.nSG + b) * H, tag);
     raise_flag(fl + G.nR + G.nSG + b, tag);
   }
@@ -574,7 +592,7 @@ __global__ __launch_bounds__(F_THREADS, 4) void k_decode1(LayerDev L, const uint
   else if ((int)blockIdx.x >= extra0) d = first + ((int)blockIdx.x - extra0);
   if (d >= 0 && d < G.nD) {
     wait_flags(fl + G.nR, nP, flags_needed(nP), tag, ws.sync);
-    role_reduce(part, nP, H, d * F_RD, y, reinterpret_cast<float*>(smem), tag, ws.sync);
+    role_reduce(part, nP, H, d * F_RD, y, s_red, tag, ws.sync);
   }
   finish(ws.sync);
 }
@@ -583,10 +601,8 @@ __global__ __launch_bounds__(F_THREADS, 4) void k_decode1(LayerDev L, const uint
 // Host side
 // ---------------------------------------------------------------------------
 size_t decode1_lds(int H, int I, int k, bool has_shared) {
-  (void)I; (void)k; (void)has_shared;
-  // the prefetch fills all F_RPT blocks of F_THREADS rows (rows past H take a slot each)
-  const size_t a = lds_down_off(H) + (size_t)F_RPT * F_THREADS * 16, r = F_THREADS * 4;
-  return a > r ? a : r;
+  (void)H; (void)I; (void)k; (void)has_shared;
+  return 0;  // static arrays only
 }
 
 static int producers(int I, int k, bool has_shared) { return (has_shared ? I / 8 : 0) + k * (I / 32); }
@@ -600,9 +616,10 @@ size_t decode1_part_words(int H, int I, int k, bool has_shared) {
 }
 
 bool decode1_fits(int E, int H, int I, int k, bool has_shared) {
-  // F_NV logits per lane in the top-k, F_RPT down rows per thread, a 64 KiB
-  // LDS budget
-  return E <= 64 * F_NV && H <= F_RPT * F_THREADS && I <= 1024 && decode1_lds(H, I, k, has_shared) <= 65536;
+  // F_NV logits per lane in the top-k, F_RPT down rows per thread (the LDS
+  // arrays are sized for H <= F_HMAX)
+  (void)k; (void)has_shared;
+  return E <= 64 * F_NV && H <= F_HMAX && I <= 1024;
 }
 
 template <int WT, int SWT>
