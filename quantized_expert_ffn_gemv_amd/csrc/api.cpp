@@ -135,6 +135,7 @@ size_t carve_prefill(const moe_layer* L, int T, uint8_t* base, moe::PrefillWs* w
   w.counts = reinterpret_cast<int32_t*>(take(E * 4));
   w.offsets = reinterpret_cast<int32_t*>(take((E + 1) * 4));
   w.tile_start = reinterpret_cast<int32_t*>(take((E + 1) * 4));
+  w.tile_info = reinterpret_cast<int32_t*>(take(((size_t)T * k / moe::PF_BM + 1 + E) * moe::PF_TILE_INFO * 4));
   w.perm = reinterpret_cast<int32_t*>(take((size_t)T * k * 4));
   w.inv = reinterpret_cast<int32_t*>(take((size_t)T * k * 4));
   w.h = reinterpret_cast<uint16_t*>(take((size_t)T * k * I * 2));

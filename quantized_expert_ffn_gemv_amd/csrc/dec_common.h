@@ -113,10 +113,10 @@ __device__ __forceinline__ float wave_total_f32(float v) {
 //      = the key of rank k-1, and tv = the smallest fp64 value whose key
 //      truncates to tau's. Any value below tv is beaten by k lane bests, so
 //      it cannot be in the top-k;
-//   3. candidates = values >= tv, compacted to LDS without branches (a
-//      non-candidate writes to its lane's scratch slot);
+//   3. candidates = values >= tv, compacted to LDS (candidate lanes write);
 //   4. exact rank of each candidate among the candidates (fp64 value, then
-//      index) picks and orders the k winners.
+//      index; each candidate broadcast through scalar registers) picks and
+//      orders the k winners.
 // Only massively tied logits (more than TOPK_CMAX candidates) take the slow
 // path: k rounds of a wave arg-max. Order: larger logit first, lower expert
 // index on ties. Lane r < k ends with expert r and its renormalised gate,
@@ -183,7 +183,8 @@ __device__ __forceinline__ void wave_topk(const double (&v)[NV], int E, int k, i
   const uint64_t sel = __ballot(rank == k - 1);
   const uint32_t tau = (uint32_t)__builtin_amdgcn_readlane((int)key, __ffsll((long long)sel) - 1) & ~63u;
   const double tv = key_floor_value(tau);
-  // 3. candidates, compacted in (slot, lane) order
+  // 3. candidates, compacted in (slot, lane) order; only candidate lanes
+  //    write (a few per slot)
   int base = 0;
 #pragma unroll
   for (int i = 0; i < NV; i++) {
@@ -192,27 +193,26 @@ __device__ __forceinline__ void wave_topk(const double (&v)[NV], int E, int k, i
       const bool cand = (e < E) & (v[i] >= tv);
       const uint64_t bal = __ballot(cand);
       const int pos = base + __popcll(bal & ((1ull << lane) - 1ull));
-      const int slot = (cand & (pos < TOPK_CMAX)) ? pos : TOPK_CMAX + lane;
-      S_c[slot].v = v[i];
-      S_c[slot].i = e;
+      if (cand & (pos < TOPK_CMAX)) {
+        S_c[pos].v = v[i];
+        S_c[pos].i = e;
+      }
       base += __popcll(bal);
     }
   }
   const int nc = base;
   wave_lds_sync();
   if (nc <= 64) {
-    // 4. exact ranks: one candidate per lane against all (LDS broadcast reads)
-    const double cvv = (lane < nc) ? S_c[lane].v : -__builtin_inf();
-    const int cii = (lane < nc) ? S_c[lane].i : 0x7FFFFFFF;
-    int q0 = 0, q1 = 0, q2 = 0, q3 = 0;
-    for (int j = 0; j < nc; j += 4) {  // slots past nc hold scratch; masked
-      const TopkSlot a0 = S_c[j], a1 = S_c[j + 1], a2 = S_c[j + 2], a3 = S_c[j + 3];
-      q0 += topk_before(a0.v, a0.i, cvv, cii);
-      q1 += (j + 1 < nc) & topk_before(a1.v, a1.i, cvv, cii);
-      q2 += (j + 2 < nc) & topk_before(a2.v, a2.i, cvv, cii);
-      q3 += (j + 3 < nc) & topk_before(a3.v, a3.i, cvv, cii);
+    // 4. exact ranks: candidate c sits in lane c; each candidate in turn is
+    //    broadcast through scalar registers and every lane compares
+    const double cvv = (lane < nc) ? S_c[lane < nc ? lane : 0].v : -__builtin_inf();
+    const int cii = (lane < nc) ? S_c[lane < nc ? lane : 0].i : 0x7FFFFFFF;
+    int rk = 0;
+    for (int j = 0; j < nc; j++) {
+      const double sv = readlane_f64(cvv, j);
+      const int si = __builtin_amdgcn_readlane(cii, j);
+      rk += topk_before(sv, si, cvv, cii);
     }
-    const int rk = (q0 + q1) + (q2 + q3);
     if (lane < nc && rk < k) {
       S_o[rk].v = cvv;
       S_o[rk].i = cii;

@@ -68,6 +68,7 @@ struct PrefillWs {
   int32_t* counts;    // [E]
   int32_t* offsets;   // [E+1]
   int32_t* tile_start;// [E+1] routed GEMM M-tiles per expert, prefix summed
+  int32_t* tile_info; // [T*k/PF_BM + E][PF_TILE_INFO] per M tile: expert, first tile, tiles, row offset, rows
   int32_t* perm;      // [T*k] sorted position -> slot
   int32_t* inv;       // [T*k] slot -> sorted position
   uint16_t* h;        // [T*k][I] bf16, sorted order
@@ -96,6 +97,7 @@ hipError_t launch_fill(void* p, size_t bytes, hipStream_t st);
 
 // Prefill tiling constants shared by host sizing and kernels.
 constexpr int PF_BM = 96;           // max rows (tokens) per grouped-GEMM tile
+constexpr int PF_TILE_INFO = 8;     // int32 words per M-tile record (5 used, 32-byte aligned)
 constexpr int PF_TOK_PER_BLK = 256; // tokens per histogram block
 
 // Timer hooks (api.cpp). When the timer is on, a launch carries a start and

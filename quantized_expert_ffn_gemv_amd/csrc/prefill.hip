@@ -182,7 +182,7 @@ __global__ __launch_bounds__(256) void k_pf_count(const int32_t* __restrict__ id
 __global__ __launch_bounds__(1024) void k_pf_scan(const int32_t* __restrict__ blk_counts, int nblk, int E,
                                                    int32_t* __restrict__ blk_base, int32_t* __restrict__ counts,
                                                    int32_t* __restrict__ offsets, int32_t* __restrict__ tile_start,
-                                                   int32_t* counts_out) {
+                                                   int32_t* __restrict__ tile_info, int32_t* counts_out) {
   __shared__ int s_tot[1024];
   __shared__ int s_til[1024];
   const int e = threadIdx.x;
@@ -205,7 +205,15 @@ __global__ __launch_bounds__(1024) void k_pf_scan(const int32_t* __restrict__ bl
     const int off = s_tot[e] - tot;
     counts[e] = tot;
     offsets[e] = off;
-    tile_start[e] = s_til[e] - (tot + PF_BM - 1) / PF_BM;
+    const int ntiles = (tot + PF_BM - 1) / PF_BM;
+    const int ts = s_til[e] - ntiles;
+    tile_start[e] = ts;
+    // per M tile: its expert and the expert's tile range and rows, so a GEMM
+    // workgroup finds its tile with one lookup
+    for (int t = 0; t < ntiles; t++) {
+      int32_t* ti = tile_info + (size_t)PF_TILE_INFO * (ts + t);
+      ti[0] = e; ti[1] = ts; ti[2] = ntiles; ti[3] = off; ti[4] = tot;
+    }
     if (counts_out) counts_out[e] = tot;
     int run = off;
     for (int b = 0; b < nblk; b++) {
@@ -281,6 +289,7 @@ struct GemmArgs {
   // routed tiling (NULL offsets => single "expert" owning rows 0..M_total)
   const int32_t* offsets;     // [E+1]
   const int32_t* tile_start;  // [E+1]
+  const int32_t* tile_info;   // [tiles][PF_TILE_INFO]: expert, its first tile, its tiles, its row offset, its rows
   int E;
   int M_total;            // rows when offsets == NULL
   uint16_t* out;          // gate/up: h [rows][N/2]; down: Y [rows][N]
@@ -419,20 +428,14 @@ __global__ __launch_bounds__(G_THREADS, 2) void k_pf_gemm(GemmArgs g) {
 
   int e = 0, m0 = 0, M = 0, pos0 = 0, nt = 0;
   if (g.offsets) {
-    const int q = logical / NT;
-    int lo = 0, hi = g.E - 1;  // largest e with tile_start[e] <= q (a non-empty expert)
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (g.tile_start[mid] <= q) lo = mid; else hi = mid - 1;
-    }
-    e = lo;
-    const int ntiles = g.tile_start[e + 1] - g.tile_start[e];
-    const int pos = logical - NT * g.tile_start[e];
+    const int32_t* ti = g.tile_info + (size_t)PF_TILE_INFO * (logical / NT);  // M tile q = logical / NT
+    e = ti[0];
+    const int ntiles = ti[2];
+    const int pos = logical - NT * ti[1];
     nt = pos / ntiles;
     m0 = (pos - nt * ntiles) * PF_BM;
-    const int cnt = g.offsets[e + 1] - g.offsets[e];
-    M = min(PF_BM, cnt - m0);
-    pos0 = g.offsets[e] + m0;
+    M = min(PF_BM, ti[4] - m0);
+    pos0 = ti[3] + m0;
   } else {
     nt = logical / mt_total;
     m0 = (logical - nt * mt_total) * PF_BM;
@@ -646,19 +649,14 @@ __global__ __launch_bounds__(G_THREADS, 2) void k_pf_gemm_q(GemmArgs g) {
   if (ix >= per || logical >= total) return;
   int e = 0, m0 = 0, M = 0, pos0 = 0, nt = 0;
   if (g.offsets) {
-    const int q = logical / NT;
-    int lo = 0, hi = g.E - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (g.tile_start[mid] <= q) lo = mid; else hi = mid - 1;
-    }
-    e = lo;
-    const int ntiles = g.tile_start[e + 1] - g.tile_start[e];
-    const int pos = logical - NT * g.tile_start[e];
+    const int32_t* ti = g.tile_info + (size_t)PF_TILE_INFO * (logical / NT);  // M tile q = logical / NT
+    e = ti[0];
+    const int ntiles = ti[2];
+    const int pos = logical - NT * ti[1];
     nt = pos / ntiles;
     m0 = (pos - nt * ntiles) * PF_BM;
-    M = min(PF_BM, g.offsets[e + 1] - g.offsets[e] - m0);
-    pos0 = g.offsets[e] + m0;
+    M = min(PF_BM, ti[4] - m0);
+    pos0 = ti[3] + m0;
   } else {
     nt = logical / mt_total;
     m0 = (logical - nt * mt_total) * PF_BM;
@@ -671,13 +669,20 @@ __global__ __launch_bounds__(G_THREADS, 2) void k_pf_gemm_q(GemmArgs g) {
 
   // A rows of this lane's loads: load i covers slot rows 4 (G_ALOADS wave + i) + lane / 16
   // (rows past M read row 0 of the matrix: finite values whose results are dropped)
+  // (loads unconditional with clamped indices: a load inside a branch makes
+  // the compiler wait for it before going on, one round trip per row)
   uint32_t arow[G_ALOADS];
+  int pv[G_ALOADS];
 #pragma unroll
   for (int i = 0; i < G_ALOADS; i++) {
     const int row = 4 * (G_ALOADS * wave + i) + (lane >> 4);
-    int r = 0;
-    if (row < M) r = (KIND == GK_GATE_UP && g.perm) ? g.perm[pos0 + row] / g.k : pos0 + row;
-    arow[i] = (uint32_t)r;
+    pv[i] = (KIND == GK_GATE_UP && g.perm) ? g.perm[pos0 + min(row, M - 1)] : 0;
+  }
+#pragma unroll
+  for (int i = 0; i < G_ALOADS; i++) {
+    const int row = 4 * (G_ALOADS * wave + i) + (lane >> 4);
+    const int r = (KIND == GK_GATE_UP && g.perm) ? pv[i] / g.k : pos0 + row;
+    arow[i] = (uint32_t)(row < M ? r : 0);
   }
 
   floatx4_t acc[G_MSUB][NSW];
@@ -903,7 +908,7 @@ static hipError_t route_steps(const LayerDev& L, const uint16_t* x, int T, int32
   const int nblk = (T + PF_TOK_PER_BLK - 1) / PF_TOK_PER_BLK;
   (void)launch_k(KC_PF_COUNT, k_pf_count, dim3(nblk), dim3(256), E * sizeof(int), st, ws.idx, T, E, k, ws.blk_counts);
   (void)launch_k(KC_PF_SCAN, k_pf_scan, dim3(1), dim3(1024), 0, st, ws.blk_counts, nblk, E, ws.blk_base, ws.counts,
-                     ws.offsets, ws.tile_start, counts_out);
+                     ws.offsets, ws.tile_start, ws.tile_info, counts_out);
   if (!permute) return hipGetLastError();
   (void)launch_k(KC_PF_SCATTER, k_pf_scatter, dim3(nblk), dim3(256), E * sizeof(int), st, ws.idx, T, E, k, ws.blk_base, ws.perm,
                      ws.inv);
@@ -951,7 +956,7 @@ hipError_t launch_prefill(const LayerDev& L, const uint16_t* x, int T, uint16_t*
     GemmArgs g{};
     g.w = L.gu; g.ws = quant ? L.gu_s : nullptr; g.w_stride = L.gu_stride; g.ws_stride = L.gu_s_stride;
     g.N = 2 * I; g.K = H; g.a = x; g.perm = ws.perm; g.k = k;
-    g.offsets = ws.offsets; g.tile_start = ws.tile_start; g.E = E; g.out = ws.h;
+    g.offsets = ws.offsets; g.tile_start = ws.tile_start; g.tile_info = ws.tile_info; g.E = E; g.out = ws.h;
     gemm_dispatch<GK_GATE_UP>(KC_PF_GATE_UP, L.wt, g, max_tiles, st);
   }
   // shared gate/up
@@ -966,7 +971,7 @@ hipError_t launch_prefill(const LayerDev& L, const uint16_t* x, int T, uint16_t*
     GemmArgs g{};
     g.w = L.dn; g.ws = quant ? L.dn_s : nullptr; g.w_stride = L.dn_stride; g.ws_stride = L.dn_s_stride;
     g.N = H; g.K = I; g.a = ws.h; g.perm = nullptr; g.k = k;
-    g.offsets = ws.offsets; g.tile_start = ws.tile_start; g.E = E; g.out = ws.Y;
+    g.offsets = ws.offsets; g.tile_start = ws.tile_start; g.tile_info = ws.tile_info; g.E = E; g.out = ws.Y;
     gemm_dispatch<GK_DOWN>(KC_PF_DOWN, L.wt, g, max_tiles, st);
   }
   if (L.swt != MOE_W_NONE) {
