@@ -49,16 +49,17 @@ def decode_expert_bytes(L):
     return gu, dn, sgu, sdn
 
 
-def run_decode(moe, torch, L, x_bits, steps, warmup):
+def run_decode(moe, torch, L, x_bits, steps, warmup, B=1):
+    """Consecutive decode calls of B tokens over x; (eager s, graph s) per pass."""
     T, H = x_bits.shape
     dev = torch.device("cuda")
     xd = torch.from_numpy(x_bits.view(np.int16)).to(dev)
     y = torch.empty((T, H), dtype=torch.int16, device=dev)
-    ws = moe.make_workspace(L, 1, 0)
+    ws = moe.make_workspace(L, B, 0)
 
     def seq():
-        for t in range(T):
-            moe.moe_forward_decode(L, xd[t:t + 1], y[t:t + 1], ws)
+        for t in range(0, T, B):
+            moe.moe_forward_decode(L, xd[t:t + B], y[t:t + B], ws)
 
     # eager
     seq()
@@ -87,6 +88,47 @@ def run_decode(moe, torch, L, x_bits, steps, warmup):
     torch.cuda.synchronize()
     graph_s = (time.perf_counter() - t0) / steps
     return eager_s, graph_s, g
+
+
+def run_c2(moe, torch, synth, steps, warmup):
+    """The Q3 / Zipf-routed layer: 256 tokens as batch-1 calls and as 32
+    batch-8 calls (graph replays). Bytes per call count each unique routed
+    expert once (the weights an expert chosen by several tokens of a call
+    are read once), plus the shared expert and the router."""
+    name = "decode_q3_zipf"
+    host = synth.make_layer(name, threads=16)
+    x = synth.make_tokens(name)
+    L = moe.DeviceLayer(host)
+    T = x.shape[0]
+    gu, dn, sgu, sdn = decode_expert_bytes(L)
+    router_bytes = L.E * L.H * 4
+    out = {"workload": "one MoE layer, Q3 experts (32-elem blocks, fp16 scales), Zipf-skewed router bias "
+                       "(hottest 20% of experts take 80% of selections), bf16 shared, fp32 router; 256 tokens"}
+    dev = torch.device("cuda")
+    xd = torch.from_numpy(x.view(np.int16)).to(dev)
+    for B in (1, 8):
+        _, graph_s, g = run_decode(moe, torch, L, x, steps, warmup, B=B)
+        del g
+        # unique routed experts per call, from the routing of the same calls
+        idx = torch.empty((T, L.k), dtype=torch.int32, device=dev)
+        yy = torch.empty_like(xd)
+        ws = moe.make_workspace(L, B, 0)
+        for t in range(0, T, B):
+            moe.moe_forward_decode(L, xd[t:t + B], yy[t:t + B], ws, topk_idx=idx[t:t + B])
+        torch.cuda.synchronize()
+        ih = idx.cpu().numpy()
+        uniq = [len(np.unique(ih[t:t + B])) for t in range(0, T, B)]
+        calls = len(uniq)
+        bytes_total = sum(u * (gu + dn) for u in uniq) + calls * (sgu + sdn + router_bytes)
+        out["b%d" % B] = {
+            "tokens_per_s": round(T / graph_s, 1),
+            "us_per_call": round(graph_s / calls * 1e6, 3),
+            "unique_experts_per_call": round(float(np.mean(uniq)), 2),
+            "weight_bytes_per_call": round(bytes_total / calls),
+            "effective_GBps": round(bytes_total / graph_s / 1e9, 1),
+            "frac_of_hbm": round(bytes_total / graph_s / 1e9 / HBM_PEAK_GBS, 4),
+        }
+    return out
 
 
 def kernel_times(moe, torch, fn, reps=1):
@@ -387,6 +429,12 @@ def main():
         },
     }
     del g
+
+    # ---------------------------------------------------------------- Q3 / Zipf decode, batch 1 and 8 (secondary)
+    if not args.no_prefill:
+        log("decode Q3 Zipf, batch 1 and 8 ...")
+        result["decode_q3_zipf"] = run_c2(moe, torch, synth, args.steps, args.warmup)
+        log("decode_q3_zipf:", json.dumps(result["decode_q3_zipf"]))
 
     # ---------------------------------------------------------------- prefill (secondary)
     if not args.no_prefill:

@@ -152,11 +152,14 @@ __global__ __launch_bounds__(DA_THREADS) void k_dec_a(LayerDev L, const uint16_t
     for (int t = 0; t < MAXB; t++) acc[t] = 0.0;
     for (int c0 = 0; c0 < n4; c0 += 64 * A_CPR) {
       float4 w[A_CPR];
+      // loads with clamped indices and no branch (a load inside a branch makes
+      // the compiler wait for every load in flight where the branch joins);
+      // elements past the row are masked after
 #pragma unroll
-      for (int i = 0; i < A_CPR; i++) {
-        const int c = c0 + lane + 64 * i;
-        w[i] = (valid && c < n4) ? wr[c] : make_float4(0.f, 0.f, 0.f, 0.f);
-      }
+      for (int i = 0; i < A_CPR; i++) w[i] = wr[min(c0 + lane + 64 * i, n4 - 1)];
+#pragma unroll
+      for (int i = 0; i < A_CPR; i++)
+        if (!(valid && c0 + lane + 64 * i < n4)) w[i] = make_float4(0.f, 0.f, 0.f, 0.f);
       if (c0 == 0) {
         stage_tokens<DA_THREADS>(x, B, H, xs, nullptr);
         __syncthreads();
@@ -204,20 +207,16 @@ __global__ __launch_bounds__(DA_THREADS) void k_dec_a(LayerDev L, const uint16_t
   // first batch of down pieces is issued together with the gate/up loads
   DownPiece<SWT, 4> dp[A_RPT];
 #pragma unroll
-  for (int i = 0; i < A_RPT; i++) {
-    const int rw = threadIdx.x + DA_THREADS * i;
-    if (rw < H) load_down_piece<SWT, 4>(L.sdn, nullptr, H, rw, col0, dp[i]);
-  }
+  for (int i = 0; i < A_RPT; i++)  // clamped, unconditional (rows past H are not used)
+    load_down_piece<SWT, 4>(L.sdn, nullptr, H, min((int)threadIdx.x + DA_THREADS * i, H - 1), col0, dp[i]);
   float acc[MAXB];
 #pragma unroll
   for (int t = 0; t < MAXB; t++) acc[t] = 0.0f;
   for (int c0 = 0; c0 < nc; c0 += 64 * A_CPS) {
     Raw raw[A_CPS];
 #pragma unroll
-    for (int i = 0; i < A_CPS; i++) {
-      const int c = c0 + kp + 64 * i;
-      if (c < nc) raw[i] = load_chunk<SWT>(L.sgu, (size_t)c * R + row);
-    }
+    for (int i = 0; i < A_CPS; i++)  // clamped, unconditional (chunks past the row are not used)
+      raw[i] = load_chunk<SWT>(L.sgu, (size_t)min(c0 + kp + 64 * i, nc - 1) * R + row);
     if (c0 == 0) {
       stage_tokens<DA_THREADS>(x, B, H, xs, nullptr);
       __syncthreads();
@@ -261,10 +260,8 @@ __global__ __launch_bounds__(DA_THREADS) void k_dec_a(LayerDev L, const uint16_t
   for (int r0 = 0; r0 < H; r0 += DA_THREADS * A_RPT) {
     if (r0 > 0) {
 #pragma unroll
-      for (int i = 0; i < A_RPT; i++) {
-        const int rw = r0 + threadIdx.x + DA_THREADS * i;
-        if (rw < H) load_down_piece<SWT, 4>(L.sdn, nullptr, H, rw, col0, dp[i]);
-      }
+      for (int i = 0; i < A_RPT; i++)
+        load_down_piece<SWT, 4>(L.sdn, nullptr, H, min(r0 + (int)threadIdx.x + DA_THREADS * i, H - 1), col0, dp[i]);
     }
 #pragma unroll
     for (int i = 0; i < A_RPT; i++) {
@@ -314,10 +311,11 @@ __global__ __launch_bounds__(DB_THREADS) void k_dec_b(LayerDev L, const uint16_t
   double lv[16];
   const int tw = wave;  // B <= 8 = waves: one token per wave
 #pragma unroll
-  for (int i = 0; i < 16; i++) {
-    const int e = lane + 64 * i;
-    lv[i] = (tw < B && e < E) ? ws.logits[(size_t)tw * E + e] : -__builtin_inf();
-  }
+  for (int i = 0; i < 16; i++)  // clamped, unconditional; masked after
+    lv[i] = ws.logits[(size_t)min(tw, B - 1) * E + min(lane + 64 * i, E - 1)];
+#pragma unroll
+  for (int i = 0; i < 16; i++)
+    if (!(tw < B && lane + 64 * i < E)) lv[i] = -__builtin_inf();
   stage_tokens<DB_THREADS>(x, B, H, xs, QT ? xsum : nullptr);
   if (tw < B) {
     int mi;
@@ -392,10 +390,8 @@ __global__ __launch_bounds__(DB_THREADS) void k_dec_b(LayerDev L, const uint16_t
   const int col0 = 16 * q;
   DownPiece<WT, 16> dp[B_RPT];
 #pragma unroll
-  for (int i = 0; i < B_RPT; i++) {
-    const int rw = threadIdx.x + DB_THREADS * i;
-    if (rw < H) load_down_piece<WT, 16>(wdn, wds, H, rw, col0, dp[i]);
-  }
+  for (int i = 0; i < B_RPT; i++)  // clamped, unconditional (rows past H are not used)
+    load_down_piece<WT, 16>(wdn, wds, H, min((int)threadIdx.x + DB_THREADS * i, H - 1), col0, dp[i]);
   const int nb = H >> 5;
   float acc[MAXB];
 #pragma unroll
@@ -404,12 +400,11 @@ __global__ __launch_bounds__(DB_THREADS) void k_dec_b(LayerDev L, const uint16_t
     Raw raw[B_CPT];
     float sc[B_CPT];
 #pragma unroll
-    for (int i = 0; i < B_CPT; i++) {
-      const int c = c0 + kp + 16 * i;
-      if (c < nc) {
-        raw[i] = load_chunk<WT>(wgu, (size_t)c * R + row);
-        if constexpr (QT) sc[i] = f16_to_f32(wgs[(size_t)c * R + row]);
-      }
+    for (int i = 0; i < B_CPT; i++)  // clamped, unconditional (chunks past the row are not used)
+      raw[i] = load_chunk<WT>(wgu, (size_t)min(c0 + kp + 16 * i, nc - 1) * R + row);
+    if constexpr (QT) {
+#pragma unroll
+      for (int i = 0; i < B_CPT; i++) sc[i] = f16_to_f32(wgs[(size_t)min(c0 + kp + 16 * i, nc - 1) * R + row]);
     }
 #pragma unroll
     for (int t = 0; t < MAXB; t++) {
@@ -467,10 +462,8 @@ __global__ __launch_bounds__(DB_THREADS) void k_dec_b(LayerDev L, const uint16_t
   for (int r0 = 0; r0 < H; r0 += DB_THREADS * B_RPT) {
     if (r0 > 0) {
 #pragma unroll
-      for (int i = 0; i < B_RPT; i++) {
-        const int rw = r0 + threadIdx.x + DB_THREADS * i;
-        if (rw < H) load_down_piece<WT, 16>(wdn, wds, H, rw, col0, dp[i]);
-      }
+      for (int i = 0; i < B_RPT; i++)
+        load_down_piece<WT, 16>(wdn, wds, H, min(r0 + (int)threadIdx.x + DB_THREADS * i, H - 1), col0, dp[i]);
     }
 #pragma unroll
     for (int i = 0; i < B_RPT; i++) {
