@@ -112,6 +112,7 @@ size_t carve_decode(const moe_layer* L, int B, uint8_t* base, moe::DecodeWs* ws)
     w.part_words = reinterpret_cast<uint64_t*>(take(8 * moe::decode1_part_words(L->hidden, L->inter, L->top_k, has_s)));
   } else {
     w.part = reinterpret_cast<float*>(take((size_t)B * (k * (I / 16) + I / 4) * L->hidden * 4));
+    w.route = reinterpret_cast<int32_t*>(take((4 + 4 * 8 * 16) * 4));
   }
   if (ws) *ws = w;
   return off;
@@ -195,7 +196,7 @@ const char* const kKernelNames[moe::KC_COUNT] = {
     "dec_fused",         "dec_router_shared", "dec_routed", "dec_reduce",         "pf_router",         "pf_topk",
     "pf_count",          "pf_scan",     "pf_scatter",       "pf_gate_up",        "pf_down",
     "pf_shared_gate_up", "pf_shared_down", "pf_combine",    "rmsnorm",           "residual_add",
-    "fill"};
+    "fill",              "dec_route"};
 
 }  // namespace
 

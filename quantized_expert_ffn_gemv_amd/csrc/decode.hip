@@ -280,34 +280,31 @@ __global__ __launch_bounds__(DA_THREADS) void k_dec_a(LayerDev L, const uint16_t
 }
 
 // ---------------------------------------------------------------------------
-// Kernel B: routing + routed experts, one (unique expert, 16 columns) each
+// Routing of the batch (one workgroup): top-k of each token (one wave per
+// token) and the unique experts of the batch in first-occurrence (slot)
+// order with the tokens using each, written to the workspace for kernel B.
+// Route record: [0] unique count, then idx[MAXB*16], gate bits[MAXB*16],
+// unique experts[MAXB*16], token masks[MAXB*16].
 // ---------------------------------------------------------------------------
-constexpr int B_CPT = 4;  // gate/up chunks per lane and batch
-constexpr int B_RPT = 4;  // down rows per thread and batch
+constexpr int ROUTE_MAXS = 8 * 16;  // slots of the largest batch
+__device__ __forceinline__ int32_t* route_idx(int32_t* r) { return r + 4; }
+__device__ __forceinline__ int32_t* route_gate(int32_t* r) { return r + 4 + ROUTE_MAXS; }
+__device__ __forceinline__ int32_t* route_uniq(int32_t* r) { return r + 4 + 2 * ROUTE_MAXS; }
+__device__ __forceinline__ int32_t* route_mask(int32_t* r) { return r + 4 + 3 * ROUTE_MAXS; }
 
-template <int WT, int MAXB>
-__global__ __launch_bounds__(DB_THREADS) void k_dec_b(LayerDev L, const uint16_t* __restrict__ x, int B, DecodeWs ws,
-                                                      int32_t* idx_out, float* gate_out) {
-  const int H = L.H, I = L.I, E = L.E, k = L.k;
+template <int MAXB>
+__global__ __launch_bounds__(DB_THREADS) void k_dec_route(int E, int k, int B, DecodeWs ws, int32_t* idx_out,
+                                                          float* gate_out) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   __shared__ int s_idx[MAXB * 16];
   __shared__ float s_gate[MAXB * 16];
-  __shared__ int s_uniq[MAXB * 16];
-  __shared__ uint32_t s_mask[MAXB * 16];
   __shared__ int s_uid[MAXB * 16];
+  __shared__ uint32_t s_msk[MAXB * 16];
   __shared__ int s_wcnt[DB_THREADS / 64];
-  __shared__ int s_nu;
-  __shared__ float s_gu[MAXB * 32];
-  __shared__ uint32_t s_hp[MAXB * 8];
-  __shared__ float s_hs[MAXB];
   extern __shared__ __align__(16) uint8_t smem[];
-  constexpr bool QT = is_q<WT>();
-  uint16_t* xs = reinterpret_cast<uint16_t*>(smem);
-  float* xsum = reinterpret_cast<float*>(smem + (size_t)B * H * 2);
-  uint8_t* tks = reinterpret_cast<uint8_t*>(xsum + (QT ? ((B * (H >> 5) + 1) & ~1) : 0));
-  int* mark = reinterpret_cast<int*>(tks);  // reuses the top-k scratch after the top-k
-
-  // 1. logits of this wave's token (issued first), the activations, then the top-k
+  uint8_t* tks = smem;                        // [B] top-k scratch
+  int* mark = reinterpret_cast<int*>(smem);   // reuses it after the top-k
+  int32_t* rt = ws.route;
   double lv[16];
   const int tw = wave;  // B <= 8 = waves: one token per wave
 #pragma unroll
@@ -316,7 +313,6 @@ __global__ __launch_bounds__(DB_THREADS) void k_dec_b(LayerDev L, const uint16_t
 #pragma unroll
   for (int i = 0; i < 16; i++)
     if (!(tw < B && lane + 64 * i < E)) lv[i] = -__builtin_inf();
-  stage_tokens<DB_THREADS>(x, B, H, xs, QT ? xsum : nullptr);
   if (tw < B) {
     int mi;
     float mg;
@@ -328,14 +324,19 @@ __global__ __launch_bounds__(DB_THREADS) void k_dec_b(LayerDev L, const uint16_t
   }
   __syncthreads();
   const int nslot = B * k;
+  for (int i = threadIdx.x; i < nslot; i += DB_THREADS) {
+    route_idx(rt)[i] = s_idx[i];
+    route_gate(rt)[i] = __float_as_int(s_gate[i]);
+    if (idx_out) idx_out[i] = s_idx[i];
+    if (gate_out) gate_out[i] = s_gate[i];
+  }
   if constexpr (MAXB == 1) {
     if ((int)threadIdx.x < k) {
-      s_uniq[threadIdx.x] = s_idx[threadIdx.x];
-      s_mask[threadIdx.x] = 1u;
+      route_uniq(rt)[threadIdx.x] = s_idx[threadIdx.x];
+      route_mask(rt)[threadIdx.x] = 1;
     }
-    if (threadIdx.x == 0) s_nu = k;
+    if (threadIdx.x == 0) rt[0] = k;
   } else {
-    // unique experts in first-occurrence (slot) order and the tokens using each
     for (int e = threadIdx.x; e < E; e += DB_THREADS) mark[e] = 0x7FFFFFFF;
     __syncthreads();
     if ((int)threadIdx.x < nslot) atomicMin(&mark[s_idx[threadIdx.x]], (int)threadIdx.x);
@@ -347,36 +348,71 @@ __global__ __launch_bounds__(DB_THREADS) void k_dec_b(LayerDev L, const uint16_t
     int base = 0;
     for (int wv = 0; wv < wave; wv++) base += s_wcnt[wv];
     const int rank = base + __popcll(bal & ((1ull << lane) - 1ull));
-    if (first) {
-      s_uniq[rank] = s_idx[threadIdx.x];
-      s_mask[rank] = 0u;
-      s_uid[threadIdx.x] = rank;
+    if (first) s_uid[threadIdx.x] = rank;
+    if ((int)threadIdx.x < nslot) s_msk[threadIdx.x] = 0u;
+    __syncthreads();
+    // each unique expert's token mask: the bits of the tokens that chose it
+    if ((int)threadIdx.x < nslot) {
+      const int u = s_uid[mark[s_idx[threadIdx.x]]];
+      if (first) route_uniq(rt)[u] = s_idx[threadIdx.x];
+      atomicOr(&s_msk[u], 1u << (threadIdx.x / k));
     }
+    __syncthreads();
+    if ((int)threadIdx.x < nslot) route_mask(rt)[threadIdx.x] = (int32_t)s_msk[threadIdx.x];
     if (threadIdx.x == 0) {
       int n = 0;
       for (int wv = 0; wv < DB_THREADS / 64; wv++) n += s_wcnt[wv];
-      s_nu = n;
+      rt[0] = n;
     }
-    __syncthreads();
-    if ((int)threadIdx.x < nslot) atomicOr(&s_mask[s_uid[mark[s_idx[threadIdx.x]]]], 1u << (threadIdx.x / k));
   }
+}
+
+// ---------------------------------------------------------------------------
+// Kernel B: routed experts, one (unique expert, 16 columns) each
+// ---------------------------------------------------------------------------
+constexpr int B_CPT = 4;  // gate/up chunks per lane and batch
+constexpr int B_RPT = 4;  // down rows per thread and batch
+
+template <int WT, int MAXB>
+__global__ __launch_bounds__(DB_THREADS) void k_dec_b(LayerDev L, const uint16_t* __restrict__ x, int B, DecodeWs ws) {
+  const int H = L.H, I = L.I, k = L.k;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __shared__ int s_idx[MAXB * 16];
+  __shared__ float s_gate[MAXB * 16];
+  __shared__ int s_uniq[MAXB * 16];
+  __shared__ uint32_t s_mask[MAXB * 16];
+  __shared__ int s_nu;
+  __shared__ float s_gu[MAXB * 32];
+  __shared__ uint32_t s_hp[MAXB * 8];
+  __shared__ float s_hs[MAXB];
+  extern __shared__ __align__(16) uint8_t smem[];
+  constexpr bool QT = is_q<WT>();
+  uint16_t* xs = reinterpret_cast<uint16_t*>(smem);
+  float* xsum = reinterpret_cast<float*>(smem + (size_t)B * H * 2);
+  (void)lane;
+
+  // 1. the batch's routing (from the routing kernel)
+  const int32_t* rt = ws.route;
+  const int nslot = B * k;
+  if ((int)threadIdx.x < nslot) {
+    s_idx[threadIdx.x] = route_idx(ws.route)[threadIdx.x];
+    s_gate[threadIdx.x] = __int_as_float(route_gate(ws.route)[threadIdx.x]);
+    s_uniq[threadIdx.x] = route_uniq(ws.route)[threadIdx.x];
+    s_mask[threadIdx.x] = (uint32_t)route_mask(ws.route)[threadIdx.x];
+  }
+  if (threadIdx.x == 0) s_nu = rt[0];
   __syncthreads();
   const int nu = s_nu;
-  if (blockIdx.x == 0) {
-    for (int i = threadIdx.x; i < nslot; i += DB_THREADS) {
-      if (idx_out) idx_out[i] = s_idx[i];
-      if (gate_out) gate_out[i] = s_gate[i];
-    }
-  }
   const int gpe = I >> 4;  // 16-column groups per expert
   const int u = blockIdx.x / gpe;
-  if (u >= nu) return;
+  if (u >= nu) return;  // uniform
   const int q = blockIdx.x - u * gpe;
   const int e = s_uniq[u];
   const uint32_t mask = s_mask[u];
 
   // 2. loads: 32 gate/up rows (wave w: rows 4w..4w+3 of group q; lane -> row 4w + lane/16,
-  //    kpart lane%16) and the 16-column down piece of rows tid + 512 i
+  //    kpart lane%16) and the 16-column down piece of rows tid + 512 i; every load of the
+  //    first batch is issued before any wait (unconditional, clamped indices)
   constexpr int KC = kchunk<WT>();
   const int R = 2 * I;
   const int rr = 4 * wave + (lane >> 4);
@@ -390,22 +426,23 @@ __global__ __launch_bounds__(DB_THREADS) void k_dec_b(LayerDev L, const uint16_t
   const int col0 = 16 * q;
   DownPiece<WT, 16> dp[B_RPT];
 #pragma unroll
-  for (int i = 0; i < B_RPT; i++)  // clamped, unconditional (rows past H are not used)
+  for (int i = 0; i < B_RPT; i++)  // rows past H are not used
     load_down_piece<WT, 16>(wdn, wds, H, min((int)threadIdx.x + DB_THREADS * i, H - 1), col0, dp[i]);
   const int nb = H >> 5;
   float acc[MAXB];
 #pragma unroll
   for (int t = 0; t < MAXB; t++) acc[t] = 0.0f;
-  for (int c0 = 0; c0 < nc; c0 += 16 * B_CPT) {
-    Raw raw[B_CPT];
-    float sc[B_CPT];
+  Raw raw[B_CPT];
+  float sc[B_CPT];
+  auto load_batch = [&](int c0) {  // chunks past the row are not used
 #pragma unroll
-    for (int i = 0; i < B_CPT; i++)  // clamped, unconditional (chunks past the row are not used)
-      raw[i] = load_chunk<WT>(wgu, (size_t)min(c0 + kp + 16 * i, nc - 1) * R + row);
+    for (int i = 0; i < B_CPT; i++) raw[i] = load_chunk<WT>(wgu, (size_t)min(c0 + kp + 16 * i, nc - 1) * R + row);
     if constexpr (QT) {
 #pragma unroll
       for (int i = 0; i < B_CPT; i++) sc[i] = f16_to_f32(wgs[(size_t)min(c0 + kp + 16 * i, nc - 1) * R + row]);
     }
+  };
+  auto compute_batch = [&](int c0) {
 #pragma unroll
     for (int t = 0; t < MAXB; t++) {
       if (t < B && (mask >> t & 1u)) {
@@ -421,6 +458,40 @@ __global__ __launch_bounds__(DB_THREADS) void k_dec_b(LayerDev L, const uint16_t
         }
       }
     }
+  };
+  load_batch(0);
+  // the activations of this expert's tokens only (a token's row at xs + t H),
+  // with their 32-element block sums, while the weights are in flight
+  {
+    const int na = __popc(mask & ((1u << B) - 1u));
+    const int n16 = H / 8;
+    for (int i = threadIdx.x; i < na * n16; i += DB_THREADS) {
+      const int a = i / n16;
+      uint32_t m = mask;
+      for (int j = 0; j < a; j++) m &= m - 1u;  // drop the a lowest tokens
+      const int t = __ffs(m) - 1;
+      const int c = i - a * n16;
+      reinterpret_cast<uint4*>(xs + (size_t)t * H)[c] = reinterpret_cast<const uint4*>(x + (size_t)t * H)[c];
+    }
+    if (QT) {
+      __syncthreads();
+      for (int i = threadIdx.x; i < B * nb; i += DB_THREADS) {
+        const int t = i / nb;
+        if (mask >> t & 1u) {
+          const uint32_t* v = reinterpret_cast<const uint32_t*>(xs + (size_t)i * 32);
+          float sum = 0.0f;
+#pragma unroll
+          for (int j = 0; j < 16; j++) sum += bf16_lo(v[j]) + bf16_hi(v[j]);
+          xsum[i] = sum;
+        }
+      }
+    }
+    __syncthreads();
+  }
+  compute_batch(0);
+  for (int c0 = 16 * B_CPT; c0 < nc; c0 += 16 * B_CPT) {
+    load_batch(c0);
+    compute_batch(c0);
   }
 #pragma unroll
   for (int t = 0; t < MAXB; t++) {
@@ -527,11 +598,10 @@ __global__ __launch_bounds__(DC_THREADS) void k_dec_c(const float* __restrict__ 
 // Host launch
 // ---------------------------------------------------------------------------
 size_t decode_lds_b(int wt, int B, int H, int E, int k) {
+  (void)E; (void)k;
   const bool q = (wt == MOE_W_Q4 || wt == MOE_W_Q3);
   const size_t xsb = q ? (size_t)((B * (H / 32) + 1) & ~1) * 4 : 0;
-  const size_t tk = (size_t)B * TOPK_SCRATCH;
-  const size_t mk = (B > 1) ? (size_t)E * 4 : 0;
-  return (size_t)B * H * 2 + xsb + (tk > mk ? tk : mk);
+  return (size_t)B * H * 2 + xsb;
 }
 
 template <int WT, int SWT, int MAXB>
@@ -548,10 +618,16 @@ static hipError_t launch_t(const LayerDev& L, const uint16_t* x, int B, uint16_t
     if (err != hipSuccess) return err;
   }
   {
+    const size_t tk = (size_t)B * TOPK_SCRATCH, mk = (size_t)E * 4;
+    (void)launch_k(KC_DEC_ROUTE, (k_dec_route<MAXB>), dim3(1), dim3(DB_THREADS), tk > mk ? tk : mk, st, E, k, B, ws,
+                   idx_out, gate_out);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  {
     const int maxU = (B * k < E) ? B * k : E;
     const size_t lds = decode_lds_b(WT, B, H, E, k);
-    (void)launch_k(KC_DEC_GATE_UP, (k_dec_b<WT, MAXB>), dim3(maxU * (I / 16)), dim3(DB_THREADS), lds, st, L, x, B, ws, idx_out,
-                       gate_out);
+    (void)launch_k(KC_DEC_GATE_UP, (k_dec_b<WT, MAXB>), dim3(maxU * (I / 16)), dim3(DB_THREADS), lds, st, L, x, B, ws);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }

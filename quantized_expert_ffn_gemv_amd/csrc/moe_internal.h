@@ -13,7 +13,7 @@ namespace moe {
 enum KernelClass {
   KC_DEC_FUSED = 0,          // batch-1 decode, one kernel
   KC_DEC_ROUTER_SHARED,      // router logits + the whole shared expert
-  KC_DEC_GATE_UP,            // top-k + routed experts (gate/up, SwiGLU, partial down)
+  KC_DEC_GATE_UP,            // routed experts (gate/up, SwiGLU, partial down)
   KC_DEC_DOWN,               // sum of the partial down products
   KC_PF_ROUTER,
   KC_PF_TOPK,
@@ -28,6 +28,7 @@ enum KernelClass {
   KC_NORM,
   KC_RESIDUAL,
   KC_FILL,
+  KC_DEC_ROUTE,              // top-k of a batch and its unique experts (B > 1 path)
   KC_COUNT
 };
 
@@ -56,6 +57,7 @@ struct DecodeWs {
   float* part;     // three-kernel path: [B*k*(I/16) + B*(I/4)][H] partial down products
   uint64_t* flags; // one-kernel path: per-producer tagged flag words, rotating slots
   uint64_t* part_words;  // one-kernel path: [producers][H] tagged partial down products (fp32 bits)
+  int32_t* route;        // three-kernel path: the batch's routing (count, idx, gates, unique experts, masks)
 };
 
 // Prefill workspace.
