@@ -173,8 +173,9 @@ moe_status moe_route(const moe_layer *layer, const void *x, int32_t T,
  * fused dequantise-GEMV streams each selected expert once per call (experts
  * chosen by several tokens of the batch are read once). B = 1 runs as one
  * kernel (router, top-k, gate/up, SwiGLU, down and combine) when
- * I <= 1024 and its LDS need fits 64 KiB; otherwise, and for B > 1, as
- * three kernels. topk_idx/topk_gate ([B][k]) are optional outputs (NULL to
+ * E <= 512, H <= 2048 and I <= 1024; otherwise, and for B > 1, as four
+ * kernels (router and shared expert, routing of the batch, routed experts,
+ * sum of the partial products). topk_idx/topk_gate ([B][k]) are optional outputs (NULL to
  * skip). Workspace: moe_workspace_bytes(layer, B, 0), initialised once as
  * described above. */
 moe_status moe_forward_decode(const moe_layer *layer, const void *x, int32_t B, void *y,

@@ -1,19 +1,22 @@
-// Decode path: one MoE layer for B <= 8 tokens as three kernels. (Batch 1
+// Decode path: one MoE layer for B <= 8 tokens as four kernels. (Batch 1
 // takes the one-kernel path of decode1.hip whenever its shape fits there.)
 //
-//   A  k_dec_a : router logits in fp64 (one wave per expert row; an fp32
-//                weight times a bf16 activation is exact in fp64), and the
-//                whole shared expert: each workgroup owns 4 intermediate
-//                columns, computes them (gate/up GEMV + SwiGLU) and their
-//                contribution to every output row (a partial down product).
-//   B  k_dec_b : ordered top-k and renormalised gates (every workgroup
-//                derives them from the logits), the batch's unique-expert
-//                list, then per (selected expert, 16 intermediate columns):
-//                fused dequantise-GEMV of the 32 gate/up rows, SwiGLU, and
-//                the gated partial down product over those 16 columns. The
-//                down weights are loaded together with the gate/up weights,
-//                so the down projection adds no memory round trip.
-//   C  k_dec_c : y = sum of the partial products, in a fixed order.
+//   A  k_dec_a     : router logits in fp64 (one wave per expert row; an fp32
+//                    weight times a bf16 activation is exact in fp64), and
+//                    the whole shared expert: each workgroup owns 4
+//                    intermediate columns, computes them (gate/up GEMV +
+//                    SwiGLU) and their contribution to every output row (a
+//                    partial down product).
+//   R  k_dec_route : one workgroup: ordered top-k and renormalised gates of
+//                    every token, the batch's unique-expert list and, per
+//                    unique expert, the mask of the tokens that chose it.
+//   B  k_dec_b     : per (unique expert, 16 intermediate columns): fused
+//                    dequantise-GEMV of the 32 gate/up rows for the tokens
+//                    in the expert's mask, SwiGLU, and the gated partial down
+//                    product over those 16 columns. The down weights are
+//                    loaded together with the gate/up weights, so the down
+//                    projection adds no memory round trip.
+//   C  k_dec_c     : y = sum of the partial products, in a fixed order.
 //
 // No float atomics: every partial lands in its own fp32 slot and the sum
 // order is fixed, so results are bitwise reproducible. Threads issue all

@@ -34,7 +34,7 @@
 // chip, which 256 CUs rule out.
 //
 // Hand-off without cache flushes. Every value one workgroup passes to
-// another (logits, h) travels in a 64-bit word whose high half is a tag
+// another (logits, partial down products) travels in a 64-bit word whose high half is a tag
 // that is new for every call (the call's epoch + 1), written and read with
 // agent-scope relaxed atomics: each word is single-copy atomic and coherent
 // across the chip's L2 slices on its own, and a reader uses a word only once
