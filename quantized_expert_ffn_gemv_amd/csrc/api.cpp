@@ -103,10 +103,10 @@ size_t carve_decode(const moe_layer* L, int B, uint8_t* base, moe::DecodeWs* ws)
   };
   moe::DecodeWs w{};
   w.sync = reinterpret_cast<uint32_t*>(take(DECODE_SYNC_BYTES));
-  // logits: [B][E] fp64 (three kernels) or 4 rotating slots of [E] x 16 B tagged words (one kernel)
-  w.logits = reinterpret_cast<double*>(take((size_t)E * 64));
   const bool has_s = L->shared_wtype != MOE_W_NONE;
   const bool one_kernel = B == 1 && moe::decode1_fits(L->n_experts, L->hidden, L->inter, L->top_k, has_s);
+  // logits: [B][E] fp64 (four kernels) or rotating slots of per-XCD-group [E] x 16 B tagged words (one kernel)
+  w.logits = reinterpret_cast<double*>(take(one_kernel ? 8 * moe::decode1_logit_words((int)E) : (size_t)E * 64));
   if (one_kernel) {
     w.flags = reinterpret_cast<uint64_t*>(take(8 * moe::decode1_flag_words(L->n_experts, L->inter, L->top_k, has_s)));
     w.part_words = reinterpret_cast<uint64_t*>(take(8 * moe::decode1_part_words(L->hidden, L->inter, L->top_k, has_s)));

@@ -153,6 +153,20 @@ struct TopkSlot {  // 16 bytes in LDS
   int pad;
 };
 
+// Gates of the k ordered winners S_o[0 .. k) (k <= 16: lanes 0..15, one
+// DPP row): lane r < k ends with expert r and the softmax of the k selected
+// logits, exp in fp32 of the fp64 difference to the largest, summed in fp64.
+__device__ __forceinline__ void topk_gates(const TopkSlot* S_o, int E, int k, int lane, int& my_idx, float& my_gate) {
+  const TopkSlot o = S_o[lane < k ? lane : 0];
+  const double mv = S_o[0].v;
+  const float ef = (lane < k) ? expf((float)(o.v - mv)) : 0.0f;
+  const double z = sum16_f64((double)ef);
+  int ix = (lane < k) ? o.i : 0;
+  ix = ix < 0 ? 0 : (ix >= E ? E - 1 : ix);  // in range whatever the logits held
+  my_idx = ix;
+  my_gate = (lane < k) ? (float)((double)ef / z) : 0.0f;
+}
+
 template <int NV>
 __device__ __forceinline__ void wave_topk(const double (&v)[NV], int E, int k, int lane, uint8_t* scratch, int& my_idx,
                                           float& my_gate) {
@@ -255,15 +269,7 @@ __device__ __forceinline__ void wave_topk(const double (&v)[NV], int E, int k, i
     }
   }
   wave_lds_sync();
-  // gates (k <= 16: the winners sit in lanes 0..15, one DPP row)
-  const TopkSlot o = S_o[lane < k ? lane : 0];
-  const double mv = S_o[0].v;
-  const float ef = (lane < k) ? expf((float)(o.v - mv)) : 0.0f;
-  const double z = sum16_f64((double)ef);
-  int ix = (lane < k) ? o.i : 0;
-  ix = ix < 0 ? 0 : (ix >= E ? E - 1 : ix);  // in range whatever the logits held
-  my_idx = ix;
-  my_gate = (lane < k) ? (float)((double)ef / z) : 0.0f;
+  topk_gates(S_o, E, k, lane, my_idx, my_gate);
 }
 
 }  // namespace moe

@@ -1,26 +1,26 @@
 // Batch-1 decode of one MoE layer as a single kernel.
 //
-// Workgroups take roles by index:
+// Workgroups take roles by index (nA = max(nR, nSG) first workgroups, then
+// the routed ones, then extra reducers if needed; at most one workgroup per
+// CU at the shapes of interest, so no role shares a CU's VALUs with another):
 //
-//   [0, nR)        router: 8 expert rows each, fp64 logits (an fp32 weight
-//                  times a bf16 activation is exact in fp64).
-//   [nR, +nSG)     shared expert: 8 intermediates each (16 gate/up rows),
-//                  gate/up GEMV + SwiGLU -> h (bf16, in LDS), then those 8
-//                  columns of the shared down matrix times h: a partial y
-//                  over all H rows.                         waits: logits
-//                  (only so the router's bytes reach the chip first; the
-//                  shared bytes then fill the memory-idle top-k window)
-//   [.., +nRG)     routed experts: (slot, 32 intermediates) each; ordered
+//   [0, nA)        b < nR: router, 8 expert rows each, fp64 logits (an fp32
+//                  weight times a bf16 activation is exact in fp64); then
+//                  b < nSG: shared expert, 8 intermediates each (16 gate/up
+//                  rows), gate/up GEMV + SwiGLU -> h (bf16, in LDS), then
+//                  those 8 columns of the shared down matrix times h: a
+//                  partial y over all H rows. The shared bytes stream while
+//                  the routed workgroups wait for the logits and select.
+//   [nA, +nRG)     routed experts: (slot, 32 intermediates) each; ordered
 //                  top-k from the logits, then fused dequantise-GEMV of the
 //                  64 gate/up rows + SwiGLU -> h (bf16, in LDS), then the
 //                  matching 32-column block of the expert's down matrix
 //                  (loaded with the gate/up rows) times h, scaled by the
 //                  slot's gate: a partial y over all H rows. waits: logits
 //   reducers       F_RD output rows each: y = the sum of the partials of
-//                  all shared and routed workgroups in a fixed order.
-//                  Reducer d runs on workgroup d once its router or shared
-//                  role is done (extra workgroups after the routed ones take
-//                  reducers beyond nR + nSG), so the grid fits on the chip.
+//                  all shared and routed roles in a fixed order. Reducers
+//                  run on the last nD workgroups (routed ones after their
+//                  own role; extra workgroups when nD > nRG).
 //                                                waits: every partial
 //
 // The down product is split along the intermediate dimension (split-K), so
@@ -28,23 +28,26 @@
 // together with the gate/up weights; the only hand-off after the top-k is
 // the partials, read by the reducers.
 //
-// Progress: the routed and shared workgroups wait only on the router, which
-// never waits, so they always finish; a reducer waits on them, and can only
-// hold a slot they need if nR + nSG workgroups filled every slot on the
-// chip, which 256 CUs rule out.
+// Progress: the routed workgroups wait only on the router roles, which
+// never wait, and the shared roles never wait, so every partial gets
+// written once every workgroup is resident; a reducer waits on producers
+// dispatched after it, so the path is taken only when the whole grid fits
+// on the chip at once (two workgroups per CU).
 //
 // Hand-off without cache flushes. Every value one workgroup passes to
-// another (logits, partial down products) travels in a 64-bit word whose high half is a tag
-// that is new for every call (the call's epoch + 1), written and read with
-// agent-scope relaxed atomics: each word is single-copy atomic and coherent
-// across the chip's L2 slices on its own, and a reader uses a word only once
-// its tag is current, so no release/acquire fence (an L2 write-back or
-// invalidate per workgroup) is needed. Each producer workgroup also writes
-// one tagged flag word once its values are issued; a consumer polls the
-// flags of its producers (one wave, a few words per lane) and then reads and
-// checks the values. Flags are plain stores, one per producer: a shared
-// counter bumped by hundreds of producers serialises its atomics at the
-// memory side and was measured to add microseconds. Every spin is bounded;
+// another (logits, partial down products) travels in a 64-bit word whose
+// high half is a tag that is new for every call (the call's epoch + 1),
+// written and read with agent-scope relaxed atomics: each word is
+// single-copy atomic and coherent across the chip's L2 slices on its own,
+// and a reader uses a word only once its tag is current, so no
+// release/acquire fence (an L2 write-back or invalidate per workgroup) is
+// needed. Each router role also writes one tagged flag word once its
+// logits are issued; a routed workgroup polls those flags (one wave, one
+// word per lane) and then reads and checks the logits; reducers poll the
+// partial words directly. Flags are plain stores, one 128-byte line each:
+// a shared counter bumped by hundreds of producers serialises its atomics
+// at the memory side, and lines polled by hundreds of workgroups serve them
+// one after another (both measured to add microseconds). Every spin is bounded;
 // one that runs out sets an error bit in the workspace and lets the
 // workgroup finish, so the kernel always ends. The last workgroup to finish
 // (a per-XCD count, then a count of the XCD groups) resets the counts and
@@ -79,8 +82,9 @@ static_assert(SY_WORDS * 4 <= 4096, "sync area");
 constexpr int F_SLOTS = 4;  // logits and flag buffers rotate over this many calls
 
 struct FusedGeo {
-  int nR, nSG, nRG;  // router, shared, routed workgroups
-  int nD;            // reducers: reducer d < nR + nSG runs on workgroup d after its first role,
+  int nR, nSG, nRG;  // router, shared, routed roles
+  int nA;            // workgroups [0, nA) take the router role (b < nR), then the shared role (b < nSG)
+  int nD;            // reducers: reducer d < nA runs on workgroup d after its first roles,
                      // the rest on extra workgroups after the routed ones
 };
 
@@ -103,14 +107,18 @@ __device__ __forceinline__ int my_rep() { return blockIdx.x & (SY_NREP - 1); }
 
 // The workgroup's flag: written by one thread once every thread's tagged
 // stores are issued (the flag may become visible before them; readers
-// check the values' tags).
-__device__ __forceinline__ void raise_flag(uint64_t* flag, uint32_t tag) {
+// check the values' tags). Each flag has a 128-byte line of its own: with
+// hundreds of workgroups polling, flags packed into a few lines made every
+// poll queue behind the others at those lines (a hand-off took ~2 us
+// instead of ~0.85 us, measured).
+constexpr int F_FLAG_STRIDE = 16;  // uint64 words between flags
+__device__ __forceinline__ void raise_flag(uint64_t* flags, int i, uint32_t tag) {
   __syncthreads();
-  if (threadIdx.x == 0) st_word(flag, 0u, tag);
+  if (threadIdx.x == 0) st_word(flags + (size_t)F_FLAG_STRIDE * i, 0u, tag);
 }
 
-// Bounded wait until at least `need` of flags[0 .. n) carry the current tag
-// (need <= n): wave 0 polls, eight flags per lane per pass; the whole
+// Bounded wait until at least `need` of flags 0 .. n-1 carry the current tag
+// (need <= n <= 64): wave 0 polls, one flag per lane per pass; the whole
 // workgroup leaves together. Callers that pass need < n then read the
 // values with per-word tag checks (settle), so the loads of the last
 // producers' values overlap their arrival instead of following it.
@@ -120,17 +128,8 @@ __device__ __forceinline__ void wait_flags(const uint64_t* flags, int n, int nee
     const uint64_t t0 = wall_clock64();
     int it = 0;
     while (true) {
-      int have = 0;
-      for (int base = 0; base < n; base += 64 * 8) {
-        uint64_t v[8];
-#pragma unroll
-        for (int j = 0; j < 8; j++) v[j] = ld_word_coherent(flags + min(base + lane + 64 * j, n - 1));
-#pragma unroll
-        for (int j = 0; j < 8; j++) {
-          const bool ok = (base + lane + 64 * j < n) && (uint32_t)(v[j] >> 32) == tag;
-          have += __popcll(__builtin_amdgcn_ballot_w64(ok));
-        }
-      }
+      const uint64_t v = ld_word_coherent(flags + (size_t)F_FLAG_STRIDE * min(lane, n - 1));
+      const int have = __popcll(__builtin_amdgcn_ballot_w64((lane < n) && (uint32_t)(v >> 32) == tag));
       if (have >= need) break;
       __builtin_amdgcn_s_sleep(1);
       if ((++it & 15) == 0 && wall_clock64() - t0 > F_WAIT_TICKS) {
@@ -191,7 +190,11 @@ __device__ __forceinline__ void finish(uint32_t* sync) {
 }
 
 // ---------------------------------------------------------------------------
-// Router: wave w of workgroup b computes the logit of expert 8b + w.
+// Router: wave w of workgroup b computes the logit of expert 8b + w. The
+// logits are written once per XCD group (SY_NREP replicas): the routed
+// workgroups of a group read their own copy, so each line has a few
+// readers instead of all of them (lines read by hundreds of workgroups at
+// once serve them one after another).
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ void role_router(const LayerDev& L, const uint16_t* __restrict__ x, uint64_t* logits, int b,
                                             uint32_t tag) {
@@ -201,6 +204,10 @@ __device__ __forceinline__ void role_router(const LayerDev& L, const uint16_t* _
   const int n4 = L.H >> 2;
   const float4* wr = reinterpret_cast<const float4*>(L.router_w + (size_t)(valid ? e : 0) * L.H);
   const uint2* xv = reinterpret_cast<const uint2*>(x);
+  // the bias is loaded with the weights (not after the sum: a load there is
+  // one more memory round trip on the way to the top-k)
+  const float* bp = L.router_b ? L.router_b + (valid ? e : 0) : L.router_w;
+  const float bias_raw = *bp;
   double a0 = 0.0, a1 = 0.0;
   for (int c0 = 0; c0 < n4; c0 += 64 * F_RCPL) {
     float4 w[F_RCPL];
@@ -230,11 +237,13 @@ __device__ __forceinline__ void role_router(const LayerDev& L, const uint16_t* _
     }
   }
   const double tot = wave_total_f64(a0 + a1);
-  if (valid && lane == 0) {
-    const uint64_t v = (uint64_t)__double_as_longlong(tot + (L.router_b ? (double)L.router_b[e] : 0.0));
-    // two words (low, high half of the fp64 logit), each with the tag
-    st_word(logits + 2 * e, (uint32_t)v, tag);
-    st_word(logits + 2 * e + 1, (uint32_t)(v >> 32), tag);
+  if (valid && lane < SY_NREP) {
+    const uint64_t v = (uint64_t)__double_as_longlong(tot + (L.router_b ? (double)bias_raw : 0.0));
+    // two words (low, high half of the fp64 logit), each with the tag, in
+    // every XCD group's replica (lane r writes replica r)
+    uint64_t* rl = logits + (size_t)lane * 2 * L.E;
+    st_word(rl + 2 * e, (uint32_t)v, tag);
+    st_word(rl + 2 * e + 1, (uint32_t)(v >> 32), tag);
   }
 }
 
@@ -278,10 +287,10 @@ __device__ __forceinline__ float qdot32_reg(const Raw& r, const uint16_t* a, flo
 // ---------------------------------------------------------------------------
 constexpr int F_GU_NB = 8;  // chunks per thread and batch
 
-template <int WT, int RPW>
+template <int WT, int RPW, typename After>
 __device__ __forceinline__ float gate_up_h(const uint8_t* __restrict__ gu, const uint16_t* __restrict__ gus, int H, int R,
                                            int q, int hf, const uint16_t* xs, const float* xsum, float* s_red,
-                                           uint16_t* s_h) {
+                                           uint16_t* s_h, After&& after_first_issue) {
   constexpr int KC = kchunk<WT>();
   constexpr int NKP = F_THREADS / RPW;  // k-parts
   constexpr int NB = F_GU_NB;
@@ -301,14 +310,18 @@ __device__ __forceinline__ float gate_up_h(const uint8_t* __restrict__ gu, const
   for (int bt = 0; bt < NBATCH; bt++) {
     const int c0 = bt * NKP * NB;
     Raw raw[NB];
-    float sc[NB];
+    uint16_t sc[NB];  // fp16 bits: converted after the barrier, so no wait comes before it
+    // clamped, unconditional loads (see role_router); each chunk's scale
+    // right after it, so chunk i is computed as soon as its own two loads
+    // are in (the waits count down in issue order) while later chunks
+    // still stream
 #pragma unroll
-    for (int i = 0; i < NB; i++)  // clamped, unconditional loads (see role_router)
-      raw[i] = load_chunk<WT>(gu, (size_t)min(c0 + kp + NKP * i, nc - 1) * R + row);
-    if constexpr (is_q<WT>()) {
-#pragma unroll
-      for (int i = 0; i < NB; i++) sc[i] = f16_to_f32(gus[(size_t)min(c0 + kp + NKP * i, nc - 1) * R + row]);
+    for (int i = 0; i < NB; i++) {
+      const size_t o = (size_t)min(c0 + kp + NKP * i, nc - 1) * R + row;
+      raw[i] = load_chunk<WT>(gu, o);
+      if constexpr (is_q<WT>()) sc[i] = gus[o];
     }
+    if (bt == 0) after_first_issue();  // loads needed later (the down columns) queue behind these
     __builtin_amdgcn_sched_barrier(0);  // every load of the batch is issued before the first wait
     // every chunk is computed (no branch around the dot products): a chunk
     // past the row reads a valid chunk and contributes zero
@@ -317,7 +330,7 @@ __device__ __forceinline__ float gate_up_h(const uint8_t* __restrict__ gu, const
       const bool in = c0 + kp + NKP * i < nc;
       const int c = min(c0 + kp + NKP * i, nc - 1);
       if constexpr (is_q<WT>()) {
-        acc = __builtin_fmaf(in ? sc[i] : 0.0f, qdot32_reg<WT>(raw[i], xs + 32 * c, xsum[c], magic), acc);
+        acc = __builtin_fmaf(in ? f16_to_f32(sc[i]) : 0.0f, qdot32_reg<WT>(raw[i], xs + 32 * c, xsum[c], magic), acc);
       } else {
         const float t = ddot<WT>(raw[i], xs + (size_t)c * KC, 0.0f);
         acc += in ? t : 0.0f;
@@ -366,35 +379,117 @@ __device__ __forceinline__ void stage_x(const uint16_t* __restrict__ x, int H, u
 
 constexpr int F_NV = 8;  // logits per lane in the top-k: E <= 512 on this path
 
-// Top-k of the token by wave 0 from the tagged logits; the workgroup reads
-// idx/gates from LDS after.
+// Ordered top-k of the token by the whole workgroup (thread t holds expert
+// t; E <= F_THREADS), from the tagged logits:
+//   1. each thread's 32-bit sortable key (leading bits of the fp64 logit,
+//      the low 9 bits replaced by 511 - t: distinct keys that never
+//      contradict value order at the bits they keep); the maximum of each
+//      16-thread row (32 rows);
+//   2. tau = the k-th largest row maximum (every wave computes it from LDS;
+//      each lane ranks one row maximum against half of the others), tv =
+//      the smallest fp64 value with tau's leading bits. k rows hold a value
+//      >= tv, so every top-k value is >= tv;
+//   3. candidates (values >= tv) appended to LDS (one LDS atomic per wave);
+//   4. wave 0 ranks the candidates exactly (value, then index): four lanes
+//      per candidate when there are at most 16 (the usual case: about 12),
+//      one lane per candidate up to 64, else the one-wave top-k over all
+//      values (massive ties);
+//   5. gates of the k winners as in the one-wave top-k (same arithmetic).
+// The workgroup reads idx/gates from LDS after.
+struct BlockTopk {
+  double val[F_THREADS];         // every logit (-inf past E), for the tie path
+  uint32_t rowmax[F_THREADS / 16];
+  uint32_t cnt;                  // candidates appended
+  uint32_t pad[3];
+  TopkSlot cand[64];
+  TopkSlot out[16];
+  uint8_t wave_scratch[TOPK_SCRATCH];
+};
+static_assert(64 * F_NV <= F_THREADS, "one logit per thread");
+
 __device__ __forceinline__ void block_topk(const uint64_t* logits, int E, int k, uint32_t tag, uint32_t* sync,
-                                           uint8_t* scratch, int* s_idx, float* s_gate) {
-  const int lane = threadIdx.x & 63;
-  if (threadIdx.x < 64) {
-    uint64_t wl[F_NV], wh[F_NV];
+                                           BlockTopk& S, int* s_idx, float* s_gate) {
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  // 1. one logit per thread: coherent loads (a line another call left in
+  //    this XCD's L2 is never used), clamped and unconditional
+  const int e = min(t, E - 1);
+  uint64_t wl = ld_word_coherent(logits + 2 * e);
+  uint64_t wh = ld_word_coherent(logits + 2 * e + 1);
+  if (t == 0) S.cnt = 0;
+  wl = settle(logits + 2 * e, wl, tag, sync);
+  wh = settle(logits + 2 * e + 1, wh, tag, sync);
+  const double v = (t < E) ? __longlong_as_double((long long)(((wh & 0xFFFFFFFFull) << 32) | (wl & 0xFFFFFFFFull)))
+                           : -__builtin_inf();
+  S.val[t] = v;
+  const uint32_t key = (sort_key_hi(v) & ~511u) | (uint32_t)(511 - t);
+  uint32_t m = key;
+  m = max(m, (uint32_t)dpp_i32<DPP_XOR1>((int)m));
+  m = max(m, (uint32_t)dpp_i32<DPP_XOR2>((int)m));
+  m = max(m, (uint32_t)dpp_i32<DPP_HALF_MIRROR>((int)m));
+  m = max(m, (uint32_t)dpp_i32<DPP_MIRROR>((int)m));
+  if ((lane & 15) == 0) S.rowmax[t >> 4] = m;
+  __syncthreads();
+  // 2. threshold
+  const uint32_t mine = S.rowmax[lane & 31];
+  const uint4* rm = reinterpret_cast<const uint4*>(S.rowmax) + 4 * (lane >> 5);
+  int r = 0;
 #pragma unroll
-    for (int i = 0; i < F_NV; i++) {
-      // coherent loads (a line another call left in this XCD's L2 is never
-      // used), clamped and unconditional (see role_router)
-      const int e = min(lane + 64 * i, E - 1);
-      wl[i] = ld_word_coherent(logits + 2 * e);
-      wh[i] = ld_word_coherent(logits + 2 * e + 1);
-    }
-    double lv[F_NV];
-#pragma unroll
-    for (int i = 0; i < F_NV; i++) {
-      const int e = lane + 64 * i;
-      lv[i] = -__builtin_inf();
-      if (e < E) {
-        const uint64_t lo = settle(logits + 2 * e, wl[i], tag, sync);
-        const uint64_t hi = settle(logits + 2 * e + 1, wh[i], tag, sync);
-        lv[i] = __longlong_as_double((long long)(((hi & 0xFFFFFFFFull) << 32) | (lo & 0xFFFFFFFFull)));
-      }
-    }
+  for (int j = 0; j < 4; j++) {
+    const uint4 q = rm[j];
+    r += (int)(q.x > mine) + (int)(q.y > mine) + (int)(q.z > mine) + (int)(q.w > mine);
+  }
+  r += __shfl_xor(r, 32, 64);
+  const uint64_t sel = __ballot((lane < 32) & (r == k - 1));
+  const uint32_t tau = (uint32_t)__builtin_amdgcn_readlane((int)mine, __ffsll((long long)sel) - 1) & ~511u;
+  const double tv = key_floor_value(tau);
+  // 3. candidates
+  const bool cand = (t < E) & (v >= tv);
+  const uint64_t bal = __ballot(cand);
+  uint32_t base = 0;
+  if (lane == 0) base = atomicAdd(&S.cnt, (uint32_t)__popcll(bal));
+  base = (uint32_t)__builtin_amdgcn_readfirstlane((int)base);
+  const uint32_t pos = base + (uint32_t)__popcll(bal & ((1ull << lane) - 1ull));
+  if (cand & (pos < 64u)) {
+    S.cand[pos].v = v;
+    S.cand[pos].i = t;
+  }
+  __syncthreads();
+  // 4. exact order, 5. gates
+  if (wave == 0) {
+    const int nc = (int)S.cnt;
     int mi;
     float mg;
-    wave_topk(lv, E, k, lane, scratch, mi, mg);
+    if (nc <= 64) {
+      if (nc <= 16) {
+        const int c = lane >> 2, g = lane & 3;
+        const TopkSlot me = S.cand[c < nc ? c : 0];
+        int rk = 0;
+#pragma unroll
+        for (int jj = 0; jj < 4; jj++) {
+          const int j = g + 4 * jj;
+          const TopkSlot o = S.cand[j < nc ? j : 0];
+          rk += (int)((j < nc) & topk_before(o.v, o.i, me.v, me.i));
+        }
+        rk += dpp_i32<DPP_XOR1>(rk);
+        rk += dpp_i32<DPP_XOR2>(rk);
+        if ((g == 0) & (c < nc) & (rk < k)) S.out[rk] = me;
+      } else {
+        const TopkSlot me = S.cand[lane < nc ? lane : 0];
+        int rk = 0;
+        for (int j = 0; j < nc; j++) {
+          const TopkSlot o = S.cand[j];
+          rk += (int)topk_before(o.v, o.i, me.v, me.i);
+        }
+        if ((lane < nc) & (rk < k)) S.out[rk] = me;
+      }
+      wave_lds_sync();
+      topk_gates(S.out, E, k, lane, mi, mg);
+    } else {
+      double w[F_NV];
+#pragma unroll
+      for (int i = 0; i < F_NV; i++) w[i] = S.val[lane + 64 * i];
+      wave_topk<F_NV>(w, E, k, lane, S.wave_scratch, mi, mg);
+    }
     if (lane < k) {
       s_idx[lane] = mi;
       s_gate[lane] = mg;
@@ -423,7 +518,7 @@ template <int WT, int NCOL> struct DownPlan {
 template <int WT>
 struct DownPre {
   Raw r[F_RPT];
-  float s[F_RPT];
+  uint16_t s[F_RPT];  // fp16 bits, converted at the use (a conversion here would wait for the load)
 };
 
 // issue the prefetch of this thread's rows (columns from c0) into registers;
@@ -441,7 +536,7 @@ __device__ __forceinline__ void down_prefetch(const uint8_t* __restrict__ d, con
     if constexpr (is_q<WT>()) {
 #pragma unroll
       for (int n = 0; n < F_RPT; n++)
-        pre.s[n] = f16_to_f32(ds[(size_t)cb * H + min((int)threadIdx.x + F_THREADS * n, H - 1)]);
+        pre.s[n] = ds[(size_t)cb * H + min((int)threadIdx.x + F_THREADS * n, H - 1)];
     }
   }
 }
@@ -458,7 +553,7 @@ __device__ __forceinline__ void down_store(const uint8_t* __restrict__ d, int H,
     if (row < H) {
       float v = 0.0f;
       if constexpr (DownPlan<WT, NCOL>::PRE) {
-        if constexpr (is_q<WT>()) v = pre.s[n] * qdot32<WT>(pre.r[n], s_h, hsum);
+        if constexpr (is_q<WT>()) v = f16_to_f32(pre.s[n]) * qdot32<WT>(pre.r[n], s_h, hsum);
         else v = ddot<WT>(pre.r[n], s_h, 0.0f);
       } else {
 #pragma unroll
@@ -471,8 +566,11 @@ __device__ __forceinline__ void down_store(const uint8_t* __restrict__ d, int H,
 
 // ---------------------------------------------------------------------------
 // Reducer: output rows r0 .. r0 + F_RD - 1, y = sum over the nP partials in
-// producer order (shared workgroups, then routed), each thread summing a
-// fixed subset and the workgroup adding the subsets in a fixed order.
+// producer order (shared roles, then routed), each thread summing a fixed
+// subset and the workgroup adding the subsets in a fixed order. The reducer
+// polls the partial words themselves (no flags): a pass costs one request
+// per producer line, as a flag poll would, and the data is there as soon as
+// the poll sees it.
 // ---------------------------------------------------------------------------
 constexpr int F_RD = 16;                   // output rows per reducer
 constexpr int F_RG = F_THREADS / F_RD;     // producer groups per reducer (32)
@@ -482,19 +580,37 @@ __device__ __forceinline__ void role_reduce(const uint64_t* part, int nP, int H,
   const int rr = threadIdx.x % F_RD, pg = threadIdx.x / F_RD;
   const int row = r0 + rr;
   float acc = 0.0f;
-  if (row < H) {
-    constexpr int NB = 8;
-    for (int p0 = pg; p0 < nP; p0 += F_RG * NB) {
-      uint64_t w[NB];
+  const int rowc = min(row, H - 1);
+  constexpr int NB = 8;  // F_RG * NB >= the producers of the usual shapes: one batch of loads
+  for (int p0 = pg; p0 < nP; p0 += F_RG * NB) {
+    uint64_t w[NB];
 #pragma unroll
-      for (int n = 0; n < NB; n++)  // clamped, unconditional loads (see role_router)
-        w[n] = ld_word_coherent(part + (size_t)min(p0 + F_RG * n, nP - 1) * H + row);
+    for (int n = 0; n < NB; n++)  // clamped, unconditional loads (see role_router)
+      w[n] = ld_word_coherent(part + (size_t)min(p0 + F_RG * n, nP - 1) * H + rowc);
+    // words of producers that are not done yet: the wave reloads its whole
+    // batch (unconditional loads, one round trip per pass) until every tag
+    // is current, so late producers cost one round trip, not one per word
+    const uint64_t t0 = wall_clock64();
+    int it = 0;
+    while (true) {
+      bool stale = false;
 #pragma unroll
-      for (int n = 0; n < NB; n++) {
-        const int p = p0 + F_RG * n;
-        if (p < nP) acc += __uint_as_float((uint32_t)settle(part + (size_t)p * H + row, w[n], tag, sync));
+      for (int n = 0; n < NB; n++) stale |= (uint32_t)(w[n] >> 32) != tag;
+      if (__builtin_amdgcn_ballot_w64(stale) == 0) break;
+      __builtin_amdgcn_s_sleep(2);
+      uint64_t r[NB];
+#pragma unroll
+      for (int n = 0; n < NB; n++) r[n] = ld_word_coherent(part + (size_t)min(p0 + F_RG * n, nP - 1) * H + rowc);
+#pragma unroll
+      for (int n = 0; n < NB; n++) w[n] = ((uint32_t)(w[n] >> 32) == tag) ? w[n] : r[n];
+      if ((++it & 15) == 0 && wall_clock64() - t0 > F_WAIT_TICKS) {
+        flag_error(sync, 2u);
+        break;
       }
     }
+#pragma unroll
+    for (int n = 0; n < NB; n++)
+      if (p0 + F_RG * n < nP) acc += __uint_as_float((uint32_t)w[n]);
   }
   s_red[threadIdx.x] = acc;
   __syncthreads();
@@ -520,7 +636,7 @@ __global__ __launch_bounds__(F_THREADS, 4) void k_decode1(LayerDev L, const uint
   __shared__ __align__(16) uint16_t s_x[F_HMAX];
   __shared__ __align__(16) float s_xsum[F_HMAX / 32];
   __shared__ __align__(16) float s_red[F_THREADS];
-  __shared__ __align__(16) uint8_t s_tk[TOPK_SCRATCH];
+  __shared__ __align__(16) BlockTopk s_tk;
   __shared__ int s_idx[16];
   __shared__ float s_gate[16];
   __shared__ __align__(16) uint16_t s_h[32];
@@ -529,34 +645,37 @@ __global__ __launch_bounds__(F_THREADS, 4) void k_decode1(LayerDev L, const uint
   const int nP = G.nSG + G.nRG;  // partial producers: shared workgroups, then routed
   // this call's tag: the epoch (stable until every workgroup is done) + 1
   const uint32_t tag = ld_u32(ws.sync + SY_EPOCH + SY_LINE * my_rep()) + 1u;
-  uint64_t* tl = reinterpret_cast<uint64_t*>(ws.logits) + (size_t)(tag % F_SLOTS) * 2 * L.E;
-  // flags: router workgroups [0, nR), then the partial producers
-  uint64_t* fl = ws.flags + (size_t)(tag % F_SLOTS) * (G.nR + nP);
+  uint64_t* tl = reinterpret_cast<uint64_t*>(ws.logits) + (size_t)(tag % F_SLOTS) * SY_NREP * 2 * L.E;
+  // flags of the router roles
+  uint64_t* fl = ws.flags + (size_t)(tag % F_SLOTS) * G.nR * F_FLAG_STRIDE;
   uint64_t* part = ws.part_words;  // [nP][H]
   int b = blockIdx.x;
-  if (b < G.nR) {
-    role_router(L, x, tl, b, tag);
-    raise_flag(fl + b, tag);
-  } else if ((b -= G.nR) < G.nSG) {
-    // shared expert, intermediates 16q + 8hf .. +7
-    constexpr int SW = (SWT == MOE_W_F32) ? MOE_W_F32 : MOE_W_BF16;
-    uint16_t* xs = s_x;
-    const int q = b >> 1, hf = b & 1;
-    stage_x(x, H, xs, nullptr);
-    wait_flags(fl, G.nR, G.nR, tag, ws.sync);  // the router's bytes first; these fill the top-k window
-    DownPre<SW> pre;
-    down_prefetch<SW, 8>(L.sdn, nullptr, H, 16 * q + 8 * hf, pre);
-    gate_up_h<SW, 16>(L.sgu, nullptr, H, 2 * I, q, hf, xs, nullptr, s_red, s_h);
-    __syncthreads();
-    down_store<SW, 8>(L.sdn, H, 16 * q + 8 * hf, pre, s_h, 0.0f, 1.0f, part + (size_t)b * H, tag);
-    raise_flag(fl + G.nR + b, tag);
-  } else if ((b -= G.nSG) < G.nRG) {
+  if (b < G.nA) {
+    if (b < G.nR) {
+      role_router(L, x, tl, b, tag);
+      raise_flag(fl, b, tag);
+    }
+    if (b < G.nSG) {
+      // shared expert, intermediates 16q + 8hf .. +7, right after the router
+      // rows (its bytes fill the memory-idle top-k window)
+      constexpr int SW = (SWT == MOE_W_F32) ? MOE_W_F32 : MOE_W_BF16;
+      const uint16_t* xs = s_x;
+      const int q = b >> 1, hf = b & 1;
+      stage_x(x, H, s_x, nullptr);  // after the router's loads (x is then in this XCD's L2)
+      __syncthreads();
+      DownPre<SW> pre;
+      gate_up_h<SW, 16>(L.sgu, nullptr, H, 2 * I, q, hf, xs, nullptr, s_red, s_h,
+                        [&] { down_prefetch<SW, 8>(L.sdn, nullptr, H, 16 * q + 8 * hf, pre); });
+      __syncthreads();
+      down_store<SW, 8>(L.sdn, H, 16 * q + 8 * hf, pre, s_h, 0.0f, 1.0f, part + (size_t)b * H, tag);
+    }
+  } else if ((b -= G.nA) < G.nRG) {
     // routed slot u, intermediates 32q .. 32q+31
     uint16_t* xs = s_x;
     float* xsum = s_xsum;
     stage_x(x, H, xs, is_q<WT>() ? xsum : nullptr);
     wait_flags(fl, G.nR, flags_needed(G.nR), tag, ws.sync);
-    block_topk(tl, L.E, L.k, tag, ws.sync, s_tk, s_idx, s_gate);
+    block_topk(tl + (size_t)my_rep() * 2 * L.E, L.E, L.k, tag, ws.sync, s_tk, s_idx, s_gate);
     const int gpe = I >> 5;
     const int u = b / gpe, q = b - u * gpe;
     if (b == 0 && (int)threadIdx.x < L.k) {
@@ -567,10 +686,9 @@ __global__ __launch_bounds__(F_THREADS, 4) void k_decode1(LayerDev L, const uint
     const uint8_t* dn = L.dn + (size_t)e * L.dn_stride;
     const uint16_t* dns = is_q<WT>() ? L.dn_s + (size_t)e * L.dn_s_stride : nullptr;
     DownPre<WT> pre;
-    down_prefetch<WT, 32>(dn, dns, H, 32 * q, pre);
     const float hv = gate_up_h<WT, 64>(L.gu + (size_t)e * L.gu_stride,
                                        is_q<WT>() ? L.gu_s + (size_t)e * L.gu_s_stride : nullptr, H, 2 * I, q, 0, xs, xsum,
-                                       s_red, s_h);
+                                       s_red, s_h, [&] { down_prefetch<WT, 32>(dn, dns, H, 32 * q, pre); });
     if constexpr (is_q<WT>()) {
       // block sum of the 32 bf16 h values (threads 0..31 of wave 0), fixed order
       float t = hv;
@@ -583,15 +701,11 @@ __global__ __launch_bounds__(F_THREADS, 4) void k_decode1(LayerDev L, const uint
     __syncthreads();
     down_store<WT, 32>(dn, H, 32 * q, pre, s_h, is_q<WT>() ? s_hsum : 0.0f, s_gate[u],
                        part + (size_t)(G.nSG + b) * H, tag);
-    raise_flag(fl + G.nR + G.nSG + b, tag);
   }
-  // reducers
-  const int first = G.nR + G.nSG, extra0 = first + G.nRG;
-  int d = -1;
-  if ((int)blockIdx.x < first) d = blockIdx.x;
-  else if ((int)blockIdx.x >= extra0) d = first + ((int)blockIdx.x - extra0);
-  if (d >= 0 && d < G.nD) {
-    wait_flags(fl + G.nR, nP, flags_needed(nP), tag, ws.sync);
+  // reducers: the last nD workgroups of the grid, all routed or extra ones
+  const int d = (int)blockIdx.x - ((int)gridDim.x - G.nD);
+  if (d >= 0) {
+    __syncthreads();  // s_red is reused
     role_reduce(part, nP, H, d * F_RD, y, s_red, tag, ws.sync);
   }
   finish(ws.sync);
@@ -607,8 +721,35 @@ size_t decode1_lds(int H, int I, int k, bool has_shared) {
 
 static int producers(int I, int k, bool has_shared) { return (has_shared ? I / 8 : 0) + k * (I / 32); }
 
+size_t decode1_logit_words(int E) { return (size_t)F_SLOTS * SY_NREP * 2 * E; }
+
 size_t decode1_flag_words(int E, int I, int k, bool has_shared) {
-  return (size_t)F_SLOTS * ((E + 7) / 8 + producers(I, k, has_shared));
+  (void)I; (void)k; (void)has_shared;
+  return (size_t)F_SLOTS * ((E + 7) / 8) * F_FLAG_STRIDE;
+}
+
+// Workgroups: router/shared, routed, and extra reducers when the reducers
+// outnumber the routed workgroups (reducers are the last ones).
+static int decode1_grid(int E, int H, int I, int k, bool has_shared) {
+  const int nR = (E + 7) / 8, nSG = has_shared ? I / 8 : 0, nRG = k * (I / 32);
+  const int nA = nR > nSG ? nR : nSG, nD = (H + F_RD - 1) / F_RD;
+  return nA + (nRG > nD ? nRG : nD);
+}
+
+// Workgroups that are sure to be resident together: two per CU (the launch
+// bounds keep a workgroup within half a CU's registers; its LDS is ~16 KB).
+// Reducers wait for producers dispatched before and after them, so the
+// whole grid must be resident at once.
+static int decode1_capacity() {
+  static int cap[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (cap[dev] == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    cap[dev] = 2 * cus;
+  }
+  return cap[dev];
 }
 
 size_t decode1_part_words(int H, int I, int k, bool has_shared) {
@@ -617,9 +758,8 @@ size_t decode1_part_words(int H, int I, int k, bool has_shared) {
 
 bool decode1_fits(int E, int H, int I, int k, bool has_shared) {
   // F_NV logits per lane in the top-k, F_RPT down rows per thread (the LDS
-  // arrays are sized for H <= F_HMAX)
-  (void)k; (void)has_shared;
-  return E <= 64 * F_NV && H <= F_HMAX && I <= 1024;
+  // arrays are sized for H <= F_HMAX), a grid that is resident at once
+  return E <= 64 * F_NV && H <= F_HMAX && I <= 1024 && decode1_grid(E, H, I, k, has_shared) <= decode1_capacity();
 }
 
 template <int WT, int SWT>
@@ -629,10 +769,10 @@ static hipError_t launch_fused_t(const LayerDev& L, const uint16_t* x, uint16_t*
   G.nR = (L.E + 7) / 8;
   G.nSG = (SWT == MOE_W_NONE) ? 0 : L.I / 8;
   G.nRG = L.k * (L.I / 32);
+  G.nA = G.nR > G.nSG ? G.nR : G.nSG;
   G.nD = (L.H + F_RD - 1) / F_RD;
   const size_t lds = decode1_lds(L.H, L.I, L.k, SWT != MOE_W_NONE);
-  const int extra = G.nD > G.nR + G.nSG ? G.nD - (G.nR + G.nSG) : 0;
-  const int grid = G.nR + G.nSG + G.nRG + extra;
+  const int grid = decode1_grid(L.E, L.H, L.I, L.k, SWT != MOE_W_NONE);
   return launch_k(KC_DEC_FUSED, k_decode1<WT, SWT>, dim3(grid), dim3(F_THREADS), lds, st, L, x, y, idx_out, gate_out,
                   ws, G);
 }

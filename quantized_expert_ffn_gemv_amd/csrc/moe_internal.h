@@ -82,6 +82,7 @@ struct PrefillWs {
 // Launch wrappers (return hipError_t of the launch).
 size_t decode_lds_b(int wt, int B, int H, int E, int k);  // LDS bytes of the routed-expert kernel
 size_t decode1_lds(int H, int I, int k, bool has_shared);  // LDS bytes of the one-kernel batch-1 path
+size_t decode1_logit_words(int E);  // rotating slots x XCD-group replicas x [E][2] tagged words
 size_t decode1_flag_words(int E, int I, int k, bool has_shared);
 size_t decode1_part_words(int H, int I, int k, bool has_shared);
 bool decode1_fits(int E, int H, int I, int k, bool has_shared);  // shape handled by the one-kernel path
