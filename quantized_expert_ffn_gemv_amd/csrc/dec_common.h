@@ -167,12 +167,13 @@ __device__ __forceinline__ void topk_gates(const TopkSlot* S_o, int E, int k, in
   my_gate = (lane < k) ? (float)((double)ef / z) : 0.0f;
 }
 
+// The k ordered winners to S_o[0 .. k) (LDS; visible to the wave after
+// wave_lds_sync).
 template <int NV>
-__device__ __forceinline__ void wave_topk(const double (&v)[NV], int E, int k, int lane, uint8_t* scratch, int& my_idx,
-                                          float& my_gate) {
+__device__ __forceinline__ void wave_topk_order(const double (&v)[NV], int E, int k, int lane, uint8_t* scratch,
+                                                TopkSlot* S_o) {
   uint32_t* S_key = reinterpret_cast<uint32_t*>(scratch);
   TopkSlot* S_c = reinterpret_cast<TopkSlot*>(scratch + 256);  // [TOPK_CMAX] candidates + [64] per-lane scratch
-  TopkSlot* S_o = S_c + TOPK_CMAX + 64;                          // [16] ordered winners
   const int nv = (E + 63) >> 6;  // value slots in use (uniform)
   // 1. lane best and its distinct key
   double bv = -__builtin_inf();
@@ -268,6 +269,13 @@ __device__ __forceinline__ void wave_topk(const double (&v)[NV], int E, int k, i
       }
     }
   }
+}
+
+template <int NV>
+__device__ __forceinline__ void wave_topk(const double (&v)[NV], int E, int k, int lane, uint8_t* scratch, int& my_idx,
+                                          float& my_gate) {
+  TopkSlot* S_o = reinterpret_cast<TopkSlot*>(scratch + 256) + TOPK_CMAX + 64;  // [16] ordered winners
+  wave_topk_order(v, E, k, lane, scratch, S_o);
   wave_lds_sync();
   topk_gates(S_o, E, k, lane, my_idx, my_gate);
 }

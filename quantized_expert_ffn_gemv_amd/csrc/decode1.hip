@@ -144,23 +144,25 @@ __device__ __forceinline__ void wait_flags(const uint64_t* flags, int n, int nee
 // how many producer flags a consumer waits for before it reads the values
 __device__ __forceinline__ int flags_needed(int n) { return n - n / 8; }
 
-// A word loaded once: if its tag is not current yet (the producer's store
-// is still on its way), reload it (bounded).
-__device__ __forceinline__ uint64_t settle(const uint64_t* p, uint64_t w, uint32_t tag, uint32_t* sync) {
-  if ((uint32_t)(w >> 32) != tag) {
+// A pair of words written together and loaded once: while either tag is
+// not current (the producer's stores are still on their way), reload both
+// (bounded).
+__device__ __forceinline__ void settle2(const uint64_t* p0, const uint64_t* p1, uint64_t& w0, uint64_t& w1, uint32_t tag,
+                                        uint32_t* sync) {
+  if (((uint32_t)(w0 >> 32) != tag) | ((uint32_t)(w1 >> 32) != tag)) {
     const uint64_t t0 = wall_clock64();
-    w = ld_word_coherent(p);
     int it = 0;
-    while ((uint32_t)(w >> 32) != tag) {
-      __builtin_amdgcn_s_sleep(4);
-      w = ld_word_coherent(p);
+    while (true) {
+      __builtin_amdgcn_s_sleep(2);
+      w0 = ld_word_coherent(p0);
+      w1 = ld_word_coherent(p1);
+      if (((uint32_t)(w0 >> 32) == tag) & ((uint32_t)(w1 >> 32) == tag)) break;
       if ((++it & 15) == 0 && wall_clock64() - t0 > F_WAIT_TICKS) {
         flag_error(sync, 2u);
         break;
       }
     }
   }
-  return w;
 }
 
 // Count the workgroup out: first in its XCD group, then the group's last
@@ -385,17 +387,17 @@ constexpr int F_NV = 8;  // logits per lane in the top-k: E <= 512 on this path
 //      the low 9 bits replaced by 511 - t: distinct keys that never
 //      contradict value order at the bits they keep); the maximum of each
 //      16-thread row (32 rows);
-//   2. tau = the k-th largest row maximum (every wave computes it from LDS;
-//      each lane ranks one row maximum against half of the others), tv =
-//      the smallest fp64 value with tau's leading bits. k rows hold a value
-//      >= tv, so every top-k value is >= tv;
+//   2. tau = the k-th largest row maximum (every wave computes it from LDS:
+//      lane r < 32 counts the row maxima above row r's), tv = the smallest
+//      fp64 value with tau's leading bits. k rows hold a value >= tv, so
+//      every top-k value is >= tv;
 //   3. candidates (values >= tv) appended to LDS (one LDS atomic per wave);
 //   4. wave 0 ranks the candidates exactly (value, then index): four lanes
 //      per candidate when there are at most 16 (the usual case: about 12),
 //      one lane per candidate up to 64, else the one-wave top-k over all
-//      values (massive ties);
-//   5. gates of the k winners as in the one-wave top-k (same arithmetic).
-// The workgroup reads idx/gates from LDS after.
+//      values (massive ties). The winners land in S.out[0 .. k) in order.
+// The gates (block_topk_gates) are not needed to pick the experts, so the
+// caller computes them once its weight loads are in flight.
 struct BlockTopk {
   double val[F_THREADS];         // every logit (-inf past E), for the tie path
   uint32_t rowmax[F_THREADS / 16];
@@ -408,7 +410,7 @@ struct BlockTopk {
 static_assert(64 * F_NV <= F_THREADS, "one logit per thread");
 
 __device__ __forceinline__ void block_topk(const uint64_t* logits, int E, int k, uint32_t tag, uint32_t* sync,
-                                           BlockTopk& S, int* s_idx, float* s_gate) {
+                                           BlockTopk& S) {
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   // 1. one logit per thread: coherent loads (a line another call left in
   //    this XCD's L2 is never used), clamped and unconditional
@@ -416,8 +418,7 @@ __device__ __forceinline__ void block_topk(const uint64_t* logits, int E, int k,
   uint64_t wl = ld_word_coherent(logits + 2 * e);
   uint64_t wh = ld_word_coherent(logits + 2 * e + 1);
   if (t == 0) S.cnt = 0;
-  wl = settle(logits + 2 * e, wl, tag, sync);
-  wh = settle(logits + 2 * e + 1, wh, tag, sync);
+  settle2(logits + 2 * e, logits + 2 * e + 1, wl, wh, tag, sync);  // the last router rows may be on their way
   const double v = (t < E) ? __longlong_as_double((long long)(((wh & 0xFFFFFFFFull) << 32) | (wl & 0xFFFFFFFFull)))
                            : -__builtin_inf();
   S.val[t] = v;
@@ -431,15 +432,15 @@ __device__ __forceinline__ void block_topk(const uint64_t* logits, int E, int k,
   __syncthreads();
   // 2. threshold
   const uint32_t mine = S.rowmax[lane & 31];
-  const uint4* rm = reinterpret_cast<const uint4*>(S.rowmax) + 4 * (lane >> 5);
-  int r = 0;
+  const uint4* rm = reinterpret_cast<const uint4*>(S.rowmax);
+  int r0 = 0, r1 = 0;
 #pragma unroll
-  for (int j = 0; j < 4; j++) {
-    const uint4 q = rm[j];
-    r += (int)(q.x > mine) + (int)(q.y > mine) + (int)(q.z > mine) + (int)(q.w > mine);
+  for (int j = 0; j < 8; j += 2) {
+    const uint4 q = rm[j], q2 = rm[j + 1];
+    r0 += (int)(q.x > mine) + (int)(q.y > mine) + (int)(q.z > mine) + (int)(q.w > mine);
+    r1 += (int)(q2.x > mine) + (int)(q2.y > mine) + (int)(q2.z > mine) + (int)(q2.w > mine);
   }
-  r += __shfl_xor(r, 32, 64);
-  const uint64_t sel = __ballot((lane < 32) & (r == k - 1));
+  const uint64_t sel = __ballot((lane < 32) & (r0 + r1 == k - 1));
   const uint32_t tau = (uint32_t)__builtin_amdgcn_readlane((int)mine, __ffsll((long long)sel) - 1) & ~511u;
   const double tv = key_floor_value(tau);
   // 3. candidates
@@ -454,48 +455,53 @@ __device__ __forceinline__ void block_topk(const uint64_t* logits, int E, int k,
     S.cand[pos].i = t;
   }
   __syncthreads();
-  // 4. exact order, 5. gates
+  // 4. exact order
   if (wave == 0) {
     const int nc = (int)S.cnt;
-    int mi;
-    float mg;
-    if (nc <= 64) {
-      if (nc <= 16) {
-        const int c = lane >> 2, g = lane & 3;
-        const TopkSlot me = S.cand[c < nc ? c : 0];
-        int rk = 0;
+    if (nc <= 16) {
+      const int c = lane >> 2, g = lane & 3;
+      const TopkSlot me = S.cand[c < nc ? c : 0];
+      int rk = 0;
 #pragma unroll
-        for (int jj = 0; jj < 4; jj++) {
-          const int j = g + 4 * jj;
-          const TopkSlot o = S.cand[j < nc ? j : 0];
-          rk += (int)((j < nc) & topk_before(o.v, o.i, me.v, me.i));
-        }
-        rk += dpp_i32<DPP_XOR1>(rk);
-        rk += dpp_i32<DPP_XOR2>(rk);
-        if ((g == 0) & (c < nc) & (rk < k)) S.out[rk] = me;
-      } else {
-        const TopkSlot me = S.cand[lane < nc ? lane : 0];
-        int rk = 0;
-        for (int j = 0; j < nc; j++) {
-          const TopkSlot o = S.cand[j];
-          rk += (int)topk_before(o.v, o.i, me.v, me.i);
-        }
-        if ((lane < nc) & (rk < k)) S.out[rk] = me;
+      for (int jj = 0; jj < 4; jj++) {
+        const int j = g + 4 * jj;
+        const TopkSlot o = S.cand[j < nc ? j : 0];
+        rk += (int)((j < nc) & topk_before(o.v, o.i, me.v, me.i));
       }
-      wave_lds_sync();
-      topk_gates(S.out, E, k, lane, mi, mg);
+      rk += dpp_i32<DPP_XOR1>(rk);
+      rk += dpp_i32<DPP_XOR2>(rk);
+      if ((g == 0) & (c < nc) & (rk < k)) S.out[rk] = me;
+    } else if (nc <= 64) {
+      const TopkSlot me = S.cand[lane < nc ? lane : 0];
+      int rk = 0;
+      for (int j = 0; j < nc; j++) {
+        const TopkSlot o = S.cand[j];
+        rk += (int)topk_before(o.v, o.i, me.v, me.i);
+      }
+      if ((lane < nc) & (rk < k)) S.out[rk] = me;
     } else {
       double w[F_NV];
 #pragma unroll
       for (int i = 0; i < F_NV; i++) w[i] = S.val[lane + 64 * i];
-      wave_topk<F_NV>(w, E, k, lane, S.wave_scratch, mi, mg);
+      wave_topk_order<F_NV>(w, E, k, lane, S.wave_scratch, S.out);
     }
+  }
+  __syncthreads();
+}
+
+// Gates of the k winners by wave 0 into s_idx/s_gate (the workgroup reads
+// them after a barrier).
+__device__ __forceinline__ void block_topk_gates(const BlockTopk& S, int E, int k, int* s_idx, float* s_gate) {
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    int mi;
+    float mg;
+    topk_gates(S.out, E, k, lane, mi, mg);
     if (lane < k) {
       s_idx[lane] = mi;
       s_gate[lane] = mg;
     }
   }
-  __syncthreads();
 }
 
 // ---------------------------------------------------------------------------
@@ -675,20 +681,26 @@ __global__ __launch_bounds__(F_THREADS, 4) void k_decode1(LayerDev L, const uint
     float* xsum = s_xsum;
     stage_x(x, H, xs, is_q<WT>() ? xsum : nullptr);
     wait_flags(fl, G.nR, flags_needed(G.nR), tag, ws.sync);
-    block_topk(tl + (size_t)my_rep() * 2 * L.E, L.E, L.k, tag, ws.sync, s_tk, s_idx, s_gate);
+    block_topk(tl + (size_t)my_rep() * 2 * L.E, L.E, L.k, tag, ws.sync, s_tk);
     const int gpe = I >> 5;
     const int u = b / gpe, q = b - u * gpe;
+    const int e = min(max(s_tk.out[u].i, 0), L.E - 1);  // in range whatever the logits held
+    const uint8_t* dn = L.dn + (size_t)e * L.dn_stride;
+    const uint16_t* dns = is_q<WT>() ? L.dn_s + (size_t)e * L.dn_s_stride : nullptr;
+    DownPre<WT> pre;
+    if constexpr (!is_q<WT>()) block_topk_gates(s_tk, L.E, L.k, s_idx, s_gate);
+    const float hv = gate_up_h<WT, 64>(L.gu + (size_t)e * L.gu_stride,
+                                       is_q<WT>() ? L.gu_s + (size_t)e * L.gu_s_stride : nullptr, H, 2 * I, q, 0, xs, xsum,
+                                       s_red, s_h, [&] {
+                                         down_prefetch<WT, 32>(dn, dns, H, 32 * q, pre);
+                                         // the gates, while the weights stream (read after gate_up_h's
+                                         // barrier); dense weights have no registers to spare there
+                                         if constexpr (is_q<WT>()) block_topk_gates(s_tk, L.E, L.k, s_idx, s_gate);
+                                       });
     if (b == 0 && (int)threadIdx.x < L.k) {
       if (idx_out) idx_out[threadIdx.x] = s_idx[threadIdx.x];
       if (gate_out) gate_out[threadIdx.x] = s_gate[threadIdx.x];
     }
-    const int e = s_idx[u];
-    const uint8_t* dn = L.dn + (size_t)e * L.dn_stride;
-    const uint16_t* dns = is_q<WT>() ? L.dn_s + (size_t)e * L.dn_s_stride : nullptr;
-    DownPre<WT> pre;
-    const float hv = gate_up_h<WT, 64>(L.gu + (size_t)e * L.gu_stride,
-                                       is_q<WT>() ? L.gu_s + (size_t)e * L.gu_s_stride : nullptr, H, 2 * I, q, 0, xs, xsum,
-                                       s_red, s_h, [&] { down_prefetch<WT, 32>(dn, dns, H, 32 * q, pre); });
     if constexpr (is_q<WT>()) {
       // block sum of the 32 bf16 h values (threads 0..31 of wave 0), fixed order
       float t = hv;
