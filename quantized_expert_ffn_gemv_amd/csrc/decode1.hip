@@ -251,29 +251,34 @@ __device__ __forceinline__ void role_router(const LayerDev& L, const uint16_t* _
 
 // qdot32 with the magic exponent held in a register: each code pair is one
 // shift and one and-or (the constants then need no instruction of their own).
+// The 32 bf16 activations come as four registers of eight (av).
 template <int WT>
-__device__ __forceinline__ float qdot32_reg(const Raw& r, const uint16_t* a, float asum, uint32_t magic) {
+__device__ __forceinline__ float qdot32_regs(const Raw& r, const uint4 (&av)[4], float asum, uint32_t magic) {
+  uint32_t p[16];
   if constexpr (WT == MOE_W_Q4) {
-    uint32_t p[16];
 #pragma unroll
     for (int j = 0; j < 4; j++)
 #pragma unroll
       for (int t = 0; t < 4; t++) p[4 * j + t] = ((r.w[j] >> (4 * t)) & 0x000F000Fu) | magic;
-    const uint4* av = reinterpret_cast<const uint4*>(a);
-    float c0 = -(128.0f + (float)QOff<WT>::v) * asum, c1 = 0.0f, c2 = 0.0f, c3 = 0.0f;
-#pragma unroll
-    for (int q = 0; q < 4; q++) {
-      const uint4 v = av[q];
-      c0 = dot2_bf16(p[4 * q + 0], v.x, c0);
-      c1 = dot2_bf16(p[4 * q + 1], v.y, c1);
-      c2 = dot2_bf16(p[4 * q + 2], v.z, c2);
-      c3 = dot2_bf16(p[4 * q + 3], v.w, c3);
-    }
-    return (c0 + c1) + (c2 + c3);
   } else {
     (void)magic;
-    return qdot32<WT>(r, a, asum);
+    q3_pairs<BF16_MAGIC2>(r.w[0], r.w[1], r.w[2], p);
   }
+  float c0 = -(128.0f + (float)QOff<WT>::v) * asum, c1 = 0.0f, c2 = 0.0f, c3 = 0.0f;
+#pragma unroll
+  for (int q = 0; q < 4; q++) {
+    c0 = dot2_bf16(p[4 * q + 0], av[q].x, c0);
+    c1 = dot2_bf16(p[4 * q + 1], av[q].y, c1);
+    c2 = dot2_bf16(p[4 * q + 2], av[q].z, c2);
+    c3 = dot2_bf16(p[4 * q + 3], av[q].w, c3);
+  }
+  return (c0 + c1) + (c2 + c3);
+}
+template <int WT>
+__device__ __forceinline__ float qdot32_reg(const Raw& r, const uint16_t* a, float asum, uint32_t magic) {
+  const uint4* ap = reinterpret_cast<const uint4*>(a);
+  const uint4 av[4] = {ap[0], ap[1], ap[2], ap[3]};
+  return qdot32_regs<WT>(r, av, asum, magic);
 }
 
 // ---------------------------------------------------------------------------
@@ -553,6 +558,21 @@ __device__ __forceinline__ void down_store(const uint8_t* __restrict__ d, int H,
                                            const uint16_t* s_h, float hsum, float scale, uint64_t* part, uint32_t tag) {
   constexpr int KC = DownPlan<WT, NCOL>::KC;
   constexpr int NCH = DownPlan<WT, NCOL>::NCH;
+  if constexpr (DownPlan<WT, NCOL>::PRE && is_q<WT>()) {
+    // h (32 bf16) in registers once; every row computed (rows past H hold
+    // row H - 1's chunk), only the store is conditional
+    const uint4* hp = reinterpret_cast<const uint4*>(s_h);
+    const uint4 hv[4] = {hp[0], hp[1], hp[2], hp[3]};
+    uint32_t magic = BF16_MAGIC2;
+    asm volatile("" : "+v"(magic));
+#pragma unroll
+    for (int n = 0; n < F_RPT; n++) {
+      const int row = (int)threadIdx.x + F_THREADS * n;
+      const float v = f16_to_f32(pre.s[n]) * qdot32_regs<WT>(pre.r[n], hv, hsum, magic);
+      if (row < H) st_word(part + row, __float_as_uint(v * scale), tag);
+    }
+    return;
+  }
 #pragma unroll
   for (int n = 0; n < F_RPT; n++) {
     const int row = (int)threadIdx.x + F_THREADS * n;
