@@ -4,8 +4,9 @@
 // the routed ones, then extra reducers if needed; at most one workgroup per
 // CU at the shapes of interest, so no role shares a CU's VALUs with another):
 //
-//   [0, nA)        b < nR: router, 8 expert rows each, fp64 logits (an fp32
-//                  weight times a bf16 activation is exact in fp64); then
+//   [0, nA)        b < nR: router, 8 expert rows each (two waves a row),
+//                  fp64 logits (an fp32 weight times a bf16 activation is
+//                  exact in fp64); then
 //                  b < nSG: shared expert, 8 intermediates each (16 gate/up
 //                  rows), gate/up GEMV + SwiGLU -> h (bf16, in LDS), then
 //                  those 8 columns of the shared down matrix times h: a
@@ -32,7 +33,7 @@
 // never wait, and the shared roles never wait, so every partial gets
 // written once every workgroup is resident; a reducer waits on producers
 // dispatched after it, so the path is taken only when the whole grid fits
-// on the chip at once (two workgroups per CU).
+// on the chip at once (one workgroup per CU).
 //
 // Hand-off without cache flushes. Every value one workgroup passes to
 // another (logits, partial down products) travels in a 64-bit word whose
@@ -62,10 +63,14 @@
 
 namespace moe {
 
-constexpr int F_THREADS = 512;
-constexpr int F_RPT = 4;                        // down rows per thread (H <= F_RPT * F_THREADS)
+// 16 waves per workgroup, one workgroup per CU: four waves per SIMD keep
+// the dequantise-dot chains busy (two waves per SIMD left the SIMDs idle
+// through LDS and dependency latencies: the same work took 1.76x as long).
+constexpr int F_THREADS = 1024;
+constexpr int F_WAVES = F_THREADS / 64;
+constexpr int F_RPT = 2;                        // down rows per thread (H <= F_RPT * F_THREADS)
 constexpr int F_HMAX = F_RPT * F_THREADS;       // largest H of this path (LDS arrays are sized for it)
-constexpr int F_RCPL = 8;                       // router float4 chunks per lane and batch
+constexpr int F_RCPL = 4;                       // router float4 chunks per lane and batch
 constexpr uint64_t F_WAIT_TICKS = 1ull << 25;   // ~0.34 s of the 100 MHz wall clock
 
 // Workspace sync area (uint32 words; every count in its own 128-byte line).
@@ -192,18 +197,20 @@ __device__ __forceinline__ void finish(uint32_t* sync) {
 }
 
 // ---------------------------------------------------------------------------
-// Router: wave w of workgroup b computes the logit of expert 8b + w. The
+// Router: waves w and w + 8 of workgroup b compute the two halves of the
+// logit of expert 8b + w (summed in that order). The
 // logits are written once per XCD group (SY_NREP replicas): the routed
 // workgroups of a group read their own copy, so each line has a few
 // readers instead of all of them (lines read by hundreds of workgroups at
 // once serve them one after another).
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ void role_router(const LayerDev& L, const uint16_t* __restrict__ x, uint64_t* logits, int b,
-                                            uint32_t tag) {
+                                            double* s_rt, uint32_t tag) {
+  static_assert(F_WAVES == 16, "two waves per router row");
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int e = b * 8 + wave;
+  const int e = b * 8 + (wave & 7), hh = wave >> 3;
   const bool valid = e < L.E;
-  const int n4 = L.H >> 2;
+  const int n4 = L.H >> 2, c_lo = hh * (n4 >> 1), c_hi = hh ? n4 : (n4 >> 1);
   const float4* wr = reinterpret_cast<const float4*>(L.router_w + (size_t)(valid ? e : 0) * L.H);
   const uint2* xv = reinterpret_cast<const uint2*>(x);
   // the bias is loaded with the weights (not after the sum: a load there is
@@ -211,7 +218,7 @@ __device__ __forceinline__ void role_router(const LayerDev& L, const uint16_t* _
   const float* bp = L.router_b ? L.router_b + (valid ? e : 0) : L.router_w;
   const float bias_raw = *bp;
   double a0 = 0.0, a1 = 0.0;
-  for (int c0 = 0; c0 < n4; c0 += 64 * F_RCPL) {
+  for (int c0 = c_lo; c0 < c_hi; c0 += 64 * F_RCPL) {
     float4 w[F_RCPL];
     uint2 xx[F_RCPL];
     // loads with clamped indices and no branch (a load inside a branch makes
@@ -219,13 +226,13 @@ __device__ __forceinline__ void role_router(const LayerDev& L, const uint16_t* _
     // elements past the row are masked after
 #pragma unroll
     for (int i = 0; i < F_RCPL; i++) {
-      const int c = min(c0 + lane + 64 * i, n4 - 1);
+      const int c = min(c0 + lane + 64 * i, c_hi - 1);
       w[i] = wr[c];
       xx[i] = xv[c];
     }
 #pragma unroll
     for (int i = 0; i < F_RCPL; i++) {
-      if (!(valid && c0 + lane + 64 * i < n4)) {
+      if (!(valid && c0 + lane + 64 * i < c_hi)) {
         w[i] = make_float4(0.f, 0.f, 0.f, 0.f);
         xx[i] = make_uint2(0u, 0u);
       }
@@ -238,8 +245,11 @@ __device__ __forceinline__ void role_router(const LayerDev& L, const uint16_t* _
       a1 = __builtin_fma((double)w[i].w, (double)bf16_hi(xx[i].y), a1);
     }
   }
-  const double tot = wave_total_f64(a0 + a1);
-  if (valid && lane < SY_NREP) {
+  const double part = wave_total_f64(a0 + a1);
+  if (hh == 1 && lane == 0) s_rt[wave & 7] = part;
+  __syncthreads();
+  if (hh == 0 && valid && lane < SY_NREP) {
+    const double tot = part + s_rt[wave];
     const uint64_t v = (uint64_t)__double_as_longlong(tot + (L.router_b ? (double)bias_raw : 0.0));
     // two words (low, high half of the fp64 logit), each with the tag, in
     // every XCD group's replica (lane r writes replica r)
@@ -292,7 +302,7 @@ __device__ __forceinline__ float qdot32_reg(const Raw& r, const uint16_t* a, flo
 // Threads j < RPW/2 end holding intermediate j's value (returned, 0 for
 // others), also stored to s_h[j].
 // ---------------------------------------------------------------------------
-constexpr int F_GU_NB = 8;  // chunks per thread and batch
+constexpr int F_GU_NB = 4;  // chunks per thread and batch
 
 template <int WT, int RPW, typename After>
 __device__ __forceinline__ float gate_up_h(const uint8_t* __restrict__ gu, const uint16_t* __restrict__ gus, int H, int R,
@@ -391,7 +401,7 @@ constexpr int F_NV = 8;  // logits per lane in the top-k: E <= 512 on this path
 //   1. each thread's 32-bit sortable key (leading bits of the fp64 logit,
 //      the low 9 bits replaced by 511 - t: distinct keys that never
 //      contradict value order at the bits they keep); the maximum of each
-//      16-thread row (32 rows);
+//      16-thread row (the first 32 rows hold the E <= 512 logits);
 //   2. tau = the k-th largest row maximum (every wave computes it from LDS:
 //      lane r < 32 counts the row maxima above row r's), tv = the smallest
 //      fp64 value with tau's leading bits. k rows hold a value >= tv, so
@@ -427,7 +437,7 @@ __device__ __forceinline__ void block_topk(const uint64_t* logits, int E, int k,
   const double v = (t < E) ? __longlong_as_double((long long)(((wh & 0xFFFFFFFFull) << 32) | (wl & 0xFFFFFFFFull)))
                            : -__builtin_inf();
   S.val[t] = v;
-  const uint32_t key = (sort_key_hi(v) & ~511u) | (uint32_t)(511 - t);
+  const uint32_t key = (sort_key_hi(v) & ~511u) | (uint32_t)(511 - min(t, 511));
   uint32_t m = key;
   m = max(m, (uint32_t)dpp_i32<DPP_XOR1>((int)m));
   m = max(m, (uint32_t)dpp_i32<DPP_XOR2>((int)m));
@@ -435,29 +445,31 @@ __device__ __forceinline__ void block_topk(const uint64_t* logits, int E, int k,
   m = max(m, (uint32_t)dpp_i32<DPP_MIRROR>((int)m));
   if ((lane & 15) == 0) S.rowmax[t >> 4] = m;
   __syncthreads();
-  // 2. threshold
-  const uint32_t mine = S.rowmax[lane & 31];
-  const uint4* rm = reinterpret_cast<const uint4*>(S.rowmax);
-  int r0 = 0, r1 = 0;
+  // 2. threshold, 3. candidates (waves holding experts only)
+  if (wave * 64 < E) {
+    const uint32_t mine = S.rowmax[lane & 31];
+    const uint4* rm = reinterpret_cast<const uint4*>(S.rowmax);
+    int r0 = 0, r1 = 0;
 #pragma unroll
-  for (int j = 0; j < 8; j += 2) {
-    const uint4 q = rm[j], q2 = rm[j + 1];
-    r0 += (int)(q.x > mine) + (int)(q.y > mine) + (int)(q.z > mine) + (int)(q.w > mine);
-    r1 += (int)(q2.x > mine) + (int)(q2.y > mine) + (int)(q2.z > mine) + (int)(q2.w > mine);
-  }
-  const uint64_t sel = __ballot((lane < 32) & (r0 + r1 == k - 1));
-  const uint32_t tau = (uint32_t)__builtin_amdgcn_readlane((int)mine, __ffsll((long long)sel) - 1) & ~511u;
-  const double tv = key_floor_value(tau);
-  // 3. candidates
-  const bool cand = (t < E) & (v >= tv);
-  const uint64_t bal = __ballot(cand);
-  uint32_t base = 0;
-  if (lane == 0) base = atomicAdd(&S.cnt, (uint32_t)__popcll(bal));
-  base = (uint32_t)__builtin_amdgcn_readfirstlane((int)base);
-  const uint32_t pos = base + (uint32_t)__popcll(bal & ((1ull << lane) - 1ull));
-  if (cand & (pos < 64u)) {
-    S.cand[pos].v = v;
-    S.cand[pos].i = t;
+    for (int j = 0; j < 8; j += 2) {
+      const uint4 q = rm[j], q2 = rm[j + 1];
+      r0 += (int)(q.x > mine) + (int)(q.y > mine) + (int)(q.z > mine) + (int)(q.w > mine);
+      r1 += (int)(q2.x > mine) + (int)(q2.y > mine) + (int)(q2.z > mine) + (int)(q2.w > mine);
+    }
+    const uint64_t sel = __ballot((lane < 32) & (r0 + r1 == k - 1));
+    const uint32_t tau = (uint32_t)__builtin_amdgcn_readlane((int)mine, __ffsll((long long)sel) - 1) & ~511u;
+    const double tv = key_floor_value(tau);
+    // 3. candidates
+    const bool cand = (t < E) & (v >= tv);
+    const uint64_t bal = __ballot(cand);
+    uint32_t base = 0;
+    if (lane == 0) base = atomicAdd(&S.cnt, (uint32_t)__popcll(bal));
+    base = (uint32_t)__builtin_amdgcn_readfirstlane((int)base);
+    const uint32_t pos = base + (uint32_t)__popcll(bal & ((1ull << lane) - 1ull));
+    if (cand & (pos < 64u)) {
+      S.cand[pos].v = v;
+      S.cand[pos].i = t;
+    }
   }
   __syncthreads();
   // 4. exact order
@@ -599,7 +611,7 @@ __device__ __forceinline__ void down_store(const uint8_t* __restrict__ d, int H,
 // the poll sees it.
 // ---------------------------------------------------------------------------
 constexpr int F_RD = 16;                   // output rows per reducer
-constexpr int F_RG = F_THREADS / F_RD;     // producer groups per reducer (32)
+constexpr int F_RG = F_THREADS / F_RD;     // producer groups per reducer (64)
 
 __device__ __forceinline__ void role_reduce(const uint64_t* part, int nP, int H, int r0, uint16_t* __restrict__ y,
                                             float* s_red, uint32_t tag, uint32_t* sync) {
@@ -607,7 +619,7 @@ __device__ __forceinline__ void role_reduce(const uint64_t* part, int nP, int H,
   const int row = r0 + rr;
   float acc = 0.0f;
   const int rowc = min(row, H - 1);
-  constexpr int NB = 8;  // F_RG * NB >= the producers of the usual shapes: one batch of loads
+  constexpr int NB = 4;  // F_RG * NB >= the producers of the usual shapes: one batch of loads
   for (int p0 = pg; p0 < nP; p0 += F_RG * NB) {
     uint64_t w[NB];
 #pragma unroll
@@ -638,13 +650,19 @@ __device__ __forceinline__ void role_reduce(const uint64_t* part, int nP, int H,
     for (int n = 0; n < NB; n++)
       if (p0 + F_RG * n < nP) acc += __uint_as_float((uint32_t)w[n]);
   }
-  s_red[threadIdx.x] = acc;
+  // a wave holds four producer groups of the same 16 rows (lanes rr + 16j):
+  // fold them in the wave ((g0 + g1) + (g2 + g3)), then the wave sums
+  static_assert(F_RD == 16, "four groups per wave");
+  float a = acc + __shfl_xor(acc, 16, 64);
+  a += __shfl_xor(a, 32, 64);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane < F_RD) s_red[wave * F_RD + lane] = a;
   __syncthreads();
   if ((int)threadIdx.x < F_RD && row < H) {
-    float a = 0.0f;
-#pragma unroll 8
-    for (int g = 0; g < F_RG; g++) a += s_red[g * F_RD + rr];
-    y[row] = f32_to_bf16(a);
+    float t = 0.0f;
+#pragma unroll
+    for (int w = 0; w < F_WAVES; w++) t += s_red[w * F_RD + rr];
+    y[row] = f32_to_bf16(t);
   }
 }
 
@@ -662,6 +680,7 @@ __global__ __launch_bounds__(F_THREADS, 4) void k_decode1(LayerDev L, const uint
   __shared__ __align__(16) uint16_t s_x[F_HMAX];
   __shared__ __align__(16) float s_xsum[F_HMAX / 32];
   __shared__ __align__(16) float s_red[F_THREADS];
+  __shared__ double s_rt[8];
   __shared__ __align__(16) BlockTopk s_tk;
   __shared__ int s_idx[16];
   __shared__ float s_gate[16];
@@ -678,7 +697,7 @@ __global__ __launch_bounds__(F_THREADS, 4) void k_decode1(LayerDev L, const uint
   int b = blockIdx.x;
   if (b < G.nA) {
     if (b < G.nR) {
-      role_router(L, x, tl, b, tag);
+      role_router(L, x, tl, b, s_rt, tag);
       raise_flag(fl, b, tag);
     }
     if (b < G.nSG) {
@@ -768,8 +787,8 @@ static int decode1_grid(int E, int H, int I, int k, bool has_shared) {
   return nA + (nRG > nD ? nRG : nD);
 }
 
-// Workgroups that are sure to be resident together: two per CU (the launch
-// bounds keep a workgroup within half a CU's registers; its LDS is ~16 KB).
+// Workgroups that are sure to be resident together: one per CU (the launch
+// bounds keep a workgroup within a CU's registers; its LDS is ~24 KB).
 // Reducers wait for producers dispatched before and after them, so the
 // whole grid must be resident at once.
 static int decode1_capacity() {
@@ -779,7 +798,7 @@ static int decode1_capacity() {
   if (cap[dev] == 0) {
     int cus = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-    cap[dev] = 2 * cus;
+    cap[dev] = cus;
   }
   return cap[dev];
 }
