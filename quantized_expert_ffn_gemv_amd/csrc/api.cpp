@@ -129,6 +129,8 @@ size_t carve_prefill(const moe_layer* L, int T, uint8_t* base, moe::PrefillWs* w
   };
   moe::PrefillWs w{};
   w.logits = reinterpret_cast<double*>(take((size_t)T * E * 8));
+  w.rsplit = reinterpret_cast<uint16_t*>(take(E * H * 2 * 2));
+  w.wnorm = reinterpret_cast<double*>(take(E * 8));
   w.idx = reinterpret_cast<int32_t*>(take((size_t)T * k * 4));
   w.gates = reinterpret_cast<float*>(take((size_t)T * k * 4));
   w.blk_counts = reinterpret_cast<int32_t*>(take(nblk * E * 4));
@@ -196,7 +198,7 @@ const char* const kKernelNames[moe::KC_COUNT] = {
     "dec_fused",         "dec_router_shared", "dec_routed", "dec_reduce",         "pf_router",         "pf_topk",
     "pf_count",          "pf_scan",     "pf_scatter",       "pf_gate_up",        "pf_down",
     "pf_shared_gate_up", "pf_shared_down", "pf_combine",    "rmsnorm",           "residual_add",
-    "fill",              "dec_route"};
+    "fill",              "dec_route",       "pf_rsplit"};
 
 }  // namespace
 

@@ -127,20 +127,6 @@ constexpr int TOPK_CMAX = 128;
 // bytes per wave: 64 keys, (TOPK_CMAX + 64) candidate slots, 16 outputs; slots are 16 B (value, index)
 constexpr size_t TOPK_SCRATCH = 64 * 4 + (size_t)(TOPK_CMAX + 64) * 16 + 16 * 16;
 
-__device__ __forceinline__ uint32_t sort_key_hi(double v) {
-  const uint64_t b = (uint64_t)__double_as_longlong(v);
-  const uint64_t k = (b >> 63) ? ~b : (b | 0x8000000000000000ull);
-  return (uint32_t)(k >> 32);
-}
-
-// Smallest fp64 value whose sortable key has high word `hi` (low word 0).
-__device__ __forceinline__ double key_floor_value(uint32_t hi) {
-  const uint64_t k = (uint64_t)hi << 32;
-  const uint64_t b = (k >> 63) ? (k & 0x7FFFFFFFFFFFFFFFull) : ~k;
-  const double v = __longlong_as_double((long long)b);
-  return (v == v) ? v : -__builtin_inf();  // a NaN pattern (keys of -inf or below) admits every value
-}
-
 __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();

@@ -212,4 +212,20 @@ __device__ __forceinline__ void wave_argmax(double& v, int& i) {
   v = bv;
   i = bi;
 }
+// Sortable 32-bit key of an fp64 value: its leading 32 bits, ordered as
+// unsigned integers the way the values order.
+__device__ __forceinline__ uint32_t sort_key_hi(double v) {
+  const uint64_t b = (uint64_t)__double_as_longlong(v);
+  const uint64_t k = (b >> 63) ? ~b : (b | 0x8000000000000000ull);
+  return (uint32_t)(k >> 32);
+}
+
+// Smallest fp64 value whose sortable key has high word `hi` (low word 0).
+__device__ __forceinline__ double key_floor_value(uint32_t hi) {
+  const uint64_t k = (uint64_t)hi << 32;
+  const uint64_t b = (k >> 63) ? (k & 0x7FFFFFFFFFFFFFFFull) : ~k;
+  const double v = __longlong_as_double((long long)b);
+  return (v == v) ? v : -__builtin_inf();  // a NaN pattern (keys of -inf or below) admits every value
+}
+
 }  // namespace moe

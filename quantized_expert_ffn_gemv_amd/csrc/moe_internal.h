@@ -29,6 +29,7 @@ enum KernelClass {
   KC_RESIDUAL,
   KC_FILL,
   KC_DEC_ROUTE,              // top-k of a batch and its unique experts (B > 1 path)
+  KC_PF_RSPLIT,              // router weights split into two bf16 halves + row norms
   KC_COUNT
 };
 
@@ -62,7 +63,9 @@ struct DecodeWs {
 
 // Prefill workspace.
 struct PrefillWs {
-  double* logits;     // [T][E]
+  double* logits;     // [T][E] (approximate fp32 logits in the first half)
+  uint16_t* rsplit;   // [2][E][H] router weights as bf16 hi, then lo
+  double* wnorm;      // [E] router row norms
   int32_t* idx;       // [T][k]
   float* gates;       // [T][k]
   int32_t* blk_counts;// [nblk][E]

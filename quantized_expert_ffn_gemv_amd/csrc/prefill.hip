@@ -1,7 +1,9 @@
 // Prefill path: T tokens through one MoE layer.
 //
-//   k_pf_router      router logits, fp64 MFMA (exact products, fp64 sums)
-//   k_pf_topk        ordered top-k and renormalised gates, one wave per token
+//   k_pf_rsplit      router weights -> two bf16 halves and row norms
+//   k_pf_rapprox     approximate router logits, bf16 MFMA (error bounded)
+//   k_pf_rselect     per token: candidates from the bounds, their exact fp64
+//                    logits, ordered top-k and renormalised gates
 //   k_pf_count       per-block expert histograms (LDS atomics: order-free)
 //   k_pf_scan        exclusive scans: expert offsets, per-block bases, GEMM tiles
 //   k_pf_scatter     stable permutation: slots sorted by expert, token order
@@ -19,146 +21,246 @@
 namespace moe {
 
 // ---------------------------------------------------------------------------
-// Router: logits[t][e] = sum_h W[e][h] x[t][h] + b[e] in fp64
+// Router: logits[t][e] = sum_h W[e][h] x[t][h] + b[e] in fp64, then the
+// ordered top-k. Selection needs the exact fp64 order only near the k-th
+// largest logit, so the logits are filtered first and verified after:
+//   k_pf_rsplit   W (fp32) -> W_hi = bf16(W), W_lo = bf16(W - W_hi) and
+//                 ||W_e||_2 in fp64 (|W - W_hi - W_lo| <= 2^-16 |W|);
+//   k_pf_gemm<bf16, GK_F32> (the dense grouped GEMM, one "expert" of 2E
+//                 rows) computes W_hi x and W_lo x with bf16 MFMA, fp32
+//                 sums; a[t][e] = (W_hi x + W_lo x) + b in fp32;
+//   k_pf_rselect  per token: |a - l| <= B_e = C ||W_e|| ||x_t|| + 2^-22 |a|
+//                 + 2^-100 (below); L = the k-th largest a - B; candidates =
+//                 experts with a + B >= L (every top-k expert is one: k
+//                 experts have l >= L, and a + B < L means l < L); their
+//                 exact fp64 logits (fp32 weight x bf16 activation is exact
+//                 in fp64, sums in fp64), ordered top-k among them (value,
+//                 then lower index), renormalised gates.
+// The bound: the split leaves 2^-16 S (S = sum |W x| <= ||W|| ||x||); each
+// accumulator sums 2048-ish exact products (bf16 x bf16 fits fp32) in fp32,
+// error <= gamma_n S with gamma_n = n u / (1 - n u), taken with u = 2^-23
+// (directed rounding) and n = H + 32 (the MFMA's own partial sums); the
+// final adds cost 2^-23 (|a| + |b|) each. C covers all of it with a factor > 1.1
+// spare; 2^-110 ||x|| + 2^-100 absorb flushed denormal weights and sums.
 // ---------------------------------------------------------------------------
-// fp64 MFMA (v_mfma_f64_16x16x4f64): an fp32 weight times a bf16 activation
-// is exact in fp64 and the sum accumulates in fp64, as the definition has it.
-// Operand layout of the instruction: A[m][k] in lane 16k + m, B[k][n] in lane
-// 16k + n, D[m][n] in lane 16 (m % 4) + n, element m / 4. In each 16-wide
-// hidden step lane (k, .) supplies hidden positions 4k .. 4k+3, one per MFMA
-// step j (the same permutation on both operands), so it loads 4 consecutive
-// weights (16 B) and 4 consecutive activations (8 B) per step.
-// Tile: workgroup 64 tokens x 128 experts, wave 32 tokens x 64 experts.
-constexpr int RT_TM = 64, RT_TN = 128;
-
-typedef double double4_t __attribute__((ext_vector_type(4)));
-
-__global__ __launch_bounds__(256) void k_pf_router(const float* __restrict__ W, const float* __restrict__ bias,
-                                                    const uint16_t* __restrict__ x, int T, int E, int H,
-                                                    double* __restrict__ logits) {
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int t0 = blockIdx.x * RT_TM + 32 * (wave & 1);
-  const int e0 = blockIdx.y * RT_TN + 64 * (wave >> 1);
-  const int kq = lane >> 4, r16 = lane & 15;
-  // rows this lane loads (clamped into range; results for rows past T / E are not stored)
-  const uint16_t* xa[2];
-  const float* wb[4];
+// The halves land as one chunk-major bf16 matrix of 2E rows (hi rows, then lo
+// rows; chunk c of row r = elements 8c .. 8c+7 at [c][r]), the layout the
+// dense grouped GEMM reads.
+__global__ __launch_bounds__(256) void k_pf_rsplit(const float* __restrict__ W, int E, int H, uint16_t* __restrict__ split,
+                                                   double* __restrict__ wnorm) {
+  // one workgroup per expert row; thread: chunks c = threadIdx.x + 256 j
+  __shared__ double s_ss[4];
+  const int e = blockIdx.x, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const float* w = W + (size_t)e * H;
+  double ss = 0.0;
+  for (int c = threadIdx.x; c < (H >> 3); c += 256) {
+    const float4 v0 = *reinterpret_cast<const float4*>(w + 8 * c);
+    const float4 v1 = *reinterpret_cast<const float4*>(w + 8 * c + 4);
+    const float f[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+    uint32_t ph[4], pl[4];
 #pragma unroll
-  for (int i = 0; i < 2; i++) {
-    const int t = t0 + 16 * i + r16;
-    xa[i] = x + (size_t)(t < T ? t : T - 1) * H + 4 * kq;
-  }
-#pragma unroll
-  for (int j = 0; j < 4; j++) {
-    const int e = e0 + 16 * j + r16;
-    wb[j] = W + (size_t)(e < E ? e : E - 1) * H + 4 * kq;
-  }
-  double4_t acc[2][4];
-#pragma unroll
-  for (int i = 0; i < 2; i++)
-#pragma unroll
-    for (int j = 0; j < 4; j++) acc[i][j] = double4_t{0.0, 0.0, 0.0, 0.0};
-  uint2 ra[2][2];
-  float4 rb[2][4];
-  auto load = [&](int h0, int slot) {
-#pragma unroll
-    for (int i = 0; i < 2; i++) ra[slot][i] = *reinterpret_cast<const uint2*>(xa[i] + h0);
-#pragma unroll
-    for (int j = 0; j < 4; j++) rb[slot][j] = *reinterpret_cast<const float4*>(wb[j] + h0);
-  };
-  auto step = [&](int slot) {
-    double a[2][4], b[4][4];
-#pragma unroll
-    for (int i = 0; i < 2; i++) {
-      a[i][0] = (double)bf16_lo(ra[slot][i].x);
-      a[i][1] = (double)bf16_hi(ra[slot][i].x);
-      a[i][2] = (double)bf16_lo(ra[slot][i].y);
-      a[i][3] = (double)bf16_hi(ra[slot][i].y);
+    for (int q = 0; q < 4; q++) {
+      ph[q] = pack_bf16x2(f[2 * q], f[2 * q + 1]);
+      pl[q] = pack_bf16x2(f[2 * q] - bf16_lo(ph[q]), f[2 * q + 1] - bf16_hi(ph[q]));
     }
+    *reinterpret_cast<uint4*>(split + ((size_t)c * 2 * E + e) * 8) = make_uint4(ph[0], ph[1], ph[2], ph[3]);
+    *reinterpret_cast<uint4*>(split + ((size_t)c * 2 * E + E + e) * 8) = make_uint4(pl[0], pl[1], pl[2], pl[3]);
 #pragma unroll
-    for (int j = 0; j < 4; j++) {
-      b[j][0] = (double)rb[slot][j].x;
-      b[j][1] = (double)rb[slot][j].y;
-      b[j][2] = (double)rb[slot][j].z;
-      b[j][3] = (double)rb[slot][j].w;
-    }
-#pragma unroll
-    for (int q = 0; q < 4; q++)
-#pragma unroll
-      for (int i = 0; i < 2; i++)
-#pragma unroll
-        for (int j = 0; j < 4; j++) acc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[i][q], b[j][q], acc[i][j], 0, 0, 0);
-  };
-  // two register stages: the loads of step s + 1 are in flight while step s computes
-  load(0, 0);
-  for (int h0 = 0; h0 < H; h0 += 32) {
-    if (h0 + 16 < H) load(h0 + 16, 1);
-    step(0);
-    if (h0 + 16 >= H) break;
-    if (h0 + 32 < H) load(h0 + 32, 0);
-    step(1);
+    for (int q = 0; q < 8; q++) ss = __builtin_fma((double)f[q], (double)f[q], ss);
   }
-  // D[m][n]: lane 16 (m % 4) + n, element m / 4
-#pragma unroll
-  for (int i = 0; i < 2; i++)
-#pragma unroll
-    for (int j = 0; j < 4; j++) {
-      const int e = e0 + 16 * j + r16;
-      const double bv = (bias && e < E) ? (double)bias[e] : 0.0;
-#pragma unroll
-      for (int q = 0; q < 4; q++) {
-        const int t = t0 + 16 * i + 4 * q + kq;
-        if (t < T && e < E) logits[(size_t)t * E + e] = acc[i][j][q] + bv;
-      }
-    }
+  ss = wave_total_f64(ss);
+  if (lane == 0) s_ss[wave] = ss;
+  __syncthreads();
+  if (threadIdx.x == 0) wnorm[e] = __builtin_sqrt((s_ss[0] + s_ss[1]) + (s_ss[2] + s_ss[3]));
 }
 
-// ---------------------------------------------------------------------------
-// Top-k: one wave per token
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void k_pf_topk(const double* __restrict__ logits, int T, int E, int k,
-                                                  int32_t* __restrict__ idx, float* __restrict__ gates,
-                                                  int32_t* idx_out, float* gate_out) {
-  const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= T) return;
-  const double* l = logits + (size_t)t * E;
-  double v[16];
+// One wave per token (E <= 1024: lane holds experts lane + 64 i); approx is
+// [T][2E]: the W_hi x and W_lo x sums. The
+// token's activations stay in registers (NXH chunks of 512: lane holds
+// hidden 512 j + 8 lane .. + 7); candidates go four at a time (their weight
+// rows load together), each exact logit summed across the wave in a fixed
+// order (DPP rows, then the four row sums).
+constexpr int RS_NV = 16;
+template <int NXH>
+__global__ __launch_bounds__(256) void k_pf_rselect(const float* __restrict__ W, const float* __restrict__ bias,
+                                                    const uint16_t* __restrict__ x, const float* __restrict__ approx,
+                                                    const double* __restrict__ wnorm, int T, int E, int H, int k,
+                                                    int32_t* __restrict__ idx, float* __restrict__ gates,
+                                                    int32_t* idx_out, float* gate_out) {
+  __shared__ int s_ce[4][64 * RS_NV];     // candidate experts, ascending
+  __shared__ uint32_t s_key[4][64];       // lane maxima of the lower ends (sortable keys)
+  __shared__ double s_ov[4][16];          // winners in order
+  __shared__ int s_oe[4][16];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int t = blockIdx.x * 4 + wave;
+  if (t >= T) return;  // whole wave; no workgroup barrier below
+  int* cl = s_ce[wave];
+  const uint16_t* xt = x + (size_t)t * H;
+  // activations and ||x_t||_2 (fp64)
+  uint4 xr[NXH];
+  double xs = 0.0;
 #pragma unroll
-  for (int i = 0; i < 16; i++) {
+  for (int j = 0; j < NXH; j++) {
+    const int h = 512 * j + 8 * lane;
+    const uint4 v = *reinterpret_cast<const uint4*>(xt + min(h, H - 8));
+    xr[j] = (h < H) ? v : make_uint4(0u, 0u, 0u, 0u);
+    const uint32_t p[4] = {xr[j].x, xr[j].y, xr[j].z, xr[j].w};
+#pragma unroll
+    for (int q = 0; q < 4; q++) {
+      const double a = bf16_lo(p[q]), b = bf16_hi(p[q]);
+      xs = __builtin_fma(a, a, xs);
+      xs = __builtin_fma(b, b, xs);
+    }
+  }
+  const double xn = __builtin_sqrt(wave_total_f64(xs));
+  // bounds; lower ends a_e - B_e, upper ends a_e + B_e
+  const double C = (1.1 * ((double)(H + 32) * 0x1p-23 / (1.0 - (double)(H + 32) * 0x1p-23)) + 0x1p-15) * (1.0 + 1e-9);
+  double lo[RS_NV], up[RS_NV];
+#pragma unroll
+  for (int i = 0; i < RS_NV; i++) {
     const int e = lane + 64 * i;
-    v[i] = (e < E) ? l[e] : -__builtin_inf();
+    const int ec = min(e, E - 1);
+    const float bv = bias ? bias[ec] : 0.0f;
+    const double a = (double)((approx[(size_t)t * 2 * E + ec] + approx[(size_t)t * 2 * E + E + ec]) + bv);
+    const double B = C * wnorm[ec] * xn + 0x1p-22 * (__builtin_fabs(a) + __builtin_fabs((double)bv)) + 0x1p-110 * xn + 0x1p-100;
+    lo[i] = (e < E) ? a - B : -__builtin_inf();
+    up[i] = (e < E) ? a + B : -__builtin_inf();
   }
-  double m = 0.0, myv = -__builtin_inf();
-  int myi = 0;
-  for (int r = 0; r < k; r++) {
-    double best = -__builtin_inf();
-    int bi = 0x7FFFFFFF;
+  // L = a lower bound of the k-th largest lower end: the k-th largest of the
+  // lanes' maxima (k lanes hold a lower end >= it), by the leading 26 bits
+  // of its sortable key (ties between lanes broken by lane, so the 64 keys
+  // are distinct); L = the smallest fp64 value with those leading bits.
+  double lmax = -__builtin_inf();
 #pragma unroll
-    for (int i = 0; i < 16; i++) {
-      const int e = lane + 64 * i;
-      if (e < E && v[i] > best) { best = v[i]; bi = e; }
+  for (int i = 0; i < RS_NV; i++) lmax = lo[i] > lmax ? lo[i] : lmax;
+  const uint32_t key = (sort_key_hi(lmax) & ~63u) | (uint32_t)(63 - lane);
+  s_key[wave][lane] = key;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  int rk0 = 0, rk1 = 0;
+  const uint4* kv = reinterpret_cast<const uint4*>(s_key[wave]);
+#pragma unroll
+  for (int j = 0; j < 16; j += 2) {
+    const uint4 q = kv[j], q2 = kv[j + 1];
+    rk0 += (int)(q.x > key) + (int)(q.y > key) + (int)(q.z > key) + (int)(q.w > key);
+    rk1 += (int)(q2.x > key) + (int)(q2.y > key) + (int)(q2.z > key) + (int)(q2.w > key);
+  }
+  const uint64_t selk = __ballot(rk0 + rk1 == k - 1);
+  const double L = key_floor_value((uint32_t)__builtin_amdgcn_readlane((int)key, __ffsll((long long)selk) - 1) & ~63u);
+  // candidates, in expert order
+  int nc = 0;
+#pragma unroll
+  for (int i = 0; i < RS_NV; i++) {
+    const bool c = up[i] >= L;
+    const uint64_t bal = __ballot(c);
+    if (c) cl[nc + __popcll(bal & ((1ull << lane) - 1ull))] = lane + 64 * i;
+    nc += __popcll(bal);
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  // exact logits, four candidates per pass
+  double cv[RS_NV];
+#pragma unroll
+  for (int i = 0; i < RS_NV; i++) cv[i] = -__builtin_inf();
+  for (int c0 = 0; c0 < nc; c0 += 4) {
+    int e[4];
+    double acc[4];
+#pragma unroll
+    for (int q = 0; q < 4; q++) {
+      e[q] = cl[min(c0 + q, nc - 1)];
+      acc[q] = 0.0;
+    }
+    constexpr int UJ = NXH <= 4 ? NXH : 2;  // weight loads in flight per pass
+#pragma unroll UJ
+    for (int j = 0; j < NXH; j++) {
+      const int h = min(512 * j + 8 * lane, H - 8);  // lanes past H: x is zero there
+      float4 w[4][2];
+#pragma unroll
+      for (int q = 0; q < 4; q++) {
+        const float* we = W + (size_t)e[q] * H + h;
+        w[q][0] = *reinterpret_cast<const float4*>(we);
+        w[q][1] = *reinterpret_cast<const float4*>(we + 4);
+      }
+      const uint32_t p[4] = {xr[j].x, xr[j].y, xr[j].z, xr[j].w};
+#pragma unroll
+      for (int q = 0; q < 4; q++) {
+        acc[q] = __builtin_fma((double)w[q][0].x, (double)bf16_lo(p[0]), acc[q]);
+        acc[q] = __builtin_fma((double)w[q][0].y, (double)bf16_hi(p[0]), acc[q]);
+        acc[q] = __builtin_fma((double)w[q][0].z, (double)bf16_lo(p[1]), acc[q]);
+        acc[q] = __builtin_fma((double)w[q][0].w, (double)bf16_hi(p[1]), acc[q]);
+        acc[q] = __builtin_fma((double)w[q][1].x, (double)bf16_lo(p[2]), acc[q]);
+        acc[q] = __builtin_fma((double)w[q][1].y, (double)bf16_hi(p[2]), acc[q]);
+        acc[q] = __builtin_fma((double)w[q][1].z, (double)bf16_lo(p[3]), acc[q]);
+        acc[q] = __builtin_fma((double)w[q][1].w, (double)bf16_hi(p[3]), acc[q]);
+      }
     }
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-      const double ov = __shfl_xor(best, o, 64);
-      const int oi = __shfl_xor(bi, o, 64);
-      if (ov > best || (ov == best && oi < bi)) { best = ov; bi = oi; }
-    }
+    for (int q = 0; q < 4; q++) {
+      const double l = wave_total_f64(acc[q]) + (bias ? (double)bias[e[q]] : 0.0);
+      const int c = c0 + q;  // uniform: lane c % 64 keeps it in slot c / 64
 #pragma unroll
-    for (int i = 0; i < 16; i++)
-      if (lane + 64 * i == bi) v[i] = -__builtin_inf();
-    if (r == 0) m = best;
-    if (lane == r) { myv = best; myi = bi; }
+      for (int i = 0; i < RS_NV; i++)
+        if (c < nc && c == lane + 64 * i) cv[i] = l;
+    }
   }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  // ordered top-k among the candidates (value, then lower expert index)
+  if (nc <= 64) {
+    // rank of candidate c (lane c) by counting the candidates before it
+    const double myc = cv[0];
+    const int mye = cl[min(lane, nc - 1)];
+    int rk = 0;
+    for (int j = 0; j < nc; j++) {
+      const double vj = readlane_f64(myc, j);
+      const int ej = __builtin_amdgcn_readlane(mye, j);
+      rk += (int)((vj > myc) | ((vj == myc) & (ej < mye)));
+    }
+    if (lane < nc && rk < k) {
+      s_ov[wave][rk] = myc;
+      s_oe[wave][rk] = mye;
+    }
+  } else {
+    int ce[RS_NV];
+#pragma unroll
+    for (int i = 0; i < RS_NV; i++) {
+      const int c = lane + 64 * i;
+      ce[i] = (c < nc) ? cl[min(c, nc - 1)] : 0x7FFFFFFF;
+    }
+    for (int r = 0; r < k; r++) {
+      double best = -__builtin_inf();
+      int bi = 0x7FFFFFFF;
+#pragma unroll
+      for (int i = 0; i < RS_NV; i++)
+        if (cv[i] > best || (cv[i] == best && ce[i] < bi)) { best = cv[i]; bi = ce[i]; }
+      wave_argmax(best, bi);
+#pragma unroll
+      for (int i = 0; i < RS_NV; i++)
+        if (ce[i] == bi) cv[i] = -__builtin_inf(), ce[i] = 0x7FFFFFFF;
+      if (lane == 0) {
+        s_ov[wave][r] = best;
+        s_oe[wave][r] = bi;
+      }
+    }
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  // renormalised gates: softmax of the k selected fp64 logits
+  const double m = s_ov[wave][0];
+  const double myv = s_ov[wave][lane < k ? lane : 0];
+  const int myi = s_oe[wave][lane < k ? lane : 0];
   const double ev = (lane < k) ? exp(myv - m) : 0.0;
-  const double z = wave_sum_f64(ev);
+  const double z = wave_total_f64(ev);
   if (lane < k) {
     const float g = (float)(ev / z);
-    idx[(size_t)t * k + lane] = myi;
+    const int ix = (myi >= 0 && myi < E) ? myi : 0;  // in range whatever the inputs held
+    idx[(size_t)t * k + lane] = ix;
     gates[(size_t)t * k + lane] = g;
-    if (idx_out) idx_out[(size_t)t * k + lane] = myi;
+    if (idx_out) idx_out[(size_t)t * k + lane] = ix;
     if (gate_out) gate_out[(size_t)t * k + lane] = g;
   }
 }
@@ -274,7 +376,7 @@ constexpr int G_THREADS = 256;     // 4 waves; wave w owns columns [16 NSW w, 16
 constexpr int G_BK = 128;          // K per pipeline stage (4 MFMA K-steps of 32)
 constexpr int G_MSUB = PF_BM / 16; // 16-row subtiles per tile
 
-enum GemmKind { GK_GATE_UP = 0, GK_DOWN = 1 };
+enum GemmKind { GK_GATE_UP = 0, GK_DOWN = 1, GK_F32 = 2 };  // GK_F32: plain product, fp32 out (dense weights)
 
 struct GemmArgs {
   // weights of expert 0 (routed) or the shared expert; chunk-major [K/kc][N][cb]
@@ -293,6 +395,7 @@ struct GemmArgs {
   int E;
   int M_total;            // rows when offsets == NULL
   uint16_t* out;          // gate/up: h [rows][N/2]; down: Y [rows][N]
+  float* out_f32;         // GK_F32: [rows][N]
 };
 
 // ---------------------------------------------------------------------------
@@ -578,7 +681,10 @@ __global__ __launch_bounds__(G_THREADS, 2) void k_pf_gemm(GemmArgs g) {
 #pragma unroll
           for (int r = 0; r < 4; r++) {
             const int m = 16 * i + 4 * (lane >> 4) + r;
-            if (m < M && col < g.N) g.out[(size_t)(pos0 + m) * g.N + col] = f32_to_bf16(acc[i][j][r]);
+            if (m < M && col < g.N) {
+              if (KIND == GK_F32) g.out_f32[(size_t)(pos0 + m) * g.N + col] = acc[i][j][r];
+              else g.out[(size_t)(pos0 + m) * g.N + col] = f32_to_bf16(acc[i][j][r]);
+            }
           }
         }
       }
@@ -897,13 +1003,38 @@ __global__ __launch_bounds__(256) void k_pf_combine(const uint16_t* __restrict__
 // ---------------------------------------------------------------------------
 // Host launch
 // ---------------------------------------------------------------------------
+template <int WT, int KIND>
+static void gemm_launch(int kc, const GemmArgs& g, int tiles_x, hipStream_t st) {
+  // tiles_x: an upper bound on the M tiles; the kernel reads the real count and
+  // maps workgroups XCD-major, so the grid is a multiple of 8
+  const int nt = (g.N + g_bn<WT>() - 1) / g_bn<WT>();
+  const int total = tiles_x * nt;
+  if constexpr (WT == MOE_W_Q4 || WT == MOE_W_Q3) {
+    static_assert(GQ_BN == g_bn<WT>(), "tile width");
+    (void)launch_k(kc, k_pf_gemm_q<WT, KIND>, dim3(8 * ((total + 7) / 8)), dim3(G_THREADS), 0, st, g);
+  } else {
+    (void)launch_k(kc, k_pf_gemm<WT, KIND>, dim3(8 * ((total + 7) / 8)), dim3(G_THREADS), 0, st, g);
+  }
+}
+
 static hipError_t route_steps(const LayerDev& L, const uint16_t* x, int T, int32_t* idx_out, float* gate_out,
                               int32_t* counts_out, const PrefillWs& ws, hipStream_t st, bool permute) {
   const int E = L.E, k = L.k, H = L.H;
-  (void)launch_k(KC_PF_ROUTER, k_pf_router, dim3((T + RT_TM - 1) / RT_TM, (E + RT_TN - 1) / RT_TN), dim3(256), 0, st, L.router_w,
-                     L.router_b, x, T, E, H, ws.logits);
-  (void)launch_k(KC_PF_TOPK, k_pf_topk, dim3((T + 3) / 4), dim3(256), 0, st, ws.logits, T, E, k, ws.idx, ws.gates, idx_out,
-                     gate_out);
+  float* approx = reinterpret_cast<float*>(ws.logits);  // [T][2E] fp32 in the [T][E] fp64 area
+  (void)launch_k(KC_PF_RSPLIT, k_pf_rsplit, dim3(E), dim3(256), 0, st, L.router_w, E, H, ws.rsplit, ws.wnorm);
+  {
+    GemmArgs g{};
+    g.w = reinterpret_cast<const uint8_t*>(ws.rsplit); g.N = 2 * E; g.K = H; g.a = x; g.perm = nullptr; g.k = 1;
+    g.offsets = nullptr; g.M_total = T; g.out_f32 = approx;
+    gemm_launch<MOE_W_BF16, GK_F32>(KC_PF_ROUTER, g, (T + PF_BM - 1) / PF_BM, st);
+  }
+  {
+    const int nxh = (H + 511) / 512;
+    auto sel = nxh <= 1 ? k_pf_rselect<1> : nxh <= 2 ? k_pf_rselect<2> : nxh <= 4 ? k_pf_rselect<4>
+             : nxh <= 8 ? k_pf_rselect<8> : k_pf_rselect<16>;
+    (void)launch_k(KC_PF_TOPK, sel, dim3((T + 3) / 4), dim3(256), 0, st, L.router_w, L.router_b, x, approx, ws.wnorm, T, E,
+                   H, k, ws.idx, ws.gates, idx_out, gate_out);
+  }
   if (!permute && !counts_out) return hipGetLastError();
   const int nblk = (T + PF_TOK_PER_BLK - 1) / PF_TOK_PER_BLK;
   (void)launch_k(KC_PF_COUNT, k_pf_count, dim3(nblk), dim3(256), E * sizeof(int), st, ws.idx, T, E, k, ws.blk_counts);
@@ -918,20 +1049,6 @@ static hipError_t route_steps(const LayerDev& L, const uint16_t* x, int T, int32
 hipError_t launch_route(const LayerDev& L, const uint16_t* x, int T, int32_t* idx_out, float* gate_out,
                         int32_t* counts_out, const PrefillWs& ws, hipStream_t st) {
   return route_steps(L, x, T, idx_out, gate_out, counts_out, ws, st, false);
-}
-
-template <int WT, int KIND>
-static void gemm_launch(int kc, const GemmArgs& g, int tiles_x, hipStream_t st) {
-  // tiles_x: an upper bound on the M tiles; the kernel reads the real count and
-  // maps workgroups XCD-major, so the grid is a multiple of 8
-  const int nt = (g.N + g_bn<WT>() - 1) / g_bn<WT>();
-  const int total = tiles_x * nt;
-  if constexpr (WT == MOE_W_Q4 || WT == MOE_W_Q3) {
-    static_assert(GQ_BN == g_bn<WT>(), "tile width");
-    (void)launch_k(kc, k_pf_gemm_q<WT, KIND>, dim3(8 * ((total + 7) / 8)), dim3(G_THREADS), 0, st, g);
-  } else {
-    (void)launch_k(kc, k_pf_gemm<WT, KIND>, dim3(8 * ((total + 7) / 8)), dim3(G_THREADS), 0, st, g);
-  }
 }
 
 template <int KIND>
