@@ -227,6 +227,40 @@ def test_route_entry_counts(moe, prefill_q4):
     assert np.array_equal(counts.cpu().numpy(), np.bincount(idx.cpu().numpy().ravel(), minlength=L.E))
 
 
+def test_route_exact_and_near_ties(moe):
+    """Prefill routing where the approximate logits cannot decide: experts
+    1-3 copy expert 0's router row (exact ties, lower index first), expert 5
+    is expert 4's row scaled by 1 + 2^-20 (a gap far below the approximation's
+    error bound, above the tie tolerance), and some tokens are zero (every
+    logit equals its bias). Routing must match the oracle's fp64 order."""
+    host = synth.random_layer(64, 8, 256, 32, "q4", "bf16", seed=7, router_sd=0.3)
+    w = host.router_w
+    w[1:4] = w[0]
+    w[5] = (w[4].astype(np.float64) * (1.0 + 2.0 ** -20)).astype(np.float32)
+    if host.router_b is not None:
+        host.router_b[1:4] = host.router_b[0]
+        host.router_b[5] = host.router_b[4]
+    L = moe.DeviceLayer(host)
+    x = synth.normal_bf16(synth.key(7, 5, 5, 5, 5), (96, 256), 1.0)
+    x[5] = 0
+    x[40] = 0
+    # pull expert 0 and 4 into the top-k for many tokens: tokens aligned with their rows
+    x[10:20] = oracle.round_to_bf16_bits(np.tile(w[0].astype(np.float64), (10, 1)) * 0.5)
+    x[20:30] = oracle.round_to_bf16_bits(np.tile(w[4].astype(np.float64), (10, 1)) * 0.5)
+    T = x.shape[0]
+    ws = moe.make_workspace(L, T, 1)
+    idx = torch.empty((T, L.k), dtype=torch.int32, device="cuda")
+    g = torch.empty((T, L.k), dtype=torch.float32, device="cuda")
+    moe.moe_route(L, to_dev(x), idx, g, ws)
+    torch.cuda.synchronize()
+    idx_ref, g_ref, logits = oracle.route(host, x)
+    check_routing(idx.cpu().numpy(), idx_ref, logits, "ties")
+    check_gates(g.cpu().numpy(), g_ref, "ties")
+    got = idx.cpu().numpy()
+    assert all(list(got[t][:4]) == [0, 1, 2, 3] for t in range(10, 20)), got[10:20, :4]
+    assert all(list(got[t][:2]) == [5, 4] for t in range(20, 30)), got[20:30, :2]
+
+
 def test_prefill_matches_decode(moe, decode_q4):
     host, L, x = decode_q4
     xs = x[:32]
