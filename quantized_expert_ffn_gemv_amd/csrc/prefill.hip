@@ -97,14 +97,21 @@ __global__ __launch_bounds__(256) void k_pf_rselect(const float* __restrict__ W,
   int* cl = s_ce[wave];
   const uint16_t* xt = x + (size_t)t * H;
   // activations and ||x_t||_2 (fp64)
-  uint4 xr[NXH];
+  // (held in registers for H <= 2048; longer rows are reloaded per chunk, an
+  // L1 hit, instead of living in an array the compiler would put in memory)
+  constexpr bool XR = NXH <= 4;
+  auto x_chunk = [&](int j) {
+    const int h = 512 * j + 8 * lane;
+    const uint4 v = *reinterpret_cast<const uint4*>(xt + min(h, H - 8));
+    return (h < H) ? v : make_uint4(0u, 0u, 0u, 0u);
+  };
+  uint4 xr[XR ? NXH : 1];
   double xs = 0.0;
 #pragma unroll
   for (int j = 0; j < NXH; j++) {
-    const int h = 512 * j + 8 * lane;
-    const uint4 v = *reinterpret_cast<const uint4*>(xt + min(h, H - 8));
-    xr[j] = (h < H) ? v : make_uint4(0u, 0u, 0u, 0u);
-    const uint32_t p[4] = {xr[j].x, xr[j].y, xr[j].z, xr[j].w};
+    const uint4 v = x_chunk(j);
+    if constexpr (XR) xr[j] = v;
+    const uint32_t p[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
     for (int q = 0; q < 4; q++) {
       const double a = bf16_lo(p[q]), b = bf16_hi(p[q]);
@@ -183,17 +190,26 @@ __global__ __launch_bounds__(256) void k_pf_rselect(const float* __restrict__ W,
         w[q][0] = *reinterpret_cast<const float4*>(we);
         w[q][1] = *reinterpret_cast<const float4*>(we + 4);
       }
-      const uint32_t p[4] = {xr[j].x, xr[j].y, xr[j].z, xr[j].w};
+      double xj[8];
+      uint4 xv;
+      if constexpr (XR) xv = xr[j];
+      else xv = x_chunk(j);
+      const uint32_t p[4] = {xv.x, xv.y, xv.z, xv.w};
+#pragma unroll
+      for (int r = 0; r < 4; r++) {
+        xj[2 * r] = bf16_lo(p[r]);
+        xj[2 * r + 1] = bf16_hi(p[r]);
+      }
 #pragma unroll
       for (int q = 0; q < 4; q++) {
-        acc[q] = __builtin_fma((double)w[q][0].x, (double)bf16_lo(p[0]), acc[q]);
-        acc[q] = __builtin_fma((double)w[q][0].y, (double)bf16_hi(p[0]), acc[q]);
-        acc[q] = __builtin_fma((double)w[q][0].z, (double)bf16_lo(p[1]), acc[q]);
-        acc[q] = __builtin_fma((double)w[q][0].w, (double)bf16_hi(p[1]), acc[q]);
-        acc[q] = __builtin_fma((double)w[q][1].x, (double)bf16_lo(p[2]), acc[q]);
-        acc[q] = __builtin_fma((double)w[q][1].y, (double)bf16_hi(p[2]), acc[q]);
-        acc[q] = __builtin_fma((double)w[q][1].z, (double)bf16_lo(p[3]), acc[q]);
-        acc[q] = __builtin_fma((double)w[q][1].w, (double)bf16_hi(p[3]), acc[q]);
+        acc[q] = __builtin_fma((double)w[q][0].x, xj[0], acc[q]);
+        acc[q] = __builtin_fma((double)w[q][0].y, xj[1], acc[q]);
+        acc[q] = __builtin_fma((double)w[q][0].z, xj[2], acc[q]);
+        acc[q] = __builtin_fma((double)w[q][0].w, xj[3], acc[q]);
+        acc[q] = __builtin_fma((double)w[q][1].x, xj[4], acc[q]);
+        acc[q] = __builtin_fma((double)w[q][1].y, xj[5], acc[q]);
+        acc[q] = __builtin_fma((double)w[q][1].z, xj[6], acc[q]);
+        acc[q] = __builtin_fma((double)w[q][1].w, xj[7], acc[q]);
       }
     }
 #pragma unroll
@@ -847,25 +863,30 @@ __global__ __launch_bounds__(G_THREADS, 2) void k_pf_gemm_q(GemmArgs g) {
       Q4Scale qs[NSW];
 #pragma unroll
       for (int sub = 0; sub < NSW; sub++) qs[sub] = q4_scale(sc[sub] & ((okbits >> sub) & 1u ? 0xFFFFu : 0u));
+      // each lane's 16-byte chunks in one 128-bit read per subtile (lanes
+      // contiguous: no bank conflicts; four 32-bit reads at a 16-byte lane
+      // stride put four lanes on every bank)
+      uint4 wq[NSW];
+#pragma unroll
+      for (int sub = 0; sub < NSW; sub++) wq[sub] = reinterpret_cast<const uint4*>(sb + (wave * NSW + sub) * GQ_REGION)[lane];
 #pragma unroll
       for (int t = 0; t < 4; t++) {
         bf16x8_t bfrag[NSW];
 #pragma unroll
         for (int sub = 0; sub < NSW; sub++) {
-          const uint32_t wd = reinterpret_cast<const uint32_t*>(sb + (wave * NSW + sub) * GQ_REGION)[4 * lane + t];
+          const uint32_t wd = t == 0 ? wq[sub].x : t == 1 ? wq[sub].y : t == 2 ? wq[sub].z : wq[sub].w;
           bfrag[sub] = q4_frag(wd, qs[sub], magic);
         }
+        {  // all row subtiles' A fragments of the step read together
+          bf16x8_t afrag[G_MSUB];
 #pragma unroll
-        for (int h = 0; h < G_MSUB; h += G_MSUB / 2) {
-          bf16x8_t afrag[G_MSUB / 2];
+          for (int i = 0; i < G_MSUB; i++)
+            afrag[i] = __builtin_bit_cast(bf16x8_t, A[(16 * i + m) * 16 + ((4 * bj + t) ^ m)]);
 #pragma unroll
-          for (int i = 0; i < G_MSUB / 2; i++)
-            afrag[i] = __builtin_bit_cast(bf16x8_t, A[(16 * (h + i) + m) * 16 + ((4 * bj + t) ^ m)]);
-#pragma unroll
-          for (int i = 0; i < G_MSUB / 2; i++)
+          for (int i = 0; i < G_MSUB; i++)
 #pragma unroll
             for (int sub = 0; sub < NSW; sub++)
-              acc[h + i][sub] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afrag[i], bfrag[sub], acc[h + i][sub], 0, 0, 0);
+              acc[i][sub] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afrag[i], bfrag[sub], acc[i][sub], 0, 0, 0);
           __builtin_amdgcn_sched_barrier(0);
         }
       }
@@ -884,17 +905,16 @@ __global__ __launch_bounds__(G_THREADS, 2) void k_pf_gemm_q(GemmArgs g) {
         bf16x8_t bfrag[NSW];
 #pragma unroll
         for (int sub = 0; sub < NSW; sub++) bfrag[sub] = frag_b<WT>(r[sub], t);
+        {  // all row subtiles' A fragments of the step read together
+          bf16x8_t afrag[G_MSUB];
 #pragma unroll
-        for (int h = 0; h < G_MSUB; h += G_MSUB / 2) {
-          bf16x8_t afrag[G_MSUB / 2];
+          for (int i = 0; i < G_MSUB; i++)
+            afrag[i] = __builtin_bit_cast(bf16x8_t, A[(16 * i + m) * 16 + ((4 * bj + t) ^ m)]);
 #pragma unroll
-          for (int i = 0; i < G_MSUB / 2; i++)
-            afrag[i] = __builtin_bit_cast(bf16x8_t, A[(16 * (h + i) + m) * 16 + ((4 * bj + t) ^ m)]);
-#pragma unroll
-          for (int i = 0; i < G_MSUB / 2; i++)
+          for (int i = 0; i < G_MSUB; i++)
 #pragma unroll
             for (int sub = 0; sub < NSW; sub++)
-              acc[h + i][sub] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afrag[i], bfrag[sub], acc[h + i][sub], 0, 0, 0);
+              acc[i][sub] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afrag[i], bfrag[sub], acc[i][sub], 0, 0, 0);
           __builtin_amdgcn_sched_barrier(0);
         }
       }
