@@ -90,26 +90,22 @@ def run_decode(moe, torch, L, x_bits, steps, warmup, B=1):
     return eager_s, graph_s, g
 
 
-def run_c2(moe, torch, synth, steps, warmup):
-    """The Q3 / Zipf-routed layer: 256 tokens as batch-1 calls and as 32
-    batch-8 calls (graph replays). Bytes per call count each unique routed
-    expert once (the weights an expert chosen by several tokens of a call
-    are read once), plus the shared expert and the router."""
-    name = "decode_q3_zipf"
-    host = synth.make_layer(name, threads=16)
-    x = synth.make_tokens(name)
-    L = moe.DeviceLayer(host)
-    T = x.shape[0]
+def decode_batches(moe, torch, L, x, steps, warmup, batches):
+    """Decode of the tokens x as graph-replayed calls of B tokens, for each B in
+    batches (x cut to a multiple of B). Bytes per call count each unique
+    routed expert once (the weights of an expert chosen by several tokens of a
+    call are read once), plus the shared expert and the router."""
     gu, dn, sgu, sdn = decode_expert_bytes(L)
     router_bytes = L.E * L.H * 4
-    out = {"workload": "one MoE layer, Q3 experts (32-elem blocks, fp16 scales), Zipf-skewed router bias "
-                       "(hottest 20% of experts take 80% of selections), bf16 shared, fp32 router; 256 tokens"}
     dev = torch.device("cuda")
-    xd = torch.from_numpy(x.view(np.int16)).to(dev)
-    for B in (1, 8):
-        _, graph_s, g = run_decode(moe, torch, L, x, steps, warmup, B=B)
+    out = {}
+    for B in batches:
+        xb = x[: (x.shape[0] // B) * B]
+        T = xb.shape[0]
+        _, graph_s, g = run_decode(moe, torch, L, xb, steps, warmup, B=B)
         del g
         # unique routed experts per call, from the routing of the same calls
+        xd = torch.from_numpy(xb.view(np.int16)).to(dev)
         idx = torch.empty((T, L.k), dtype=torch.int32, device=dev)
         yy = torch.empty_like(xd)
         ws = moe.make_workspace(L, B, 0)
@@ -128,6 +124,30 @@ def run_c2(moe, torch, synth, steps, warmup):
             "effective_GBps": round(bytes_total / graph_s / 1e9, 1),
             "frac_of_hbm": round(bytes_total / graph_s / 1e9 / HBM_PEAK_GBS, 4),
         }
+    return out
+
+
+def run_c2(moe, torch, synth, steps, warmup):
+    """The Q3 / Zipf-routed layer: 256 tokens as batch-1 calls and as 32
+    batch-8 calls (graph replays)."""
+    name = "decode_q3_zipf"
+    host = synth.make_layer(name, threads=16)
+    x = synth.make_tokens(name)
+    L = moe.DeviceLayer(host)
+    out = {"workload": "one MoE layer, Q3 experts (32-elem blocks, fp16 scales), Zipf-skewed router bias "
+                       "(hottest 20% of experts take 80% of selections), bf16 shared, fp32 router; 256 tokens"}
+    out.update(decode_batches(moe, torch, L, x, steps, warmup, (1, 8)))
+    return out
+
+
+def run_spec_verify(moe, torch, L, x, steps, warmup):
+    """Speculative-verify shapes on the batch-1 layer: one call checks the
+    current token and d = 2..4 drafts (B = 1 + d). Independent tokens stand in
+    for the drafts, the worst case for sharing experts within a call (drafts
+    of one sequence route alike more often)."""
+    out = {"workload": "the batch-1 Q4 layer at B = 3, 4, 5 tokens per call (verify of 2-4 drafts); "
+                       "independent synthetic tokens as drafts"}
+    out.update(decode_batches(moe, torch, L, x, steps, warmup, (3, 4, 5)))
     return out
 
 
@@ -429,6 +449,12 @@ def main():
         },
     }
     del g
+
+    # ---------------------------------------------------------------- speculative-verify batches (secondary)
+    if not args.no_prefill:
+        log("decode Q4, B = 3..5 (verify of 2-4 drafts) ...")
+        result["decode_spec_verify"] = run_spec_verify(moe, torch, L, x, args.steps, args.warmup)
+        log("decode_spec_verify:", json.dumps(result["decode_spec_verify"]))
 
     # ---------------------------------------------------------------- Q3 / Zipf decode, batch 1 and 8 (secondary)
     if not args.no_prefill:

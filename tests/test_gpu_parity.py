@@ -172,6 +172,27 @@ def test_decode_q4_sequence_sampled(moe, decode_q4):
     _check_all(host, x[sample], y[sample], idx[sample], g[sample], "decode_q4 B=1")
 
 
+@pytest.mark.parametrize("B", [3, 4, 5])
+def test_decode_q4_verify_batches(moe, decode_q4, B):
+    # speculative-verify shapes: one call holds the current token and 2-4
+    # drafts. 12 consecutive calls, every token checked; then calls whose
+    # tokens repeat (drafts that route to the same experts: each expert's
+    # weights serve several tokens of the call)
+    host, L, x = decode_q4
+    log("decode_q4: B=%d, 12 calls + 3 calls with repeated tokens" % B)
+    xs = x[: 12 * B]
+    y, idx, g = _decode_calls(moe, L, xs, B)
+    _check_all(host, xs, y, idx, g, "decode_q4 B=%d" % B)
+    rep = np.concatenate([x[[7] * B], x[[9, 9] + [11] * (B - 2)], x[[13, 14] * (B // 2) + [13] * (B % 2)]])
+    y, idx, g = _decode_calls(moe, L, rep, B)
+    _check_all(host, rep, y, idx, g, "decode_q4 B=%d repeated tokens" % B)
+    for c in range(3):
+        toks = rep[c * B:(c + 1) * B]
+        for i in range(B):
+            j = [jj for jj in range(B) if np.array_equal(toks[jj], toks[i])][0]
+            assert np.array_equal(y[c * B + i], y[c * B + j]), "identical tokens of one call must give identical outputs"
+
+
 @pytest.fixture(scope="module")
 def decode_q3(moe):
     host = synth.make_layer("decode_q3_zipf")
