@@ -32,15 +32,20 @@ __device__ __forceinline__ Raw load_chunk(const uint8_t* base, size_t ci) {
 }
 
 // sum_k (code_k - OFF) * a_k over a 32-element chunk (`a`: 32 bf16 values in
-// LDS, asum their sum). Four independent dot2 chains. The caller scales.
+// LDS, asum their sum), in two parts: qunpack32 turns the chunk into 16 bf16
+// pairs (128 + code each, exact), qdot32_p dots them with the activations in
+// four independent dot2 chains (so a chunk used by several tokens is
+// unpacked once); qdot32 does both. The caller scales.
 template <int WT>
-__device__ __forceinline__ float qdot32(const Raw& r, const uint16_t* a, float asum) {
-  uint32_t p[16];
+__device__ __forceinline__ void qunpack32(const Raw& r, uint32_t (&p)[16]) {
   if constexpr (WT == MOE_W_Q4) {
     q4_pairs<BF16_MAGIC2>(make_uint4(r.w[0], r.w[1], r.w[2], r.w[3]), p);
   } else {
     q3_pairs<BF16_MAGIC2>(r.w[0], r.w[1], r.w[2], p);
   }
+}
+template <int WT>
+__device__ __forceinline__ float qdot32_p(const uint32_t (&p)[16], const uint16_t* a, float asum) {
   const uint4* av = reinterpret_cast<const uint4*>(a);
   float c0 = -(128.0f + (float)QOff<WT>::v) * asum, c1 = 0.0f, c2 = 0.0f, c3 = 0.0f;
 #pragma unroll
@@ -52,6 +57,12 @@ __device__ __forceinline__ float qdot32(const Raw& r, const uint16_t* a, float a
     c3 = dot2_bf16(p[4 * q + 3], v.w, c3);
   }
   return (c0 + c1) + (c2 + c3);
+}
+template <int WT>
+__device__ __forceinline__ float qdot32(const Raw& r, const uint16_t* a, float asum) {
+  uint32_t p[16];
+  qunpack32<WT>(r, p);
+  return qdot32_p<WT>(p, a, asum);
 }
 
 // Dot of one dense chunk (8 bf16 or 4 fp32 weights) with bf16 activations.

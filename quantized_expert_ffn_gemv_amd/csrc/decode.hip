@@ -85,6 +85,39 @@ __device__ __forceinline__ void load_down_piece(const uint8_t* dn, const uint16_
   }
 }
 
+// the 8 code pairs of a quantised piece as bf16 (128 + code), once per piece
+template <int WT, int NCOL>
+__device__ __forceinline__ void down_piece_unpack(const DownPiece<WT, NCOL>& d, int half, uint32_t (&p)[8]) {
+  if constexpr (is_q<WT>()) {
+    if constexpr (WT == MOE_W_Q4) {
+#pragma unroll
+      for (int w = 0; w < 2; w++)
+#pragma unroll
+        for (int s = 0; s < 4; s++) p[4 * w + s] = ((d.w[w] >> (4 * s)) & 0x000F000Fu) | BF16_MAGIC2;
+    } else {
+      const uint32_t hsh = d.w[1] >> (8 * half);
+#pragma unroll
+      for (int i = 0; i < 8; i++) {
+        const uint32_t v = ((d.w[0] >> (2 * i)) & 0x00030003u) | BF16_MAGIC2;
+        const uint32_t h = (i >= 2) ? (hsh >> (i - 2)) : (hsh << (2 - i));
+        p[i] = v | (h & 0x00040004u);
+      }
+    }
+  }
+}
+// its dot with one token's 16 bf16 h values (hp, 8 pairs) whose sum is hs
+template <int WT, int NCOL>
+__device__ __forceinline__ float down_piece_dot_p(const DownPiece<WT, NCOL>& d, const uint32_t (&p)[8],
+                                                  const uint32_t* hp, float hs) {
+  float c0 = -(128.0f + (float)QOff<WT>::v) * hs, c1 = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; i += 2) {
+    c0 = dot2_bf16(p[i], hp[i], c0);
+    c1 = dot2_bf16(p[i + 1], hp[i + 1], c1);
+  }
+  return d.s * (c0 + c1);
+}
+
 template <int WT, int NCOL>
 __device__ __forceinline__ float down_piece_dot(const DownPiece<WT, NCOL>& d, int half, const uint32_t* hp, float hs) {
   if constexpr (is_q<WT>()) {
@@ -446,17 +479,28 @@ __global__ __launch_bounds__(DB_THREADS) void k_dec_b(LayerDev L, const uint16_t
     }
   };
   auto compute_batch = [&](int c0) {
+    if constexpr (QT) {
+      // each chunk unpacked once, then dotted with every token of the expert
 #pragma unroll
-    for (int t = 0; t < MAXB; t++) {
-      if (t < B && (mask >> t & 1u)) {
+      for (int i = 0; i < B_CPT; i++) {
+        const int c = c0 + kp + 16 * i;
+        if (c < nc) {
+          uint32_t p[16];
+          qunpack32<WT>(raw[i], p);
 #pragma unroll
-        for (int i = 0; i < B_CPT; i++) {
-          const int c = c0 + kp + 16 * i;
-          if (c < nc) {
-            if constexpr (QT)
-              acc[t] = __builtin_fmaf(sc[i], qdot32<WT>(raw[i], xs + (size_t)t * H + 32 * c, xsum[t * nb + c]), acc[t]);
-            else
-              acc[t] = ddot<WT>(raw[i], xs + (size_t)t * H + (size_t)c * KC, acc[t]);
+          for (int t = 0; t < MAXB; t++)
+            if (t < B && (mask >> t & 1u))
+              acc[t] = __builtin_fmaf(sc[i], qdot32_p<WT>(p, xs + (size_t)t * H + 32 * c, xsum[t * nb + c]), acc[t]);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int t = 0; t < MAXB; t++) {
+        if (t < B && (mask >> t & 1u)) {
+#pragma unroll
+          for (int i = 0; i < B_CPT; i++) {
+            const int c = c0 + kp + 16 * i;
+            if (c < nc) acc[t] = ddot<WT>(raw[i], xs + (size_t)t * H + (size_t)c * KC, acc[t]);
           }
         }
       }
@@ -543,10 +587,14 @@ __global__ __launch_bounds__(DB_THREADS) void k_dec_b(LayerDev L, const uint16_t
     for (int i = 0; i < B_RPT; i++) {
       const int rw = r0 + threadIdx.x + DB_THREADS * i;
       if (rw < H) {
+        uint32_t p[8];
+        if constexpr (QT) down_piece_unpack<WT, 16>(dp[i], q & 1, p);  // once for all tokens
 #pragma unroll
         for (int t = 0; t < MAXB; t++) {
           if (slot[t] >= 0) {
-            const float v = down_piece_dot<WT, 16>(dp[i], q & 1, s_hp + 8 * t, s_hs[t]);
+            float v;
+            if constexpr (QT) v = down_piece_dot_p<WT, 16>(dp[i], p, s_hp + 8 * t, s_hs[t]);
+            else v = down_piece_dot<WT, 16>(dp[i], q & 1, s_hp + 8 * t, s_hs[t]);
             ws.part[((size_t)slot[t] * gpe + q) * H + rw] = gt[t] * v;
           }
         }
