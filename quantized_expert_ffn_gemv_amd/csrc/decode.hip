@@ -10,10 +10,11 @@
 //   R  k_dec_route : one workgroup: ordered top-k and renormalised gates of
 //                    every token, the batch's unique-expert list and, per
 //                    unique expert, the mask of the tokens that chose it.
-//   B  k_dec_b     : per (unique expert, 16 intermediate columns): fused
-//                    dequantise-GEMV of the 32 gate/up rows for the tokens
+//   B  k_dec_b     : per (unique expert, G intermediate columns; G = 32 for
+//                    quantised weights, 16 for dense): fused
+//                    dequantise-GEMV of the 2G gate/up rows for the tokens
 //                    in the expert's mask, SwiGLU, and the gated partial down
-//                    product over those 16 columns. The down weights are
+//                    product over those G columns. The down weights are
 //                    loaded together with the gate/up weights, so the down
 //                    projection adds no memory round trip.
 //   C  k_dec_c     : y = sum of the partial products, in a fixed order.
@@ -172,7 +173,7 @@ constexpr int A_RPT = 4;  // shared down rows per thread and batch
 
 template <int SWT, int MAXB>
 __global__ __launch_bounds__(DA_THREADS) void k_dec_a(LayerDev L, const uint16_t* __restrict__ x, int B, DecodeWs ws,
-                                                      int nRB) {
+                                                      int nRB, int rg) {
   extern __shared__ __align__(16) uint8_t smem[];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int H = L.H, E = L.E, I = L.I;
@@ -292,7 +293,7 @@ __global__ __launch_bounds__(DA_THREADS) void k_dec_a(LayerDev L, const uint16_t
     s_hs[threadIdx.x] = (bf16_to_f32(hh[0]) + bf16_to_f32(hh[1])) + (bf16_to_f32(hh[2]) + bf16_to_f32(hh[3]));
   }
   __syncthreads();
-  const size_t pbase = (size_t)B * L.k * (I >> 4);  // shared partials follow the routed ones
+  const size_t pbase = (size_t)B * L.k * rg;  // shared partials follow the routed ones (rg groups per slot)
   for (int r0 = 0; r0 < H; r0 += DA_THREADS * A_RPT) {
     if (r0 > 0) {
 #pragma unroll
@@ -409,23 +410,37 @@ __global__ __launch_bounds__(DB_THREADS) void k_dec_route(int E, int k, int B, D
 constexpr int B_CPT = 4;  // gate/up chunks per lane and batch
 constexpr int B_RPT = 4;  // down rows per thread and batch
 
-template <int WT, int MAXB>
+// Kernel B: one workgroup per (unique expert u, group q of GCOL intermediate
+// columns). Quantised weights take GCOL = 32 (or 64): the workgroup streams
+// the 2 GCOL gate/up rows and whole chunks of each down row, so a call has
+// half (a quarter) of the workgroups and of the partial products that
+// 16-column groups give; dense weights take GCOL = 16 (a wider dense down row
+// would not fit the registers).
+//   gate/up: wave w owns rows GCOL/4 w .. (+GCOL/4) of the group, 64/(GCOL/4)
+//   lanes per row split the K chunks; two batches of chunk loads in flight.
+//   down: rows tid + 512 i, i < B_RPT, per pass over H.
+template <int WT, int MAXB, int GCOL>
 __global__ __launch_bounds__(DB_THREADS) void k_dec_b(LayerDev L, const uint16_t* __restrict__ x, int B, DecodeWs ws) {
+  static_assert(GCOL == 16 || ((GCOL == 32 || GCOL == 64) && is_q<WT>()), "whole-chunk groups for quantised weights only");
+  constexpr bool WHOLE = GCOL >= 32;  // down rows as whole chunks (GCOL / 32 per row)
+  constexpr int DCH = WHOLE ? GCOL / 32 : 1;
   const int H = L.H, I = L.I, k = L.k;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  constexpr int RPW = GCOL / 4;  // gate/up rows per wave
+  constexpr int LPR = 64 / RPW;  // lanes (K parts) per row
+  constexpr int NHS = GCOL >= 32 ? GCOL / 32 : 1;  // h block sums per token
   __shared__ int s_idx[MAXB * 16];
   __shared__ float s_gate[MAXB * 16];
   __shared__ int s_uniq[MAXB * 16];
   __shared__ uint32_t s_mask[MAXB * 16];
   __shared__ int s_nu;
-  __shared__ float s_gu[MAXB * 32];
-  __shared__ uint32_t s_hp[MAXB * 8];
-  __shared__ float s_hs[MAXB];
+  __shared__ float s_gu[MAXB * 2 * GCOL];
+  __shared__ __align__(16) uint32_t s_hp[MAXB * GCOL / 2];  // h of token t: bf16 pairs at s_hp + GCOL/2 t
+  __shared__ float s_hs[MAXB * NHS];
   extern __shared__ __align__(16) uint8_t smem[];
   constexpr bool QT = is_q<WT>();
   uint16_t* xs = reinterpret_cast<uint16_t*>(smem);
   float* xsum = reinterpret_cast<float*>(smem + (size_t)B * H * 2);
-  (void)lane;
 
   // 1. the batch's routing (from the routing kernel)
   const int32_t* rt = ws.route;
@@ -439,74 +454,98 @@ __global__ __launch_bounds__(DB_THREADS) void k_dec_b(LayerDev L, const uint16_t
   if (threadIdx.x == 0) s_nu = rt[0];
   __syncthreads();
   const int nu = s_nu;
-  const int gpe = I >> 4;  // 16-column groups per expert
+  const int gpe = I / GCOL;  // column groups per expert
   const int u = blockIdx.x / gpe;
   if (u >= nu) return;  // uniform
   const int q = blockIdx.x - u * gpe;
   const int e = s_uniq[u];
   const uint32_t mask = s_mask[u];
 
-  // 2. loads: 32 gate/up rows (wave w: rows 4w..4w+3 of group q; lane -> row 4w + lane/16,
-  //    kpart lane%16) and the 16-column down piece of rows tid + 512 i; every load of the
-  //    first batch is issued before any wait (unconditional, clamped indices)
+  // 2. loads: the group's gate/up rows and its down pieces; every load of the
+  //    first batches is issued before any wait (unconditional, clamped indices)
   constexpr int KC = kchunk<WT>();
   const int R = 2 * I;
-  const int rr = 4 * wave + (lane >> 4);
-  const int row = 32 * q + rr;
-  const int kp = lane & 15;
+  const int rr = RPW * wave + lane / LPR;
+  const int row = 2 * GCOL * q + rr;
+  const int kp = lane % LPR;
   const int nc = H / KC;
   const uint8_t* wgu = L.gu + (size_t)e * L.gu_stride;
   const uint16_t* wgs = QT ? L.gu_s + (size_t)e * L.gu_s_stride : nullptr;
   const uint8_t* wdn = L.dn + (size_t)e * L.dn_stride;
   const uint16_t* wds = QT ? L.dn_s + (size_t)e * L.dn_s_stride : nullptr;
-  const int col0 = 16 * q;
-  DownPiece<WT, 16> dp[B_RPT];
+  const int col0 = GCOL * q;
+  // down pieces of the first pass: GCOL = 16 a half chunk per row (DownPiece),
+  // GCOL = 64 two chunks per row with their scales (raw fp16 bits)
+  constexpr int RPT = DCH == 2 ? 2 : B_RPT;   // down rows per thread and pass
+  constexpr int CPT = WHOLE ? 2 : B_CPT;      // gate/up chunks per lane and batch (two batches in flight)
+  DownPiece<WT, 16> dp[WHOLE ? 1 : B_RPT];
+  Raw dr[WHOLE ? RPT : 1][DCH];
+  uint16_t dsb[WHOLE ? RPT : 1][DCH];
+  auto load_down = [&](int r0) {  // rows past H are not used
+    if constexpr (!WHOLE) {
 #pragma unroll
-  for (int i = 0; i < B_RPT; i++)  // rows past H are not used
-    load_down_piece<WT, 16>(wdn, wds, H, min((int)threadIdx.x + DB_THREADS * i, H - 1), col0, dp[i]);
+      for (int i = 0; i < B_RPT; i++)
+        load_down_piece<WT, 16>(wdn, wds, H, min(r0 + (int)threadIdx.x + DB_THREADS * i, H - 1), col0, dp[i]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < RPT; i++) {
+        const int rw = min(r0 + (int)threadIdx.x + DB_THREADS * i, H - 1);
+#pragma unroll
+        for (int h = 0; h < DCH; h++) {
+          dr[i][h] = load_chunk<WT>(wdn, (size_t)(col0 / 32 + h) * H + rw);
+          dsb[i][h] = wds[(size_t)(col0 / 32 + h) * H + rw];
+        }
+      }
+    }
+  };
   const int nb = H >> 5;
   float acc[MAXB];
 #pragma unroll
   for (int t = 0; t < MAXB; t++) acc[t] = 0.0f;
-  Raw raw[B_CPT];
-  float sc[B_CPT];
-  auto load_batch = [&](int c0) {  // chunks past the row are not used
+  Raw raw[2][CPT];
+  uint16_t sc[2][CPT];
+  auto load_batch = [&](int c0, Raw (&rw)[CPT], uint16_t (&sw)[CPT]) {  // chunks past the row are not used
 #pragma unroll
-    for (int i = 0; i < B_CPT; i++) raw[i] = load_chunk<WT>(wgu, (size_t)min(c0 + kp + 16 * i, nc - 1) * R + row);
+    for (int i = 0; i < CPT; i++) rw[i] = load_chunk<WT>(wgu, (size_t)min(c0 + kp + LPR * i, nc - 1) * R + row);
     if constexpr (QT) {
 #pragma unroll
-      for (int i = 0; i < B_CPT; i++) sc[i] = f16_to_f32(wgs[(size_t)min(c0 + kp + 16 * i, nc - 1) * R + row]);
+      for (int i = 0; i < CPT; i++) sw[i] = wgs[(size_t)min(c0 + kp + LPR * i, nc - 1) * R + row];
     }
   };
-  auto compute_batch = [&](int c0) {
+  auto compute_batch = [&](int c0, const Raw (&rw)[CPT], const uint16_t (&sw)[CPT]) {
     if constexpr (QT) {
       // each chunk unpacked once, then dotted with every token of the expert
 #pragma unroll
-      for (int i = 0; i < B_CPT; i++) {
-        const int c = c0 + kp + 16 * i;
+      for (int i = 0; i < CPT; i++) {
+        const int c = c0 + kp + LPR * i;
         if (c < nc) {
           uint32_t p[16];
-          qunpack32<WT>(raw[i], p);
+          qunpack32<WT>(rw[i], p);
+          const float scl = f16_to_f32(sw[i]);
 #pragma unroll
           for (int t = 0; t < MAXB; t++)
             if (t < B && (mask >> t & 1u))
-              acc[t] = __builtin_fmaf(sc[i], qdot32_p<WT>(p, xs + (size_t)t * H + 32 * c, xsum[t * nb + c]), acc[t]);
+              acc[t] = __builtin_fmaf(scl, qdot32_p<WT>(p, xs + (size_t)t * H + 32 * c, xsum[t * nb + c]), acc[t]);
         }
       }
     } else {
+      (void)sw;
 #pragma unroll
       for (int t = 0; t < MAXB; t++) {
         if (t < B && (mask >> t & 1u)) {
 #pragma unroll
-          for (int i = 0; i < B_CPT; i++) {
-            const int c = c0 + kp + 16 * i;
-            if (c < nc) acc[t] = ddot<WT>(raw[i], xs + (size_t)t * H + (size_t)c * KC, acc[t]);
+          for (int i = 0; i < CPT; i++) {
+            const int c = c0 + kp + LPR * i;
+            if (c < nc) acc[t] = ddot<WT>(rw[i], xs + (size_t)t * H + (size_t)c * KC, acc[t]);
           }
         }
       }
     }
   };
-  load_batch(0);
+  constexpr int CPB = LPR * CPT;  // chunks per batch of the workgroup's rows
+  load_batch(0, raw[0], sc[0]);
+  if constexpr (!WHOLE) load_down(0);  // whole chunks: after the gate/up rows (registers)
+  if (CPB < nc) load_batch(CPB, raw[1], sc[1]);
   // the activations of this expert's tokens only (a token's row at xs + t H),
   // with their 32-element block sums, while the weights are in flight
   {
@@ -535,31 +574,60 @@ __global__ __launch_bounds__(DB_THREADS) void k_dec_b(LayerDev L, const uint16_t
     }
     __syncthreads();
   }
-  compute_batch(0);
-  for (int c0 = 16 * B_CPT; c0 < nc; c0 += 16 * B_CPT) {
-    load_batch(c0);
-    compute_batch(c0);
+  // batches two at a time: batch n + 2 is issued before batch n + 1 is computed
+  for (int c0 = 0; c0 < nc; c0 += 2 * CPB) {
+    compute_batch(c0, raw[0], sc[0]);
+    if (c0 + 2 * CPB < nc) load_batch(c0 + 2 * CPB, raw[0], sc[0]);
+    if (c0 + CPB < nc) {
+      compute_batch(c0 + CPB, raw[1], sc[1]);
+      if (c0 + 3 * CPB < nc) load_batch(c0 + 3 * CPB, raw[1], sc[1]);
+    }
   }
+  if constexpr (WHOLE) load_down(0);  // in flight through the SwiGLU below
+  // fold the LPR lanes of each row (fixed order)
 #pragma unroll
   for (int t = 0; t < MAXB; t++) {
     if (t < B && (mask >> t & 1u)) {
-      const float v = sum16_f32(acc[t]);
-      if (kp == 0) s_gu[t * 32 + rr] = v;
+      float v = acc[t];
+      static_assert(LPR == 16 || LPR == 8 || LPR == 4, "lanes per row");
+      if constexpr (LPR == 16) {
+        v = sum16_f32(v);
+      } else if constexpr (LPR == 8) {
+        v = sum8_f32(v);
+      } else {
+        v += dpp_f32<DPP_XOR1>(v);
+        v += dpp_f32<DPP_XOR2>(v);
+      }
+      if (kp == 0) s_gu[t * 2 * GCOL + rr] = v;
     }
   }
   __syncthreads();
-  // 3. SwiGLU (bf16 h) and the sum of the 16 bf16 h values; thread = 16 t + j
+  // 3. SwiGLU (bf16 h) and the block sums of h; intermediate j of the group:
+  //    gate row 32 (j / 16) + j % 16, up row + 16
+  for (int i = threadIdx.x; i < MAXB * GCOL; i += DB_THREADS) {
+    const int t = i / GCOL, j = i % GCOL;
+    if (t < B && (mask >> t & 1u)) {
+      const int gr = 32 * (j >> 4) + (j & 15);
+      reinterpret_cast<uint16_t*>(s_hp)[t * GCOL + j] =
+          f32_to_bf16(silu_f32(s_gu[t * 2 * GCOL + gr]) * s_gu[t * 2 * GCOL + gr + 16]);
+    }
+  }
+  __syncthreads();
   {
-    const int t = threadIdx.x >> 4, j = threadIdx.x & 15;
-    const bool act = t < B && (mask >> t & 1u);
+    // sums of 16 (GCOL = 16) or 32 (GCOL = 64) consecutive bf16 h values: one
+    // group of 16 lanes per sum, fixed order
+    constexpr int HG = GCOL >= 32 ? 32 : 16;
+    const int g = threadIdx.x >> 4, j = threadIdx.x & 15;
+    const int t = g / NHS, hb = g % NHS;
     float hv = 0.0f;
+    const bool act = g < MAXB * NHS && t < B && (mask >> t & 1u);
     if (act) {
-      const uint16_t hb = f32_to_bf16(silu_f32(s_gu[t * 32 + j]) * s_gu[t * 32 + 16 + j]);
-      reinterpret_cast<uint16_t*>(s_hp)[t * 16 + j] = hb;
-      hv = bf16_to_f32(hb);
+      const uint16_t* hh = reinterpret_cast<const uint16_t*>(s_hp) + t * GCOL + HG * hb;
+      hv = bf16_to_f32(hh[j]);
+      if constexpr (HG == 32) hv += bf16_to_f32(hh[j + 16]);
     }
     hv = sum16_f32(hv);
-    if (act && j == 0) s_hs[t] = hv;
+    if (act && j == 0) s_hs[t * NHS + hb] = hv;
   }
   __syncthreads();
   // 4. gated partial down products of this expert's tokens
@@ -577,25 +645,43 @@ __global__ __launch_bounds__(DB_THREADS) void k_dec_b(LayerDev L, const uint16_t
         }
     }
   }
-  for (int r0 = 0; r0 < H; r0 += DB_THREADS * B_RPT) {
-    if (r0 > 0) {
+  for (int r0 = 0; r0 < H; r0 += DB_THREADS * RPT) {
+    if (r0 > 0) load_down(r0);
 #pragma unroll
-      for (int i = 0; i < B_RPT; i++)
-        load_down_piece<WT, 16>(wdn, wds, H, min(r0 + (int)threadIdx.x + DB_THREADS * i, H - 1), col0, dp[i]);
-    }
-#pragma unroll
-    for (int i = 0; i < B_RPT; i++) {
+    for (int i = 0; i < RPT; i++) {
       const int rw = r0 + threadIdx.x + DB_THREADS * i;
       if (rw < H) {
-        uint32_t p[8];
-        if constexpr (QT) down_piece_unpack<WT, 16>(dp[i], q & 1, p);  // once for all tokens
+        if constexpr (WHOLE) {
+          uint32_t pc[DCH][16];  // the row's chunks unpacked once for all tokens
+          float sd[DCH];
 #pragma unroll
-        for (int t = 0; t < MAXB; t++) {
-          if (slot[t] >= 0) {
-            float v;
-            if constexpr (QT) v = down_piece_dot_p<WT, 16>(dp[i], p, s_hp + 8 * t, s_hs[t]);
-            else v = down_piece_dot<WT, 16>(dp[i], q & 1, s_hp + 8 * t, s_hs[t]);
-            ws.part[((size_t)slot[t] * gpe + q) * H + rw] = gt[t] * v;
+          for (int h = 0; h < DCH; h++) {
+            qunpack32<WT>(dr[i][h], pc[h]);
+            sd[h] = f16_to_f32(dsb[i][h]);
+          }
+#pragma unroll
+          for (int t = 0; t < MAXB; t++) {
+            if (slot[t] >= 0) {
+              const uint16_t* ht = reinterpret_cast<const uint16_t*>(s_hp) + t * GCOL;
+              float v = sd[0] * qdot32_p<WT>(pc[0], ht, s_hs[t * NHS]);
+              if constexpr (DCH == 2) v += sd[1] * qdot32_p<WT>(pc[1], ht + 32, s_hs[t * NHS + 1]);
+              ws.part[((size_t)slot[t] * gpe + q) * H + rw] = gt[t] * v;
+            }
+            // one token's h (32 registers) at a time: hoisting the reads of
+            // every token would not fit the registers
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        } else {
+          uint32_t p[8];
+          if constexpr (QT) down_piece_unpack<WT, 16>(dp[i], q & 1, p);  // once for all tokens
+#pragma unroll
+          for (int t = 0; t < MAXB; t++) {
+            if (slot[t] >= 0) {
+              float v;
+              if constexpr (QT) v = down_piece_dot_p<WT, 16>(dp[i], p, s_hp + 8 * t, s_hs[t]);
+              else v = down_piece_dot<WT, 16>(dp[i], q & 1, s_hp + 8 * t, s_hs[t]);
+              ws.part[((size_t)slot[t] * gpe + q) * H + rw] = gt[t] * v;
+            }
           }
         }
       }
@@ -605,17 +691,17 @@ __global__ __launch_bounds__(DB_THREADS) void k_dec_b(LayerDev L, const uint16_t
 
 // ---------------------------------------------------------------------------
 // Kernel C: y[t][r] = sum over token t's partials (routed slots in order,
-// 16-column groups in order, then the shared expert's 4-column groups)
+// their column groups in order, then the shared expert's 4-column groups)
 // ---------------------------------------------------------------------------
 constexpr int DC_BATCH = 24;  // partial loads in flight per thread
 
 __global__ __launch_bounds__(DC_THREADS) void k_dec_c(const float* __restrict__ part, int H, int k, int I, int B,
-                                                      uint16_t* __restrict__ y, int has_shared) {
+                                                      uint16_t* __restrict__ y, int has_shared, int rg) {
   __shared__ float red[DC_SPLIT][DC_ROWS];
   const int t = blockIdx.y;
   const int rr = threadIdx.x % DC_ROWS, sp = threadIdx.x / DC_ROWS;
   const int r = blockIdx.x * DC_ROWS + rr;
-  const int nr = k * (I >> 4);  // routed partials of this token, then its shared-expert partials
+  const int nr = k * rg;  // routed partials of this token (rg column groups per slot), then its shared-expert partials
   const int ns = has_shared ? (I >> 2) : 0;
   const size_t rbase = (size_t)t * nr;
   const size_t sbase = (size_t)B * nr + (size_t)t * ns;
@@ -660,11 +746,18 @@ static hipError_t launch_t(const LayerDev& L, const uint16_t* x, int B, uint16_t
                            const DecodeWs& ws, hipStream_t st) {
   const int H = L.H, I = L.I, E = L.E, k = L.k;
   constexpr int SW = (SWT == MOE_W_F32) ? MOE_W_F32 : MOE_W_BF16;
+  // kernel B's intermediate columns per workgroup (and per routed partial):
+  // one whole chunk per down row for quantised weights (measured at B = 4 and
+  // 8 on the Zipf-routed Q3 layer: 32 columns beat 16 and 64; 64 makes the
+  // workgroups of an expert chosen by every token of the batch the long pole)
+  constexpr int gcol = is_q<WT>() ? 32 : 16;
+  const int rg = I / gcol;
   {
     const int nRB = (E + 7) / 8;
     const int nSB = (SWT == MOE_W_NONE) ? 0 : I / 4;
     const size_t lds = (size_t)B * H * 2 + (size_t)(8 * MAXB * 8 + MAXB * 2 + MAXB) * 4;
-    (void)launch_k(KC_DEC_ROUTER_SHARED, (k_dec_a<SW, MAXB>), dim3(nRB + nSB), dim3(DA_THREADS), lds, st, L, x, B, ws, nRB);
+    (void)launch_k(KC_DEC_ROUTER_SHARED, (k_dec_a<SW, MAXB>), dim3(nRB + nSB), dim3(DA_THREADS), lds, st, L, x, B, ws, nRB,
+                   rg);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
@@ -678,12 +771,12 @@ static hipError_t launch_t(const LayerDev& L, const uint16_t* x, int B, uint16_t
   {
     const int maxU = (B * k < E) ? B * k : E;
     const size_t lds = decode_lds_b(WT, B, H, E, k);
-    (void)launch_k(KC_DEC_GATE_UP, (k_dec_b<WT, MAXB>), dim3(maxU * (I / 16)), dim3(DB_THREADS), lds, st, L, x, B, ws);
+    (void)launch_k(KC_DEC_GATE_UP, (k_dec_b<WT, MAXB, gcol>), dim3(maxU * rg), dim3(DB_THREADS), lds, st, L, x, B, ws);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
   (void)launch_k(KC_DEC_DOWN, k_dec_c, dim3((H + DC_ROWS - 1) / DC_ROWS, B), dim3(DC_THREADS), 0, st, ws.part, H, k, I, B, y,
-                     SWT == MOE_W_NONE ? 0 : 1);
+                 SWT == MOE_W_NONE ? 0 : 1, rg);
   return hipGetLastError();
 }
 
