@@ -199,6 +199,22 @@ moe_status moe_forward_prefill(const moe_layer *layer, const void *x, int32_t T,
 moe_status moe_rmsnorm(const void *h, void *z, int32_t T, int32_t H, float eps, hipStream_t stream);
 moe_status moe_residual_add(void *h, const void *y, int32_t T, int32_t H, hipStream_t stream);
 
+/* One decode step of a stacked layer (the pages give no layer formula; the
+ * stack's form is the plain pre-norm residual one), in place on the
+ * residual stream h (bf16 [B][H], B in 1..MOE_DECODE_MAX_TOKENS): z = RMSNorm(h) as
+ * moe_rmsnorm computes it, y = moe_forward_decode(z), h = bf16(h + y) as
+ * moe_residual_add computes it. At batch 1, when the one-kernel decode path
+ * takes the shape, all three run in that one kernel (every workgroup that
+ * reads the token normalises it itself; the reducers add the residual);
+ * otherwise as the three calls in turn. z_out, y_out ([B][H] bf16) receive
+ * z and y when not NULL; topk_idx/topk_gate as in moe_forward_decode.
+ * Workspace: moe_workspace_bytes(layer, B, 0), as for moe_forward_decode
+ * (the two may share one). Errors as moe_forward_decode, and MOE_ERR_SHAPE
+ * for eps < 0. */
+moe_status moe_stack_decode_layer(const moe_layer *layer, void *h, int32_t B, float eps, void *z_out, void *y_out,
+                                  int32_t *topk_idx, float *topk_gate, void *ws, size_t ws_bytes,
+                                  hipStream_t stream);
+
 /* ------------------------------------------------------------------------ */
 /* Host-side packing (no device work; host pointers)                        */
 /* ------------------------------------------------------------------------ */

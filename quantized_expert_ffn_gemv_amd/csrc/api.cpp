@@ -114,6 +114,9 @@ size_t carve_decode(const moe_layer* L, int B, uint8_t* base, moe::DecodeWs* ws)
     w.part = reinterpret_cast<float*>(take((size_t)B * (k * (I / 16) + I / 4) * L->hidden * 4));
     w.route = reinterpret_cast<int32_t*>(take((4 + 4 * 8 * 16) * 4));
   }
+  // z and y of a stack layer run as separate kernels (moe_stack_decode_layer)
+  w.zb = reinterpret_cast<uint16_t*>(take((size_t)B * L->hidden * 2));
+  w.yb = reinterpret_cast<uint16_t*>(take((size_t)B * L->hidden * 2));
   if (ws) *ws = w;
   return off;
 }
@@ -291,6 +294,32 @@ moe_status moe_forward_decode(const moe_layer* layer, const void* x, int32_t B, 
   return hip_status(moe::launch_decode(to_dev(layer), static_cast<const uint16_t*>(x), B, static_cast<uint16_t*>(y),
                                        topk_idx, topk_gate, w, stream),
                     "moe_forward_decode launch");
+}
+
+moe_status moe_stack_decode_layer(const moe_layer* layer, void* h, int32_t B, float eps, void* z_out, void* y_out,
+                                  int32_t* topk_idx, float* topk_gate, void* ws, size_t ws_bytes, hipStream_t stream) {
+  moe_status st = check_layer(layer);
+  if (st != MOE_OK) return st;
+  if (!h || !ws) return fail(MOE_ERR_NULL, "h and ws are required");
+  if (B < 1 || B > MOE_DECODE_MAX_TOKENS) return fail(MOE_ERR_SHAPE, "B=%d not in [1, %d]", B, MOE_DECODE_MAX_TOKENS);
+  if ((int64_t)B * layer->hidden > 8 * 2048)
+    return fail(MOE_ERR_SHAPE, "B*H=%d exceeds the decode staging limit %d", B * layer->hidden, 8 * 2048);
+  if (!(eps >= 0.0f)) return fail(MOE_ERR_SHAPE, "eps must be >= 0");
+  const bool one_kernel =
+      B == 1 && moe::decode1_fits(layer->n_experts, layer->hidden, layer->inter, layer->top_k, layer->shared_wtype != MOE_W_NONE);
+  if (!one_kernel && moe::decode_lds_b(layer->expert_wtype, B, layer->hidden, layer->n_experts, layer->top_k) > 65536)
+    return fail(MOE_ERR_SHAPE, "B=%d with H=%d, E=%d, k=%d needs more than 64 KiB of LDS", B, layer->hidden,
+                layer->n_experts, layer->top_k);
+  if (!aligned16(h) || !aligned16(ws) || (z_out && !aligned16(z_out)) || (y_out && !aligned16(y_out)))
+    return fail(MOE_ERR_ALIGN, "h, ws, z_out and y_out must be 16-byte aligned");
+  const size_t need = carve_decode(layer, B, nullptr, nullptr);
+  if (ws_bytes < need) return fail(MOE_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+  moe::DecodeWs w;
+  carve_decode(layer, B, static_cast<uint8_t*>(ws), &w);
+  return hip_status(moe::launch_stack_decode(to_dev(layer), static_cast<uint16_t*>(h), B, eps,
+                                             static_cast<uint16_t*>(z_out), static_cast<uint16_t*>(y_out), topk_idx,
+                                             topk_gate, w, stream),
+                    "moe_stack_decode_layer launch");
 }
 
 moe_status moe_forward_prefill(const moe_layer* layer, const void* x, int32_t T, void* y, int32_t* topk_idx,

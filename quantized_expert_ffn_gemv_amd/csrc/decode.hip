@@ -797,6 +797,25 @@ static hipError_t launch_s(const LayerDev& L, const uint16_t* x, int B, uint16_t
   }
 }
 
+// One stack layer at decode: the one-kernel path with the norm and the
+// residual inside when batch 1 fits there, else RMSNorm, the decode kernels
+// and the residual add in turn (z and y in the caller's buffers or the
+// workspace's).
+hipError_t launch_stack_decode(const LayerDev& L, uint16_t* h, int B, float eps, uint16_t* z_out, uint16_t* y_out,
+                               int32_t* idx_out, float* gate_out, const DecodeWs& ws, hipStream_t st) {
+  if (B == 1 && decode1_fits(L.E, L.H, L.I, L.k, L.swt != MOE_W_NONE)) {
+    const StackIo S{h, z_out, y_out, eps};
+    return launch_decode_fused(L, nullptr, nullptr, idx_out, gate_out, ws, st, &S);
+  }
+  uint16_t* z = z_out ? z_out : ws.zb;
+  uint16_t* y = y_out ? y_out : ws.yb;
+  hipError_t e = launch_rmsnorm(h, z, B, L.H, eps, st);
+  if (e != hipSuccess) return e;
+  e = launch_decode(L, z, B, y, idx_out, gate_out, ws, st);
+  if (e != hipSuccess) return e;
+  return launch_residual(h, y, B, L.H, st);
+}
+
 hipError_t launch_decode(const LayerDev& L, const uint16_t* x, int B, uint16_t* y, int32_t* idx_out, float* gate_out,
                          const DecodeWs& ws, hipStream_t st) {
   if (B == 1 && decode1_fits(L.E, L.H, L.I, L.k, L.swt != MOE_W_NONE))

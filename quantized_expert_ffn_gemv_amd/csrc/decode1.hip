@@ -196,6 +196,36 @@ __device__ __forceinline__ void finish(uint32_t* sync) {
   }
 }
 
+// Stack layers: z = RMSNorm(h) computed by every workgroup that reads the
+// token, with the sum order of the library's RMSNorm kernel (threads
+// 0..255 square and add 8 consecutive values each, each wave sums its lanes,
+// then the four wave totals in order), so every workgroup and the separate
+// kernel produce the same z. hv: the thread's 8 values of h (threads
+// < H / 8; H <= F_HMAX = 256 x 8). Returns 1 / sqrt(mean(h^2) + eps) to every
+// thread.
+__device__ __forceinline__ float stack_inv(uint4 hv, int H, float eps, float* s_n) {
+  float ss = 0.0f;
+  if ((int)threadIdx.x * 8 < H) {
+    const uint32_t vv[4] = {hv.x, hv.y, hv.z, hv.w};
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      const float a = bf16_lo(vv[i]), b = bf16_hi(vv[i]);
+      ss = __builtin_fmaf(a, a, ss);
+      ss = __builtin_fmaf(b, b, ss);
+    }
+  }
+  if (threadIdx.x < 256) {
+    ss = group_sum_f32(ss, 64);
+    if ((threadIdx.x & 63) == 0) s_n[threadIdx.x >> 6] = ss;
+  }
+  __syncthreads();
+  const float tot = s_n[0] + s_n[1] + s_n[2] + s_n[3];
+  return 1.0f / sqrtf(tot / (float)H + eps);
+}
+__device__ __forceinline__ uint32_t scale_pair(uint32_t v, float inv) {
+  return pack_bf16x2(bf16_lo(v) * inv, bf16_hi(v) * inv);
+}
+
 // ---------------------------------------------------------------------------
 // Router: waves w and w + 8 of workgroup b compute the two halves of the
 // logit of expert 8b + w (summed in that order). The
@@ -205,7 +235,7 @@ __device__ __forceinline__ void finish(uint32_t* sync) {
 // once serve them one after another).
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ void role_router(const LayerDev& L, const uint16_t* __restrict__ x, uint64_t* logits, int b,
-                                            double* s_rt, uint32_t tag) {
+                                            double* s_rt, uint32_t tag, bool stk, float eps, float* s_n) {
   static_assert(F_WAVES == 16, "two waves per router row");
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int e = b * 8 + (wave & 7), hh = wave >> 3;
@@ -229,6 +259,15 @@ __device__ __forceinline__ void role_router(const LayerDev& L, const uint16_t* _
       const int c = min(c0 + lane + 64 * i, c_hi - 1);
       w[i] = wr[c];
       xx[i] = xv[c];
+    }
+    if (stk) {
+      // stack layer: x is h, the activations are z = RMSNorm(h). Half a row
+      // is one pass on this path (H <= F_HMAX), so the norm's loads go out
+      // with the weights' and cost no round trip of their own.
+      const uint4 hv = reinterpret_cast<const uint4*>(x)[min((int)threadIdx.x, (L.H >> 3) - 1)];
+      const float inv = stack_inv(hv, L.H, eps, s_n);
+#pragma unroll
+      for (int i = 0; i < F_RCPL; i++) xx[i] = make_uint2(scale_pair(xx[i].x, inv), scale_pair(xx[i].y, inv));
     }
 #pragma unroll
     for (int i = 0; i < F_RCPL; i++) {
@@ -388,6 +427,25 @@ __device__ __forceinline__ void stage_x(const uint16_t* __restrict__ x, int H, u
       float s = ((bf16_lo(v.x) + bf16_hi(v.x)) + (bf16_lo(v.y) + bf16_hi(v.y))) +
                 ((bf16_lo(v.z) + bf16_hi(v.z)) + (bf16_lo(v.w) + bf16_hi(v.w)));
       s += dpp_f32<DPP_XOR1>(s);  // chunks 4b..4b+3 are lanes 4b'..4b'+3 of one quad
+      s += dpp_f32<DPP_XOR2>(s);
+      if ((i & 3) == 0) xsum[i >> 2] = s;
+    }
+  }
+}
+
+// z = RMSNorm(h) -> LDS (bf16) and, for quantised weights, its 32-element
+// block sums (the stack-layer counterpart of stage_x).
+__device__ __forceinline__ void stage_z(const uint16_t* h, int H, float eps, uint16_t* xs, float* xsum, float* s_n) {
+  const int n8 = H >> 3, i = threadIdx.x;
+  const uint4 hv = reinterpret_cast<const uint4*>(h)[min(i, n8 - 1)];  // clamped, unconditional
+  const float inv = stack_inv(hv, H, eps, s_n);
+  if (i < n8) {
+    const uint4 v = make_uint4(scale_pair(hv.x, inv), scale_pair(hv.y, inv), scale_pair(hv.z, inv), scale_pair(hv.w, inv));
+    reinterpret_cast<uint4*>(xs)[i] = v;
+    if (xsum) {
+      float s = ((bf16_lo(v.x) + bf16_hi(v.x)) + (bf16_lo(v.y) + bf16_hi(v.y))) +
+                ((bf16_lo(v.z) + bf16_hi(v.z)) + (bf16_lo(v.w) + bf16_hi(v.w)));
+      s += dpp_f32<DPP_XOR1>(s);
       s += dpp_f32<DPP_XOR2>(s);
       if ((i & 3) == 0) xsum[i >> 2] = s;
     }
@@ -614,7 +672,7 @@ constexpr int F_RD = 16;                   // output rows per reducer
 constexpr int F_RG = F_THREADS / F_RD;     // producer groups per reducer (64)
 
 __device__ __forceinline__ void role_reduce(const uint64_t* part, int nP, int H, int r0, uint16_t* __restrict__ y,
-                                            float* s_red, uint32_t tag, uint32_t* sync) {
+                                            float* s_red, uint32_t tag, uint32_t* sync, const StackIo& S) {
   const int rr = threadIdx.x % F_RD, pg = threadIdx.x / F_RD;
   const int row = r0 + rr;
   float acc = 0.0f;
@@ -662,7 +720,16 @@ __device__ __forceinline__ void role_reduce(const uint64_t* part, int nP, int H,
     float t = 0.0f;
 #pragma unroll
     for (int w = 0; w < F_WAVES; w++) t += s_red[w * F_RD + rr];
-    y[row] = f32_to_bf16(t);
+    const uint16_t yb = f32_to_bf16(t);
+    if (S.h) {
+      // stack layer: h = bf16(h + y) for this reducer's rows. Every workgroup
+      // that reads h has read it before its output (logits, partials) could
+      // reach a reducer, and the reducers wait for all of them.
+      S.h[row] = f32_to_bf16(bf16_to_f32(S.h[row]) + bf16_to_f32(yb));
+      if (S.y_out) S.y_out[row] = yb;
+    } else {
+      y[row] = yb;
+    }
   }
 }
 
@@ -676,7 +743,7 @@ __device__ __forceinline__ void role_reduce(const uint64_t* part, int nP, int H,
 template <int WT, int SWT>
 __global__ __launch_bounds__(F_THREADS, 4) void k_decode1(LayerDev L, const uint16_t* __restrict__ x,
                                                        uint16_t* __restrict__ y, int32_t* idx_out, float* gate_out,
-                                                       DecodeWs ws, FusedGeo G) {
+                                                       DecodeWs ws, FusedGeo G, StackIo S) {
   __shared__ __align__(16) uint16_t s_x[F_HMAX];
   __shared__ __align__(16) float s_xsum[F_HMAX / 32];
   __shared__ __align__(16) float s_red[F_THREADS];
@@ -686,7 +753,9 @@ __global__ __launch_bounds__(F_THREADS, 4) void k_decode1(LayerDev L, const uint
   __shared__ float s_gate[16];
   __shared__ __align__(16) uint16_t s_h[32];
   __shared__ float s_hsum;
+  __shared__ float s_n[4];
   const int H = L.H, I = L.I;
+  const bool stk = S.h != nullptr;  // stack layer: the token is h, the activations z = RMSNorm(h)
   const int nP = G.nSG + G.nRG;  // partial producers: shared workgroups, then routed
   // this call's tag: the epoch (stable until every workgroup is done) + 1
   const uint32_t tag = ld_u32(ws.sync + SY_EPOCH + SY_LINE * my_rep()) + 1u;
@@ -697,7 +766,7 @@ __global__ __launch_bounds__(F_THREADS, 4) void k_decode1(LayerDev L, const uint
   int b = blockIdx.x;
   if (b < G.nA) {
     if (b < G.nR) {
-      role_router(L, x, tl, b, s_rt, tag);
+      role_router(L, stk ? S.h : x, tl, b, s_rt, tag, stk, S.eps, s_n);
       raise_flag(fl, b, tag);
     }
     if (b < G.nSG) {
@@ -706,7 +775,8 @@ __global__ __launch_bounds__(F_THREADS, 4) void k_decode1(LayerDev L, const uint
       constexpr int SW = (SWT == MOE_W_F32) ? MOE_W_F32 : MOE_W_BF16;
       const uint16_t* xs = s_x;
       const int q = b >> 1, hf = b & 1;
-      stage_x(x, H, s_x, nullptr);  // after the router's loads (x is then in this XCD's L2)
+      if (stk) stage_z(S.h, H, S.eps, s_x, nullptr, s_n);
+      else stage_x(x, H, s_x, nullptr);  // after the router's loads (x is then in this XCD's L2)
       __syncthreads();
       DownPre<SW> pre;
       gate_up_h<SW, 16>(L.sgu, nullptr, H, 2 * I, q, hf, xs, nullptr, s_red, s_h,
@@ -718,8 +788,12 @@ __global__ __launch_bounds__(F_THREADS, 4) void k_decode1(LayerDev L, const uint
     // routed slot u, intermediates 32q .. 32q+31
     uint16_t* xs = s_x;
     float* xsum = s_xsum;
-    stage_x(x, H, xs, is_q<WT>() ? xsum : nullptr);
-    wait_flags(fl, G.nR, flags_needed(G.nR), tag, ws.sync);
+    if (stk) stage_z(S.h, H, S.eps, xs, is_q<WT>() ? xsum : nullptr, s_n);
+    else stage_x(x, H, xs, is_q<WT>() ? xsum : nullptr);
+    wait_flags(fl, G.nR, flags_needed(G.nR), tag, ws.sync);  // (its barrier also publishes xs)
+    if (stk && S.z_out && b == 0)
+      for (int i = threadIdx.x; i < (H >> 3); i += F_THREADS)
+        reinterpret_cast<uint4*>(S.z_out)[i] = reinterpret_cast<const uint4*>(xs)[i];
     block_topk(tl + (size_t)my_rep() * 2 * L.E, L.E, L.k, tag, ws.sync, s_tk);
     const int gpe = I >> 5;
     const int u = b / gpe, q = b - u * gpe;
@@ -757,7 +831,7 @@ __global__ __launch_bounds__(F_THREADS, 4) void k_decode1(LayerDev L, const uint
   const int d = (int)blockIdx.x - ((int)gridDim.x - G.nD);
   if (d >= 0) {
     __syncthreads();  // s_red is reused
-    role_reduce(part, nP, H, d * F_RD, y, s_red, tag, ws.sync);
+    role_reduce(part, nP, H, d * F_RD, y, s_red, tag, ws.sync, S);
   }
   finish(ws.sync);
 }
@@ -815,7 +889,7 @@ bool decode1_fits(int E, int H, int I, int k, bool has_shared) {
 
 template <int WT, int SWT>
 static hipError_t launch_fused_t(const LayerDev& L, const uint16_t* x, uint16_t* y, int32_t* idx_out, float* gate_out,
-                                 const DecodeWs& ws, hipStream_t st) {
+                                 const DecodeWs& ws, hipStream_t st, const StackIo& S) {
   FusedGeo G;
   G.nR = (L.E + 7) / 8;
   G.nSG = (SWT == MOE_W_NONE) ? 0 : L.I / 8;
@@ -825,24 +899,25 @@ static hipError_t launch_fused_t(const LayerDev& L, const uint16_t* x, uint16_t*
   const size_t lds = decode1_lds(L.H, L.I, L.k, SWT != MOE_W_NONE);
   const int grid = decode1_grid(L.E, L.H, L.I, L.k, SWT != MOE_W_NONE);
   return launch_k(KC_DEC_FUSED, k_decode1<WT, SWT>, dim3(grid), dim3(F_THREADS), lds, st, L, x, y, idx_out, gate_out,
-                  ws, G);
+                  ws, G, S);
 }
 
 template <int WT>
 static hipError_t launch_fused_w(const LayerDev& L, const uint16_t* x, uint16_t* y, int32_t* io, float* go,
-                                 const DecodeWs& ws, hipStream_t st) {
-  if (L.swt == MOE_W_NONE) return launch_fused_t<WT, MOE_W_NONE>(L, x, y, io, go, ws, st);
-  if (L.swt == MOE_W_F32) return launch_fused_t<WT, MOE_W_F32>(L, x, y, io, go, ws, st);
-  return launch_fused_t<WT, MOE_W_BF16>(L, x, y, io, go, ws, st);
+                                 const DecodeWs& ws, hipStream_t st, const StackIo& S) {
+  if (L.swt == MOE_W_NONE) return launch_fused_t<WT, MOE_W_NONE>(L, x, y, io, go, ws, st, S);
+  if (L.swt == MOE_W_F32) return launch_fused_t<WT, MOE_W_F32>(L, x, y, io, go, ws, st, S);
+  return launch_fused_t<WT, MOE_W_BF16>(L, x, y, io, go, ws, st, S);
 }
 
 hipError_t launch_decode_fused(const LayerDev& L, const uint16_t* x, uint16_t* y, int32_t* idx_out, float* gate_out,
-                               const DecodeWs& ws, hipStream_t st) {
+                               const DecodeWs& ws, hipStream_t st, const StackIo* stack) {
+  const StackIo S = stack ? *stack : StackIo{nullptr, nullptr, nullptr, 0.0f};
   switch (L.wt) {
-    case MOE_W_Q4: return launch_fused_w<MOE_W_Q4>(L, x, y, idx_out, gate_out, ws, st);
-    case MOE_W_Q3: return launch_fused_w<MOE_W_Q3>(L, x, y, idx_out, gate_out, ws, st);
-    case MOE_W_BF16: return launch_fused_w<MOE_W_BF16>(L, x, y, idx_out, gate_out, ws, st);
-    default: return launch_fused_w<MOE_W_F32>(L, x, y, idx_out, gate_out, ws, st);
+    case MOE_W_Q4: return launch_fused_w<MOE_W_Q4>(L, x, y, idx_out, gate_out, ws, st, S);
+    case MOE_W_Q3: return launch_fused_w<MOE_W_Q3>(L, x, y, idx_out, gate_out, ws, st, S);
+    case MOE_W_BF16: return launch_fused_w<MOE_W_BF16>(L, x, y, idx_out, gate_out, ws, st, S);
+    default: return launch_fused_w<MOE_W_F32>(L, x, y, idx_out, gate_out, ws, st, S);
   }
 }
 

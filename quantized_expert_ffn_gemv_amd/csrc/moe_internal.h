@@ -59,6 +59,8 @@ struct DecodeWs {
   uint64_t* flags; // one-kernel path: per-producer tagged flag words, rotating slots
   uint64_t* part_words;  // one-kernel path: [producers][H] tagged partial down products (fp32 bits)
   int32_t* route;        // three-kernel path: the batch's routing (count, idx, gates, unique experts, masks)
+  uint16_t* zb;          // [B][H] bf16: z of a stack layer taken as separate kernels
+  uint16_t* yb;          // [B][H] bf16: its y
 };
 
 // Prefill workspace.
@@ -89,10 +91,20 @@ size_t decode1_logit_words(int E);  // rotating slots x XCD-group replicas x [E]
 size_t decode1_flag_words(int E, int I, int k, bool has_shared);
 size_t decode1_part_words(int H, int I, int k, bool has_shared);
 bool decode1_fits(int E, int H, int I, int k, bool has_shared);  // shape handled by the one-kernel path
+// One layer of a pre-norm residual stack, in place on the residual stream h:
+// z = RMSNorm(h), y = MoE(z), h = bf16(h + y); z_out / y_out optional copies.
+struct StackIo {
+  uint16_t* h;      // [H] bf16 residual stream (NULL: plain decode, x -> y)
+  uint16_t* z_out;  // [H] or NULL
+  uint16_t* y_out;  // [H] or NULL
+  float eps;
+};
 hipError_t launch_decode_fused(const LayerDev& L, const uint16_t* x, uint16_t* y, int32_t* idx_out,
-                               float* gate_out, const DecodeWs& ws, hipStream_t st);
+                               float* gate_out, const DecodeWs& ws, hipStream_t st, const StackIo* stack = nullptr);
 hipError_t launch_decode(const LayerDev& L, const uint16_t* x, int B, uint16_t* y, int32_t* idx_out,
                          float* gate_out, const DecodeWs& ws, hipStream_t st);
+hipError_t launch_stack_decode(const LayerDev& L, uint16_t* h, int B, float eps, uint16_t* z_out, uint16_t* y_out,
+                               int32_t* idx_out, float* gate_out, const DecodeWs& ws, hipStream_t st);
 hipError_t launch_route(const LayerDev& L, const uint16_t* x, int T, int32_t* idx_out, float* gate_out,
                         int32_t* counts_out, const PrefillWs& ws, hipStream_t st);
 hipError_t launch_prefill(const LayerDev& L, const uint16_t* x, int T, uint16_t* y, int32_t* idx_out,

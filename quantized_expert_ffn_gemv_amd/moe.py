@@ -25,7 +25,8 @@ DECODE_MAX_TOKENS = 8
 # every entry point declared in include/moe.h
 EXPORTS = [
     "moe_matrix_bytes", "moe_matrix_scales", "moe_workspace_bytes", "moe_route", "moe_forward_decode",
-    "moe_forward_prefill", "moe_rmsnorm", "moe_residual_add", "moe_pack_matrix", "moe_pack_gate_up",
+    "moe_forward_prefill", "moe_rmsnorm", "moe_residual_add", "moe_stack_decode_layer", "moe_pack_matrix",
+    "moe_pack_gate_up",
     "moe_status_string", "moe_last_error", "moe_kernel_class_count", "moe_kernel_class_name",
     "moe_timer_enable", "moe_timer_reset", "moe_timer_read", "moe_workspace_init", "moe_workspace_check",
 ]
@@ -71,6 +72,8 @@ def lib():
         L.moe_forward_prefill.argtypes = [P, vp, i32, vp, vp, vp, vp, sz, vp]
         L.moe_rmsnorm.restype = i32; L.moe_rmsnorm.argtypes = [vp, vp, i32, i32, ctypes.c_float, vp]
         L.moe_residual_add.restype = i32; L.moe_residual_add.argtypes = [vp, vp, i32, i32, vp]
+        L.moe_stack_decode_layer.restype = i32
+        L.moe_stack_decode_layer.argtypes = [P, vp, i32, ctypes.c_float, vp, vp, vp, vp, vp, sz, vp]
         L.moe_pack_matrix.restype = i32; L.moe_pack_matrix.argtypes = [i32, i32, i32, vp, vp, vp, vp]
         L.moe_pack_gate_up.restype = i32
         L.moe_pack_gate_up.argtypes = [i32, i32, i32, vp, vp, vp, vp, vp, vp]
@@ -273,6 +276,16 @@ def moe_residual_add(h, y, stream=None):
     _check(lib().moe_residual_add(_tptr(h), _tptr(y), T, H, _stream(stream)), "moe_residual_add")
 
 
+def moe_stack_decode_layer(layer, h, ws, eps: float = 1e-6, z_out=None, y_out=None, topk_idx=None, topk_gate=None,
+                           stream=None):
+    """One stacked layer at decode, in place on h (bf16 [B, H]): z = RMSNorm(h),
+    y = MoE(z), h = bf16(h + y); z_out / y_out receive z and y when given."""
+    B = h.shape[0]
+    _check(lib().moe_stack_decode_layer(ctypes.byref(layer.c), _tptr(h), B, eps, _tptr(z_out), _tptr(y_out),
+                                        _tptr(topk_idx), _tptr(topk_gate), _tptr(ws), ws.numel(), _stream(stream)),
+           "moe_stack_decode_layer")
+
+
 class StackBuffers:
     """Per-call tensors of a layer stack over T tokens (z, y, routing)."""
 
@@ -287,16 +300,23 @@ class StackBuffers:
 def stack_forward(layers, h, ws, decode: bool, buf: "StackBuffers", eps: float = 1e-6, stream=None,
                   each_layer=None):
     """Pre-norm residual stack of MoE layers over h (bf16 [T, H], updated in
-    place): per layer z = RMSNorm(h), y = MoE(z), h = bf16(h + y). Every step
-    is a library call on the same stream; each_layer(l, buf), when given, runs
-    after layer l's MoE call and before its residual add."""
-    fwd = moe_forward_decode if decode else moe_forward_prefill
+    place): per layer z = RMSNorm(h), y = MoE(z), h = bf16(h + y). Decode runs
+    each layer as one moe_stack_decode_layer call (one kernel at batch 1);
+    prefill as moe_rmsnorm, moe_forward_prefill and moe_residual_add. Every
+    step is a library call on the same stream. each_layer(l, buf), when given,
+    runs after layer l, with buf.z, buf.y and the routing of that layer filled
+    in (for decode they are written only when each_layer is given)."""
     for l, layer in enumerate(layers):
-        moe_rmsnorm(h, buf.z, eps, stream)
-        fwd(layer, buf.z, buf.y, ws, buf.idx, buf.gate, stream)
+        if decode:
+            want = each_layer is not None
+            moe_stack_decode_layer(layer, h, ws, eps, buf.z if want else None, buf.y if want else None, buf.idx,
+                                   buf.gate, stream)
+        else:
+            moe_rmsnorm(h, buf.z, eps, stream)
+            moe_forward_prefill(layer, buf.z, buf.y, ws, buf.idx, buf.gate, stream)
+            moe_residual_add(h, buf.y, stream)
         if each_layer is not None:
             each_layer(l, buf)
-        moe_residual_add(h, buf.y, stream)
     return h
 
 

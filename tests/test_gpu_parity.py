@@ -193,6 +193,42 @@ def test_decode_q4_verify_batches(moe, decode_q4, B):
             assert np.array_equal(y[c * B + i], y[c * B + j]), "identical tokens of one call must give identical outputs"
 
 
+@pytest.mark.parametrize("B", [1, 3])
+def test_stack_decode_layer_matches_separate_calls(moe, decode_q4, B):
+    # moe_stack_decode_layer (one kernel at batch 1: norm, MoE, residual)
+    # against moe_rmsnorm -> moe_forward_decode -> moe_residual_add on the
+    # same h: z, y, routing and the new h bit for bit (same sum orders); the
+    # separate calls are themselves checked against the oracle elsewhere
+    host, L, x = decode_q4
+    log("stack decode layer, B=%d, 4 calls: fused against separate calls" % B)
+    H, k = L.H, L.k
+    ws = moe.make_workspace(L, B, 0)
+    for c in range(4):
+        h = to_dev(x[c * B:(c + 1) * B]) if c % 2 == 0 else to_dev((x[c * B:(c + 1) * B].astype(np.uint32) + 0x0080).astype(np.uint16))
+        h1, h2 = h.clone(), h.clone()
+        z1, y1, z2, y2 = (torch.empty((B, H), dtype=torch.int16, device="cuda") for _ in range(4))
+        i1, i2 = (torch.empty((B, k), dtype=torch.int32, device="cuda") for _ in range(2))
+        g1, g2 = (torch.empty((B, k), dtype=torch.float32, device="cuda") for _ in range(2))
+        moe.moe_stack_decode_layer(L, h1, ws, 1e-6, z1, y1, i1, g1)
+        moe.moe_rmsnorm(h2, z2, 1e-6)
+        moe.moe_forward_decode(L, z2, y2, ws, i2, g2)
+        moe.moe_residual_add(h2, y2)
+        torch.cuda.synchronize()
+        for a_, b_, n in ((z1, z2, "z"), (y1, y2, "y"), (h1, h2, "h"), (i1, i2, "idx"), (g1, g2, "gate")):
+            assert torch.equal(a_, b_), "call %d: %s differs" % (c, n)
+    moe.moe_workspace_check(ws)
+    # without the optional outputs (the bench's form)
+    h1 = to_dev(x[:B])
+    h2 = h1.clone()
+    moe.moe_stack_decode_layer(L, h1, ws, 1e-6)
+    z2, y2 = (torch.empty((B, H), dtype=torch.int16, device="cuda") for _ in range(2))
+    moe.moe_rmsnorm(h2, z2, 1e-6)
+    moe.moe_forward_decode(L, z2, y2, ws)
+    moe.moe_residual_add(h2, y2)
+    torch.cuda.synchronize()
+    assert torch.equal(h1, h2)
+
+
 @pytest.fixture(scope="module")
 def decode_q3(moe):
     host = synth.make_layer("decode_q3_zipf")

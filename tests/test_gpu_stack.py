@@ -2,6 +2,9 @@
 residual, 48 independent layers of the 512-expert Q4 model (own router,
 Zipf bias and shared expert per layer), all resident on the GPU (44 GB).
 
+Decode runs each layer as one moe_stack_decode_layer call (at batch 1 one
+kernel: norm, MoE and residual); prefill as the three separate calls.
+
 The check is teacher-forced, layer by layer, on sampled tokens: the oracle's
 MoE layer l consumes the GPU's own bf16 z_l, so a routing decision at one
 layer cannot make every later layer disagree. Per layer and token: routing
@@ -113,15 +116,16 @@ def test_stack48_decode_teacher_forced(moe, stack):
     rec = {n: [] for n in ("h_in", "z", "y", "idx", "g", "h_out")}
     for t in range(x.shape[0]):
         h = to_dev(x[t:t + 1])
+        h0 = h.clone()
         per = {n: [] for n in rec}
 
-        def grab(l, b):
-            per["h_in"].append(h.clone()); per["z"].append(b.z.clone()); per["y"].append(b.y.clone())
+        def grab(l, b):  # after layer l (one fused kernel: norm, MoE, residual)
+            per["h_out"].append(h.clone()); per["z"].append(b.z.clone()); per["y"].append(b.y.clone())
             per["idx"].append(b.idx.clone()); per["g"].append(b.gate.clone())
 
         moe.stack_forward(layers, h, ws, True, buf, EPS, each_layer=grab)
         torch.cuda.synchronize()
-        per["h_out"] = per["h_in"][1:] + [h.clone()]
+        per["h_in"] = [h0] + per["h_out"][:-1]
         for n in rec:
             rec[n].append(torch.stack(per[n]).cpu().numpy())
     moe.moe_workspace_check(ws)
@@ -147,16 +151,17 @@ def test_stack48_prefill_teacher_forced(moe, stack):
     ws = moe.make_workspace(layers[0], T, 1)
     buf = moe.StackBuffers(T, H, k)
     h = to_dev(x)
-    per = {n: [] for n in ("h_in", "z", "y", "idx", "g")}
+    h0 = h.index_select(0, sample)
+    per = {n: [] for n in ("h_out", "z", "y", "idx", "g")}
 
-    def grab(l, b):
-        per["h_in"].append(h.index_select(0, sample)); per["z"].append(b.z.index_select(0, sample))
+    def grab(l, b):  # after layer l's residual add
+        per["h_out"].append(h.index_select(0, sample)); per["z"].append(b.z.index_select(0, sample))
         per["y"].append(b.y.index_select(0, sample)); per["idx"].append(b.idx.index_select(0, sample))
         per["g"].append(b.gate.index_select(0, sample))
 
     moe.stack_forward(layers, h, ws, False, buf, EPS, each_layer=grab)
     torch.cuda.synchronize()
-    per["h_out"] = per["h_in"][1:] + [h.index_select(0, sample)]
+    per["h_in"] = [h0] + per["h_out"][:-1]
     arr = {n: torch.stack(v).cpu().numpy() for n, v in per.items()}
     u16 = lambda a: a.view(np.uint16)
     _check_layers(hosts, u16(arr["h_in"]), u16(arr["z"]), u16(arr["y"]), arr["idx"], arr["g"],
