@@ -101,6 +101,17 @@ def test_call_validation_codes():
     assert L.moe_rmsnorm(16, 16, 1, 12, ctypes.c_float(1e-6), None) == moe.MOE_ERR_SHAPE
     assert L.moe_rmsnorm(16, 16, 1, 2048, ctypes.c_float(-1.0), None) == moe.MOE_ERR_SHAPE
     assert L.moe_residual_add(None, 16, 1, 2048, None) == moe.MOE_ERR_NULL
+    # moe_stack_decode_layer(layer, h, B, eps, z_out, y_out, idx, gate, ws, ws_bytes, stream)
+    S, f, lr = L.moe_stack_decode_layer, ctypes.c_float, ctypes.byref(layer)
+    assert S(lr, None, 1, f(1e-6), None, None, None, None, 16, big, None) == moe.MOE_ERR_NULL
+    assert S(lr, 16, 1, f(1e-6), None, None, None, None, None, big, None) == moe.MOE_ERR_NULL
+    assert S(lr, 16, 0, f(1e-6), None, None, None, None, 16, big, None) == moe.MOE_ERR_SHAPE
+    assert S(lr, 16, 9, f(1e-6), None, None, None, None, 16, big, None) == moe.MOE_ERR_SHAPE
+    assert S(lr, 16, 1, f(-1.0), None, None, None, None, 16, big, None) == moe.MOE_ERR_SHAPE
+    assert S(lr, 8, 1, f(1e-6), None, None, None, None, 16, big, None) == moe.MOE_ERR_ALIGN
+    assert S(lr, 16, 1, f(1e-6), 24, None, None, None, 16, big, None) == moe.MOE_ERR_ALIGN
+    assert S(lr, 16, 1, f(1e-6), None, 40, None, None, 16, big, None) == moe.MOE_ERR_ALIGN
+    assert S(lr, 16, 1, f(1e-6), None, None, None, None, 16, 100, None) == moe.MOE_ERR_WORKSPACE
 
 
 # ----------------------------------------------------------------------------- packing
