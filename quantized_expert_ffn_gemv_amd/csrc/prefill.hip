@@ -291,7 +291,15 @@ __global__ __launch_bounds__(256) void k_pf_count(const int32_t* __restrict__ id
   __syncthreads();
   const int t0 = blockIdx.x * PF_TOK_PER_BLK;
   const int t1 = min(T, t0 + PF_TOK_PER_BLK);
-  for (int s = t0 * k + threadIdx.x; s < t1 * k; s += 256) atomicAdd(&hist[idx[s]], 1);
+  // all of the thread's slots loaded first (clamped, unconditional), then counted
+  constexpr int NPASS = PF_TOK_PER_BLK * 16 / 256;  // k <= 16
+  const int s0 = t0 * k, s1 = t1 * k;
+  int ev[NPASS];
+#pragma unroll
+  for (int q = 0; q < NPASS; q++) ev[q] = idx[min(s0 + 256 * q + (int)threadIdx.x, s1 - 1)];
+#pragma unroll
+  for (int q = 0; q < NPASS; q++)
+    if (s0 + 256 * q + (int)threadIdx.x < s1) atomicAdd(&hist[ev[q]], 1);
   __syncthreads();
   for (int e = threadIdx.x; e < E; e += 256) blk_counts[(size_t)blockIdx.x * E + e] = hist[e];
 }
@@ -304,9 +312,19 @@ __global__ __launch_bounds__(1024) void k_pf_scan(const int32_t* __restrict__ bl
   __shared__ int s_tot[1024];
   __shared__ int s_til[1024];
   const int e = threadIdx.x;
+  // the expert's block counts, eight loads in flight at a time (clamped,
+  // unconditional; one round trip per eight blocks instead of one per block)
+  constexpr int SB = 8;
+  const int ec = min(e, E - 1);
   int tot = 0;
-  if (e < E)
-    for (int b = 0; b < nblk; b++) tot += blk_counts[(size_t)b * E + e];
+  for (int b0 = 0; b0 < nblk; b0 += SB) {
+    int v[SB];
+#pragma unroll
+    for (int j = 0; j < SB; j++) v[j] = blk_counts[(size_t)min(b0 + j, nblk - 1) * E + ec];
+#pragma unroll
+    for (int j = 0; j < SB; j++) tot += (b0 + j < nblk) ? v[j] : 0;
+  }
+  if (e >= E) tot = 0;
   s_tot[e] = (e < E) ? tot : 0;
   s_til[e] = (e < E) ? (tot + PF_BM - 1) / PF_BM : 0;
   __syncthreads();
@@ -334,9 +352,17 @@ __global__ __launch_bounds__(1024) void k_pf_scan(const int32_t* __restrict__ bl
     }
     if (counts_out) counts_out[e] = tot;
     int run = off;
-    for (int b = 0; b < nblk; b++) {
-      blk_base[(size_t)b * E + e] = run;
-      run += blk_counts[(size_t)b * E + e];
+    for (int b0 = 0; b0 < nblk; b0 += SB) {
+      int v[SB];
+#pragma unroll
+      for (int j = 0; j < SB; j++) v[j] = blk_counts[(size_t)min(b0 + j, nblk - 1) * E + e];
+#pragma unroll
+      for (int j = 0; j < SB; j++) {
+        if (b0 + j < nblk) {
+          blk_base[(size_t)(b0 + j) * E + e] = run;
+          run += v[j];
+        }
+      }
     }
     if (e == E - 1) {
       offsets[E] = s_tot[e];
@@ -346,22 +372,41 @@ __global__ __launch_bounds__(1024) void k_pf_scan(const int32_t* __restrict__ bl
 }
 
 // Positions of the slots of one token block, in slot order within each expert.
+// Per pass of 256 slots: each wave groups its lanes by expert (ballots),
+// each group's leader posts the group's size for its wave, and a slot's
+// position is the expert's running count + the sizes posted by the earlier
+// waves + its rank in its group; then the running counts advance.
 __global__ __launch_bounds__(256) void k_pf_scatter(const int32_t* __restrict__ idx, int T, int E, int k,
                                                      const int32_t* __restrict__ blk_base, int32_t* __restrict__ perm,
                                                      int32_t* __restrict__ inv) {
-  extern __shared__ int cnt[];
+  extern __shared__ int cnt[];  // [E] running counts, then [4][E] per-wave group sizes
+  int* wcnt = cnt + E;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  for (int e = threadIdx.x; e < E; e += 256) cnt[e] = blk_base[(size_t)blockIdx.x * E + e];
+  for (int e = threadIdx.x; e < E; e += 256) {
+    cnt[e] = blk_base[(size_t)blockIdx.x * E + e];
+#pragma unroll
+    for (int w = 0; w < 4; w++) wcnt[w * E + e] = 0;
+  }
   __syncthreads();
   const int t0 = blockIdx.x * PF_TOK_PER_BLK;
   const int t1 = min(T, t0 + PF_TOK_PER_BLK);
   const int s0 = t0 * k, s1 = t1 * k;
   int ebits = 0;
   while ((1 << ebits) < E) ebits++;
-  for (int base = s0; base < s1; base += 256) {
+  // every pass's expert index loaded up front (clamped, unconditional): one
+  // round trip for the block instead of one per pass; the pass loop is
+  // unrolled so the values stay in registers
+  constexpr int NPASS = PF_TOK_PER_BLK * 16 / 256;  // k <= 16
+  int ev[NPASS];
+#pragma unroll
+  for (int q = 0; q < NPASS; q++) ev[q] = idx[min(s0 + 256 * q + (int)threadIdx.x, s1 - 1)];
+#pragma unroll
+  for (int q = 0; q < NPASS; q++) {
+    const int base = s0 + 256 * q;
+    if (base >= s1) break;  // uniform
     const int s = base + threadIdx.x;
     const bool act = s < s1;
-    const int e = act ? idx[s] : 0;
+    const int e = act ? ev[q] : 0;
     // lanes of this wave with the same expert
     uint64_t peers = __ballot(act);
     for (int b = 0; b < ebits; b++) {
@@ -371,17 +416,20 @@ __global__ __launch_bounds__(256) void k_pf_scatter(const int32_t* __restrict__ 
     if (!act) peers = 0;
     const int before = __popcll(peers & ((1ull << lane) - 1ull));
     const bool leader = act && before == 0;
-    // waves in order, so earlier slots get earlier positions
-    for (int w = 0; w < 4; w++) {
-      if (wave == w && act) {
-        const int pos = cnt[e] + before;
-        perm[pos] = s;
-        inv[s] = pos;
-      }
-      __syncthreads();
-      if (wave == w && leader) cnt[e] += __popcll(peers);
-      __syncthreads();
+    if (leader) wcnt[wave * E + e] = __popcll(peers);
+    __syncthreads();
+    if (act) {
+      int pos = cnt[e] + before;
+      for (int w = 0; w < wave; w++) pos += wcnt[w * E + e];  // earlier waves' slots come first
+      perm[pos] = s;
+      inv[s] = pos;
     }
+    __syncthreads();
+    if (leader) {
+      atomicAdd(&cnt[e], __popcll(peers));
+      wcnt[wave * E + e] = 0;
+    }
+    __syncthreads();
   }
 }
 
@@ -1061,7 +1109,7 @@ static hipError_t route_steps(const LayerDev& L, const uint16_t* x, int T, int32
   (void)launch_k(KC_PF_SCAN, k_pf_scan, dim3(1), dim3(1024), 0, st, ws.blk_counts, nblk, E, ws.blk_base, ws.counts,
                      ws.offsets, ws.tile_start, ws.tile_info, counts_out);
   if (!permute) return hipGetLastError();
-  (void)launch_k(KC_PF_SCATTER, k_pf_scatter, dim3(nblk), dim3(256), E * sizeof(int), st, ws.idx, T, E, k, ws.blk_base, ws.perm,
+  (void)launch_k(KC_PF_SCATTER, k_pf_scatter, dim3(nblk), dim3(256), 5 * E * sizeof(int), st, ws.idx, T, E, k, ws.blk_base, ws.perm,
                      ws.inv);
   return hipGetLastError();
 }
