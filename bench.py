@@ -13,11 +13,12 @@ the 4096-token prefill of a layer of the same shape, the per-kernel roofline
 of the dominant decode kernel (HIP events on the launch stream), and the CPU
 oracle timed on a bounded sample of the headline workload.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-prefill] [--no-cpu] [--stack]
-       (--stack adds the 48-layer stack: 512 batch-1 decode tokens and a 32768-token
-        prefill through 48 resident layers)
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-prefill] [--no-cpu] [--no-stack]
+       (the run includes the 48-layer stack: 512 batch-1 decode tokens and a
+        32768-token prefill through 48 resident layers, about 20 s more;
+        --no-stack skips it)
        python bench.py --profile-sample   (short eager run for hardware-counter passes:
-                                           a 256 MiB elementwise copy, then 32 decode
+                                           a 2 GiB elementwise copy, then 32 decode
                                            tokens and one 4096-token prefill)
 """
 import argparse
@@ -355,7 +356,8 @@ def main():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--profile-sample", action="store_true")
-    ap.add_argument("--stack", action="store_true", help="also run the 48-layer stack (about a minute to build)")
+    ap.add_argument("--no-stack", action="store_true", help="skip the 48-layer stack (about 20 s with its set-up)")
+    ap.add_argument("--stack", action="store_true", help=argparse.SUPPRESS)  # the stack runs by default
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (use --gpus 1)", file=sys.stderr)
@@ -499,8 +501,8 @@ def main():
         }
         log("prefill:", json.dumps(result["prefill"]))
 
-    # ---------------------------------------------------------------- 48-layer stack (opt-in)
-    if args.stack:
+    # ---------------------------------------------------------------- 48-layer stack
+    if not args.no_stack:
         log("48-layer stack ...")
         Lp = L = None  # release the single layers first
         result["stack48"] = run_stack(moe, torch, synth, args.steps)
