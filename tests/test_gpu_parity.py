@@ -91,6 +91,24 @@ def test_ragged_shapes(moe, wtype, shared):
         _check_all(host, xs, y, idx, g, "ragged decode B=%d %s" % (B, wtype))
 
 
+@pytest.mark.parametrize("wtype,H", [("q4", 8192), ("q3", 4096)])
+def test_large_hidden(moe, wtype, H):
+    # hidden sizes past the one-kernel decode path (H > 2048; 8192 is the
+    # largest the library takes): batch-1 and batch-2 decode on the four-kernel
+    # path (B * H at its 16384 limit), and a ragged prefill whose router reads
+    # x in 512-element chunks
+    log("large hidden: E=16 k=4 H=%d I=96 %s" % (H, wtype))
+    host = synth.random_layer(16, 4, H, 96, wtype, "bf16", seed=21, router_sd=0.05)
+    L = moe.DeviceLayer(host)
+    x = synth.normal_bf16(synth.key(21, 2, 2, 2, 2), (100, H), 1.0)
+    y, idx, g = _prefill(moe, L, x)
+    _check_all(host, x, y, idx, g, "large-H prefill %s" % wtype)
+    xs = x[:6]
+    for B in (1, 2):
+        y, idx, g = _decode_calls(moe, L, xs, B)
+        _check_all(host, xs, y, idx, g, "large-H decode B=%d %s" % (B, wtype))
+
+
 @pytest.mark.parametrize("E,k", [(1, 1), (4, 4), (64, 16), (1024, 16)])
 def test_edge_expert_counts(moe, E, k):
     log("edge E=%d k=%d" % (E, k))
