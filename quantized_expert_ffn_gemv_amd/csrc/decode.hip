@@ -36,8 +36,9 @@ constexpr int DC_SPLIT = DC_THREADS / DC_ROWS;
 
 // ---------------------------------------------------------------------------
 // Down-projection pieces: NCOL consecutive intermediate columns (16 for a
-// routed workgroup, 4 for a shared-expert workgroup) of one output row of a
-// chunk-major D[H][I], and their dot with NCOL bf16 h values (NCOL/2 pairs).
+// routed workgroup over dense weights, 4 for a shared-expert workgroup) of
+// one output row of a chunk-major D[H][I], and their dot with NCOL bf16 h
+// values (NCOL/2 pairs). Quantised routed workgroups take whole chunks.
 // ---------------------------------------------------------------------------
 template <int WT, int NCOL>
 struct DownPiece {
@@ -405,7 +406,7 @@ __global__ __launch_bounds__(DB_THREADS) void k_dec_route(int E, int k, int B, D
 }
 
 // ---------------------------------------------------------------------------
-// Kernel B: routed experts, one (unique expert, 16 columns) each
+// Kernel B: routed experts, one (unique expert, column group) each
 // ---------------------------------------------------------------------------
 constexpr int B_CPT = 4;  // gate/up chunks per lane and batch
 constexpr int B_RPT = 4;  // down rows per thread and batch
