@@ -798,42 +798,15 @@ constexpr int GQ_BN = 64 * GQ_NSW;              // weight rows per tile
 constexpr int GQ_REGION = 64 * 16;              // bytes per (wave, subtile) weight region
 constexpr int GQ_BSLOT = (G_THREADS / 64) * GQ_NSW * GQ_REGION;  // 16 KB
 
-template <int WT, int KIND>
-__global__ __launch_bounds__(G_THREADS, 2) void k_pf_gemm_q(GemmArgs g) {
-  static_assert(WT == MOE_W_Q4 || WT == MOE_W_Q3, "quantised weights only");
-  __shared__ __align__(16) uint4 sA0[G_SLOT_U4];
-  __shared__ __align__(16) uint4 sA1[G_SLOT_U4];
-  __shared__ __align__(16) uint8_t sB0[GQ_BSLOT];
-  __shared__ __align__(16) uint8_t sB1[GQ_BSLOT];
+// The tile's work with MSUB 16-row subtiles (5 when the tile has at most 80
+// rows, else 6): a tile's padding subtile costs no MFMAs (chosen per tile,
+// so the loops stay branch-free).
+template <int WT, int KIND, int MSUB>
+__device__ __forceinline__ void gemm_q_tile(const GemmArgs& g, uint4* sA0, uint4* sA1, uint8_t* sB0, uint8_t* sB1, int e,
+                                            int M, int pos0, int n0) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  constexpr int NSW = GQ_NSW, BN = GQ_BN;
-
-  // ---- tile (as k_pf_gemm)
-  const int NT = (g.N + BN - 1) / BN;
-  const int mt_total = g.offsets ? g.tile_start[g.E] : (g.M_total + PF_BM - 1) / PF_BM;
-  const int total = mt_total * NT;
-  const int per = (total + 7) >> 3;
-  const int ix = blockIdx.x >> 3;
-  const int logical = (blockIdx.x & 7) * per + ix;
-  if (ix >= per || logical >= total) return;
-  int e = 0, m0 = 0, M = 0, pos0 = 0, nt = 0;
-  if (g.offsets) {
-    const int32_t* ti = g.tile_info + (size_t)PF_TILE_INFO * (logical / NT);  // M tile q = logical / NT
-    e = ti[0];
-    const int ntiles = ti[2];
-    const int pos = logical - NT * ti[1];
-    nt = pos / ntiles;
-    m0 = (pos - nt * ntiles) * PF_BM;
-    M = min(PF_BM, ti[4] - m0);
-    pos0 = ti[3] + m0;
-  } else {
-    nt = logical / mt_total;
-    m0 = (logical - nt * mt_total) * PF_BM;
-    M = min(PF_BM, g.M_total - m0);
-    pos0 = m0;
-  }
-  const int n0 = nt * BN;
+  constexpr int NSW = GQ_NSW;
   const uint8_t* w = g.w + (size_t)e * g.w_stride;
   const uint16_t* wsc = g.ws + (size_t)e * g.ws_stride;
 
@@ -855,9 +828,9 @@ __global__ __launch_bounds__(G_THREADS, 2) void k_pf_gemm_q(GemmArgs g) {
     arow[i] = (uint32_t)(row < M ? r : 0);
   }
 
-  floatx4_t acc[G_MSUB][NSW];
+  floatx4_t acc[MSUB][NSW];
 #pragma unroll
-  for (int i = 0; i < G_MSUB; i++)
+  for (int i = 0; i < MSUB; i++)
 #pragma unroll
     for (int j = 0; j < NSW; j++) acc[i][j] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 
@@ -926,12 +899,12 @@ __global__ __launch_bounds__(G_THREADS, 2) void k_pf_gemm_q(GemmArgs g) {
           bfrag[sub] = q4_frag(wd, qs[sub], magic);
         }
         {  // all row subtiles' A fragments of the step read together
-          bf16x8_t afrag[G_MSUB];
+          bf16x8_t afrag[MSUB];
 #pragma unroll
-          for (int i = 0; i < G_MSUB; i++)
+          for (int i = 0; i < MSUB; i++)
             afrag[i] = __builtin_bit_cast(bf16x8_t, A[(16 * i + m) * 16 + ((4 * bj + t) ^ m)]);
 #pragma unroll
-          for (int i = 0; i < G_MSUB; i++)
+          for (int i = 0; i < MSUB; i++)
 #pragma unroll
             for (int sub = 0; sub < NSW; sub++)
               acc[i][sub] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afrag[i], bfrag[sub], acc[i][sub], 0, 0, 0);
@@ -954,12 +927,12 @@ __global__ __launch_bounds__(G_THREADS, 2) void k_pf_gemm_q(GemmArgs g) {
 #pragma unroll
         for (int sub = 0; sub < NSW; sub++) bfrag[sub] = frag_b<WT>(r[sub], t);
         {  // all row subtiles' A fragments of the step read together
-          bf16x8_t afrag[G_MSUB];
+          bf16x8_t afrag[MSUB];
 #pragma unroll
-          for (int i = 0; i < G_MSUB; i++)
+          for (int i = 0; i < MSUB; i++)
             afrag[i] = __builtin_bit_cast(bf16x8_t, A[(16 * i + m) * 16 + ((4 * bj + t) ^ m)]);
 #pragma unroll
-          for (int i = 0; i < G_MSUB; i++)
+          for (int i = 0; i < MSUB; i++)
 #pragma unroll
             for (int sub = 0; sub < NSW; sub++)
               acc[i][sub] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afrag[i], bfrag[sub], acc[i][sub], 0, 0, 0);
@@ -995,7 +968,7 @@ __global__ __launch_bounds__(G_THREADS, 2) void k_pf_gemm_q(GemmArgs g) {
   if (KIND == GK_GATE_UP) {
     const int I = g.N / 2;
 #pragma unroll
-    for (int i = 0; i < G_MSUB; i++) {
+    for (int i = 0; i < MSUB; i++) {
       if (i < nsub) {
 #pragma unroll
         for (int gg = 0; gg < NSW / 2; gg++) {
@@ -1013,7 +986,7 @@ __global__ __launch_bounds__(G_THREADS, 2) void k_pf_gemm_q(GemmArgs g) {
     }
   } else {
 #pragma unroll
-    for (int i = 0; i < G_MSUB; i++) {
+    for (int i = 0; i < MSUB; i++) {
       if (i < nsub) {
 #pragma unroll
         for (int j = 0; j < NSW; j++) {
@@ -1027,6 +1000,44 @@ __global__ __launch_bounds__(G_THREADS, 2) void k_pf_gemm_q(GemmArgs g) {
       }
     }
   }
+}
+
+template <int WT, int KIND>
+__global__ __launch_bounds__(G_THREADS, 2) void k_pf_gemm_q(GemmArgs g) {
+  static_assert(WT == MOE_W_Q4 || WT == MOE_W_Q3, "quantised weights only");
+  __shared__ __align__(16) uint4 sA0[G_SLOT_U4];
+  __shared__ __align__(16) uint4 sA1[G_SLOT_U4];
+  __shared__ __align__(16) uint8_t sB0[GQ_BSLOT];
+  __shared__ __align__(16) uint8_t sB1[GQ_BSLOT];
+  constexpr int BN = GQ_BN;
+
+  // ---- tile (as k_pf_gemm)
+  const int NT = (g.N + BN - 1) / BN;
+  const int mt_total = g.offsets ? g.tile_start[g.E] : (g.M_total + PF_BM - 1) / PF_BM;
+  const int total = mt_total * NT;
+  const int per = (total + 7) >> 3;
+  const int ix = blockIdx.x >> 3;
+  const int logical = (blockIdx.x & 7) * per + ix;
+  if (ix >= per || logical >= total) return;
+  int e = 0, m0 = 0, M = 0, pos0 = 0, nt = 0;
+  if (g.offsets) {
+    const int32_t* ti = g.tile_info + (size_t)PF_TILE_INFO * (logical / NT);  // M tile q = logical / NT
+    e = ti[0];
+    const int ntiles = ti[2];
+    const int pos = logical - NT * ti[1];
+    nt = pos / ntiles;
+    m0 = (pos - nt * ntiles) * PF_BM;
+    M = min(PF_BM, ti[4] - m0);
+    pos0 = ti[3] + m0;
+  } else {
+    nt = logical / mt_total;
+    m0 = (logical - nt * mt_total) * PF_BM;
+    M = min(PF_BM, g.M_total - m0);
+    pos0 = m0;
+  }
+  const int n0 = nt * BN;
+  if (M <= 5 * 16) gemm_q_tile<WT, KIND, 5>(g, sA0, sA1, sB0, sB1, e, M, pos0, n0);
+  else gemm_q_tile<WT, KIND, 6>(g, sA0, sA1, sB0, sB1, e, M, pos0, n0);
 }
 
 // ---------------------------------------------------------------------------
