@@ -798,9 +798,9 @@ constexpr int GQ_BN = 64 * GQ_NSW;              // weight rows per tile
 constexpr int GQ_REGION = 64 * 16;              // bytes per (wave, subtile) weight region
 constexpr int GQ_BSLOT = (G_THREADS / 64) * GQ_NSW * GQ_REGION;  // 16 KB
 
-// The tile's work with MSUB 16-row subtiles (5 when the tile has at most 80
-// rows, else 6): a tile's padding subtile costs no MFMAs (chosen per tile,
-// so the loops stay branch-free).
+// The tile's work with MSUB 16-row subtiles (2, 4, 5 or 6: the fewest that
+// hold the tile's rows), so padding subtiles cost no MFMAs (an expert's last
+// tile is often short; chosen per tile, so the loops stay branch-free).
 template <int WT, int KIND, int MSUB>
 __device__ __forceinline__ void gemm_q_tile(const GemmArgs& g, uint4* sA0, uint4* sA1, uint8_t* sB0, uint8_t* sB1, int e,
                                             int M, int pos0, int n0) {
@@ -1036,7 +1036,9 @@ __global__ __launch_bounds__(G_THREADS, 2) void k_pf_gemm_q(GemmArgs g) {
     pos0 = m0;
   }
   const int n0 = nt * BN;
-  if (M <= 5 * 16) gemm_q_tile<WT, KIND, 5>(g, sA0, sA1, sB0, sB1, e, M, pos0, n0);
+  if (M <= 2 * 16) gemm_q_tile<WT, KIND, 2>(g, sA0, sA1, sB0, sB1, e, M, pos0, n0);
+  else if (M <= 4 * 16) gemm_q_tile<WT, KIND, 4>(g, sA0, sA1, sB0, sB1, e, M, pos0, n0);
+  else if (M <= 5 * 16) gemm_q_tile<WT, KIND, 5>(g, sA0, sA1, sB0, sB1, e, M, pos0, n0);
   else gemm_q_tile<WT, KIND, 6>(g, sA0, sA1, sB0, sB1, e, M, pos0, n0);
 }
 
