@@ -207,10 +207,11 @@ moe_status moe_residual_add(void *h, const void *y, int32_t T, int32_t H, hipStr
  * takes the shape, all three run in that one kernel (every workgroup that
  * reads the token normalises it itself; the reducers add the residual);
  * otherwise as the three calls in turn. z_out, y_out ([B][H] bf16) receive
- * z and y when not NULL; topk_idx/topk_gate as in moe_forward_decode.
+ * z and y when not NULL and must not overlap h or each other;
+ * topk_idx/topk_gate as in moe_forward_decode.
  * Workspace: moe_workspace_bytes(layer, B, 0), as for moe_forward_decode
  * (the two may share one). Errors as moe_forward_decode, and MOE_ERR_SHAPE
- * for eps < 0. */
+ * for eps < 0 or overlapping h, z_out, y_out. */
 moe_status moe_stack_decode_layer(const moe_layer *layer, void *h, int32_t B, float eps, void *z_out, void *y_out,
                                   int32_t *topk_idx, float *topk_gate, void *ws, size_t ws_bytes,
                                   hipStream_t stream);

@@ -312,6 +312,18 @@ moe_status moe_stack_decode_layer(const moe_layer* layer, void* h, int32_t B, fl
                 layer->n_experts, layer->top_k);
   if (!aligned16(h) || !aligned16(ws) || (z_out && !aligned16(z_out)) || (y_out && !aligned16(y_out)))
     return fail(MOE_ERR_ALIGN, "h, ws, z_out and y_out must be 16-byte aligned");
+  {
+    // z_out / y_out must not overlap h (the one-kernel path reads h while they are written) or each other
+    const size_t n = (size_t)B * layer->hidden * 2;
+    auto overlap = [n](const void* a, const void* b) {
+      if (!a || !b) return false;
+      const uint8_t* p = static_cast<const uint8_t*>(a);
+      const uint8_t* q = static_cast<const uint8_t*>(b);
+      return p < q + n && q < p + n;
+    };
+    if (overlap(z_out, h) || overlap(y_out, h) || overlap(z_out, y_out))
+      return fail(MOE_ERR_SHAPE, "z_out and y_out must not overlap h or each other");
+  }
   const size_t need = carve_decode(layer, B, nullptr, nullptr);
   if (ws_bytes < need) return fail(MOE_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
   moe::DecodeWs w;

@@ -112,6 +112,10 @@ def test_call_validation_codes():
     assert S(lr, 16, 1, f(1e-6), 24, None, None, None, 16, big, None) == moe.MOE_ERR_ALIGN
     assert S(lr, 16, 1, f(1e-6), None, 40, None, None, 16, big, None) == moe.MOE_ERR_ALIGN
     assert S(lr, 16, 1, f(1e-6), None, None, None, None, 16, 100, None) == moe.MOE_ERR_WORKSPACE
+    # overlapping outputs (h spans B * H * 2 = 4 KiB here)
+    assert S(lr, 1 << 20, 1, f(1e-6), (1 << 20) + 16, None, None, None, 16, big, None) == moe.MOE_ERR_SHAPE
+    assert S(lr, 1 << 20, 1, f(1e-6), None, (1 << 20) - 16, None, None, 16, big, None) == moe.MOE_ERR_SHAPE
+    assert S(lr, 1 << 20, 1, f(1e-6), 1 << 22, (1 << 22) + 16, None, None, 16, big, None) == moe.MOE_ERR_SHAPE
 
 
 # ----------------------------------------------------------------------------- packing
