@@ -31,7 +31,7 @@ namespace moe {
 constexpr int DA_THREADS = 512;  // kernel A: 8 waves
 constexpr int DB_THREADS = 512;  // kernel B: 8 waves
 constexpr int DC_THREADS = 256;  // kernel C
-constexpr int DC_ROWS = 16;      // output rows per kernel-C workgroup
+constexpr int DC_ROWS = 32;      // output rows per kernel-C workgroup (128-byte row segments per partial)
 constexpr int DC_SPLIT = DC_THREADS / DC_ROWS;
 
 // ---------------------------------------------------------------------------
