@@ -3,7 +3,7 @@
 //
 //   A  k_dec_a     : router logits in fp64 (one wave per expert row; an fp32
 //                    weight times a bf16 activation is exact in fp64), and
-//                    the whole shared expert: each workgroup owns 4
+//                    the whole shared expert: each workgroup owns 8
 //                    intermediate columns, computes them (gate/up GEMV +
 //                    SwiGLU) and their contribution to every output row (a
 //                    partial down product).
@@ -36,7 +36,7 @@ constexpr int DC_SPLIT = DC_THREADS / DC_ROWS;
 
 // ---------------------------------------------------------------------------
 // Down-projection pieces: NCOL consecutive intermediate columns (16 for a
-// routed workgroup over dense weights, 4 for a shared-expert workgroup) of
+// routed workgroup over dense weights, 8 for a shared-expert workgroup) of
 // one output row of a chunk-major D[H][I], and their dot with NCOL bf16 h
 // values (NCOL/2 pairs). Quantised routed workgroups take whole chunks.
 // ---------------------------------------------------------------------------
@@ -228,33 +228,35 @@ __global__ __launch_bounds__(DA_THREADS) void k_dec_a(LayerDev L, const uint16_t
     }
     return;
   }
-  // ---- shared expert: intermediate columns 4p .. 4p+3 (p = workgroup index)
+  // ---- shared expert: intermediate columns 8p .. 8p+7 (p = workgroup index)
   constexpr int KC = kchunk<SWT>();
+  constexpr int SCPT = 8;  // gate/up chunks per lane and batch (32 K parts x 8 = 256 chunks)
   const int R = 2 * I;
   const int p = blockIdx.x - nRB;
-  const int q = p >> 2, j0 = (p & 3) * 4;
-  // lane -> (row r = lane / 8: 0..3 gate rows j0.., 4..7 up rows; kpart = lane % 8 + 8 wave)
-  const int r = lane >> 3;
-  const int row = 32 * q + (r < 4 ? j0 + r : 16 + j0 + (r - 4));
-  const int kp = (lane & 7) + 8 * wave;
+  const int q = p >> 1, j0 = (p & 1) * 8;
+  // lane -> (row r = lane / 4: 0..7 gate rows j0.., 8..15 up rows; kpart = lane % 4 + 4 wave):
+  // the eight gate (up) rows are consecutive, so a load reads 8 x 16 B in a row
+  const int r = lane >> 2;
+  const int row = 32 * q + (r < 8 ? j0 + r : 16 + j0 + (r - 8));
+  const int kp = (lane & 3) + 4 * wave;
   const int nc = H / KC;
-  float* s_gu = reinterpret_cast<float*>(smem + (size_t)B * H * 2);  // [8 waves][MAXB][8 rows]
-  uint32_t* s_hp = reinterpret_cast<uint32_t*>(s_gu + 8 * MAXB * 8);  // [MAXB][2] bf16 pairs
-  float* s_hs = reinterpret_cast<float*>(s_hp + MAXB * 2);            // [MAXB]
-  const int col0 = 4 * p;
+  float* s_gu = reinterpret_cast<float*>(smem + (size_t)B * H * 2);  // [8 waves][MAXB][16 rows]
+  uint32_t* s_hp = reinterpret_cast<uint32_t*>(s_gu + 8 * MAXB * 16);  // [MAXB][4] bf16 pairs
+  float* s_hs = reinterpret_cast<float*>(s_hp + MAXB * 4);             // [MAXB]
+  const int col0 = 8 * p;
   // first batch of down pieces is issued together with the gate/up loads
-  DownPiece<SWT, 4> dp[A_RPT];
+  DownPiece<SWT, 8> dp[A_RPT];
 #pragma unroll
   for (int i = 0; i < A_RPT; i++)  // clamped, unconditional (rows past H are not used)
-    load_down_piece<SWT, 4>(L.sdn, nullptr, H, min((int)threadIdx.x + DA_THREADS * i, H - 1), col0, dp[i]);
+    load_down_piece<SWT, 8>(L.sdn, nullptr, H, min((int)threadIdx.x + DA_THREADS * i, H - 1), col0, dp[i]);
   float acc[MAXB];
 #pragma unroll
   for (int t = 0; t < MAXB; t++) acc[t] = 0.0f;
-  for (int c0 = 0; c0 < nc; c0 += 64 * A_CPS) {
-    Raw raw[A_CPS];
+  for (int c0 = 0; c0 < nc; c0 += 32 * SCPT) {
+    Raw raw[SCPT];
 #pragma unroll
-    for (int i = 0; i < A_CPS; i++)  // clamped, unconditional (chunks past the row are not used)
-      raw[i] = load_chunk<SWT>(L.sgu, (size_t)min(c0 + kp + 64 * i, nc - 1) * R + row);
+    for (int i = 0; i < SCPT; i++)  // clamped, unconditional (chunks past the row are not used)
+      raw[i] = load_chunk<SWT>(L.sgu, (size_t)min(c0 + kp + 32 * i, nc - 1) * R + row);
     if (c0 == 0) {
       stage_tokens<DA_THREADS>(x, B, H, xs, nullptr);
       __syncthreads();
@@ -263,8 +265,8 @@ __global__ __launch_bounds__(DA_THREADS) void k_dec_a(LayerDev L, const uint16_t
     for (int t = 0; t < MAXB; t++) {
       if (t < B) {
 #pragma unroll
-        for (int i = 0; i < A_CPS; i++) {
-          const int c = c0 + kp + 64 * i;
+        for (int i = 0; i < SCPT; i++) {
+          const int c = c0 + kp + 32 * i;
           if (c < nc) acc[t] = ddot<SWT>(raw[i], xs + (size_t)t * H + (size_t)c * KC, acc[t]);
         }
       }
@@ -273,25 +275,30 @@ __global__ __launch_bounds__(DA_THREADS) void k_dec_a(LayerDev L, const uint16_t
 #pragma unroll
   for (int t = 0; t < MAXB; t++) {
     if (t < B) {
-      const float v = sum8_f32(acc[t]);
-      if ((lane & 7) == 0) s_gu[(wave * MAXB + t) * 8 + r] = v;
+      float v = acc[t];
+      v += dpp_f32<DPP_XOR1>(v);  // the row's four K-part lanes, fixed order
+      v += dpp_f32<DPP_XOR2>(v);
+      if ((lane & 3) == 0) s_gu[(wave * MAXB + t) * 16 + r] = v;
     }
   }
   __syncthreads();
-  if ((int)threadIdx.x < B * 4) {
-    const int t = threadIdx.x >> 2, j = threadIdx.x & 3;
+  if ((int)threadIdx.x < B * 8) {
+    const int t = threadIdx.x >> 3, j = threadIdx.x & 7;
     float g = 0.0f, u = 0.0f;
 #pragma unroll
     for (int wv = 0; wv < 8; wv++) {
-      g += s_gu[(wv * MAXB + t) * 8 + j];
-      u += s_gu[(wv * MAXB + t) * 8 + 4 + j];
+      g += s_gu[(wv * MAXB + t) * 16 + j];
+      u += s_gu[(wv * MAXB + t) * 16 + 8 + j];
     }
-    reinterpret_cast<uint16_t*>(s_hp)[t * 4 + j] = f32_to_bf16(silu_f32(g) * u);
+    reinterpret_cast<uint16_t*>(s_hp)[t * 8 + j] = f32_to_bf16(silu_f32(g) * u);
   }
   __syncthreads();
   if ((int)threadIdx.x < B) {
-    const uint16_t* hh = reinterpret_cast<const uint16_t*>(s_hp) + threadIdx.x * 4;
-    s_hs[threadIdx.x] = (bf16_to_f32(hh[0]) + bf16_to_f32(hh[1])) + (bf16_to_f32(hh[2]) + bf16_to_f32(hh[3]));
+    const uint16_t* hh = reinterpret_cast<const uint16_t*>(s_hp) + threadIdx.x * 8;
+    float sum = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; j++) sum += bf16_to_f32(hh[j]);
+    s_hs[threadIdx.x] = sum;
   }
   __syncthreads();
   const size_t pbase = (size_t)B * L.k * rg;  // shared partials follow the routed ones (rg groups per slot)
@@ -299,7 +306,7 @@ __global__ __launch_bounds__(DA_THREADS) void k_dec_a(LayerDev L, const uint16_t
     if (r0 > 0) {
 #pragma unroll
       for (int i = 0; i < A_RPT; i++)
-        load_down_piece<SWT, 4>(L.sdn, nullptr, H, min(r0 + (int)threadIdx.x + DA_THREADS * i, H - 1), col0, dp[i]);
+        load_down_piece<SWT, 8>(L.sdn, nullptr, H, min(r0 + (int)threadIdx.x + DA_THREADS * i, H - 1), col0, dp[i]);
     }
 #pragma unroll
     for (int i = 0; i < A_RPT; i++) {
@@ -308,8 +315,8 @@ __global__ __launch_bounds__(DA_THREADS) void k_dec_a(LayerDev L, const uint16_t
 #pragma unroll
         for (int t = 0; t < MAXB; t++) {
           if (t < B) {
-            const float v = down_piece_dot<SWT, 4>(dp[i], 0, s_hp + 2 * t, s_hs[t]);
-            ws.part[(pbase + (size_t)t * (I >> 2) + p) * H + rw] = v;
+            const float v = down_piece_dot<SWT, 8>(dp[i], 0, s_hp + 4 * t, s_hs[t]);
+            ws.part[(pbase + (size_t)t * (I >> 3) + p) * H + rw] = v;
           }
         }
       }
@@ -692,7 +699,7 @@ __global__ __launch_bounds__(DB_THREADS) void k_dec_b(LayerDev L, const uint16_t
 
 // ---------------------------------------------------------------------------
 // Kernel C: y[t][r] = sum over token t's partials (routed slots in order,
-// their column groups in order, then the shared expert's 4-column groups)
+// their column groups in order, then the shared expert's 8-column groups)
 // ---------------------------------------------------------------------------
 constexpr int DC_BATCH = 24;  // partial loads in flight per thread
 
@@ -703,7 +710,7 @@ __global__ __launch_bounds__(DC_THREADS) void k_dec_c(const float* __restrict__ 
   const int rr = threadIdx.x % DC_ROWS, sp = threadIdx.x / DC_ROWS;
   const int r = blockIdx.x * DC_ROWS + rr;
   const int nr = k * rg;  // routed partials of this token (rg column groups per slot), then its shared-expert partials
-  const int ns = has_shared ? (I >> 2) : 0;
+  const int ns = has_shared ? (I >> 3) : 0;
   const size_t rbase = (size_t)t * nr;
   const size_t sbase = (size_t)B * nr + (size_t)t * ns;
   const int n = nr + ns;
@@ -755,8 +762,8 @@ static hipError_t launch_t(const LayerDev& L, const uint16_t* x, int B, uint16_t
   const int rg = I / gcol;
   {
     const int nRB = (E + 7) / 8;
-    const int nSB = (SWT == MOE_W_NONE) ? 0 : I / 4;
-    const size_t lds = (size_t)B * H * 2 + (size_t)(8 * MAXB * 8 + MAXB * 2 + MAXB) * 4;
+    const int nSB = (SWT == MOE_W_NONE) ? 0 : I / 8;
+    const size_t lds = (size_t)B * H * 2 + (size_t)(8 * MAXB * 16 + MAXB * 4 + MAXB) * 4;
     (void)launch_k(KC_DEC_ROUTER_SHARED, (k_dec_a<SW, MAXB>), dim3(nRB + nSB), dim3(DA_THREADS), lds, st, L, x, B, ws, nRB,
                    rg);
     hipError_t err = hipGetLastError();
