@@ -111,7 +111,7 @@ size_t carve_decode(const moe_layer* L, int B, uint8_t* base, moe::DecodeWs* ws)
     w.flags = reinterpret_cast<uint64_t*>(take(8 * moe::decode1_flag_words(L->n_experts, L->inter, L->top_k, has_s)));
     w.part_words = reinterpret_cast<uint64_t*>(take(8 * moe::decode1_part_words(L->hidden, L->inter, L->top_k, has_s)));
   } else {
-    w.part = reinterpret_cast<float*>(take((size_t)B * (k * (I / 16) + I / 4) * L->hidden * 4));
+    w.part = reinterpret_cast<float*>(take((size_t)B * (k * (I / 16) + I / 8) * L->hidden * 4));
     w.route = reinterpret_cast<int32_t*>(take((4 + 4 * 8 * 16) * 4));
   }
   // z and y of a stack layer run as separate kernels (moe_stack_decode_layer)

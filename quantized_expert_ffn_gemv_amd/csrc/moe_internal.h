@@ -55,7 +55,7 @@ struct LayerDev {
 struct DecodeWs {
   uint32_t* sync;  // counts and epoch of the one-kernel path (counts zero between calls)
   double* logits;  // three-kernel path: [B][E] fp64; one-kernel path: rotating slots of [E][2] tagged words
-  float* part;     // three-kernel path: [B*k*(I/16) + B*(I/4)][H] partial down products
+  float* part;     // three-kernel path: [B*k*(I/16) + B*(I/8)][H] partial down products
   uint64_t* flags; // one-kernel path: per-producer tagged flag words, rotating slots
   uint64_t* part_words;  // one-kernel path: [producers][H] tagged partial down products (fp32 bits)
   int32_t* route;        // three-kernel path: the batch's routing (count, idx, gates, unique experts, masks)
