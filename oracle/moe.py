@@ -15,8 +15,8 @@ What the layer computes, per token t with activation x (bf16 at the boundary):
 Sources. The pages fix the structure: each token uses 10 of 512 routed
 experts plus one always-on shared expert (Strata write-up, "The 30-Second
 Overview" table; explainer video, transcript at 2:01), and the outputs of a
-token's experts are summed into the one result (video, transcript at 3:36,
-"both plates land on the same ticket"). The pages give no formula for the
+token's experts are added together into that token's single result (video,
+transcript at 3:36). The pages give no formula for the
 router, the gates, the FFN or the quantisation; steps 2-5 follow the workload
 definition this build targets (softmax over router logits, then top-k with
 renormalised gates; SwiGLU FFN; signed 4-/3-bit codes in 32-element blocks
@@ -136,11 +136,15 @@ def softmax(l: np.ndarray) -> np.ndarray:
     return z / np.sum(z, axis=-1, keepdims=True)
 
 
-def select_topk(l_row: np.ndarray, k: int) -> np.ndarray:
-    """Indices of the k largest logits, ordered by (logit desc, index asc)."""
-    E = l_row.shape[0]
-    order = np.lexsort((np.arange(E), -l_row))
-    return order[:k].astype(np.int32)
+def select_topk(l: np.ndarray, k: int) -> np.ndarray:
+    """Indices of the k largest logits, ordered by (logit desc, index asc).
+
+    l: one token's logits [E], or a batch [T, E] (each row on its own)."""
+    l = np.asarray(l, np.float64)
+    E = l.shape[-1]
+    index = np.broadcast_to(np.arange(E), l.shape)
+    order = np.lexsort((index, -l), axis=-1)   # last key is the primary one
+    return order[..., :k].astype(np.int32)
 
 
 def route(layer, x_bits: np.ndarray):
@@ -150,13 +154,9 @@ def route(layer, x_bits: np.ndarray):
     x64 = bf16_bits_to_f64(x_bits)
     l = router_logits(layer, x64)
     p = softmax(l)
-    T, k = l.shape[0], layer.k
-    idx = np.empty((T, k), np.int32)
-    gates = np.empty((T, k), np.float64)
-    for t in range(T):
-        S = select_topk(l[t], k)
-        idx[t] = S
-        gates[t] = p[t, S] / np.sum(p[t, S])
+    idx = select_topk(l, layer.k)
+    pS = np.take_along_axis(p, idx.astype(np.int64), axis=1)
+    gates = pS / np.sum(pS, axis=1, keepdims=True)
     return idx, gates, l
 
 

@@ -2,14 +2,14 @@
 
 Routing is compared bit-exactly (indices in order), gates and outputs within
 the tolerances of tests/moe_testlib.py. Full-size workloads are checked on
-sampled tokens of the same launch configuration the benchmark times.
+every token, in the same launch configuration the benchmark times.
 """
 import numpy as np
 import pytest
 
 import oracle
 import synth
-from moe_testlib import check_gates, check_routing, check_y, from_dev_bits, log, to_dev
+from moe_testlib import check_gates, check_routing, check_y, from_dev_bits, log, routing_scale, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -54,12 +54,25 @@ def _prefill(m, L, x_bits):
     return from_dev_bits(y), idx.cpu().numpy(), g.cpu().numpy()
 
 
-def _check_all(host, x, y, idx, g, what):
-    y_ref, idx_ref, g_ref = oracle.moe_forward(host, x)
-    _, _, logits = oracle.route(host, x)
-    check_routing(idx, idx_ref, logits, what)
+def _check_all(host, x, y, idx, g, what, ref=None):  # noqa: C901
+    """Routing, gates and outputs of every token against the oracle (ref: a
+    precomputed (y, idx, gates, logits) of the same tokens)."""
+    if ref is None:
+        y_ref, idx_ref, g_ref = oracle.moe_forward(host, x)
+        _, _, logits = oracle.route(host, x)
+    else:
+        y_ref, idx_ref, g_ref, logits = ref
+    n = check_routing(idx, idx_ref, logits, what, scale=routing_scale(host, x))
+    if n:
+        log("  %s: %d tokens ordered differently within a near-tie" % (what, n))
     check_gates(g, g_ref, what)
     check_y(y, y_ref, what)
+
+
+def _oracle_ref(host, x):
+    y_ref, idx_ref, g_ref = oracle.moe_forward(host, x)
+    _, _, logits = oracle.route(host, x)
+    return y_ref, idx_ref, g_ref, logits
 
 
 # ----------------------------------------------------------------------------- tiny
@@ -177,17 +190,23 @@ def test_single_token_prefill_and_zero_input(moe):
 
 @pytest.fixture(scope="module")
 def decode_q4(moe):
-    host = synth.make_layer("decode_q4")
+    host = synth.make_layer("decode_q4", threads=16)
     return host, moe.DeviceLayer(host), synth.make_tokens("decode_q4")
 
 
-def test_decode_q4_sequence_sampled(moe, decode_q4):
-    # the benchmark's launch configuration: 256 consecutive batch-1 calls
+@pytest.fixture(scope="module")
+def decode_q4_ref(decode_q4):
+    host, _, x = decode_q4
+    log("oracle: 256 tokens of the Q4 decode layer")
+    return _oracle_ref(host, x)
+
+
+def test_decode_q4_sequence_all_tokens(moe, decode_q4, decode_q4_ref):
+    # the benchmark's launch configuration: 256 consecutive batch-1 calls, every token checked
     host, L, x = decode_q4
-    log("decode_q4: 256 sequential B=1 calls, 24 sampled tokens checked")
+    log("decode_q4: 256 sequential B=1 calls, all tokens checked")
     y, idx, g = _decode_calls(moe, L, x, 1)
-    sample = np.arange(0, 256, 11)
-    _check_all(host, x[sample], y[sample], idx[sample], g[sample], "decode_q4 B=1")
+    _check_all(host, x, y, idx, g, "decode_q4 B=1", ref=decode_q4_ref)
 
 
 @pytest.mark.parametrize("B", [3, 4, 5])
@@ -249,43 +268,38 @@ def test_stack_decode_layer_matches_separate_calls(moe, decode_q4, B):
 
 @pytest.fixture(scope="module")
 def decode_q3(moe):
-    host = synth.make_layer("decode_q3_zipf")
-    return host, moe.DeviceLayer(host), synth.make_tokens("decode_q3_zipf")
+    host = synth.make_layer("decode_q3_zipf", threads=16)
+    x = synth.make_tokens("decode_q3_zipf")
+    log("oracle: 256 tokens of the Q3 Zipf layer")
+    return host, moe.DeviceLayer(host), x, _oracle_ref(host, x)
 
 
-def test_decode_q3_zipf_b1_sampled(moe, decode_q3):
-    host, L, x = decode_q3
-    log("decode_q3_zipf: B=1 on 20 sampled tokens")
-    sample = np.arange(3, 256, 13)
-    y, idx, g = _decode_calls(moe, L, x[sample], 1)
-    _check_all(host, x[sample], y, idx, g, "decode_q3 B=1")
+def test_decode_q3_zipf_b1_all_tokens(moe, decode_q3):
+    host, L, x, ref = decode_q3
+    log("decode_q3_zipf: 256 B=1 calls, all tokens checked")
+    y, idx, g = _decode_calls(moe, L, x, 1)
+    _check_all(host, x, y, idx, g, "decode_q3 B=1", ref=ref)
 
 
-def test_decode_q3_zipf_b8(moe, decode_q3):
-    host, L, x = decode_q3
-    log("decode_q3_zipf: B=8, 32 calls, 4 calls checked")
+def test_decode_q3_zipf_b8_all_tokens(moe, decode_q3):
+    host, L, x, ref = decode_q3
+    log("decode_q3_zipf: B=8, 32 calls, all tokens checked")
     y, idx, g = _decode_calls(moe, L, x, 8)
-    sample = np.concatenate([np.arange(0, 8), np.arange(64, 72), np.arange(128, 136), np.arange(248, 256)])
-    _check_all(host, x[sample], y[sample], idx[sample], g[sample], "decode_q3 B=8")
+    _check_all(host, x, y, idx, g, "decode_q3 B=8", ref=ref)
 
 
 @pytest.fixture(scope="module")
 def prefill_q4(moe):
-    host = synth.make_layer("prefill_q4")
+    host = synth.make_layer("prefill_q4", threads=16)
     return host, moe.DeviceLayer(host), synth.make_tokens("prefill_q4")
 
 
-def test_prefill_q4_full_routing_sampled_outputs(moe, prefill_q4):
+@pytest.mark.timeout(600)
+def test_prefill_q4_all_tokens(moe, prefill_q4):
     host, L, x = prefill_q4
-    log("prefill_q4: T=4096, all routing checked, 48 sampled token outputs")
+    log("prefill_q4: T=4096, routing, gates and outputs of every token checked")
     y, idx, g = _prefill(moe, L, x)
-    idx_ref, g_ref, logits = oracle.route(host, x)
-    n = check_routing(idx, idx_ref, logits, "prefill_q4")
-    check_gates(g, g_ref, "prefill_q4")
-    log("  routing: %d tokens differ (ties only)" % n)
-    sample = np.arange(5, 4096, 85)
-    y_ref, _, _ = oracle.moe_forward(host, x[sample])
-    check_y(y[sample], y_ref, "prefill_q4")
+    _check_all(host, x, y, idx, g, "prefill_q4")
 
 
 def test_route_entry_counts(moe, prefill_q4):
@@ -298,7 +312,7 @@ def test_route_entry_counts(moe, prefill_q4):
     moe.moe_route(L, to_dev(x), idx, g, ws, expert_counts=counts)
     torch.cuda.synchronize()
     idx_ref, g_ref, logits = oracle.route(host, x)
-    check_routing(idx.cpu().numpy(), idx_ref, logits, "moe_route")
+    check_routing(idx.cpu().numpy(), idx_ref, logits, "moe_route", scale=routing_scale(host, x))
     assert np.array_equal(counts.cpu().numpy(), np.bincount(idx.cpu().numpy().ravel(), minlength=L.E))
 
 
@@ -329,11 +343,19 @@ def test_route_exact_and_near_ties(moe):
     moe.moe_route(L, to_dev(x), idx, g, ws)
     torch.cuda.synchronize()
     idx_ref, g_ref, logits = oracle.route(host, x)
-    check_routing(idx.cpu().numpy(), idx_ref, logits, "ties")
+    sc = routing_scale(host, x)
+    check_routing(idx.cpu().numpy(), idx_ref, logits, "ties", scale=sc)
     check_gates(g.cpu().numpy(), g_ref, "ties")
     got = idx.cpu().numpy()
     assert all(list(got[t][:4]) == [0, 1, 2, 3] for t in range(10, 20)), got[10:20, :4]
     assert all(list(got[t][:2]) == [5, 4] for t in range(20, 30)), got[20:30, :2]
+    # the same tokens through the decode top-k (one-kernel batch 1; batch 4)
+    for B in (1, 4):
+        yd, idd, gd = _decode_calls(moe, L, x, B)
+        check_routing(idd, idx_ref, logits, "ties decode B=%d" % B, scale=sc)
+        check_gates(gd, g_ref, "ties decode B=%d" % B)
+        assert all(list(idd[t][:4]) == [0, 1, 2, 3] for t in range(10, 20)), idd[10:20, :4]
+        assert all(list(idd[t][:2]) == [5, 4] for t in range(20, 30)), idd[20:30, :2]
 
 
 def test_prefill_matches_decode(moe, decode_q4):

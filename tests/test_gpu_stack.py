@@ -5,12 +5,13 @@ Zipf bias and shared expert per layer), all resident on the GPU (44 GB).
 Decode runs each layer as one moe_stack_decode_layer call (at batch 1 one
 kernel: norm, MoE and residual); prefill as the three separate calls.
 
-The check is teacher-forced, layer by layer, on sampled tokens: the oracle's
-MoE layer l consumes the GPU's own bf16 z_l, so a routing decision at one
-layer cannot make every later layer disagree. Per layer and token: routing
-bit-exact and in order, gates and y_l within the usual tolerances, z_l
-against the oracle's RMSNorm of the GPU's h_l within bf16 rounding, and
-h_{l+1} against h_l + y_l within bf16 rounding. A free-running oracle pass
+The check is teacher-forced, layer by layer: the oracle's MoE layer l
+consumes the GPU's own bf16 z_l, so a routing decision at one layer cannot
+make every later layer disagree. Routing and gates are checked for every
+token at every layer (512 decode tokens, 32768 prefill tokens). On sampled
+tokens, per layer, also: y_l within the usual tolerances, z_l against the
+oracle's RMSNorm of the GPU's h_l within bf16 rounding, and h_{l+1} against
+h_l + y_l within bf16 rounding. A free-running oracle pass
 (its own z, y, h rounded to bf16 like the stack) is reported for
 information only: a near-tie in routing anywhere flips it legitimately.
 """
@@ -19,7 +20,7 @@ import pytest
 
 import oracle
 import synth
-from moe_testlib import Y_MAX_REL, Y_MIN_COS, check_gates, check_routing, log, to_dev
+from moe_testlib import Y_MAX_REL, Y_MIN_COS, check_gates, check_routing, log, routing_scale, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -79,7 +80,7 @@ def _check_layers(host_layers, h_in, z, y, idx, g, h_out, what):
         assert np.abs(zf - z_ref).max() <= 2 ** -8 * np.abs(z_ref).max(), "%s layer %d rmsnorm" % (what, l)
         y_ref, idx_ref, g_ref = oracle.moe_forward(host, z[l], experts=CodesExperts(l))
         _, _, logits = oracle.route(host, z[l])
-        check_routing(idx[l], idx_ref, logits, "%s layer %d" % (what, l))
+        check_routing(idx[l], idx_ref, logits, "%s layer %d" % (what, l), scale=routing_scale(host, z[l]))
         check_gates(g[l], g_ref, "%s layer %d" % (what, l))
         yf = oracle.bf16_bits_to_f64(y[l])
         err = np.abs(yf - y_ref).max(axis=1) / np.abs(y_ref).max(axis=1)
@@ -141,26 +142,74 @@ def test_stack48_decode_teacher_forced(moe, stack):
     log("  free-running 48-layer stack, token 0: cosine(GPU, oracle) = %.6f (information)" % cos)
 
 
+def _check_layer_routing(host, z_bits, idx, g, what):
+    """Routing and gates of every token of one layer (teacher-forced on the GPU's z)."""
+    idx_ref, g_ref, logits = oracle.route(host, z_bits)
+    n = check_routing(idx, idx_ref, logits, what, scale=routing_scale(host, z_bits))
+    check_gates(g, g_ref, what)
+    return n
+
+
+@pytest.mark.timeout(900)
+def test_stack48_decode_routing_all_tokens(moe, stack):
+    """All 512 decode tokens, batch 1, through the 48 layers (one
+    moe_stack_decode_layer call per layer and token, as the benchmark runs
+    them); the routing and gates of every token at every layer against the
+    oracle's routing of the GPU's own z_l."""
+    layers, hosts = stack
+    x = synth.make_tokens(NAME)
+    T = x.shape[0]
+    nl, H, k = len(layers), layers[0].H, layers[0].k
+    log("stack48 decode: %d tokens x %d layers, routing of every token checked" % (T, nl))
+    ws = moe.make_workspace(layers[0], 1, 0)
+    Z = torch.empty((nl, T, H), dtype=torch.int16, device="cuda")
+    IDX = torch.empty((nl, T, k), dtype=torch.int32, device="cuda")
+    G = torch.empty((nl, T, k), dtype=torch.float32, device="cuda")
+    xd = to_dev(x)
+    for t in range(T):
+        h = xd[t:t + 1].clone()
+        for l, L in enumerate(layers):
+            moe.moe_stack_decode_layer(L, h, ws, EPS, Z[l, t:t + 1], None, IDX[l, t:t + 1], G[l, t:t + 1])
+    torch.cuda.synchronize()
+    moe.moe_workspace_check(ws)
+    Zh, Ih, Gh = Z.cpu().numpy().view(np.uint16), IDX.cpu().numpy(), G.cpu().numpy()
+    near = 0
+    for l in range(nl):
+        near += _check_layer_routing(hosts[l], Zh[l], Ih[l], Gh[l], "stack48 decode layer %d" % l)
+    log("  %d token-layers checked, %d ordered differently within a near-tie" % (T * nl, near))
+
+
+@pytest.mark.timeout(900)
 def test_stack48_prefill_teacher_forced(moe, stack):
     layers, hosts = stack
     T = synth.WORKLOADS[NAME]["prefill_tokens"]
     x = synth.make_prefill_tokens(NAME)
     H, k = layers[0].H, layers[0].k
     sample = torch.tensor([17, 20000, T - 1], dtype=torch.long, device="cuda")
-    log("stack48 prefill: T=%d in one pass, 48 layers, tokens %s checked at every layer" % (T, sample.tolist()))
+    log("stack48 prefill: T=%d in one pass, 48 layers: routing of every token, outputs of tokens %s, at every layer"
+        % (T, sample.tolist()))
     ws = moe.make_workspace(layers[0], T, 1)
     buf = moe.StackBuffers(T, H, k)
     h = to_dev(x)
     h0 = h.index_select(0, sample)
     per = {n: [] for n in ("h_out", "z", "y", "idx", "g")}
 
+    near = [0]
+
     def grab(l, b):  # after layer l's residual add
         per["h_out"].append(h.index_select(0, sample)); per["z"].append(b.z.index_select(0, sample))
         per["y"].append(b.y.index_select(0, sample)); per["idx"].append(b.idx.index_select(0, sample))
         per["g"].append(b.gate.index_select(0, sample))
+        # every token's routing at this layer, on the GPU's own z
+        zl = b.z.cpu().numpy().view(np.uint16)
+        near[0] += _check_layer_routing(hosts[l], zl, b.idx.cpu().numpy(), b.gate.cpu().numpy(),
+                                        "stack48 prefill layer %d" % l)
+        if l % 12 == 0:
+            log("  stack48 prefill layer %d: routing of %d tokens checked" % (l, zl.shape[0]))
 
     moe.stack_forward(layers, h, ws, False, buf, EPS, each_layer=grab)
     torch.cuda.synchronize()
+    log("  %d token-layers routed as the oracle, %d ordered differently within a near-tie" % (T * len(layers), near[0]))
     per["h_in"] = [h0] + per["h_out"][:-1]
     arr = {n: torch.stack(v).cpu().numpy() for n, v in per.items()}
     u16 = lambda a: a.view(np.uint16)

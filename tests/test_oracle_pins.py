@@ -325,3 +325,37 @@ def test_rmsnorm_closed_forms():
     # scale invariance for eps = 0
     r = np.random.default_rng(3).normal(size=(4, 64))
     assert np.allclose(oracle.rmsnorm(7 * r, 0.0), oracle.rmsnorm(r, 0.0), rtol=1e-14)
+
+
+@pytest.mark.parametrize("wtype", ["f32", "bf16"])
+def test_single_dense_expert_is_torch_swiglu(wtype):
+    # E = 1, k = 1, no shared expert, fp32 or bf16 expert weights: the layer is
+    # a plain SwiGLU FFN. G, U and D come straight from the generated arrays
+    # (widened by torch, not by the oracle), so a swapped gate/up or a wrong
+    # widening in the oracle's dense-weight branch fails here.
+    L = _tiny_q(E=1, k=1, H=96, I=64, wtype=wtype, shared=None)
+    x = _tokens(7, 96)
+    y, idx, gates = oracle.moe_forward(L, x)
+    assert np.all(idx == 0) and np.all(gates == 1.0)
+    if wtype == "f32":
+        conv = lambda a: torch.from_numpy(np.ascontiguousarray(a)).double()
+    else:
+        conv = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).double()
+    G, U, D = conv(L.gate_f[0]), conv(L.up_f[0]), conv(L.down_f[0])
+    xt = torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).double()
+    ref = torch.nn.functional.linear(torch.nn.functional.silu(torch.nn.functional.linear(xt, G)) *
+                                     torch.nn.functional.linear(xt, U), D)
+    assert np.allclose(y, ref.numpy(), rtol=1e-12, atol=1e-13)
+    # and the gate and up projections are not interchangeable
+    swapped = torch.nn.functional.linear(torch.nn.functional.silu(torch.nn.functional.linear(xt, U)) *
+                                         torch.nn.functional.linear(xt, G), D)
+    assert not np.allclose(y, swapped.numpy(), rtol=1e-6, atol=1e-8)
+
+
+def test_batched_selection_equals_per_row_selection():
+    # the oracle selects all rows at once; each row must equal the brute-force count
+    rng = np.random.default_rng(9)
+    l = np.round(rng.normal(size=(40, 16)) * 2) / 2   # many exact ties
+    got = oracle.select_topk(l, 5)
+    for t in range(40):
+        assert got[t].tolist() == _brute_topk(l[t], 5)
