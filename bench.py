@@ -88,7 +88,20 @@ def run_decode(moe, torch, L, x_bits, steps, warmup, B=1):
         g.replay()
     torch.cuda.synchronize()
     graph_s = (time.perf_counter() - t0) / steps
+    # every call of the timed replays must have completed its device-side
+    # waits: a wait that ran out means invalid results, and the run fails
+    moe.moe_workspace_check(ws)
     return eager_s, graph_s, g
+
+
+def expert_usage(idx, E):
+    """Expert-usage telemetry of one layer's routing (idx [T, k]): experts
+    used, and the share of all selections taken by the hottest 20% of the
+    experts."""
+    counts = np.bincount(np.asarray(idx).ravel(), minlength=E)
+    hot = np.sort(counts)[::-1][: max(1, int(round(0.2 * E)))]
+    return {"experts_used": int(np.count_nonzero(counts)),
+            "hottest20_share": round(float(hot.sum()) / float(counts.sum()), 4)}
 
 
 def decode_batches(moe, torch, L, x, steps, warmup, batches):
@@ -113,6 +126,7 @@ def decode_batches(moe, torch, L, x, steps, warmup, batches):
         for t in range(0, T, B):
             moe.moe_forward_decode(L, xd[t:t + B], yy[t:t + B], ws, topk_idx=idx[t:t + B])
         torch.cuda.synchronize()
+        moe.moe_workspace_check(ws)
         ih = idx.cpu().numpy()
         uniq = [len(np.unique(ih[t:t + B])) for t in range(0, T, B)]
         calls = len(uniq)
@@ -124,6 +138,7 @@ def decode_batches(moe, torch, L, x, steps, warmup, batches):
             "weight_bytes_per_call": round(bytes_total / calls),
             "effective_GBps": round(bytes_total / graph_s / 1e9, 1),
             "frac_of_hbm": round(bytes_total / graph_s / 1e9 / HBM_PEAK_GBS, 4),
+            "expert_usage": expert_usage(ih, L.E),
         }
     return out
 
@@ -202,22 +217,78 @@ def committed_traffic():
         return None
 
 
-def cpu_baseline(host, x_bits, budget_s=12.0, max_tokens=256):
-    import oracle
+def cpu_model():
     try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:  # pragma: no cover
-        cores = os.cpu_count() or 1
-    n = 0
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(host, x_bits, per_token_bytes, budget_s=24.0, max_tokens=256):
+    """The fp64 oracle on the host cores, on the first tokens of the headline
+    workload (one oracle call per batch-1 token): about half the budget with
+    numpy's BLAS threads as configured, half with one thread."""
+    import oracle
+    from threadpoolctl import threadpool_info, threadpool_limits
+
+    def timed(limit_s):
+        n = 0
+        t0 = time.perf_counter()
+        while n < max_tokens and time.perf_counter() - t0 < limit_s:
+            oracle.moe_forward(host, x_bits[n:n + 1])
+            n += 1
+        return n, time.perf_counter() - t0
+
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    n, el = timed(budget_s / 2)
+    with threadpool_limits(limits=1):
+        n1, el1 = timed(budget_s / 2)
+    tps, tps1 = n / el, n1 / el1
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        affinity = os.cpu_count() or 1
+    return dict(value=round(tps, 3), unit="tokens/s", cores=int(threads), kind="oracle",
+                value_1thread=round(tps1, 3),
+                effective_GBps=round(per_token_bytes * tps / 1e9, 4),
+                effective_GBps_1thread=round(per_token_bytes * tps1 / 1e9, 4),
+                cpu_model=cpu_model(), host_cpus=os.cpu_count(), cpus_in_affinity=affinity,
+                sample="first %d (then %d single-thread) of the 256 batch-1 decode tokens, one call of the "
+                       "fp64 numpy oracle per token; %.1f s + %.1f s; BLAS threads %d; GB/s on the same "
+                       "%d expert-weight bytes per token as the GPU figure"
+                       % (n, n1, el, el1, threads, per_token_bytes))
+
+
+def run_tiny(moe, torch, synth, steps, warmup):
+    """The tiny layer (8 experts, top-2 + shared, hidden 64, fp32 weights; 16
+    tokens): batch-1 decode calls replayed as one graph, and one prefill of
+    the 16 tokens. Throughput only: at this size the launch sets the time."""
+    host = synth.make_layer("tiny")
+    x = synth.make_tokens("tiny")
+    L = moe.DeviceLayer(host)
+    _, graph_s, g = run_decode(moe, torch, L, x, steps, warmup)
+    del g
+    dev = torch.device("cuda")
+    xd = torch.from_numpy(x.view(np.int16)).to(dev)
+    yd = torch.empty_like(xd)
+    wsp = moe.make_workspace(L, x.shape[0], 1)
+    moe.moe_forward_prefill(L, xd, yd, wsp)
+    torch.cuda.synchronize()
+    reps = 50
     t0 = time.perf_counter()
-    while n < max_tokens and time.perf_counter() - t0 < budget_s:
-        oracle.moe_forward(host, x_bits[n:n + 1])   # one batch-1 decode call
-        n += 1
-    el = time.perf_counter() - t0
-    return dict(value=round(n / el, 3), unit="tokens/s", cores=int(cores), kind="oracle",
-                sample="first %d of the 256 batch-1 decode tokens, one oracle call per token (fp64 numpy), "
-                       "%.1f s" % (n, el))
+    for _ in range(reps):
+        moe.moe_forward_prefill(L, xd, yd, wsp)
+    torch.cuda.synchronize()
+    pf_s = (time.perf_counter() - t0) / reps
+    T = x.shape[0]
+    return {"workload": "tiny MoE layer: 8 experts, top-2 + 1 shared, hidden 64, intermediate 32, fp32 weights; "
+                        "16 tokens", "decode_tokens_per_s": round(T / graph_s, 1),
+            "decode_us_per_token": round(graph_s / T * 1e6, 3), "prefill_tokens_per_s": round(T / pf_s, 1),
+            "prefill_us": round(pf_s * 1e6, 2)}
 
 
 COPY_BYTES = 2 << 30   # 8x the 256 MB last-level cache: the copy's reads come from HBM
@@ -314,6 +385,17 @@ def run_stack(moe, torch, synth, steps):
     gu, dn, sgu, sdn = decode_expert_bytes(L0)
     per_tok = len(layers) * (L0.k * (gu + dn) + sgu + sdn)
     del g
+    # expert-usage telemetry (untimed): every token's routing at every layer
+    nl, E = len(layers), L0.E
+    IDX = torch.empty((nl, T, k), dtype=torch.int32, device=dev)
+    for t in range(T):
+        hh = xd[t:t + 1].clone()
+        for l, L in enumerate(layers):
+            moe.moe_stack_decode_layer(L, hh, ws, 1e-6, None, None, IDX[l, t:t + 1], None)
+    torch.cuda.synchronize()
+    moe.moe_workspace_check(ws)
+    dec_usage = [expert_usage(a, E) for a in IDX.cpu().numpy()]
+    del IDX
     # prefill: all tokens, one pass through the 48 layers
     xp = synth.make_prefill_tokens(name)
     Tp = xp.shape[0]
@@ -322,12 +404,19 @@ def run_stack(moe, torch, synth, steps):
     wsp = moe.make_workspace(L0, Tp, 1)
     bufp = moe.StackBuffers(Tp, H, k)
 
-    def prefill():
+    def prefill(each_layer=None):
         hp.copy_(xpd)
-        moe.stack_forward(layers, hp, wsp, False, bufp)
+        moe.stack_forward(layers, hp, wsp, False, bufp, each_layer=each_layer)
 
-    prefill()
+    pf_counts = []
+    prefill(lambda l, b: pf_counts.append(torch.bincount(b.idx.view(-1).long(), minlength=E)))
     torch.cuda.synchronize()
+    pf_usage = []
+    for c in pf_counts:
+        c = c.cpu().numpy()
+        hot = np.sort(c)[::-1][: max(1, int(round(0.2 * E)))]
+        pf_usage.append({"experts_used": int(np.count_nonzero(c)),
+                         "hottest20_share": round(float(hot.sum()) / float(c.sum()), 4)})
     t0 = time.perf_counter()
     prefill()
     torch.cuda.synchronize()
@@ -345,6 +434,12 @@ def run_stack(moe, torch, synth, steps):
         "prefill_ms": round(pf_s * 1e3, 2),
         "prefill_tokens_per_s": round(Tp / pf_s, 1),
         "prefill_expert_TFLOPs": round(flops / pf_s / 1e12, 1),
+        "expert_usage_per_layer": {
+            "decode": {"experts_used": [u["experts_used"] for u in dec_usage],
+                       "hottest20_share": [u["hottest20_share"] for u in dec_usage]},
+            "prefill": {"experts_used": [u["experts_used"] for u in pf_usage],
+                        "hottest20_share": [u["hottest20_share"] for u in pf_usage]},
+        },
     }
 
 
@@ -392,11 +487,15 @@ def main():
             moe.moe_forward_decode(L, xd[t:t + 1], yd[t:t + 1], ws)
 
     kt = kernel_times(moe, torch, one_seq, reps=2)
+    moe.moe_workspace_check(ws)
     gu, dn, sgu, sdn = decode_expert_bytes(L)
     router_bytes = L.E * L.H * 4
+    # algorithmic bytes per launch: the expert weights the token needs (its k
+    # routed experts and the shared expert); the router's 4 MiB are read in
+    # the same launch and are counted in its time, not in its bytes
     kbytes = {
-        "dec_fused": router_bytes + sgu + sdn + L.k * (gu + dn),   # the one batch-1 kernel: all weight bytes
-        "dec_router_shared": router_bytes + sgu + sdn,
+        "dec_fused": sgu + sdn + L.k * (gu + dn),
+        "dec_router_shared": sgu + sdn,
         "dec_routed": L.k * (gu + dn),
     }
     dom = max(kbytes, key=lambda k: kt.get(k, (0, 0))[1])
@@ -447,10 +546,18 @@ def main():
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": committed_traffic() if dom == "dec_fused" else None,
             "algo_bytes_per_launch": kbytes[dom],
+            "router_bytes_per_launch": router_bytes if dom == "dec_fused" else 0,
+            "achieved_incl_router": round((kbytes[dom] + (router_bytes if dom == "dec_fused" else 0))
+                                          / (avg_ms * 1e-3) / 1e9, 1),
             "avg_launch_us": round(avg_ms * 1e3, 3),
         },
     }
     del g
+
+    # ---------------------------------------------------------------- tiny layer (secondary, no roofline claim)
+    log("tiny layer ...")
+    result["tiny"] = run_tiny(moe, torch, synth, args.steps, args.warmup)
+    log("tiny:", json.dumps(result["tiny"]))
 
     # ---------------------------------------------------------------- speculative-verify batches (secondary)
     if not args.no_prefill:
@@ -511,7 +618,7 @@ def main():
     # ---------------------------------------------------------------- CPU oracle
     if not args.no_cpu:
         log("cpu oracle baseline ...")
-        result["cpu_baseline"] = cpu_baseline(host, x)
+        result["cpu_baseline"] = cpu_baseline(host, x, per_token_bytes)
     print(json.dumps(result), flush=True)
 
 

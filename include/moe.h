@@ -241,6 +241,14 @@ const char *moe_status_string(int32_t status);
 /* Description of the last failure on this thread ("" if none). */
 const char *moe_last_error(void);
 
+/* Bound of every device-side wait of the one-kernel batch-1 decode, in ticks
+ * of the GPU's 100 MHz wall clock, for the calls enqueued after this one
+ * (process-wide; 0 restores the default of 2^25 ticks, about 0.34 s). A wait
+ * that runs out lets its workgroup finish with invalid results and sets the
+ * report read by moe_workspace_check. For tests of that report: a tiny bound
+ * makes waits give up while their producers are still running. */
+moe_status moe_debug_set_wait_limit(uint64_t ticks);
+
 /* Optional per-kernel timer: when enabled, every kernel the library
  * launches carries a start and a stop HIP event in its own dispatch on its
  * stream (hipExtLaunchKernel), so each interval is that kernel's execution.

@@ -108,8 +108,9 @@ size_t carve_decode(const moe_layer* L, int B, uint8_t* base, moe::DecodeWs* ws)
   // logits: [B][E] fp64 (four kernels) or rotating slots of per-XCD-group [E] x 16 B tagged words (one kernel)
   w.logits = reinterpret_cast<double*>(take(one_kernel ? 8 * moe::decode1_logit_words((int)E) : (size_t)E * 64));
   if (one_kernel) {
-    w.flags = reinterpret_cast<uint64_t*>(take(8 * moe::decode1_flag_words(L->n_experts, L->inter, L->top_k, has_s)));
     w.part_words = reinterpret_cast<uint64_t*>(take(8 * moe::decode1_part_words(L->hidden, L->inter, L->top_k, has_s)));
+    w.xsum_words = reinterpret_cast<uint64_t*>(take(8 * moe::decode1_xsum_words(L->hidden)));
+    w.ctr = reinterpret_cast<uint32_t*>(take(4 * moe::decode1_counter_words()));
   } else {
     w.part = reinterpret_cast<float*>(take((size_t)B * (k * (I / 16) + I / 8) * L->hidden * 4));
     w.route = reinterpret_cast<int32_t*>(take((4 + 4 * 8 * 16) * 4));
@@ -500,6 +501,11 @@ const char* moe_status_string(int32_t status) {
 }
 
 const char* moe_last_error(void) { return g_err.c_str(); }
+
+moe_status moe_debug_set_wait_limit(uint64_t ticks) {
+  moe::decode1_set_wait_ticks(ticks);
+  return ok();
+}
 
 int32_t moe_kernel_class_count(void) { return moe::KC_COUNT; }
 

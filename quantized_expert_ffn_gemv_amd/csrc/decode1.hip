@@ -1,59 +1,71 @@
 // Batch-1 decode of one MoE layer as a single kernel.
 //
-// Workgroups take roles by index (nA = max(nR, nSG) first workgroups, then
-// the routed ones, then extra reducers if needed; at most one workgroup per
-// CU at the shapes of interest, so no role shares a CU's VALUs with another):
+// 256 workgroups of 1024 threads, one per CU, all resident at once.
+// Workgroups are dealt round-robin over the 8 XCDs, so the workgroups b
+// with the same b % 8 ("XCD group") share an XCD and its L2 (the first
+// XCD of the deal varies from launch to launch). The XCD groups start one
+// after another (the first about 2.3 us before the last at this size; the
+// workgroups of one group start together), so roles go by start rank
+// r(b) = (b % 8) * 32 + b / 8, the work the routing waits for first:
 //
-//   [0, nA)        b < nR: router, 8 expert rows each (two waves a row),
-//                  fp64 logits (an fp32 weight times a bf16 activation is
-//                  exact in fp64); then
-//                  b < nSG: shared expert, 8 intermediates each (16 gate/up
-//                  rows), gate/up GEMV + SwiGLU -> h (bf16, in LDS), then
-//                  those 8 columns of the shared down matrix times h: a
-//                  partial y over all H rows. The shared bytes stream while
-//                  the routed workgroups wait for the logits and select.
-//   [nA, +nRG)     routed experts: (slot, 32 intermediates) each; ordered
-//                  top-k from the logits, then fused dequantise-GEMV of the
-//                  64 gate/up rows + SwiGLU -> h (bf16, in LDS), then the
-//                  matching 32-column block of the expert's down matrix
-//                  (loaded with the gate/up rows) times h, scaled by the
-//                  slot's gate: a partial y over all H rows. waits: logits
-//   reducers       F_RD output rows each: y = the sum of the partials of
-//                  all shared and routed roles in a fixed order. Reducers
-//                  run on the last nD workgroups (routed ones after their
-//                  own role; extra workgroups when nD > nRG).
-//                                                waits: every partial
+//   ranks [0, nRW)         router: rows 8r .. 8r+7 (two waves a row), fp64
+//                          logits (an fp32 weight times a bf16 activation is
+//                          exact in fp64).
+//   ranks [0, nRG)         routed (after the router rows where both fall on
+//                          one workgroup): (slot, 32 intermediates) each;
+//                          ordered top-k from the logits, fused
+//                          dequantise-GEMV of the 64 gate/up rows + SwiGLU ->
+//                          h (bf16, in LDS), then the matching 32-column
+//                          block of the expert's down matrix (loaded with
+//                          the gate/up rows) times h, scaled by the slot's
+//                          gate: a partial y over all H rows.
+//   ranks [nRG, +nSG)      shared expert, 8 intermediates each: 16 gate/up
+//                          rows, SwiGLU -> h, then those 8 columns of the
+//                          shared down matrix times h: a partial y over all
+//                          H rows. These start last and are needed last.
 //
 // The down product is split along the intermediate dimension (split-K), so
-// h never leaves the workgroup that made it and the down weights stream
-// together with the gate/up weights; the only hand-off after the top-k is
-// the partials, read by the reducers.
+// h never leaves the workgroup that made it and the down weights stream in
+// the same window as the gate/up weights. The partials are then summed in
+// two levels:
 //
-// Progress: the routed workgroups wait only on the router roles, which
-// never wait, and the shared roles never wait, so every partial gets
-// written once every workgroup is resident; a reducer waits on producers
-// dispatched after it, so the path is taken only when the whole grid fits
-// on the chip at once (one workgroup per CU).
+//   XCD level   every workgroup of XCD group x sums, for H/32 rows, the
+//               partials of the producers of its own group, which sit in its
+//               XCD's L2 (a group that is split over XCDs would show up as a
+//               wait that runs out):
+//               producers store them with plain stores and readers load
+//               them with L1-missing agent-scope loads, served by that L2,
+//               so this hand-off stays inside the XCD (about 0.25 us, no
+//               HBM or fabric traffic).
+//               The sum goes out as one tagged word per row (agent scope).
+//   final       every workgroup sums, for H/256 rows, the 8 XCD sums in XCD
+//               order and writes y (a stack layer adds the residual).
 //
-// Hand-off without cache flushes. Every value one workgroup passes to
-// another (logits, partial down products) travels in a 64-bit word whose
-// high half is a tag that is new for every call (the call's epoch + 1),
-// written and read with agent-scope relaxed atomics: each word is
-// single-copy atomic and coherent across the chip's L2 slices on its own,
-// and a reader uses a word only once its tag is current, so no
-// release/acquire fence (an L2 write-back or invalidate per workgroup) is
-// needed. Each router role also writes one tagged flag word once its
-// logits are issued; a routed workgroup polls those flags (one wave, one
-// word per lane) and then reads and checks the logits; reducers poll the
-// partial words directly. Flags are plain stores, one 128-byte line each:
-// a shared counter bumped by hundreds of producers serialises its atomics
-// at the memory side, and lines polled by hundreds of workgroups serve them
-// one after another (both measured to add microseconds). Every spin is bounded;
-// one that runs out sets an error bit in the workspace and lets the
-// workgroup finish, so the kernel always ends. The last workgroup to finish
-// (a per-XCD count, then a count of the XCD groups) resets the counts and
-// advances the epoch, so the workspace is ready for the next call (and for
-// graph replay) without a memset.
+// Hand-off without cache flushes. Every value passed between workgroups is
+// a 64-bit word whose high half is a tag that is new for every call, so a
+// reader uses a word only once its tag is current and no release/acquire
+// fence (an L2 write-back or invalidate per workgroup) is needed: words that
+// cross XCDs are stored and loaded with agent-scope relaxed atomics
+// (coherent across the XCDs' L2s word by word), words that stay inside an
+// XCD are stored with plain stores into that XCD's L2 and read there. The
+// router's logits are written once per XCD group (copy r for the workgroups
+// with b % 8 == r), so each line has a few readers instead of all of them.
+// Every spin is bounded; one that runs out sets an error bit in the
+// workspace (1: router counts, 2: logits, 4: XCD sums' inputs, 8: final
+// sums' inputs) and lets the workgroup finish, so the kernel always ends.
+//
+// The tag is the call count each workgroup keeps for itself: workgroup b
+// reads its own counter at the start and writes it back incremented at the
+// end. Every call runs every workgroup once, so the 256 counters move in
+// lockstep and all workgroups derive the same tag, with no atomic and no
+// "last one out" count (256 workgroups finishing together serialised on one
+// counter for about 1.6 us). The workspace is ready for the next call (and
+// for graph replay) without a memset.
+//
+// Progress: routed units wait only for the routers (router rows never wait),
+// XCD sums only for producers, final sums only for XCD sums, so every value
+// gets written once every workgroup is resident; the path is taken only when
+// the grid fits the chip at one workgroup per CU.
 //
 // No float atomics: each value has one writer and every sum has a fixed
 // order, so results are bitwise reproducible.
@@ -68,29 +80,41 @@ namespace moe {
 // through LDS and dependency latencies: the same work took 1.76x as long).
 constexpr int F_THREADS = 1024;
 constexpr int F_WAVES = F_THREADS / 64;
+constexpr int F_NW = 256;                       // workgroups (one per CU)
+constexpr int F_NX = 8;                         // XCDs: workgroup b runs on XCD b % 8
+constexpr int F_PX = F_NW / F_NX;               // workgroups per XCD
 constexpr int F_RPT = 2;                        // down rows per thread (H <= F_RPT * F_THREADS)
 constexpr int F_HMAX = F_RPT * F_THREADS;       // largest H of this path (LDS arrays are sized for it)
 constexpr int F_RCPL = 4;                       // router float4 chunks per lane and batch
 constexpr uint64_t F_WAIT_TICKS = 1ull << 25;   // ~0.34 s of the 100 MHz wall clock
 
-// Workspace sync area (uint32 words; every count in its own 128-byte line).
-// The epoch has one replica per XCD group (workgroups b with b % 8 == r), so
-// the readers of one group share a line; one finish count for the grid.
+// Workspace sync area (uint32 words): the error bits in a line of their own,
+// then one call counter per workgroup (8 bytes apart).
 constexpr int SY_LINE = 32;                                   // words per line
-constexpr int SY_NREP = 8;                                    // replicas (XCD groups)
-constexpr int SY_EPOCH = 1 * SY_LINE;                         // + r * SY_LINE
-constexpr int SY_DONE = (1 + SY_NREP) * SY_LINE;
+constexpr int SY_NREP = F_NX;                                 // copies of the logits (XCD groups)
 constexpr int SY_ERR = 0;
-constexpr int SY_WORDS = (2 + SY_NREP) * SY_LINE;             // 1280 bytes
+constexpr int SY_COUNT = SY_LINE;                             // + 2 b
+constexpr int SY_WORDS = SY_COUNT + 2 * F_NW;                 // 2176 bytes
 static_assert(SY_WORDS * 4 <= 4096, "sync area");
-constexpr int F_SLOTS = 4;  // logits and flag buffers rotate over this many calls
+constexpr int F_SLOTS = 4;  // logit buffers and router counters rotate over this many calls
+constexpr int CT_STRIDE = 32;  // uint32 words between router counters (one 128-byte line each)
 
 struct FusedGeo {
-  int nR, nSG, nRG;  // router, shared, routed roles
-  int nA;            // workgroups [0, nA) take the router role (b < nR), then the shared role (b < nSG)
-  int nD;            // reducers: reducer d < nA runs on workgroup d after its first roles,
-                     // the rest on extra workgroups after the routed ones
+  int nRW;   // router workgroups (8 rows each): start ranks [0, nRW)
+  int nRG;   // routed units (slot, 32 intermediates): workgroups [0, nRG)
+  int sg0;   // shared units (8 intermediates each): workgroups [sg0, sg0 + nSG), sg0 = nRG rounded up to 8
+  int nSG;
+  int xmask; // XCD groups that hold at least one producer (bit x)
+  int rcount[F_NX];  // router workgroups per XCD group
+  uint64_t wait_ticks;  // bound of every device-side wait
 };
+__device__ __forceinline__ int start_rank(int b) { return (b % F_NX) * F_PX + b / F_NX; }
+// producer index of workgroup b: shared units first, then routed units; -1 for none
+__device__ __forceinline__ int producer_of(int b, const FusedGeo& G) {
+  if (b < G.nRG) return G.nSG + b;
+  if (b >= G.sg0 && b < G.sg0 + G.nSG) return b - G.sg0;
+  return -1;
+}
 
 // ---------------------------------------------------------------------------
 // Cross-workgroup hand-off
@@ -101,6 +125,15 @@ __device__ __forceinline__ uint64_t ld_word_coherent(const uint64_t* p) {
 __device__ __forceinline__ void st_word(uint64_t* p, uint32_t payload, uint32_t tag) {
   __hip_atomic_store(p, ((uint64_t)tag << 32) | payload, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// Words that stay inside one XCD: a plain 8-byte store (through the
+// write-through L1 into the XCD's L2, where it stays), read with the
+// agent-scope load (sc1: misses the reader's L1 and is served by the L2
+// that holds the line). Measured on one XCD: seen ~250 ns after the store,
+// against ~450 ns when the store also goes out at agent scope. (An sc0 load
+// is not enough: a poll keeps hitting the stale line in the reader's L1.)
+__device__ __forceinline__ void st_word_xcd(uint64_t* p, uint32_t payload, uint32_t tag) {
+  *p = ((uint64_t)tag << 32) | payload;
+}
 __device__ __forceinline__ uint32_t ld_u32(const uint32_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -108,51 +141,13 @@ __device__ __forceinline__ void flag_error(uint32_t* sync, uint32_t bit) {
   __hip_atomic_fetch_or(sync + SY_ERR, bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ int my_rep() { return blockIdx.x & (SY_NREP - 1); }
-
-// The workgroup's flag: written by one thread once every thread's tagged
-// stores are issued (the flag may become visible before them; readers
-// check the values' tags). Each flag has a 128-byte line of its own: with
-// hundreds of workgroups polling, flags packed into a few lines made every
-// poll queue behind the others at those lines (a hand-off took ~2 us
-// instead of ~0.85 us, measured).
-constexpr int F_FLAG_STRIDE = 16;  // uint64 words between flags
-__device__ __forceinline__ void raise_flag(uint64_t* flags, int i, uint32_t tag) {
-  __syncthreads();
-  if (threadIdx.x == 0) st_word(flags + (size_t)F_FLAG_STRIDE * i, 0u, tag);
-}
-
-// Bounded wait until at least `need` of flags 0 .. n-1 carry the current tag
-// (need <= n <= 64): wave 0 polls, one flag per lane per pass; the whole
-// workgroup leaves together. Callers that pass need < n then read the
-// values with per-word tag checks (settle), so the loads of the last
-// producers' values overlap their arrival instead of following it.
-__device__ __forceinline__ void wait_flags(const uint64_t* flags, int n, int need, uint32_t tag, uint32_t* sync) {
-  if (threadIdx.x < 64) {
-    const int lane = threadIdx.x;
-    const uint64_t t0 = wall_clock64();
-    int it = 0;
-    while (true) {
-      const uint64_t v = ld_word_coherent(flags + (size_t)F_FLAG_STRIDE * min(lane, n - 1));
-      const int have = __popcll(__builtin_amdgcn_ballot_w64((lane < n) && (uint32_t)(v >> 32) == tag));
-      if (have >= need) break;
-      __builtin_amdgcn_s_sleep(1);
-      if ((++it & 15) == 0 && wall_clock64() - t0 > F_WAIT_TICKS) {
-        if (lane == 0) flag_error(sync, 1u);
-        break;
-      }
-    }
-  }
-  __syncthreads();
-}
-
-// how many producer flags a consumer waits for before it reads the values
-__device__ __forceinline__ int flags_needed(int n) { return n - n / 8; }
+__device__ __forceinline__ bool tag_ok(uint64_t w, uint32_t tag) { return (uint32_t)(w >> 32) == tag; }
 
 // A pair of words written together and loaded once: while either tag is
-// not current (the producer's stores are still on their way), reload both
+// not current (the producer has not stored them yet), reload both
 // (bounded).
 __device__ __forceinline__ void settle2(const uint64_t* p0, const uint64_t* p1, uint64_t& w0, uint64_t& w1, uint32_t tag,
-                                        uint32_t* sync) {
+                                        uint32_t* sync, uint64_t ticks) {
   if (((uint32_t)(w0 >> 32) != tag) | ((uint32_t)(w1 >> 32) != tag)) {
     const uint64_t t0 = wall_clock64();
     int it = 0;
@@ -161,7 +156,7 @@ __device__ __forceinline__ void settle2(const uint64_t* p0, const uint64_t* p1, 
       w0 = ld_word_coherent(p0);
       w1 = ld_word_coherent(p1);
       if (((uint32_t)(w0 >> 32) == tag) & ((uint32_t)(w1 >> 32) == tag)) break;
-      if ((++it & 15) == 0 && wall_clock64() - t0 > F_WAIT_TICKS) {
+      if ((++it & 15) == 0 && wall_clock64() - t0 > ticks) {
         flag_error(sync, 2u);
         break;
       }
@@ -169,22 +164,46 @@ __device__ __forceinline__ void settle2(const uint64_t* p0, const uint64_t* p1, 
   }
 }
 
-// Count the workgroup out; the last one (every other workgroup is past all
-// of its waits) resets the count and advances the epoch for the next call.
-// One count for the grid: its atomics are spread over the kernel's second
-// half, and the last workgroup then waits one round trip, not two (a count
-// per XCD group first, measured 0.09 us slower per call).
-__device__ __forceinline__ void finish(uint32_t* sync) {
+// Router counters. A router workgroup counts itself in its XCD group's
+// counter (one 128-byte line each) right after issuing its logit stores
+// (the count can arrive first: the logits carry tags and a stale one is
+// read again); the routed workgroups poll the 8 counters (one wave, one
+// load per lane and round) and then read the logits. Polling the logit words
+// themselves (8 KB per workgroup and round) flooded the memory side while
+// the routers were still at work: the logits were seen 3.5 us after the
+// last router finished. The counters of a slot are zeroed two calls before
+// the slot comes round again.
+__device__ __forceinline__ void count_router(uint32_t* ctr) {
   __syncthreads();
-  if (threadIdx.x == 0) {
-    const uint32_t old = __hip_atomic_fetch_add(sync + SY_DONE, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (old == gridDim.x - 1) {
-      const uint32_t next = ld_u32(sync + SY_EPOCH) + 1u;
-      for (int q = 0; q < SY_NREP; q++)
-        __hip_atomic_store(sync + SY_EPOCH + SY_LINE * q, next, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(sync + SY_DONE, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (threadIdx.x == 0) __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void wait_routers(const uint32_t* ctr, const int* want, uint32_t* sync, uint64_t ticks) {
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x, g = lane & (F_NX - 1);
+    const uint32_t need = (uint32_t)want[g];
+    const uint32_t* c = ctr + CT_STRIDE * g;
+    uint64_t t0 = 0;
+    int it = 0;
+    while (true) {
+      const uint32_t v = __hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (__builtin_amdgcn_ballot_w64(v < need) == 0) break;
+      if (it == 0) t0 = wall_clock64();
+      __builtin_amdgcn_s_sleep(1);
+      if ((++it & 15) == 0 && wall_clock64() - t0 > ticks) {
+        if (lane == 0) flag_error(sync, 1u);
+        break;
+      }
     }
   }
+  __syncthreads();
+}
+
+// The workgroup's call counter: read at the start (the tag is its value + 1)
+// and written back incremented once the workgroup is past all of its waits.
+__device__ __forceinline__ uint32_t* my_counter(uint32_t* sync) { return sync + SY_COUNT + 2 * blockIdx.x; }
+__device__ __forceinline__ void finish(uint32_t* sync, uint32_t tag) {
+  __syncthreads();
+  if (threadIdx.x == 0) __hip_atomic_store(my_counter(sync), tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Stack layers: z = RMSNorm(h) computed by every workgroup that reads the
@@ -218,71 +237,81 @@ __device__ __forceinline__ uint32_t scale_pair(uint32_t v, float inv) {
 }
 
 // ---------------------------------------------------------------------------
-// Router: waves w and w + 8 of workgroup b compute the two halves of the
-// logit of expert 8b + w (summed in that order). The
-// logits are written once per XCD group (SY_NREP replicas): the routed
-// workgroups of a group read their own copy, so each line has a few
-// readers instead of all of them (lines read by hundreds of workgroups at
-// once serve them one after another).
+// Router: waves w and w + 8 of router workgroup rw compute the two halves of
+// the logit of expert 8rw + w (summed in that order). The logits are written
+// once per XCD group: the routed workgroups of a group read their own copy,
+// so each line has a few readers instead of all of them (lines read by
+// hundreds of workgroups at once serve them one after another).
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ void role_router(const LayerDev& L, const uint16_t* __restrict__ x, uint64_t* logits, int b,
-                                            double* s_rt, uint32_t tag, bool stk, float eps, float* s_n) {
+struct RouterRegs {
+  float4 w[F_RCPL];
+  float bias;
+};
+
+// Issue the loads of this workgroup's router rows (with the token's, so that
+// both are in flight together): lane l of wave w (row 8rw + w % 8, half
+// w / 8) takes float4 columns c_lo + l + 64i, clamped to the half row and
+// masked when summed. Every workgroup issues them (a load under a branch
+// makes the compiler wait for it where the branch joins); a workgroup that
+// is not a router (act false) reads the first 16 bytes of the router, once.
+__device__ __forceinline__ void router_issue(const LayerDev& L, bool act, int rw, RouterRegs& R) {
   static_assert(F_WAVES == 16, "two waves per router row");
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int e = b * 8 + (wave & 7), hh = wave >> 3;
-  const bool valid = e < L.E;
+  const int e = rw * 8 + (wave & 7), hh = wave >> 3;
+  const bool valid = act && e < L.E;
   const int n4 = L.H >> 2, c_lo = hh * (n4 >> 1), c_hi = hh ? n4 : (n4 >> 1);
   const float4* wr = reinterpret_cast<const float4*>(L.router_w + (size_t)(valid ? e : 0) * L.H);
-  const uint2* xv = reinterpret_cast<const uint2*>(x);
-  // the bias is loaded with the weights (not after the sum: a load there is
-  // one more memory round trip on the way to the top-k)
+#pragma unroll
+  for (int i = 0; i < F_RCPL; i++) R.w[i] = wr[act ? min(c_lo + lane + 64 * i, c_hi - 1) : 0];
+  // the bias with the weights (a load after the sum would be one more
+  // memory round trip on the way to the top-k), unconditionally: a load
+  // inside a branch makes the compiler wait for every load in flight where
+  // the branch joins
   const float* bp = L.router_b ? L.router_b + (valid ? e : 0) : L.router_w;
-  const float bias_raw = *bp;
+  R.bias = *bp;
+}
+
+// The logits of the rows from the staged activations xs (LDS, bf16): the
+// two halves of a row are summed in order; the logit goes out as two tagged
+// words in every XCD group's copy.
+__device__ __forceinline__ void router_finish(const LayerDev& L, const uint16_t* xs, const RouterRegs& R, int rw,
+                                              uint64_t* logits, double* s_rt, uint32_t tag) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int e = rw * 8 + (wave & 7), hh = wave >> 3;
+  const bool valid = e < L.E;
+  const int n4 = L.H >> 2, c_lo = hh * (n4 >> 1), c_hi = hh ? n4 : (n4 >> 1);
+  const uint2* xv = reinterpret_cast<const uint2*>(xs);
+  // the weights enter the arithmetic only here: without this the compiler
+  // converts them to fp64 right where they are loaded, which makes the
+  // workgroup wait for them before it stages x
+  float4 wr[F_RCPL];
+#pragma unroll
+  for (int i = 0; i < F_RCPL; i++) {
+    wr[i] = R.w[i];
+    asm volatile("" : "+v"(wr[i].x), "+v"(wr[i].y), "+v"(wr[i].z), "+v"(wr[i].w));
+  }
+  float bias = R.bias;
+  asm volatile("" : "+v"(bias));
   double a0 = 0.0, a1 = 0.0;
-  for (int c0 = c_lo; c0 < c_hi; c0 += 64 * F_RCPL) {
-    float4 w[F_RCPL];
-    uint2 xx[F_RCPL];
-    // loads with clamped indices and no branch (a load inside a branch makes
-    // the compiler wait for every load in flight where the branch joins);
-    // elements past the row are masked after
 #pragma unroll
-    for (int i = 0; i < F_RCPL; i++) {
-      const int c = min(c0 + lane + 64 * i, c_hi - 1);
-      w[i] = wr[c];
-      xx[i] = xv[c];
-    }
-    if (stk) {
-      // stack layer: x is h, the activations are z = RMSNorm(h). Half a row
-      // is one pass on this path (H <= F_HMAX), so the norm's loads go out
-      // with the weights' and cost no round trip of their own.
-      const uint4 hv = reinterpret_cast<const uint4*>(x)[min((int)threadIdx.x, (L.H >> 3) - 1)];
-      const float inv = stack_inv(hv, L.H, eps, s_n);
-#pragma unroll
-      for (int i = 0; i < F_RCPL; i++) xx[i] = make_uint2(scale_pair(xx[i].x, inv), scale_pair(xx[i].y, inv));
-    }
-#pragma unroll
-    for (int i = 0; i < F_RCPL; i++) {
-      if (!(valid && c0 + lane + 64 * i < c_hi)) {
-        w[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-        xx[i] = make_uint2(0u, 0u);
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < F_RCPL; i++) {
-      a0 = __builtin_fma((double)w[i].x, (double)bf16_lo(xx[i].x), a0);
-      a1 = __builtin_fma((double)w[i].y, (double)bf16_hi(xx[i].x), a1);
-      a0 = __builtin_fma((double)w[i].z, (double)bf16_lo(xx[i].y), a0);
-      a1 = __builtin_fma((double)w[i].w, (double)bf16_hi(xx[i].y), a1);
-    }
+  for (int i = 0; i < F_RCPL; i++) {
+    const int c = c_lo + lane + 64 * i;
+    const bool in = valid && c < c_hi;
+    const float4 w = in ? wr[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+    const uint2 xx = in ? xv[c] : make_uint2(0u, 0u);
+    a0 = __builtin_fma((double)w.x, (double)bf16_lo(xx.x), a0);
+    a1 = __builtin_fma((double)w.y, (double)bf16_hi(xx.x), a1);
+    a0 = __builtin_fma((double)w.z, (double)bf16_lo(xx.y), a0);
+    a1 = __builtin_fma((double)w.w, (double)bf16_hi(xx.y), a1);
   }
   const double part = wave_total_f64(a0 + a1);
   if (hh == 1 && lane == 0) s_rt[wave & 7] = part;
   __syncthreads();
   if (hh == 0 && valid && lane < SY_NREP) {
     const double tot = part + s_rt[wave];
-    const uint64_t v = (uint64_t)__double_as_longlong(tot + (L.router_b ? (double)bias_raw : 0.0));
+    const uint64_t v = (uint64_t)__double_as_longlong(tot + (L.router_b ? (double)bias : 0.0));
     // two words (low, high half of the fp64 logit), each with the tag, in
-    // every XCD group's replica (lane r writes replica r)
+    // every XCD group's copy (lane r writes copy r)
     uint64_t* rl = logits + (size_t)lane * 2 * L.E;
     st_word(rl + 2 * e, (uint32_t)v, tag);
     st_word(rl + 2 * e + 1, (uint32_t)(v >> 32), tag);
@@ -410,9 +439,9 @@ __device__ __forceinline__ float gate_up_h(const uint8_t* __restrict__ gu, const
 
 // x -> LDS (bf16) and, for quantised weights, its 32-element block sums.
 __device__ __forceinline__ void stage_x(const uint16_t* __restrict__ x, int H, uint16_t* xs, float* xsum) {
-  const int n8 = H >> 3;  // 16-byte chunks
-  for (int i = threadIdx.x; i < n8; i += F_THREADS) {
-    const uint4 v = reinterpret_cast<const uint4*>(x)[i];
+  const int n8 = H >> 3, i = threadIdx.x;  // 16-byte chunks: one per thread (H <= F_HMAX)
+  const uint4 v = reinterpret_cast<const uint4*>(x)[min(i, n8 - 1)];  // clamped, unconditional
+  if (i < n8) {
     reinterpret_cast<uint4*>(xs)[i] = v;
     if (xsum) {
       float s = ((bf16_lo(v.x) + bf16_hi(v.x)) + (bf16_lo(v.y) + bf16_hi(v.y))) +
@@ -474,7 +503,7 @@ struct BlockTopk {
 static_assert(64 * F_NV <= F_THREADS, "one logit per thread");
 
 __device__ __forceinline__ void block_topk(const uint64_t* logits, int E, int k, uint32_t tag, uint32_t* sync,
-                                           BlockTopk& S) {
+                                           uint64_t ticks, BlockTopk& S) {
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   // 1. one logit per thread: coherent loads (a line another call left in
   //    this XCD's L2 is never used), clamped and unconditional
@@ -482,7 +511,7 @@ __device__ __forceinline__ void block_topk(const uint64_t* logits, int E, int k,
   uint64_t wl = ld_word_coherent(logits + 2 * e);
   uint64_t wh = ld_word_coherent(logits + 2 * e + 1);
   if (t == 0) S.cnt = 0;
-  settle2(logits + 2 * e, logits + 2 * e + 1, wl, wh, tag, sync);  // the last router rows may be on their way
+  settle2(logits + 2 * e, logits + 2 * e + 1, wl, wh, tag, sync, ticks);  // the last router rows may be on their way
   const double v = (t < E) ? __longlong_as_double((long long)(((wh & 0xFFFFFFFFull) << 32) | (wl & 0xFFFFFFFFull)))
                            : -__builtin_inf();
   S.val[t] = v;
@@ -613,7 +642,8 @@ __device__ __forceinline__ void down_prefetch(const uint8_t* __restrict__ d, con
   }
 }
 
-// partial[row] = scale * (its columns . h), stored as tagged words
+// partial[row] = scale * (its columns . h), stored as tagged words that stay
+// in this XCD's L2
 template <int WT, int NCOL>
 __device__ __forceinline__ void down_store(const uint8_t* __restrict__ d, int H, int c0, const DownPre<WT>& pre,
                                            const uint16_t* s_h, float hsum, float scale, uint64_t* part, uint32_t tag) {
@@ -630,7 +660,7 @@ __device__ __forceinline__ void down_store(const uint8_t* __restrict__ d, int H,
     for (int n = 0; n < F_RPT; n++) {
       const int row = (int)threadIdx.x + F_THREADS * n;
       const float v = f16_to_f32(pre.s[n]) * qdot32_regs<WT>(pre.r[n], hv, hsum, magic);
-      if (row < H) st_word(part + row, __float_as_uint(v * scale), tag);
+      if (row < H) st_word_xcd(part + row, __float_as_uint(v * scale), tag);
     }
     return;
   }
@@ -646,76 +676,109 @@ __device__ __forceinline__ void down_store(const uint8_t* __restrict__ d, int H,
 #pragma unroll
         for (int c = 0; c < NCH; c++) v = ddot<WT>(load_chunk<WT>(d, (size_t)(c0 / KC + c) * H + row), s_h + KC * c, v);
       }
-      st_word(part + row, __float_as_uint(v * scale), tag);
+      st_word_xcd(part + row, __float_as_uint(v * scale), tag);
     }
   }
 }
 
 // ---------------------------------------------------------------------------
-// Reducer: output rows r0 .. r0 + F_RD - 1, y = sum over the nP partials in
-// producer order (shared roles, then routed), each thread summing a fixed
-// subset and the workgroup adding the subsets in a fixed order. The reducer
-// polls the partial words themselves (no flags): a pass costs one request
-// per producer line, as a flag poll would, and the data is there as soon as
-// the poll sees it.
+// XCD-level sum. Workgroup j of XCD x sums rows r0 .. r0 + H/32 - 1 (r0 =
+// j * H/32) over the partials of the producers that run on XCD x (the
+// workgroups 8j' + x, j' = 0..31, in j' order), which this XCD's L2 holds.
+// Thread t takes row t % 64 and the producers of workgroups j' = t / 64 and
+// t / 64 + 16; the 16 groups are added in order. The sums go out as tagged
+// words xs[x][row] (agent scope: the final sums read them from every XCD).
+// The reader polls the partial words themselves (inside the XCD a poll
+// costs L2 requests only).
 // ---------------------------------------------------------------------------
-constexpr int F_RD = 16;                   // output rows per reducer
-constexpr int F_RG = F_THREADS / F_RD;     // producer groups per reducer (64)
-
-__device__ __forceinline__ void role_reduce(const uint64_t* part, int nP, int H, int r0, uint16_t* __restrict__ y,
-                                            float* s_red, uint32_t tag, uint32_t* sync, const StackIo& S) {
-  const int rr = threadIdx.x % F_RD, pg = threadIdx.x / F_RD;
-  const int row = r0 + rr;
-  float acc = 0.0f;
-  const int rowc = min(row, H - 1);
-  constexpr int NB = 4;  // F_RG * NB >= the producers of the usual shapes: one batch of loads
-  for (int p0 = pg; p0 < nP; p0 += F_RG * NB) {
-    uint64_t w[NB];
+__device__ __forceinline__ void role_sum_xcd(const uint64_t* part, uint64_t* xs, const FusedGeo& G, int H, float* s_red,
+                                             uint32_t tag, uint32_t* sync) {
+  const int x = blockIdx.x % F_NX, j = blockIdx.x / F_NX;
+  const int nrow = H / F_PX, r0 = j * nrow;  // H % 32 == 0
+  const int rr = threadIdx.x & 63, g = threadIdx.x >> 6;
+  const int row = r0 + min(rr, nrow - 1);
+  int p[2];
+  const uint64_t* pw[2];
+  uint64_t w[2];
 #pragma unroll
-    for (int n = 0; n < NB; n++)  // clamped, unconditional loads (see role_router)
-      w[n] = ld_word_coherent(part + (size_t)min(p0 + F_RG * n, nP - 1) * H + rowc);
-    // words of producers that are not done yet: the wave reloads its whole
-    // batch (unconditional loads, one round trip per pass) until every tag
-    // is current, so late producers cost one round trip, not one per word
+  for (int n = 0; n < 2; n++) {
+    p[n] = producer_of(F_NX * (g + 16 * n) + x, G);
+    pw[n] = part + (size_t)max(p[n], 0) * H + row;
+    w[n] = ld_word_coherent(pw[n]);  // unconditional: a word of a non-producer is not used
+  }
+  // bounded poll of this thread's stale words (producers still computing)
+  bool stale = false;
+#pragma unroll
+  for (int n = 0; n < 2; n++) stale |= (p[n] >= 0) && !tag_ok(w[n], tag);
+  if (__builtin_amdgcn_ballot_w64(stale) != 0) {
     const uint64_t t0 = wall_clock64();
     int it = 0;
     while (true) {
-      bool stale = false;
+      __builtin_amdgcn_s_sleep(1);
+      stale = false;
 #pragma unroll
-      for (int n = 0; n < NB; n++) stale |= (uint32_t)(w[n] >> 32) != tag;
+      for (int n = 0; n < 2; n++) {
+        if ((p[n] >= 0) && !tag_ok(w[n], tag)) w[n] = ld_word_coherent(pw[n]);
+        stale |= (p[n] >= 0) && !tag_ok(w[n], tag);
+      }
       if (__builtin_amdgcn_ballot_w64(stale) == 0) break;
-      __builtin_amdgcn_s_sleep(2);
-      uint64_t r[NB];
-#pragma unroll
-      for (int n = 0; n < NB; n++) r[n] = ld_word_coherent(part + (size_t)min(p0 + F_RG * n, nP - 1) * H + rowc);
-#pragma unroll
-      for (int n = 0; n < NB; n++) w[n] = ((uint32_t)(w[n] >> 32) == tag) ? w[n] : r[n];
-      if ((++it & 15) == 0 && wall_clock64() - t0 > F_WAIT_TICKS) {
-        flag_error(sync, 2u);
+      if ((++it & 15) == 0 && wall_clock64() - t0 > G.wait_ticks) {
+        if ((threadIdx.x & 63) == 0) flag_error(sync, 4u);
         break;
       }
     }
-#pragma unroll
-    for (int n = 0; n < NB; n++)
-      if (p0 + F_RG * n < nP) acc += __uint_as_float((uint32_t)w[n]);
   }
-  // a wave holds four producer groups of the same 16 rows (lanes rr + 16j):
-  // fold them in the wave ((g0 + g1) + (g2 + g3)), then the wave sums
-  static_assert(F_RD == 16, "four groups per wave");
-  float a = acc + __shfl_xor(acc, 16, 64);
-  a += __shfl_xor(a, 32, 64);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  if (lane < F_RD) s_red[wave * F_RD + lane] = a;
+  float acc = 0.0f;
+#pragma unroll
+  for (int n = 0; n < 2; n++) acc += (p[n] >= 0) ? __uint_as_float((uint32_t)w[n]) : 0.0f;
+  s_red[g * 64 + rr] = acc;
   __syncthreads();
-  if ((int)threadIdx.x < F_RD && row < H) {
+  if (rr < nrow && threadIdx.x < 64) {
     float t = 0.0f;
 #pragma unroll
-    for (int w = 0; w < F_WAVES; w++) t += s_red[w * F_RD + rr];
+    for (int q = 0; q < F_WAVES; q++) t += s_red[q * 64 + rr];
+    st_word(xs + (size_t)x * H + r0 + rr, __float_as_uint(t), tag);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Final sum: rows row0 .. row0 + nr - 1 (nr <= 8) of y = the XCD sums in XCD
+// order (XCDs without producers add nothing). Wave 0: lane t takes row t % 8
+// and XCD t / 8.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void role_sum_final(const uint64_t* xs, const FusedGeo& G, int H, int row0, int nr,
+                                               uint16_t* __restrict__ y, uint32_t tag, uint32_t* sync,
+                                               const StackIo& S) {
+  if (threadIdx.x >= 64) return;
+  const int lane = threadIdx.x, r = lane & 7, q = lane >> 3;
+  const bool use = ((G.xmask >> q) & 1) && r < nr;
+  const uint64_t* pw = xs + (size_t)q * H + row0 + min(r, max(nr - 1, 0));
+  uint64_t w = ld_word_coherent(pw);
+  if (__builtin_amdgcn_ballot_w64(use && !tag_ok(w, tag)) != 0) {
+    const uint64_t t0 = wall_clock64();
+    int it = 0;
+    while (true) {
+      __builtin_amdgcn_s_sleep(1);
+      if (use && !tag_ok(w, tag)) w = ld_word_coherent(pw);
+      if (__builtin_amdgcn_ballot_w64(use && !tag_ok(w, tag)) == 0) break;
+      if ((++it & 15) == 0 && wall_clock64() - t0 > G.wait_ticks) {
+        if (lane == 0) flag_error(sync, 8u);
+        break;
+      }
+    }
+  }
+  // add the XCDs in order: lanes r + 8q, q = 0..7
+  float v = use ? __uint_as_float((uint32_t)w) : 0.0f;
+  float t = v;
+#pragma unroll
+  for (int qq = 1; qq < F_NX; qq++) t += __shfl(v, r + 8 * qq, 64);
+  if (lane < nr) {
+    const int row = row0 + lane;
     const uint16_t yb = f32_to_bf16(t);
     if (S.h) {
-      // stack layer: h = bf16(h + y) for this reducer's rows. Every workgroup
-      // that reads h has read it before its output (logits, partials) could
-      // reach a reducer, and the reducers wait for all of them.
+      // stack layer: h = bf16(h + y) for these rows. Every workgroup that
+      // reads h has read it before its output (logits, partials) could reach
+      // an XCD sum, and the final sums wait for all of those.
       S.h[row] = f32_to_bf16(bf16_to_f32(S.h[row]) + bf16_to_f32(yb));
       if (S.y_out) S.y_out[row] = yb;
     } else {
@@ -724,10 +787,6 @@ __device__ __forceinline__ void role_reduce(const uint64_t* part, int nP, int H,
   }
 }
 
-// ---------------------------------------------------------------------------
-// LDS: static arrays (x, x block sums, wave partials, top-k scratch) sized
-// for H <= F_HMAX.
-// ---------------------------------------------------------------------------
 // ---------------------------------------------------------------------------
 // The kernel
 // ---------------------------------------------------------------------------
@@ -747,47 +806,74 @@ __global__ __launch_bounds__(F_THREADS, 4) void k_decode1(LayerDev L, const uint
   __shared__ float s_n[4];
   const int H = L.H, I = L.I;
   const bool stk = S.h != nullptr;  // stack layer: the token is h, the activations z = RMSNorm(h)
-  const int nP = G.nSG + G.nRG;  // partial producers: shared workgroups, then routed
-  // this call's tag: the epoch (stable until every workgroup is done) + 1
-  const uint32_t tag = ld_u32(ws.sync + SY_EPOCH + SY_LINE * my_rep()) + 1u;
+  const int b = blockIdx.x, rank = start_rank(b);
+  // this call's tag: the workgroup's own call count + 1 (the same in every workgroup)
+  const uint32_t tag = ld_u32(my_counter(ws.sync)) + 1u;
   uint64_t* tl = reinterpret_cast<uint64_t*>(ws.logits) + (size_t)(tag % F_SLOTS) * SY_NREP * 2 * L.E;
-  // flags of the router roles
-  uint64_t* fl = ws.flags + (size_t)(tag % F_SLOTS) * G.nR * F_FLAG_STRIDE;
-  uint64_t* part = ws.part_words;  // [nP][H]
-  int b = blockIdx.x;
-  if (b < G.nA) {
-    if (b < G.nR) {
-      role_router(L, stk ? S.h : x, tl, b, s_rt, tag, stk, S.eps, s_n);
-      raise_flag(fl, b, tag);
+  uint32_t* ct = ws.ctr + (size_t)(tag % F_SLOTS) * F_NX * CT_STRIDE;  // router counters of this call
+  if (b == 0 && threadIdx.x < F_NX)  // the slot used two calls from now is idle: zero its counters
+    __hip_atomic_store(ws.ctr + ((size_t)((tag + 2) % F_SLOTS) * F_NX + threadIdx.x) * CT_STRIDE, 0u,
+                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  uint64_t* part = ws.part_words;  // [nSG + nRG][H], in the producers' XCD L2s
+  const bool is_router = rank < G.nRW;
+  const bool is_routed = b < G.nRG;
+  const bool is_shared = b >= G.sg0 && b < G.sg0 + G.nSG;
+  // the token and the router rows are loaded together (straight-line code:
+  // see router_issue), then x (or z = RMSNorm(h)) goes to LDS. A workgroup
+  // without a role in a stack layer reads no part of h (its source is the
+  // router's first bytes): every reader of h must precede the writers of h.
+  const bool has_role = is_router || is_routed || is_shared;
+  const uint16_t* src = (has_role || !stk) ? (stk ? S.h : x) : reinterpret_cast<const uint16_t*>(L.router_w);
+  const int n8 = H >> 3;
+  const uint4 tv = reinterpret_cast<const uint4*>(src)[min((int)threadIdx.x, n8 - 1)];  // clamped, unconditional
+  RouterRegs rrg;
+  router_issue(L, is_router, rank, rrg);
+  {
+    uint4 v = tv;
+    if (stk) {
+      const float inv = stack_inv(tv, H, S.eps, s_n);
+      v = make_uint4(scale_pair(tv.x, inv), scale_pair(tv.y, inv), scale_pair(tv.z, inv), scale_pair(tv.w, inv));
     }
-    if (b < G.nSG) {
-      // shared expert, intermediates 16q + 8hf .. +7, right after the router
-      // rows (its bytes fill the memory-idle top-k window)
-      constexpr int SW = (SWT == MOE_W_F32) ? MOE_W_F32 : MOE_W_BF16;
-      const uint16_t* xs = s_x;
-      const int q = b >> 1, hf = b & 1;
-      if (stk) stage_z(S.h, H, S.eps, s_x, nullptr, s_n);
-      else stage_x(x, H, s_x, nullptr);  // after the router's loads (x is then in this XCD's L2)
-      __syncthreads();
-      DownPre<SW> pre;
-      gate_up_h<SW, 16>(L.sgu, nullptr, H, 2 * I, q, hf, xs, nullptr, s_red, s_h,
-                        [&] { down_prefetch<SW, 8>(L.sdn, nullptr, H, 16 * q + 8 * hf, pre); });
-      __syncthreads();
-      down_store<SW, 8>(L.sdn, H, 16 * q + 8 * hf, pre, s_h, 0.0f, 1.0f, part + (size_t)b * H, tag);
+    if ((int)threadIdx.x < n8) {
+      reinterpret_cast<uint4*>(s_x)[threadIdx.x] = v;
+      if (is_routed && is_q<WT>()) {
+        // 32-element block sums: chunks 4b..4b+3 are lanes 4b'..4b'+3 of one quad
+        float sm = ((bf16_lo(v.x) + bf16_hi(v.x)) + (bf16_lo(v.y) + bf16_hi(v.y))) +
+                   ((bf16_lo(v.z) + bf16_hi(v.z)) + (bf16_lo(v.w) + bf16_hi(v.w)));
+        sm += dpp_f32<DPP_XOR1>(sm);
+        sm += dpp_f32<DPP_XOR2>(sm);
+        if ((threadIdx.x & 3) == 0) s_xsum[threadIdx.x >> 2] = sm;
+      }
     }
-  } else if ((b -= G.nA) < G.nRG) {
+  }
+  __syncthreads();
+  if (is_router) {
+    router_finish(L, s_x, rrg, rank, tl, s_rt, tag);
+    count_router(ct + CT_STRIDE * (b % F_NX));
+  }
+  if (is_shared) {
+    // shared expert, intermediates 8su .. 8su+7 (needed only by the sums)
+    constexpr int SW = (SWT == MOE_W_F32) ? MOE_W_F32 : MOE_W_BF16;
+    const int su = b - G.sg0;
+    const int q = su >> 1, hf = su & 1;
+    DownPre<SW> pre;
+    gate_up_h<SW, 16>(L.sgu, nullptr, H, 2 * I, q, hf, s_x, nullptr, s_red, s_h,
+                      [&] { down_prefetch<SW, 8>(L.sdn, nullptr, H, 16 * q + 8 * hf, pre); });
+    __syncthreads();
+    down_store<SW, 8>(L.sdn, H, 16 * q + 8 * hf, pre, s_h, 0.0f, 1.0f, part + (size_t)su * H, tag);
+  }
+  const int ru = b;  // routed unit of this workgroup (if < nRG)
+  if (is_routed) {
     // routed slot u, intermediates 32q .. 32q+31
     uint16_t* xs = s_x;
     float* xsum = s_xsum;
-    if (stk) stage_z(S.h, H, S.eps, xs, is_q<WT>() ? xsum : nullptr, s_n);
-    else stage_x(x, H, xs, is_q<WT>() ? xsum : nullptr);
-    wait_flags(fl, G.nR, flags_needed(G.nR), tag, ws.sync);  // (its barrier also publishes xs)
-    if (stk && S.z_out && b == 0)
+    if (stk && S.z_out && ru == 0)
       for (int i = threadIdx.x; i < (H >> 3); i += F_THREADS)
         reinterpret_cast<uint4*>(S.z_out)[i] = reinterpret_cast<const uint4*>(xs)[i];
-    block_topk(tl + (size_t)my_rep() * 2 * L.E, L.E, L.k, tag, ws.sync, s_tk);
+    wait_routers(ct, G.rcount, ws.sync, G.wait_ticks);
+    block_topk(tl + (size_t)my_rep() * 2 * L.E, L.E, L.k, tag, ws.sync, G.wait_ticks, s_tk);
     const int gpe = I >> 5;
-    const int u = b / gpe, q = b - u * gpe;
+    const int u = ru / gpe, q = ru - u * gpe;
     const int e = min(max(s_tk.out[u].i, 0), L.E - 1);  // in range whatever the logits held
     const uint8_t* dn = L.dn + (size_t)e * L.dn_stride;
     const uint16_t* dns = is_q<WT>() ? L.dn_s + (size_t)e * L.dn_s_stride : nullptr;
@@ -801,7 +887,7 @@ __global__ __launch_bounds__(F_THREADS, 4) void k_decode1(LayerDev L, const uint
                                          // barrier); dense weights have no registers to spare there
                                          if constexpr (is_q<WT>()) block_topk_gates(s_tk, L.E, L.k, s_idx, s_gate);
                                        });
-    if (b == 0 && (int)threadIdx.x < L.k) {
+    if (ru == 0 && (int)threadIdx.x < L.k) {
       if (idx_out) idx_out[threadIdx.x] = s_idx[threadIdx.x];
       if (gate_out) gate_out[threadIdx.x] = s_gate[threadIdx.x];
     }
@@ -816,20 +902,24 @@ __global__ __launch_bounds__(F_THREADS, 4) void k_decode1(LayerDev L, const uint
     }
     __syncthreads();
     down_store<WT, 32>(dn, H, 32 * q, pre, s_h, is_q<WT>() ? s_hsum : 0.0f, s_gate[u],
-                       part + (size_t)(G.nSG + b) * H, tag);
+                       part + (size_t)(G.nSG + ru) * H, tag);
   }
-  // reducers: the last nD workgroups of the grid, all routed or extra ones
-  const int d = (int)blockIdx.x - ((int)gridDim.x - G.nD);
-  if (d >= 0) {
+  // XCD sums (XCDs that hold producers), then the final rows
+  if ((G.xmask >> (b % F_NX)) & 1) {
     __syncthreads();  // s_red is reused
-    role_reduce(part, nP, H, d * F_RD, y, s_red, tag, ws.sync, S);
+    role_sum_xcd(part, ws.xsum_words, G, H, s_red, tag, ws.sync);
   }
-  finish(ws.sync);
+  const int row0 = rank * H / F_NW, nr = (rank + 1) * H / F_NW - row0;
+  if (nr > 0) role_sum_final(ws.xsum_words, G, H, row0, nr, y, tag, ws.sync, S);
+  finish(ws.sync, tag);
 }
 
 // ---------------------------------------------------------------------------
 // Host side
 // ---------------------------------------------------------------------------
+static uint64_t g_wait_ticks = F_WAIT_TICKS;
+void decode1_set_wait_ticks(uint64_t ticks) { g_wait_ticks = ticks ? ticks : F_WAIT_TICKS; }
+
 size_t decode1_lds(int H, int I, int k, bool has_shared) {
   (void)H; (void)I; (void)k; (void)has_shared;
   return 0;  // static arrays only
@@ -839,23 +929,14 @@ static int producers(int I, int k, bool has_shared) { return (has_shared ? I / 8
 
 size_t decode1_logit_words(int E) { return (size_t)F_SLOTS * SY_NREP * 2 * E; }
 
-size_t decode1_flag_words(int E, int I, int k, bool has_shared) {
-  (void)I; (void)k; (void)has_shared;
-  return (size_t)F_SLOTS * ((E + 7) / 8) * F_FLAG_STRIDE;
-}
+size_t decode1_part_words(int H, int I, int k, bool has_shared) { return (size_t)producers(I, k, has_shared) * H; }
 
-// Workgroups: router/shared, routed, and extra reducers when the reducers
-// outnumber the routed workgroups (reducers are the last ones).
-static int decode1_grid(int E, int H, int I, int k, bool has_shared) {
-  const int nR = (E + 7) / 8, nSG = has_shared ? I / 8 : 0, nRG = k * (I / 32);
-  const int nA = nR > nSG ? nR : nSG, nD = (H + F_RD - 1) / F_RD;
-  return nA + (nRG > nD ? nRG : nD);
-}
+size_t decode1_xsum_words(int H) { return (size_t)F_NX * H; }
+
+size_t decode1_counter_words() { return (size_t)F_SLOTS * F_NX * CT_STRIDE; }
 
 // Workgroups that are sure to be resident together: one per CU (the launch
 // bounds keep a workgroup within a CU's registers; its LDS is ~24 KB).
-// Reducers wait for producers dispatched before and after them, so the
-// whole grid must be resident at once.
 static int decode1_capacity() {
   static int cap[64] = {0};
   int dev = 0;
@@ -868,28 +949,32 @@ static int decode1_capacity() {
   return cap[dev];
 }
 
-size_t decode1_part_words(int H, int I, int k, bool has_shared) {
-  return (size_t)producers(I, k, has_shared) * H;
-}
-
 bool decode1_fits(int E, int H, int I, int k, bool has_shared) {
   // F_NV logits per lane in the top-k, F_RPT down rows per thread (the LDS
-  // arrays are sized for H <= F_HMAX), a grid that is resident at once
-  return E <= 64 * F_NV && H <= F_HMAX && I <= 1024 && decode1_grid(E, H, I, k, has_shared) <= decode1_capacity();
+  // arrays are sized for H <= F_HMAX), at most one shared or routed unit per
+  // workgroup, and a grid that is resident at once
+  const int nRW = (E + 7) / 8, nSG = has_shared ? I / 8 : 0, nRG = k * (I / 32);
+  const int sg0 = (nRG + F_NX - 1) / F_NX * F_NX;
+  return E <= 64 * F_NV && H <= F_HMAX && I <= 1024 && nRW <= F_NW && sg0 + nSG <= F_NW &&
+         F_NW <= decode1_capacity();
 }
 
 template <int WT, int SWT>
 static hipError_t launch_fused_t(const LayerDev& L, const uint16_t* x, uint16_t* y, int32_t* idx_out, float* gate_out,
                                  const DecodeWs& ws, hipStream_t st, const StackIo& S) {
   FusedGeo G;
-  G.nR = (L.E + 7) / 8;
+  G.nRW = (L.E + 7) / 8;
   G.nSG = (SWT == MOE_W_NONE) ? 0 : L.I / 8;
   G.nRG = L.k * (L.I / 32);
-  G.nA = G.nR > G.nSG ? G.nR : G.nSG;
-  G.nD = (L.H + F_RD - 1) / F_RD;
-  const size_t lds = decode1_lds(L.H, L.I, L.k, SWT != MOE_W_NONE);
-  const int grid = decode1_grid(L.E, L.H, L.I, L.k, SWT != MOE_W_NONE);
-  return launch_k(KC_DEC_FUSED, k_decode1<WT, SWT>, dim3(grid), dim3(F_THREADS), lds, st, L, x, y, idx_out, gate_out,
+  G.sg0 = (G.nRG + F_NX - 1) / F_NX * F_NX;
+  G.xmask = 0;
+  for (int g = 0; g < F_NX; g++) G.rcount[g] = 0;
+  for (int b = 0; b < F_NW; b++) {
+    if (b < G.nRG || (b >= G.sg0 && b < G.sg0 + G.nSG)) G.xmask |= 1 << (b % F_NX);
+    if ((b % F_NX) * F_PX + b / F_NX < G.nRW) G.rcount[b % F_NX]++;  // start rank < nRW: a router
+  }
+  G.wait_ticks = g_wait_ticks;
+  return launch_k(KC_DEC_FUSED, k_decode1<WT, SWT>, dim3(F_NW), dim3(F_THREADS), 0, st, L, x, y, idx_out, gate_out,
                   ws, G, S);
 }
 

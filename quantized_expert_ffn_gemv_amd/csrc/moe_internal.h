@@ -54,11 +54,12 @@ struct LayerDev {
 // Decode workspace (all device pointers inside the caller's workspace).
 struct DecodeWs {
   uint32_t* sync;  // counts and epoch of the one-kernel path (counts zero between calls)
-  double* logits;  // three-kernel path: [B][E] fp64; one-kernel path: rotating slots of [E][2] tagged words
-  float* part;     // three-kernel path: [B*k*(I/16) + B*(I/8)][H] partial down products
-  uint64_t* flags; // one-kernel path: per-producer tagged flag words, rotating slots
-  uint64_t* part_words;  // one-kernel path: [producers][H] tagged partial down products (fp32 bits)
-  int32_t* route;        // three-kernel path: the batch's routing (count, idx, gates, unique experts, masks)
+  double* logits;  // four-kernel path: [B][E] fp64; one-kernel path: rotating slots of [E][2] tagged words
+  float* part;     // four-kernel path: [B*k*(I/16) + B*(I/8)][H] partial down products
+  uint64_t* part_words;  // one-kernel path: [producers][H] tagged partial down products (fp32 bits), read within each XCD
+  uint64_t* xsum_words;  // one-kernel path: [8][H] tagged per-XCD sums of the partials
+  uint32_t* ctr;         // one-kernel path: router counters, rotating slots x XCD groups, one 128-byte line each
+  int32_t* route;        // four-kernel path: the batch's routing (count, idx, gates, unique experts, masks)
   uint16_t* zb;          // [B][H] bf16: z of a stack layer taken as separate kernels
   uint16_t* yb;          // [B][H] bf16: its y
 };
@@ -88,9 +89,11 @@ struct PrefillWs {
 size_t decode_lds_b(int wt, int B, int H, int E, int k);  // LDS bytes of the routed-expert kernel
 size_t decode1_lds(int H, int I, int k, bool has_shared);  // LDS bytes of the one-kernel batch-1 path
 size_t decode1_logit_words(int E);  // rotating slots x XCD-group replicas x [E][2] tagged words
-size_t decode1_flag_words(int E, int I, int k, bool has_shared);
 size_t decode1_part_words(int H, int I, int k, bool has_shared);
+size_t decode1_xsum_words(int H);
+size_t decode1_counter_words();
 bool decode1_fits(int E, int H, int I, int k, bool has_shared);  // shape handled by the one-kernel path
+void decode1_set_wait_ticks(uint64_t ticks);  // bound of the one-kernel path's waits (0: the default)
 // One layer of a pre-norm residual stack, in place on the residual stream h:
 // z = RMSNorm(h), y = MoE(z), h = bf16(h + y); z_out / y_out optional copies.
 struct StackIo {

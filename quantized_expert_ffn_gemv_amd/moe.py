@@ -29,6 +29,7 @@ EXPORTS = [
     "moe_pack_gate_up",
     "moe_status_string", "moe_last_error", "moe_kernel_class_count", "moe_kernel_class_name",
     "moe_timer_enable", "moe_timer_reset", "moe_timer_read", "moe_workspace_init", "moe_workspace_check",
+    "moe_debug_set_wait_limit",
 ]
 
 
@@ -83,6 +84,7 @@ def lib():
         L.moe_kernel_class_name.restype = ctypes.c_char_p; L.moe_kernel_class_name.argtypes = [i32]
         L.moe_workspace_init.restype = i32; L.moe_workspace_init.argtypes = [vp, sz, vp]
         L.moe_workspace_check.restype = i32; L.moe_workspace_check.argtypes = [vp, sz, vp]
+        L.moe_debug_set_wait_limit.restype = i32; L.moe_debug_set_wait_limit.argtypes = [ctypes.c_uint64]
         L.moe_timer_enable.restype = i32; L.moe_timer_enable.argtypes = [i32]
         L.moe_timer_reset.restype = i32; L.moe_timer_reset.argtypes = []
         L.moe_timer_read.restype = i32
@@ -318,6 +320,11 @@ def stack_forward(layers, h, ws, decode: bool, buf: "StackBuffers", eps: float =
         if each_layer is not None:
             each_layer(l, buf)
     return h
+
+
+def debug_set_wait_limit(ticks: int):
+    """Bound of the batch-1 decode kernel's device-side waits (0: the default)."""
+    _check(lib().moe_debug_set_wait_limit(int(ticks)), "moe_debug_set_wait_limit")
 
 
 # ---------------------------------------------------------------------------
