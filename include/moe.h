@@ -182,6 +182,26 @@ moe_status moe_forward_decode(const moe_layer *layer, const void *x, int32_t B, 
                               int32_t *topk_idx, float *topk_gate,
                               void *ws, size_t ws_bytes, hipStream_t stream);
 
+/* moe_forward_decode for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same kernels and results, with the workspace taken from a
+ * static device array of the library instead of the caller's. The array,
+ * MOE_NOALLOC_SCRATCH_BYTES (32 MiB) per GPU, exists on every device the
+ * library runs on until the process ends; this call allocates nothing.
+ * Arguments and outputs as moe_forward_decode; a layer and B whose
+ * workspace (moe_workspace_bytes(layer, B, 0)) exceeds the array return
+ * MOE_ERR_WORKSPACE and enqueue nothing.
+ * The first call on a device sets the array up: it looks up the array's
+ * device address, zeroes the array on `stream` and waits for that, so it
+ * must not be under graph capture (MOE_ERR_SHAPE if it is); later calls are
+ * stream-ordered and capturable. All calls on one GPU share its array, so
+ * calls that may overlap on one GPU (other streams, other threads) race
+ * and must be ordered by the caller. The device-side wait report of these
+ * calls stays in the array (moe_workspace_check needs a caller workspace). */
+#define MOE_NOALLOC_SCRATCH_BYTES (32u << 20)
+moe_status moe_forward_decode_noalloc(const moe_layer *layer, const void *x, int32_t B, void *y,
+                                      int32_t *topk_idx, float *topk_gate, hipStream_t stream);
+
 /* Prefill: T >= 1 tokens x[T][H] -> y[T][H] (bf16). Tokens are grouped by
  * expert (histogram, exclusive scan, stable permutation) and each expert's
  * tokens go through an MFMA grouped GEMM with the expert's weights

@@ -297,6 +297,64 @@ moe_status moe_forward_decode(const moe_layer* layer, const void* x, int32_t B, 
                     "moe_forward_decode launch");
 }
 
+// ---------------------------------------------------------------------------
+// Decode without a caller workspace: the workspace is a static device array
+// of the library (one per GPU, held until the process ends). Its device
+// address is looked up once per device and used everywhere host code needs
+// the array's memory; the array's name itself is only a host-side stand-in.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) uint8_t scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+struct ScratchDev {
+  void* ptr = nullptr;  // device address of `scratch` on this device (nullptr: not set up yet)
+};
+static std::mutex g_scratch_mu;
+static ScratchDev g_scratch[64];
+
+// Device address of the array on the current device; on the first call per
+// device also zero it (the decode workspace contract) and wait for that.
+static moe_status scratch_for_current_device(hipStream_t stream, void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+  if (dev < 0 || dev >= 64) return fail(MOE_ERR_HIP, "device %d out of range", dev);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch[dev].ptr) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    e = hipStreamIsCapturing(stream, &cs);
+    if (e != hipSuccess) return hip_status(e, "hipStreamIsCapturing");
+    if (cs != hipStreamCaptureStatusNone)
+      return fail(MOE_ERR_SHAPE, "the first moe_forward_decode_noalloc call on a device must not be under graph "
+                                 "capture (it sets up and zeroes the device's scratch array)");
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) return hip_status(e != hipSuccess ? e : hipErrorInvalidSymbol, "hipGetSymbolAddress(scratch)");
+    e = moe::launch_fill(p, MOE_NOALLOC_SCRATCH_BYTES, stream);
+    if (e == hipSuccess) e = hipStreamSynchronize(stream);
+    if (e != hipSuccess) return hip_status(e, "zeroing the scratch array");
+    g_scratch[dev].ptr = p;
+  }
+  *out = g_scratch[dev].ptr;
+  return MOE_OK;
+}
+
+moe_status moe_forward_decode_noalloc(const moe_layer* layer, const void* x, int32_t B, void* y, int32_t* topk_idx,
+                                      float* topk_gate, hipStream_t stream) {
+  moe_status st = check_layer(layer);
+  if (st != MOE_OK) return st;
+  if (!x || !y) return fail(MOE_ERR_NULL, "x and y are required");
+  if (B < 1 || B > MOE_DECODE_MAX_TOKENS) return fail(MOE_ERR_SHAPE, "B=%d not in [1, %d]", B, MOE_DECODE_MAX_TOKENS);
+  const size_t need = carve_decode(layer, B, nullptr, nullptr);
+  if (need > MOE_NOALLOC_SCRATCH_BYTES)
+    return fail(MOE_ERR_WORKSPACE, "this layer and B=%d need %zu workspace bytes, more than the %u bytes of the "
+                                   "library's scratch array; use moe_forward_decode with a workspace",
+                B, need, (unsigned)MOE_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  st = scratch_for_current_device(stream, &ws);
+  if (st != MOE_OK) return st;
+  return moe_forward_decode(layer, x, B, y, topk_idx, topk_gate, ws, MOE_NOALLOC_SCRATCH_BYTES, stream);
+}
+
 moe_status moe_stack_decode_layer(const moe_layer* layer, void* h, int32_t B, float eps, void* z_out, void* y_out,
                                   int32_t* topk_idx, float* topk_gate, void* ws, size_t ws_bytes, hipStream_t stream) {
   moe_status st = check_layer(layer);

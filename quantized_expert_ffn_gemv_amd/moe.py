@@ -29,7 +29,7 @@ EXPORTS = [
     "moe_pack_gate_up",
     "moe_status_string", "moe_last_error", "moe_kernel_class_count", "moe_kernel_class_name",
     "moe_timer_enable", "moe_timer_reset", "moe_timer_read", "moe_workspace_init", "moe_workspace_check",
-    "moe_debug_set_wait_limit",
+    "moe_debug_set_wait_limit", "moe_forward_decode_noalloc",
 ]
 
 
@@ -69,6 +69,8 @@ def lib():
         L.moe_route.argtypes = [P, vp, i32, vp, vp, vp, vp, sz, vp]
         L.moe_forward_decode.restype = i32
         L.moe_forward_decode.argtypes = [P, vp, i32, vp, vp, vp, vp, sz, vp]
+        L.moe_forward_decode_noalloc.restype = i32
+        L.moe_forward_decode_noalloc.argtypes = [P, vp, i32, vp, vp, vp, vp]
         L.moe_forward_prefill.restype = i32
         L.moe_forward_prefill.argtypes = [P, vp, i32, vp, vp, vp, vp, sz, vp]
         L.moe_rmsnorm.restype = i32; L.moe_rmsnorm.argtypes = [vp, vp, i32, i32, ctypes.c_float, vp]
@@ -259,6 +261,13 @@ def moe_forward_decode(layer, x, y, ws, topk_idx=None, topk_gate=None, stream=No
     B = x.shape[0]
     _check(lib().moe_forward_decode(ctypes.byref(layer.c), _tptr(x), B, _tptr(y), _tptr(topk_idx), _tptr(topk_gate),
                                     _tptr(ws), ws.numel(), _stream(stream)), "moe_forward_decode")
+
+
+def moe_forward_decode_noalloc(layer, x, y, topk_idx=None, topk_gate=None, stream=None):
+    """moe_forward_decode with the library's static scratch array as its workspace."""
+    B = x.shape[0]
+    _check(lib().moe_forward_decode_noalloc(ctypes.byref(layer.c), _tptr(x), B, _tptr(y), _tptr(topk_idx),
+                                            _tptr(topk_gate), _stream(stream)), "moe_forward_decode_noalloc")
 
 
 def moe_forward_prefill(layer, x, y, ws, topk_idx=None, topk_gate=None, stream=None):
