@@ -119,6 +119,9 @@ typedef struct {
 /* Sizes and workspace                                                      */
 /* ------------------------------------------------------------------------ */
 
+/* Sizes of the library's own packed layout above (the pages give no storage
+ * format; they only put the experts at 2-3.5 bits per weight: Strata
+ * write-up, section 1 "Low-Bit Quantization"). */
 /* Bytes of packed values of one R x K matrix of type wt (0 on bad input). */
 size_t moe_matrix_bytes(int32_t wt, int32_t rows, int32_t K);
 /* Number of fp16 scales of one R x K matrix (0 for F32/BF16). */
@@ -131,9 +134,9 @@ size_t moe_matrix_scales(int32_t wt, int32_t rows, int32_t K);
 size_t moe_workspace_bytes(const moe_layer *layer, int32_t max_tokens, int32_t mode);
 #define MOE_DECODE_MAX_TOKENS 8
 
-/* Workspace contract. A decode workspace must be all zero before its first
- * decode call: moe_workspace_init zero-fills all ws_bytes (as would any zero
- * fill). Its first 4096 bytes hold the counts and the call epoch of the
+/* Workspace contract (the library's own). A decode workspace must be all
+ * zero before its first decode call: moe_workspace_init zero-fills all
+ * ws_bytes (as would any zero fill). Its first 4096 bytes hold the counts and the call epoch of the
  * batch-1 decode kernel; the rest holds the tagged words through which its
  * workgroups hand data to each other (a word counts only when it carries the
  * current call's tag, so memory left by an earlier owner must not be reused
@@ -147,9 +150,14 @@ moe_status moe_workspace_init(void *ws, size_t ws_bytes, hipStream_t stream);
 /* Synchronises `stream`, then reports whether a device-side wait of a
  * decode call on this workspace ran out of time since the last check
  * (MOE_ERR_DEVICE: results of those calls are invalid) and clears the
- * report. A wait only runs out when the workgroups it waits for never ran,
- * which the launch order rules out; the bound exists so that a kernel can
- * never hang. */
+ * report. The one-kernel batch-1 decode needs all of its workgroups
+ * resident at once (some wait for others); the library checks that the
+ * grid fits the device, but other work on the GPU (other streams, other
+ * processes) can hold compute units long enough for a wait to reach its
+ * bound (moe_debug_set_wait_limit; about 0.34 s by default). The bound
+ * exists so that the kernel always ends; this call is how a caller learns
+ * that it ended early. Callers that share the GPU should check after a run
+ * of calls. (No passage of the pages: the check is the library's own.) */
 moe_status moe_workspace_check(void *ws, size_t ws_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------ */
@@ -157,7 +165,13 @@ moe_status moe_workspace_check(void *ws, size_t ws_bytes, hipStream_t stream);
 /* ------------------------------------------------------------------------ */
 
 /* Routing only (router GEMV/GEMM, softmax, ordered top-k, renormalised
- * gates) for T >= 1 tokens x[T][H] (bf16).
+ * gates) for T >= 1 tokens x[T][H] (bf16). Each layer's router picks k of
+ * the E routed experts for every token, 10 of 512 in the pages' model
+ * (explainer video, transcript at 1:50-2:01; Strata write-up, "The
+ * 30-Second Overview" table); the routers stay resident on the GPU (video
+ * at 2:28-2:38). The router formula, the gate normalisation and the tie
+ * rule are not on the pages: the library's reading is the one in the
+ * preamble above.
  *   topk_idx   [T][k] int32   experts in (logit desc, index asc) order
  *   topk_gate  [T][k] fp32    renormalised gates, same order
  *   expert_counts [E] int32 or NULL: number of tokens routed to each expert
@@ -167,6 +181,13 @@ moe_status moe_route(const moe_layer *layer, const void *x, int32_t T,
                      void *ws, size_t ws_bytes, hipStream_t stream);
 
 /* Decode: B in 1..MOE_DECODE_MAX_TOKENS tokens x[B][H] -> y[B][H] (bf16).
+ * The token's k selected experts and the always-on shared expert, their
+ * outputs summed into the token's one result (explainer video, transcript
+ * at 2:01 and 3:36); a decode step is paced by the expert bytes it has to
+ * move (Strata write-up, "How Strata Makes It Run" section 2 "Expert Cache
+ * and CPU/GPU Split"). B > 1 serves the short batches of speculative
+ * verification (write-up section 4 "MTP Speculative Decoding"; video at
+ * 5:09), whose drafts are a handful of tokens: B is capped at 8, not 16.
  * (B * H * 2 bytes of activations are staged in LDS: B * H must not exceed
  * 8 * 2048; larger requests return MOE_ERR_SHAPE.)
  * Batch-1 decode is bound by the bytes of the selected experts' weights: a
@@ -202,7 +223,11 @@ moe_status moe_forward_decode(const moe_layer *layer, const void *x, int32_t B, 
 moe_status moe_forward_decode_noalloc(const moe_layer *layer, const void *x, int32_t B, void *y,
                                       int32_t *topk_idx, float *topk_gate, hipStream_t stream);
 
-/* Prefill: T >= 1 tokens x[T][H] -> y[T][H] (bf16). Tokens are grouped by
+/* Prefill: T >= 1 tokens x[T][H] -> y[T][H] (bf16). Prompts are taken in
+ * large pieces, up to 8,192 tokens (Strata README, "How does it work"), and
+ * the prompt's experts run on matrix-core kernels (4090 report, "Fused
+ * prefill kernels"); the arithmetic is that of moe_forward_decode for every
+ * token. Tokens are grouped by
  * expert (histogram, exclusive scan, stable permutation) and each expert's
  * tokens go through an MFMA grouped GEMM with the expert's weights
  * dequantised to bf16 in LDS; a gather combine adds the gated expert
@@ -212,7 +237,10 @@ moe_status moe_forward_prefill(const moe_layer *layer, const void *x, int32_t T,
                                int32_t *topk_idx, float *topk_gate,
                                void *ws, size_t ws_bytes, hipStream_t stream);
 
-/* Between stacked layers (pre-norm residual stream):
+/* Between stacked layers (pre-norm residual stream). The pages' model has
+ * 48 such MoE layers (Strata write-up, section 2; explainer video at 1:37)
+ * but give no layer formula: the plain pre-norm residual form is the
+ * library's reading.
  *   moe_rmsnorm:      z = h / sqrt(mean(h^2) + eps), unit gain, fp32 math
  *   moe_residual_add: h = bf16(h + y)
  * h, z, y: bf16 [T][H]. */
@@ -240,7 +268,8 @@ moe_status moe_stack_decode_layer(const moe_layer *layer, void *h, int32_t B, fl
 /* Host-side packing (no device work; host pointers)                        */
 /* ------------------------------------------------------------------------ */
 
-/* Pack one matrix W[R][K] (row-major source) into the chunk-major layout.
+/* The layout is the library's own (see PACKED WEIGHT LAYOUT; the pages give
+ * none). Pack one matrix W[R][K] (row-major source) into the chunk-major layout.
  *   Q4/Q3: src = int8 codes [R][K] (range-checked), src_scales = fp16 [R][K/32]
  *   F32  : src = float [R][K];  BF16: src = uint16 bf16 [R][K]; src_scales NULL
  * out: moe_matrix_bytes(wt,R,K) bytes; out_scales: moe_matrix_scales(wt,R,K)
@@ -257,6 +286,7 @@ moe_status moe_pack_gate_up(int32_t wt, int32_t I, int32_t H, const void *gate,
 /* Diagnostics                                                              */
 /* ------------------------------------------------------------------------ */
 
+/* Library diagnostics (no passage of the pages). */
 const char *moe_status_string(int32_t status);
 /* Description of the last failure on this thread ("" if none). */
 const char *moe_last_error(void);
