@@ -169,7 +169,6 @@ __device__ __forceinline__ float down_piece_dot(const DownPiece<WT, NCOL>& d, in
 // Kernel A: router rows (blocks < nRB) and shared-expert column groups
 // ---------------------------------------------------------------------------
 constexpr int A_CPR = 8;  // router float4 chunks per lane and batch
-constexpr int A_CPS = 4;  // shared gate/up chunks per lane and batch
 constexpr int A_RPT = 4;  // shared down rows per thread and batch
 
 template <int SWT, int MAXB>

@@ -3,26 +3,27 @@
 // 256 workgroups of 1024 threads, one per CU, all resident at once.
 // Workgroups are dealt round-robin over the 8 XCDs, so the workgroups b
 // with the same b % 8 ("XCD group") share an XCD and its L2 (the first
-// XCD of the deal varies from launch to launch). The XCD groups start one
-// after another (the first about 2.3 us before the last at this size; the
-// workgroups of one group start together), so roles go by start rank
-// r(b) = (b % 8) * 32 + b / 8, the work the routing waits for first:
+// XCD of the deal varies from launch to launch). Back to back, as in a
+// graph replay, all XCDs start within ~0.2 us of each other (launched one
+// at a time after an idle spell, they start one after another over ~2 us).
+// Roles:
 //
-//   ranks [0, nRW)         router: rows 8r .. 8r+7 (two waves a row), fp64
-//                          logits (an fp32 weight times a bf16 activation is
-//                          exact in fp64).
-//   ranks [0, nRG)         routed (after the router rows where both fall on
-//                          one workgroup): (slot, 32 intermediates) each;
-//                          ordered top-k from the logits, fused
-//                          dequantise-GEMV of the 64 gate/up rows + SwiGLU ->
-//                          h (bf16, in LDS), then the matching 32-column
-//                          block of the expert's down matrix (loaded with
-//                          the gate/up rows) times h, scaled by the slot's
-//                          gate: a partial y over all H rows.
-//   ranks [nRG, +nSG)      shared expert, 8 intermediates each: 16 gate/up
+//   b < nR                 router: rr rows each (rr = 2 for E > 256, else 1;
+//                          16 / rr waves a row), fp64 logits (an fp32 weight
+//                          times a bf16 activation is exact in fp64), every
+//                          workgroup first, so the 4 MiB stream over all CUs.
+//   b < nRG                routed: (slot, 32 intermediates) each; ordered
+//                          top-k from the logits, fused dequantise-GEMV of
+//                          the 64 gate/up rows + SwiGLU -> h (bf16, in LDS),
+//                          then the matching 32-column block of the
+//                          expert's down matrix (loaded with the gate/up
+//                          rows) times h, scaled by the slot's gate: a
+//                          partial y over all H rows. Workgroup b < 8 is
+//                          also its XCD's forwarder of the logits.
+//   sg0 <= b < sg0 + nSG   shared expert, 8 intermediates each: 16 gate/up
 //                          rows, SwiGLU -> h, then those 8 columns of the
 //                          shared down matrix times h: a partial y over all
-//                          H rows. These start last and are needed last.
+//                          H rows (sg0 = nRG rounded up to a multiple of 8).
 //
 // The down product is split along the intermediate dimension (split-K), so
 // h never leaves the workgroup that made it and the down weights stream in
@@ -48,11 +49,12 @@
 // cross XCDs are stored and loaded with agent-scope relaxed atomics
 // (coherent across the XCDs' L2s word by word), words that stay inside an
 // XCD are stored with plain stores into that XCD's L2 and read there. The
-// router's logits are written once per XCD group (copy r for the workgroups
-// with b % 8 == r), so each line has a few readers instead of all of them.
+// router's logits cross once, to one forwarder per XCD, which copies them
+// into its XCD's L2 for the other routed workgroups there.
 // Every spin is bounded; one that runs out sets an error bit in the
-// workspace (1: router counts, 2: logits, 4: XCD sums' inputs, 8: final
-// sums' inputs) and lets the workgroup finish, so the kernel always ends.
+// workspace (1: logits or the XCD's ready word, 2: the L2 copy of the
+// logits, 4: XCD sums' inputs, 8: final sums' inputs) and lets the
+// workgroup finish, so the kernel always ends.
 //
 // The tag is the call count each workgroup keeps for itself: workgroup b
 // reads its own counter at the start and writes it back incremented at the
@@ -62,10 +64,11 @@
 // counter for about 1.6 us). The workspace is ready for the next call (and
 // for graph replay) without a memset.
 //
-// Progress: routed units wait only for the routers (router rows never wait),
-// XCD sums only for producers, final sums only for XCD sums, so every value
-// gets written once every workgroup is resident; the path is taken only when
-// the grid fits the chip at one workgroup per CU.
+// Progress: forwarders wait only for the routers (router rows never wait),
+// routed units for their forwarder, XCD sums for producers, final sums for
+// XCD sums, so every value gets written once every workgroup is resident;
+// the path is taken only when the grid fits the chip at one workgroup per
+// CU.
 //
 // No float atomics: each value has one writer and every sum has a fixed
 // order, so results are bitwise reproducible.
@@ -85,29 +88,31 @@ constexpr int F_NX = 8;                         // XCDs: workgroup b runs on XCD
 constexpr int F_PX = F_NW / F_NX;               // workgroups per XCD
 constexpr int F_RPT = 2;                        // down rows per thread (H <= F_RPT * F_THREADS)
 constexpr int F_HMAX = F_RPT * F_THREADS;       // largest H of this path (LDS arrays are sized for it)
-constexpr int F_RCPL = 4;                       // router float4 chunks per lane and batch
+constexpr int F_RRMAX = 2;                      // router rows per workgroup (E <= F_NW * F_RRMAX)
 constexpr uint64_t F_WAIT_TICKS = 1ull << 25;   // ~0.34 s of the 100 MHz wall clock
 
 // Workspace sync area (uint32 words): the error bits in a line of their own,
 // then one call counter per workgroup (8 bytes apart).
 constexpr int SY_LINE = 32;                                   // words per line
-constexpr int SY_NREP = F_NX;                                 // copies of the logits (XCD groups)
+constexpr int SY_NREP = F_NX;                                 // XCD copies of the logits
 constexpr int SY_ERR = 0;
 constexpr int SY_COUNT = SY_LINE;                             // + 2 b
 constexpr int SY_WORDS = SY_COUNT + 2 * F_NW;                 // 2176 bytes
 static_assert(SY_WORDS * 4 <= 4096, "sync area");
-constexpr int F_SLOTS = 4;  // logit buffers and router counters rotate over this many calls
-constexpr int CT_STRIDE = 32;  // uint32 words between router counters (one 128-byte line each)
+constexpr int F_SLOTS = 4;  // logit buffers rotate over this many calls
+constexpr int RDY_STRIDE = 16;  // uint64 words between the XCDs' ready words (one 128-byte line each)
 
 struct FusedGeo {
-  int nRW;   // router workgroups (8 rows each): start ranks [0, nRW)
+  int rr;    // router rows per workgroup (1 or 2)
+  int nR;    // router workgroups: [0, nR), rows rr*b .. rr*b + rr - 1
   int nRG;   // routed units (slot, 32 intermediates): workgroups [0, nRG)
   int sg0;   // shared units (8 intermediates each): workgroups [sg0, sg0 + nSG), sg0 = nRG rounded up to 8
   int nSG;
   int xmask; // XCD groups that hold at least one producer (bit x)
-  int rcount[F_NX];  // router workgroups per XCD group
   uint64_t wait_ticks;  // bound of every device-side wait
 };
+// rank of workgroup b when the workgroups are listed XCD by XCD (the final
+// sums give each XCD a contiguous block of rows)
 __device__ __forceinline__ int start_rank(int b) { return (b % F_NX) * F_PX + b / F_NX; }
 // producer index of workgroup b: shared units first, then routed units; -1 for none
 __device__ __forceinline__ int producer_of(int b, const FusedGeo& G) {
@@ -140,7 +145,6 @@ __device__ __forceinline__ uint32_t ld_u32(const uint32_t* p) {
 __device__ __forceinline__ void flag_error(uint32_t* sync, uint32_t bit) {
   __hip_atomic_fetch_or(sync + SY_ERR, bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ int my_rep() { return blockIdx.x & (SY_NREP - 1); }
 __device__ __forceinline__ bool tag_ok(uint64_t w, uint32_t tag) { return (uint32_t)(w >> 32) == tag; }
 
 // A pair of words written together and loaded once: while either tag is
@@ -164,34 +168,51 @@ __device__ __forceinline__ void settle2(const uint64_t* p0, const uint64_t* p1, 
   }
 }
 
-// Router counters. A router workgroup counts itself in its XCD group's
-// counter (one 128-byte line each) right after issuing its logit stores
-// (the count can arrive first: the logits carry tags and a stale one is
-// read again); the routed workgroups poll the 8 counters (one wave, one
-// load per lane and round) and then read the logits. Polling the logit words
-// themselves (8 KB per workgroup and round) flooded the memory side while
-// the routers were still at work: the logits were seen 3.5 us after the
-// last router finished. The counters of a slot are zeroed two calls before
-// the slot comes round again.
-__device__ __forceinline__ void count_router(uint32_t* ctr) {
-  __syncthreads();
-  if (threadIdx.x == 0) __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void wait_routers(const uint32_t* ctr, const int* want, uint32_t* sync, uint64_t ticks) {
-  if (threadIdx.x < 64) {
-    const int lane = threadIdx.x, g = lane & (F_NX - 1);
-    const uint32_t need = (uint32_t)want[g];
-    const uint32_t* c = ctr + CT_STRIDE * g;
-    uint64_t t0 = 0;
+// The logits reach the routed workgroups in two hops. The routers store
+// them once, at agent scope (one copy in memory). On each XCD one routed
+// workgroup, the forwarder, polls those words (8 KB a round: with 8
+// pollers the memory side is not flooded), copies them into its XCD's L2
+// with plain stores and then raises the XCD's ready word there; the other
+// routed workgroups of the XCD poll that one word, inside the XCD, and read
+// the logits from the L2 copy. (When every routed workgroup polled the
+// memory copy itself, 8 KB a round each, the polls flooded the memory side
+// while the routers were still at work; a counter per XCD group that the
+// routers bumped cost an atomic and then a second trip for the logits.)
+__device__ __forceinline__ void forward_logits(const uint64_t* mem, uint64_t* xc, uint64_t* rdy, int n, uint32_t tag,
+                                               uint32_t* sync, uint64_t ticks) {
+  const int t = threadIdx.x, i = min(t, n - 1);
+  uint64_t w = ld_word_coherent(mem + i);  // clamped, unconditional
+  if (__builtin_amdgcn_ballot_w64(!tag_ok(w, tag)) != 0) {
+    const uint64_t t0 = wall_clock64();
     int it = 0;
     while (true) {
-      const uint32_t v = __hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (__builtin_amdgcn_ballot_w64(v < need) == 0) break;
-      if (it == 0) t0 = wall_clock64();
       __builtin_amdgcn_s_sleep(1);
+      if (!tag_ok(w, tag)) w = ld_word_coherent(mem + i);
+      if (__builtin_amdgcn_ballot_w64(!tag_ok(w, tag)) == 0) break;
       if ((++it & 15) == 0 && wall_clock64() - t0 > ticks) {
-        if (lane == 0) flag_error(sync, 1u);
+        if ((t & 63) == 0) flag_error(sync, 1u);
         break;
+      }
+    }
+  }
+  if (t < n) st_word_xcd(xc + t, (uint32_t)w, tag);
+  __syncthreads();  // every thread's copy has reached the L2 before the ready word
+  if (t == 0) st_word_xcd(rdy, 0u, tag);
+}
+__device__ __forceinline__ void wait_ready(const uint64_t* rdy, uint32_t tag, uint32_t* sync, uint64_t ticks) {
+  if (threadIdx.x < 64) {
+    uint64_t w = ld_word_coherent(rdy);
+    if (!tag_ok(w, tag)) {
+      const uint64_t t0 = wall_clock64();
+      int it = 0;
+      while (true) {
+        __builtin_amdgcn_s_sleep(1);
+        w = ld_word_coherent(rdy);
+        if (tag_ok(w, tag)) break;
+        if ((++it & 15) == 0 && wall_clock64() - t0 > ticks) {
+          if (threadIdx.x == 0) flag_error(sync, 1u);
+          break;
+        }
       }
     }
   }
@@ -244,77 +265,66 @@ __device__ __forceinline__ uint32_t scale_pair(uint32_t v, float inv) {
 // hundreds of workgroups at once serve them one after another).
 // ---------------------------------------------------------------------------
 struct RouterRegs {
-  float4 w[F_RCPL];
+  float4 w;
   float bias;
 };
 
 // Issue the loads of this workgroup's router rows (with the token's, so that
-// both are in flight together): lane l of wave w (row 8rw + w % 8, half
-// w / 8) takes float4 columns c_lo + l + 64i, clamped to the half row and
-// masked when summed. Every workgroup issues them (a load under a branch
-// makes the compiler wait for it where the branch joins); a workgroup that
-// is not a router (act false) reads the first 16 bytes of the router, once.
-__device__ __forceinline__ void router_issue(const LayerDev& L, bool act, int rw, RouterRegs& R) {
-  static_assert(F_WAVES == 16, "two waves per router row");
+// both are in flight together): rr rows (1 or 2) of rr*b .. rr*b + rr - 1,
+// P = 16 / rr waves per row; wave w takes row w / P and the P-th part
+// w % P of its float4 columns, one per lane (H <= F_HMAX: a part holds at
+// most 64). Every workgroup issues them, clamped inside the row and masked
+// when summed (a load under a branch makes the compiler wait for it where
+// the branch joins); a workgroup that is not a router reads the first 16
+// bytes of the router.
+__device__ __forceinline__ void router_issue(const LayerDev& L, bool act, int rw, int rr, RouterRegs& R) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int e = rw * 8 + (wave & 7), hh = wave >> 3;
+  const int P = F_WAVES / rr;
+  const int e = rw * rr + wave / P;
   const bool valid = act && e < L.E;
-  const int n4 = L.H >> 2, c_lo = hh * (n4 >> 1), c_hi = hh ? n4 : (n4 >> 1);
+  const int n4 = L.H >> 2;
+  const int c = (wave % P) * n4 / P + lane;
   const float4* wr = reinterpret_cast<const float4*>(L.router_w + (size_t)(valid ? e : 0) * L.H);
-#pragma unroll
-  for (int i = 0; i < F_RCPL; i++) R.w[i] = wr[act ? min(c_lo + lane + 64 * i, c_hi - 1) : 0];
+  R.w = wr[act ? min(c, n4 - 1) : 0];
   // the bias with the weights (a load after the sum would be one more
-  // memory round trip on the way to the top-k), unconditionally: a load
-  // inside a branch makes the compiler wait for every load in flight where
-  // the branch joins
+  // memory round trip on the way to the top-k)
   const float* bp = L.router_b ? L.router_b + (valid ? e : 0) : L.router_w;
   R.bias = *bp;
 }
 
-// The logits of the rows from the staged activations xs (LDS, bf16): the
-// two halves of a row are summed in order; the logit goes out as two tagged
-// words in every XCD group's copy.
-__device__ __forceinline__ void router_finish(const LayerDev& L, const uint16_t* xs, const RouterRegs& R, int rw,
+// The logits of the rows from the staged activations xs (LDS, bf16): the P
+// parts of a row are summed in part order by the row's first wave; the
+// logit goes out as two tagged words (low and high half of the fp64 value)
+// in the memory copy.
+__device__ __forceinline__ void router_finish(const LayerDev& L, const uint16_t* xs, const RouterRegs& R, int rw, int rr,
                                               uint64_t* logits, double* s_rt, uint32_t tag) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int e = rw * 8 + (wave & 7), hh = wave >> 3;
+  const int P = F_WAVES / rr, p = wave % P;
+  const int e = rw * rr + wave / P;
   const bool valid = e < L.E;
-  const int n4 = L.H >> 2, c_lo = hh * (n4 >> 1), c_hi = hh ? n4 : (n4 >> 1);
+  const int n4 = L.H >> 2;
+  const int c = p * n4 / P + lane;
+  const bool in = valid && c < (p + 1) * n4 / P;
   const uint2* xv = reinterpret_cast<const uint2*>(xs);
   // the weights enter the arithmetic only here: without this the compiler
   // converts them to fp64 right where they are loaded, which makes the
   // workgroup wait for them before it stages x
-  float4 wr[F_RCPL];
-#pragma unroll
-  for (int i = 0; i < F_RCPL; i++) {
-    wr[i] = R.w[i];
-    asm volatile("" : "+v"(wr[i].x), "+v"(wr[i].y), "+v"(wr[i].z), "+v"(wr[i].w));
-  }
+  float4 w = R.w;
+  asm volatile("" : "+v"(w.x), "+v"(w.y), "+v"(w.z), "+v"(w.w));
   float bias = R.bias;
   asm volatile("" : "+v"(bias));
-  double a0 = 0.0, a1 = 0.0;
-#pragma unroll
-  for (int i = 0; i < F_RCPL; i++) {
-    const int c = c_lo + lane + 64 * i;
-    const bool in = valid && c < c_hi;
-    const float4 w = in ? wr[i] : make_float4(0.f, 0.f, 0.f, 0.f);
-    const uint2 xx = in ? xv[c] : make_uint2(0u, 0u);
-    a0 = __builtin_fma((double)w.x, (double)bf16_lo(xx.x), a0);
-    a1 = __builtin_fma((double)w.y, (double)bf16_hi(xx.x), a1);
-    a0 = __builtin_fma((double)w.z, (double)bf16_lo(xx.y), a0);
-    a1 = __builtin_fma((double)w.w, (double)bf16_hi(xx.y), a1);
-  }
+  if (!in) w = make_float4(0.f, 0.f, 0.f, 0.f);
+  const uint2 xx = xv[in ? c : 0];
+  double a0 = __builtin_fma((double)w.z, (double)bf16_lo(xx.y), (double)w.x * (double)bf16_lo(xx.x));
+  double a1 = __builtin_fma((double)w.w, (double)bf16_hi(xx.y), (double)w.y * (double)bf16_hi(xx.x));
   const double part = wave_total_f64(a0 + a1);
-  if (hh == 1 && lane == 0) s_rt[wave & 7] = part;
+  if (lane == 0) s_rt[wave] = part;
   __syncthreads();
-  if (hh == 0 && valid && lane < SY_NREP) {
-    const double tot = part + s_rt[wave];
+  if (p == 0 && valid && lane < 2) {
+    double tot = s_rt[wave];
+    for (int q = 1; q < P; q++) tot += s_rt[wave + q];
     const uint64_t v = (uint64_t)__double_as_longlong(tot + (L.router_b ? (double)bias : 0.0));
-    // two words (low, high half of the fp64 logit), each with the tag, in
-    // every XCD group's copy (lane r writes copy r)
-    uint64_t* rl = logits + (size_t)lane * 2 * L.E;
-    st_word(rl + 2 * e, (uint32_t)v, tag);
-    st_word(rl + 2 * e + 1, (uint32_t)(v >> 32), tag);
+    st_word(logits + 2 * e + lane, lane ? (uint32_t)(v >> 32) : (uint32_t)v, tag);
   }
 }
 
@@ -797,7 +807,7 @@ __global__ __launch_bounds__(F_THREADS, 4) void k_decode1(LayerDev L, const uint
   __shared__ __align__(16) uint16_t s_x[F_HMAX];
   __shared__ __align__(16) float s_xsum[F_HMAX / 32];
   __shared__ __align__(16) float s_red[F_THREADS];
-  __shared__ double s_rt[8];
+  __shared__ double s_rt[F_WAVES];
   __shared__ __align__(16) BlockTopk s_tk;
   __shared__ int s_idx[16];
   __shared__ float s_gate[16];
@@ -809,13 +819,12 @@ __global__ __launch_bounds__(F_THREADS, 4) void k_decode1(LayerDev L, const uint
   const int b = blockIdx.x, rank = start_rank(b);
   // this call's tag: the workgroup's own call count + 1 (the same in every workgroup)
   const uint32_t tag = ld_u32(my_counter(ws.sync)) + 1u;
-  uint64_t* tl = reinterpret_cast<uint64_t*>(ws.logits) + (size_t)(tag % F_SLOTS) * SY_NREP * 2 * L.E;
-  uint32_t* ct = ws.ctr + (size_t)(tag % F_SLOTS) * F_NX * CT_STRIDE;  // router counters of this call
-  if (b == 0 && threadIdx.x < F_NX)  // the slot used two calls from now is idle: zero its counters
-    __hip_atomic_store(ws.ctr + ((size_t)((tag + 2) % F_SLOTS) * F_NX + threadIdx.x) * CT_STRIDE, 0u,
-                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  // this call's logits: the memory copy, then one copy per XCD
+  uint64_t* tl = reinterpret_cast<uint64_t*>(ws.logits) + (size_t)(tag % F_SLOTS) * (1 + SY_NREP) * 2 * L.E;
+  uint64_t* tx = tl + (size_t)(1 + b % F_NX) * 2 * L.E;
+  uint64_t* rdy = reinterpret_cast<uint64_t*>(ws.ctr) + (size_t)(b % F_NX) * RDY_STRIDE;
   uint64_t* part = ws.part_words;  // [nSG + nRG][H], in the producers' XCD L2s
-  const bool is_router = rank < G.nRW;
+  const bool is_router = b < G.nR;
   const bool is_routed = b < G.nRG;
   const bool is_shared = b >= G.sg0 && b < G.sg0 + G.nSG;
   // the token and the router rows are loaded together (straight-line code:
@@ -827,7 +836,7 @@ __global__ __launch_bounds__(F_THREADS, 4) void k_decode1(LayerDev L, const uint
   const int n8 = H >> 3;
   const uint4 tv = reinterpret_cast<const uint4*>(src)[min((int)threadIdx.x, n8 - 1)];  // clamped, unconditional
   RouterRegs rrg;
-  router_issue(L, is_router, rank, rrg);
+  router_issue(L, is_router, b, G.rr, rrg);
   {
     uint4 v = tv;
     if (stk) {
@@ -847,10 +856,7 @@ __global__ __launch_bounds__(F_THREADS, 4) void k_decode1(LayerDev L, const uint
     }
   }
   __syncthreads();
-  if (is_router) {
-    router_finish(L, s_x, rrg, rank, tl, s_rt, tag);
-    count_router(ct + CT_STRIDE * (b % F_NX));
-  }
+  if (is_router) router_finish(L, s_x, rrg, b, G.rr, tl, s_rt, tag);
   if (is_shared) {
     // shared expert, intermediates 8su .. 8su+7 (needed only by the sums)
     constexpr int SW = (SWT == MOE_W_F32) ? MOE_W_F32 : MOE_W_BF16;
@@ -870,8 +876,9 @@ __global__ __launch_bounds__(F_THREADS, 4) void k_decode1(LayerDev L, const uint
     if (stk && S.z_out && ru == 0)
       for (int i = threadIdx.x; i < (H >> 3); i += F_THREADS)
         reinterpret_cast<uint4*>(S.z_out)[i] = reinterpret_cast<const uint4*>(xs)[i];
-    wait_routers(ct, G.rcount, ws.sync, G.wait_ticks);
-    block_topk(tl + (size_t)my_rep() * 2 * L.E, L.E, L.k, tag, ws.sync, G.wait_ticks, s_tk);
+    if (ru < F_NX) forward_logits(tl, tx, rdy, 2 * L.E, tag, ws.sync, G.wait_ticks);  // this XCD's forwarder
+    else wait_ready(rdy, tag, ws.sync, G.wait_ticks);
+    block_topk(tx, L.E, L.k, tag, ws.sync, G.wait_ticks, s_tk);
     const int gpe = I >> 5;
     const int u = ru / gpe, q = ru - u * gpe;
     const int e = min(max(s_tk.out[u].i, 0), L.E - 1);  // in range whatever the logits held
@@ -927,13 +934,13 @@ size_t decode1_lds(int H, int I, int k, bool has_shared) {
 
 static int producers(int I, int k, bool has_shared) { return (has_shared ? I / 8 : 0) + k * (I / 32); }
 
-size_t decode1_logit_words(int E) { return (size_t)F_SLOTS * SY_NREP * 2 * E; }
+size_t decode1_logit_words(int E) { return (size_t)F_SLOTS * (1 + SY_NREP) * 2 * E; }
 
 size_t decode1_part_words(int H, int I, int k, bool has_shared) { return (size_t)producers(I, k, has_shared) * H; }
 
 size_t decode1_xsum_words(int H) { return (size_t)F_NX * H; }
 
-size_t decode1_counter_words() { return (size_t)F_SLOTS * F_NX * CT_STRIDE; }
+size_t decode1_counter_words() { return (size_t)F_NX * RDY_STRIDE * 2; }  // the XCDs' ready words
 
 // Workgroups that are sure to be resident together: one per CU (the launch
 // bounds keep a workgroup within a CU's registers; its LDS is ~24 KB).
@@ -953,9 +960,9 @@ bool decode1_fits(int E, int H, int I, int k, bool has_shared) {
   // F_NV logits per lane in the top-k, F_RPT down rows per thread (the LDS
   // arrays are sized for H <= F_HMAX), at most one shared or routed unit per
   // workgroup, and a grid that is resident at once
-  const int nRW = (E + 7) / 8, nSG = has_shared ? I / 8 : 0, nRG = k * (I / 32);
+  const int nSG = has_shared ? I / 8 : 0, nRG = k * (I / 32);
   const int sg0 = (nRG + F_NX - 1) / F_NX * F_NX;
-  return E <= 64 * F_NV && H <= F_HMAX && I <= 1024 && nRW <= F_NW && sg0 + nSG <= F_NW &&
+  return E <= 64 * F_NV && E <= F_NW * F_RRMAX && H <= F_HMAX && I <= 1024 && sg0 + nSG <= F_NW &&
          F_NW <= decode1_capacity();
 }
 
@@ -963,16 +970,14 @@ template <int WT, int SWT>
 static hipError_t launch_fused_t(const LayerDev& L, const uint16_t* x, uint16_t* y, int32_t* idx_out, float* gate_out,
                                  const DecodeWs& ws, hipStream_t st, const StackIo& S) {
   FusedGeo G;
-  G.nRW = (L.E + 7) / 8;
+  G.rr = L.E > F_NW ? 2 : 1;
+  G.nR = (L.E + G.rr - 1) / G.rr;
   G.nSG = (SWT == MOE_W_NONE) ? 0 : L.I / 8;
   G.nRG = L.k * (L.I / 32);
   G.sg0 = (G.nRG + F_NX - 1) / F_NX * F_NX;
   G.xmask = 0;
-  for (int g = 0; g < F_NX; g++) G.rcount[g] = 0;
-  for (int b = 0; b < F_NW; b++) {
+  for (int b = 0; b < F_NW; b++)
     if (b < G.nRG || (b >= G.sg0 && b < G.sg0 + G.nSG)) G.xmask |= 1 << (b % F_NX);
-    if ((b % F_NX) * F_PX + b / F_NX < G.nRW) G.rcount[b % F_NX]++;  // start rank < nRW: a router
-  }
   G.wait_ticks = g_wait_ticks;
   return launch_k(KC_DEC_FUSED, k_decode1<WT, SWT>, dim3(F_NW), dim3(F_THREADS), 0, st, L, x, y, idx_out, gate_out,
                   ws, G, S);
