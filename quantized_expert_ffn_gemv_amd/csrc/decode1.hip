@@ -725,10 +725,15 @@ __device__ __forceinline__ void role_sum_xcd(const uint64_t* part, uint64_t* xs,
     int it = 0;
     while (true) {
       __builtin_amdgcn_s_sleep(1);
+      // both words again, unconditionally: a load under a branch waits for
+      // its answer before the next one is sent
+      uint64_t nw[2];
+#pragma unroll
+      for (int n = 0; n < 2; n++) nw[n] = ld_word_coherent(pw[n]);
       stale = false;
 #pragma unroll
       for (int n = 0; n < 2; n++) {
-        if ((p[n] >= 0) && !tag_ok(w[n], tag)) w[n] = ld_word_coherent(pw[n]);
+        w[n] = tag_ok(w[n], tag) ? w[n] : nw[n];
         stale |= (p[n] >= 0) && !tag_ok(w[n], tag);
       }
       if (__builtin_amdgcn_ballot_w64(stale) == 0) break;
