@@ -105,9 +105,18 @@ size_t carve_decode(const moe_layer* L, int B, uint8_t* base, moe::DecodeWs* ws)
   w.sync = reinterpret_cast<uint32_t*>(take(DECODE_SYNC_BYTES));
   const bool has_s = L->shared_wtype != MOE_W_NONE;
   const bool one_kernel = B == 1 && moe::decode1_fits(L->n_experts, L->hidden, L->inter, L->top_k, has_s);
-  // logits: [B][E] fp64 (four kernels) or rotating slots of per-XCD-group [E] x 16 B tagged words (one kernel)
-  w.logits = reinterpret_cast<double*>(take(one_kernel ? 8 * moe::decode1_logit_words((int)E) : (size_t)E * 64));
-  if (one_kernel) {
+  const bool one_kernel_b =
+      B > 1 && moe::decode1b_fits(L->expert_wtype, L->n_experts, L->hidden, L->inter, L->top_k, has_s, B);
+  // logits: [B][E] fp64 (four kernels), rotating slots of per-XCD-group [E] x 16 B tagged words (one kernel,
+  // batch 1) or [B][E] x 16 B tagged words (one kernel, batched)
+  w.logits = reinterpret_cast<double*>(take(one_kernel     ? 8 * moe::decode1_logit_words((int)E)
+                                             : one_kernel_b ? (size_t)B * E * 16
+                                                            : (size_t)E * 64));
+  if (one_kernel_b) {
+    w.part_words = reinterpret_cast<uint64_t*>(take(8 * moe::decode1b_part_words(L->hidden, B)));
+    w.xsum_words = reinterpret_cast<uint64_t*>(take(8 * moe::decode1b_xsum_words(L->hidden, B)));
+    w.res_words = reinterpret_cast<uint64_t*>(take(8 * moe::decode1b_res_words()));
+  } else if (one_kernel) {
     w.part_words = reinterpret_cast<uint64_t*>(take(8 * moe::decode1_part_words(L->hidden, L->inter, L->top_k, has_s)));
     w.xsum_words = reinterpret_cast<uint64_t*>(take(8 * moe::decode1_xsum_words(L->hidden)));
     w.ctr = reinterpret_cast<uint32_t*>(take(4 * moe::decode1_counter_words()));
@@ -282,8 +291,11 @@ moe_status moe_forward_decode(const moe_layer* layer, const void* x, int32_t B, 
   if (B < 1 || B > MOE_DECODE_MAX_TOKENS) return fail(MOE_ERR_SHAPE, "B=%d not in [1, %d]", B, MOE_DECODE_MAX_TOKENS);
   if ((int64_t)B * layer->hidden > 8 * 2048)
     return fail(MOE_ERR_SHAPE, "B*H=%d exceeds the decode staging limit %d", B * layer->hidden, 8 * 2048);
+  const bool has_s = layer->shared_wtype != MOE_W_NONE;
   const bool one_kernel =
-      B == 1 && moe::decode1_fits(layer->n_experts, layer->hidden, layer->inter, layer->top_k, layer->shared_wtype != MOE_W_NONE);
+      (B == 1 && moe::decode1_fits(layer->n_experts, layer->hidden, layer->inter, layer->top_k, has_s)) ||
+      (B > 1 && moe::decode1b_fits(layer->expert_wtype, layer->n_experts, layer->hidden, layer->inter, layer->top_k,
+                                   has_s, B));
   if (!one_kernel && moe::decode_lds_b(layer->expert_wtype, B, layer->hidden, layer->n_experts, layer->top_k) > 65536)
     return fail(MOE_ERR_SHAPE, "B=%d with H=%d, E=%d, k=%d needs more than 64 KiB of LDS", B, layer->hidden,
                 layer->n_experts, layer->top_k);
@@ -364,8 +376,11 @@ moe_status moe_stack_decode_layer(const moe_layer* layer, void* h, int32_t B, fl
   if ((int64_t)B * layer->hidden > 8 * 2048)
     return fail(MOE_ERR_SHAPE, "B*H=%d exceeds the decode staging limit %d", B * layer->hidden, 8 * 2048);
   if (!(eps >= 0.0f)) return fail(MOE_ERR_SHAPE, "eps must be >= 0");
+  const bool has_s = layer->shared_wtype != MOE_W_NONE;
   const bool one_kernel =
-      B == 1 && moe::decode1_fits(layer->n_experts, layer->hidden, layer->inter, layer->top_k, layer->shared_wtype != MOE_W_NONE);
+      (B == 1 && moe::decode1_fits(layer->n_experts, layer->hidden, layer->inter, layer->top_k, has_s)) ||
+      (B > 1 && moe::decode1b_fits(layer->expert_wtype, layer->n_experts, layer->hidden, layer->inter, layer->top_k,
+                                   has_s, B));
   if (!one_kernel && moe::decode_lds_b(layer->expert_wtype, B, layer->hidden, layer->n_experts, layer->top_k) > 65536)
     return fail(MOE_ERR_SHAPE, "B=%d with H=%d, E=%d, k=%d needs more than 64 KiB of LDS", B, layer->hidden,
                 layer->n_experts, layer->top_k);

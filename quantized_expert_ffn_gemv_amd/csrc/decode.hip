@@ -827,6 +827,8 @@ hipError_t launch_decode(const LayerDev& L, const uint16_t* x, int B, uint16_t* 
                          const DecodeWs& ws, hipStream_t st) {
   if (B == 1 && decode1_fits(L.E, L.H, L.I, L.k, L.swt != MOE_W_NONE))
     return launch_decode_fused(L, x, y, idx_out, gate_out, ws, st);
+  if (B > 1 && decode1b_fits(L.wt, L.E, L.H, L.I, L.k, L.swt != MOE_W_NONE, B))
+    return launch_decode_fused_b(L, x, B, y, idx_out, gate_out, ws, st);
   switch (L.wt) {
     case MOE_W_Q4: return launch_s<MOE_W_Q4>(L, x, B, y, idx_out, gate_out, ws, st);
     case MOE_W_Q3: return launch_s<MOE_W_Q3>(L, x, B, y, idx_out, gate_out, ws, st);

@@ -1007,4 +1007,729 @@ hipError_t launch_decode_fused(const LayerDev& L, const uint16_t* x, uint16_t* y
   }
 }
 
+
+// ===========================================================================
+// Batched decode, B = 2..8 tokens, as a single kernel
+// ===========================================================================
+// The batch-1 kernel's structure with the batch folded in:
+//   - router rows (every workgroup, as at batch 1) dotted with all B tokens;
+//   - each XCD's forwarder (b < 8) computes the B ordered top-k's (one wave
+//     per token), the batch's unique experts in order of first appearance
+//     (slot order t k + r) with the mask of the tokens that chose each, and
+//     hands that on inside its XCD as tagged words (FB_NRES of them);
+//   - shared units (8 intermediates each) on workgroups 8 .. 8 + nSG - 1,
+//     for all B tokens, while the routing is being made;
+//   - routed units (unique expert j, 32 intermediates q), nu * I/32 of
+//     them, dealt round-robin from workgroup 8 + nSG on: an expert chosen by
+//     several tokens is streamed once and dotted with each of them;
+//   - every workgroup adds its units' down products into a partial y per
+//     token (2 rows per thread and token, registers), written once for the
+//     tokens it touched; the XCD-level and final sums are those of batch 1,
+//     per token.
+// Waits: forwarders for the routers, the others for their forwarder's
+// routing words, XCD sums for the partials of the touched (workgroup,
+// token) pairs of their XCD, final sums for the XCD sums.
+constexpr int FB_MAXB = 8;
+constexpr int FB_XMAX = 16384;                         // B H: bf16 values of the staged batch
+constexpr int FB_SLOTS = FB_MAXB * 16;                 // B k <= 128
+constexpr int FB_RES_U = 1;                            // word 1 + j: expert | token mask << 16
+constexpr int FB_RES_I = FB_RES_U + FB_SLOTS;          // word FB_RES_I + s: expert of slot s = t k + r | its unique index << 16
+constexpr int FB_RES_G = FB_RES_I + FB_SLOTS;          // word FB_RES_G + s: its gate (fp32 bits)
+constexpr int FB_NRES = FB_RES_G + FB_SLOTS;           // 385 words (word 0: nu)
+constexpr int FB_RES_STRIDE = 512;                     // words per XCD
+static_assert(FB_NRES <= FB_RES_STRIDE && FB_NRES <= F_THREADS, "routing words");
+constexpr int FB_RED = FB_MAXB * F_WAVES * 64;         // floats of the reduction area (also the top-k scratch)
+static_assert(FB_MAXB * TOPK_SCRATCH <= FB_RED * 4, "top-k scratch fits the reduction area");
+
+struct BatchGeo {
+  int B;
+  int rr, nR;   // router rows per workgroup, router workgroups
+  int nSG;      // shared units: workgroups 8 .. 8 + nSG - 1
+  int gpe;      // routed units per expert (I / 32)
+  int uoff;     // routed unit u runs on workgroup (uoff + u) % 256
+  uint64_t wait_ticks;
+};
+
+// Router rows dotted with all B tokens: the parts of a row are summed in
+// part order by the row's first wave, per token (lanes 2t, 2t + 1 store
+// token t's low and high words).
+__device__ __forceinline__ void router_finish_b(const LayerDev& L, const uint16_t* xs, int B, const RouterRegs& R,
+                                                int rw, int rr, uint64_t* logits, double* s_rt, uint32_t tag) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int P = F_WAVES / rr, p = wave % P;
+  const int e = rw * rr + wave / P;
+  const bool valid = e < L.E;
+  const int n4 = L.H >> 2;
+  const int c = p * n4 / P + lane;
+  const bool in = valid && c < (p + 1) * n4 / P;
+  float4 w = R.w;
+  asm volatile("" : "+v"(w.x), "+v"(w.y), "+v"(w.z), "+v"(w.w));
+  float bias = R.bias;
+  asm volatile("" : "+v"(bias));
+  if (!in) w = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+  for (int t = 0; t < FB_MAXB; t++) {
+    if (t < B) {
+      const uint2 xx = reinterpret_cast<const uint2*>(xs + (size_t)t * L.H)[in ? c : 0];
+      const double a0 = __builtin_fma((double)w.z, (double)bf16_lo(xx.y), (double)w.x * (double)bf16_lo(xx.x));
+      const double a1 = __builtin_fma((double)w.w, (double)bf16_hi(xx.y), (double)w.y * (double)bf16_hi(xx.x));
+      const double part = wave_total_f64(a0 + a1);
+      if (lane == 0) s_rt[wave * FB_MAXB + t] = part;
+    }
+  }
+  __syncthreads();
+  if (p == 0 && valid && lane < 2 * B) {
+    const int t = lane >> 1;
+    double tot = s_rt[wave * FB_MAXB + t];
+    for (int q = 1; q < P; q++) tot += s_rt[(wave + q) * FB_MAXB + t];
+    const uint64_t v = (uint64_t)__double_as_longlong(tot + (L.router_b ? (double)bias : 0.0));
+    st_word(logits + (size_t)t * 2 * L.E + 2 * e + (lane & 1), (lane & 1) ? (uint32_t)(v >> 32) : (uint32_t)v, tag);
+  }
+}
+
+// Forwarder: the ordered top-k of token t by wave t (the memory copy of its
+// logits, polled until every word is current; bounded), then the batch's
+// unique experts and masks, published into this XCD's L2 (every word, every
+// call, so the readers can check every tag).
+__device__ __forceinline__ void fwd_routing_b(const LayerDev& L, const uint64_t* logits, int B, uint32_t tag,
+                                              uint32_t* sync, uint64_t ticks, uint8_t* scratch, int* s_mark,
+                                              int* s_urank, int* s_wcnt, int* s_nu, int* s_uexp, uint32_t* s_umask,
+                                              int* s_sidx, int* s_suid, float* s_sgate, uint64_t* res,
+                                              int32_t* idx_out, float* gate_out) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, t0 = threadIdx.x;
+  const int E = L.E, k = L.k, nslot = B * k;
+  if (wave < B) {
+    const uint64_t* lg = logits + (size_t)wave * 2 * E;
+    uint64_t wl[F_NV], wh[F_NV];
+#pragma unroll
+    for (int i = 0; i < F_NV; i++) {
+      const int e = min(lane + 64 * i, E - 1);
+      wl[i] = ld_word_coherent(lg + 2 * e);
+      wh[i] = ld_word_coherent(lg + 2 * e + 1);
+    }
+    bool stale = false;
+#pragma unroll
+    for (int i = 0; i < F_NV; i++) stale |= !tag_ok(wl[i], tag) || !tag_ok(wh[i], tag);
+    if (__builtin_amdgcn_ballot_w64(stale) != 0) {
+      const uint64_t c0 = wall_clock64();
+      int it = 0;
+      while (true) {
+        __builtin_amdgcn_s_sleep(2);
+        uint64_t nl[F_NV], nh[F_NV];
+#pragma unroll
+        for (int i = 0; i < F_NV; i++) {
+          const int e = min(lane + 64 * i, E - 1);
+          nl[i] = ld_word_coherent(lg + 2 * e);
+          nh[i] = ld_word_coherent(lg + 2 * e + 1);
+        }
+        stale = false;
+#pragma unroll
+        for (int i = 0; i < F_NV; i++) {
+          wl[i] = tag_ok(wl[i], tag) ? wl[i] : nl[i];
+          wh[i] = tag_ok(wh[i], tag) ? wh[i] : nh[i];
+          stale |= !tag_ok(wl[i], tag) || !tag_ok(wh[i], tag);
+        }
+        if (__builtin_amdgcn_ballot_w64(stale) == 0) break;
+        if ((++it & 15) == 0 && wall_clock64() - c0 > ticks) {
+          if (lane == 0) flag_error(sync, 2u);
+          break;
+        }
+      }
+    }
+    double v[F_NV];
+#pragma unroll
+    for (int i = 0; i < F_NV; i++)
+      v[i] = (lane + 64 * i < E) ? __longlong_as_double((long long)(((wh[i] & 0xFFFFFFFFull) << 32) | (wl[i] & 0xFFFFFFFFull)))
+                                 : -__builtin_inf();
+    int mi;
+    float mg;
+    wave_topk<F_NV>(v, E, k, lane, scratch + (size_t)wave * TOPK_SCRATCH, mi, mg);
+    if (lane < k) {
+      s_sidx[wave * k + lane] = mi;
+      s_sgate[wave * k + lane] = mg;
+    }
+  }
+  // unique experts in slot order of first appearance, and their token masks
+  for (int e = t0; e < E; e += F_THREADS) s_mark[e] = 0x7FFFFFFF;
+  __syncthreads();
+  if (t0 < nslot) atomicMin(&s_mark[s_sidx[t0]], t0);
+  __syncthreads();
+  const bool first = t0 < nslot && s_mark[s_sidx[t0]] == t0;
+  const uint64_t bal = __builtin_amdgcn_ballot_w64(first);
+  if (lane == 0 && wave < 2) s_wcnt[wave] = __popcll(bal);
+  if (t0 < FB_SLOTS) s_umask[t0] = 0u;
+  __syncthreads();
+  const int rank = (wave == 1 ? s_wcnt[0] : 0) + __popcll(bal & ((1ull << lane) - 1ull));
+  if (first) {
+    s_urank[t0] = rank;
+    s_uexp[rank] = s_sidx[t0];
+  }
+  __syncthreads();
+  if (t0 < nslot) atomicOr(&s_umask[s_urank[s_mark[s_sidx[t0]]]], 1u << (t0 / k));
+  if (t0 == 0) *s_nu = s_wcnt[0] + s_wcnt[1];
+  __syncthreads();
+  const int nu = *s_nu;
+  if (t0 < FB_NRES) {
+    uint32_t pl = 0u;
+    if (t0 == 0) {
+      pl = (uint32_t)nu;
+    } else if (t0 < FB_RES_I) {
+      const int j = t0 - FB_RES_U;
+      pl = j < nu ? ((uint32_t)s_uexp[j] | (s_umask[j] << 16)) : 0u;
+    } else if (t0 < FB_RES_G) {
+      const int sl = t0 - FB_RES_I;
+      pl = sl < nslot ? ((uint32_t)s_sidx[sl] | ((uint32_t)s_urank[s_mark[s_sidx[sl]]] << 16)) : 0u;
+    } else {
+      const int sl = t0 - FB_RES_G;
+      pl = sl < nslot ? __float_as_uint(s_sgate[sl]) : 0u;
+    }
+    st_word_xcd(res + t0, pl, tag);
+  }
+  if (idx_out && t0 < nslot) idx_out[t0] = s_sidx[t0];
+  if (gate_out && t0 < nslot) gate_out[t0] = s_sgate[t0];
+  if (t0 < nslot) s_suid[t0] = s_urank[s_mark[s_sidx[t0]]];
+}
+
+// The other workgroups: the XCD's routing words (bounded poll), into LDS.
+__device__ __forceinline__ void wait_routing_b(const LayerDev& L, const uint64_t* res, int B, uint32_t tag,
+                                               uint32_t* sync, uint64_t ticks, int* s_nu, int* s_uexp,
+                                               uint32_t* s_umask, int* s_sidx, int* s_suid, float* s_sgate) {
+  const int t0 = threadIdx.x;
+  if (t0 < FB_NRES) {
+    uint64_t w = ld_word_coherent(res + t0);
+    if (__builtin_amdgcn_ballot_w64(!tag_ok(w, tag)) != 0) {
+      const uint64_t c0 = wall_clock64();
+      int it = 0;
+      while (true) {
+        __builtin_amdgcn_s_sleep(1);
+        const uint64_t nw = ld_word_coherent(res + t0);
+        w = tag_ok(w, tag) ? w : nw;
+        if (__builtin_amdgcn_ballot_w64(!tag_ok(w, tag)) == 0) break;
+        if ((++it & 15) == 0 && wall_clock64() - c0 > ticks) {
+          if ((t0 & 63) == 0) flag_error(sync, 1u);
+          break;
+        }
+      }
+    }
+    const uint32_t pl = (uint32_t)w;
+    // clamped: in range whatever the words held
+    if (t0 == 0) {
+      *s_nu = (int)min(pl, (uint32_t)(B * L.k));
+    } else if (t0 < FB_RES_I) {
+      s_uexp[t0 - FB_RES_U] = min((int)(pl & 0xFFFFu), L.E - 1);
+      s_umask[t0 - FB_RES_U] = pl >> 16;
+    } else if (t0 < FB_RES_G) {
+      s_sidx[t0 - FB_RES_I] = (int)min(pl & 0xFFFFu, (uint32_t)(L.E - 1));
+      s_suid[t0 - FB_RES_I] = (int)min(pl >> 16, (uint32_t)(FB_SLOTS - 1));
+    } else {
+      s_sgate[t0 - FB_RES_G] = __uint_as_float(pl);
+    }
+  }
+  __syncthreads();
+}
+
+template <int WT>
+__device__ __forceinline__ void qunpack32_m(const Raw& r, uint32_t (&p)[16], uint32_t magic) {
+  if constexpr (WT == MOE_W_Q4) {
+#pragma unroll
+    for (int j = 0; j < 4; j++)
+#pragma unroll
+      for (int t = 0; t < 4; t++) p[4 * j + t] = ((r.w[j] >> (4 * t)) & 0x000F000Fu) | magic;
+  } else {
+    (void)magic;
+    q3_pairs<BF16_MAGIC2>(r.w[0], r.w[1], r.w[2], p);
+  }
+}
+
+// gate_up_h for the tokens in `mask` (of B): each chunk is unpacked once and
+// dotted with each of them; token t's h goes to s_hb[32 t + j], j < RPW / 2.
+// s_red holds [token][wave][RPW] row sums.
+template <int WT, int RPW, int MAXB, typename After>
+__device__ __forceinline__ void gate_up_hb(const uint8_t* __restrict__ gu, const uint16_t* __restrict__ gus, int H, int R,
+                                           int q, int hf, const uint16_t* xs, const float* xsum, int B, uint32_t mask,
+                                           float* s_red, uint16_t* s_hb, After&& after_first_issue) {
+  constexpr int KC = kchunk<WT>();
+  constexpr int NKP = F_THREADS / RPW;
+  constexpr int NB = F_GU_NB;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int rr = lane % RPW;
+  const int kp = lane / RPW + (64 / RPW) * wave;
+  const int row = (RPW == 64) ? 64 * q + rr : 32 * q + 8 * hf + (rr & 7) + ((rr >> 3) << 4);
+  const int nc = H / KC, nb = H >> 5;
+  uint32_t magic = BF16_MAGIC2;
+  asm volatile("" : "+v"(magic));
+  constexpr int NBATCH = (F_HMAX / KC + NKP * NB - 1) / (NKP * NB);
+  float acc[MAXB];
+#pragma unroll
+  for (int t = 0; t < MAXB; t++) acc[t] = 0.0f;
+#pragma unroll
+  for (int bt = 0; bt < NBATCH; bt++) {
+    const int c0 = bt * NKP * NB;
+    Raw raw[NB];
+    uint16_t sc[NB];
+#pragma unroll
+    for (int i = 0; i < NB; i++) {
+      const size_t o = (size_t)min(c0 + kp + NKP * i, nc - 1) * R + row;
+      raw[i] = load_chunk<WT>(gu, o);
+      if constexpr (is_q<WT>()) sc[i] = gus[o];
+    }
+    if (bt == 0) after_first_issue();
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < NB; i++) {
+      const bool in = c0 + kp + NKP * i < nc;
+      const int c = min(c0 + kp + NKP * i, nc - 1);
+      if constexpr (is_q<WT>()) {
+        uint32_t pr[16];
+        qunpack32_m<WT>(raw[i], pr, magic);
+        const float s = in ? f16_to_f32(sc[i]) : 0.0f;
+#pragma unroll
+        for (int t = 0; t < MAXB; t++)
+          if (t < B && ((mask >> t) & 1u))
+            acc[t] = __builtin_fmaf(s, qdot32_p<WT>(pr, xs + (size_t)t * H + 32 * c, xsum[t * nb + c]), acc[t]);
+      } else {
+#pragma unroll
+        for (int t = 0; t < MAXB; t++)
+          if (t < B && ((mask >> t) & 1u)) {
+            const float d = ddot<WT>(raw[i], xs + (size_t)t * H + (size_t)c * KC, 0.0f);
+            acc[t] += in ? d : 0.0f;
+          }
+      }
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < MAXB; t++) {
+    if (t < B && ((mask >> t) & 1u)) {
+      float a = acc[t];
+      if constexpr (RPW == 16) a += __shfl_xor(a, 16, 64);
+      if constexpr (RPW <= 32) a += __shfl_xor(a, 32, 64);
+      if (lane < RPW) s_red[(t * F_WAVES + wave) * RPW + rr] = a;
+    }
+  }
+  __syncthreads();
+  {
+    const int i = threadIdx.x, hpt = RPW / 2;
+    const int t = i / hpt, j = i - t * hpt;
+    if (t < B && ((mask >> t) & 1u)) {
+      const int gi = (RPW == 16) ? j : 32 * (j >> 4) + (j & 15);
+      const int ui = (RPW == 16) ? j + 8 : gi + 16;
+      float g = 0.0f, u = 0.0f;
+#pragma unroll
+      for (int w = 0; w < F_WAVES; w++) {
+        g += s_red[(t * F_WAVES + w) * RPW + gi];
+        u += s_red[(t * F_WAVES + w) * RPW + ui];
+      }
+      s_hb[32 * t + j] = f32_to_bf16(silu_f32(g) * u);
+    }
+  }
+  __syncthreads();
+}
+
+// A routed unit's gate/up, split so that the next unit's loads can be issued
+// while this one is still being computed: 64 rows (lane l of wave w: row
+// 64q + l, chunks w + 16 i), one batch of F_GU_NB chunks per thread
+// (H <= F_HMAX = 16 x F_GU_NB x 32).
+static_assert(F_HMAX / 32 == 16 * F_GU_NB, "one batch of gate/up loads per routed unit");
+template <int WT>
+struct GuRegs {
+  Raw raw[F_GU_NB];
+  uint16_t sc[F_GU_NB];  // fp16 bits
+};
+template <int WT>
+__device__ __forceinline__ void gu_issue64(const uint8_t* __restrict__ gu, const uint16_t* __restrict__ gus, int H,
+                                           int R, int q, GuRegs<WT>& g) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int row = 64 * q + lane, nc = H >> 5;
+#pragma unroll
+  for (int i = 0; i < F_GU_NB; i++) {
+    const size_t o = (size_t)min(wave + 16 * i, nc - 1) * R + row;
+    g.raw[i] = load_chunk<WT>(gu, o);
+    g.sc[i] = gus[o];
+  }
+}
+template <int WT, int MAXB>
+__device__ __forceinline__ void gu_dots64(const GuRegs<WT>& g, int H, const uint16_t* xs, const float* xsum, int B,
+                                          uint32_t mask, float (&acc)[MAXB], uint32_t magic) {
+  const int wave = threadIdx.x >> 6, nc = H >> 5;
+#pragma unroll
+  for (int i = 0; i < F_GU_NB; i++) {
+    const bool in = wave + 16 * i < nc;
+    const int c = min(wave + 16 * i, nc - 1);
+    uint32_t pr[16];
+    qunpack32_m<WT>(g.raw[i], pr, magic);
+    const float sc = in ? f16_to_f32(g.sc[i]) : 0.0f;
+#pragma unroll
+    for (int t = 0; t < MAXB; t++)
+      if (t < B && ((mask >> t) & 1u))
+        acc[t] = __builtin_fmaf(sc, qdot32_p<WT>(pr, xs + (size_t)t * H + 32 * c, xsum[t * nc + c]), acc[t]);
+  }
+}
+// the 16 waves' row sums, then SwiGLU: token t's h (32 bf16) at s_hb + 32 t
+template <int MAXB>
+__device__ __forceinline__ void gu_swiglu64(const float (&acc)[MAXB], int B, uint32_t mask, float* s_red,
+                                            uint16_t* s_hb) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int t = 0; t < MAXB; t++)
+    if (t < B && ((mask >> t) & 1u)) s_red[(t * F_WAVES + wave) * 64 + lane] = acc[t];
+  __syncthreads();
+  const int t = threadIdx.x >> 5, j = threadIdx.x & 31;
+  if (t < B && ((mask >> t) & 1u)) {
+    const int gi = 32 * (j >> 4) + (j & 15), ui = gi + 16;
+    float gs = 0.0f, us = 0.0f;
+#pragma unroll
+    for (int w = 0; w < F_WAVES; w++) {
+      gs += s_red[(t * F_WAVES + w) * 64 + gi];
+      us += s_red[(t * F_WAVES + w) * 64 + ui];
+    }
+    s_hb[32 * t + j] = f32_to_bf16(silu_f32(gs) * us);
+  }
+  __syncthreads();
+}
+
+template <int WT, int SWT, int MAXB>
+__global__ __launch_bounds__(F_THREADS, 4) void k_decode1b(LayerDev L, const uint16_t* __restrict__ x,
+                                                        uint16_t* __restrict__ y, int32_t* idx_out, float* gate_out,
+                                                        DecodeWs ws, BatchGeo G) {
+  static_assert(is_q<WT>(), "quantised routed experts");
+  __shared__ __align__(16) uint16_t s_x[FB_XMAX];
+  __shared__ __align__(16) float s_xsum[FB_XMAX / 32];
+  __shared__ __align__(16) float s_red[FB_RED];  // reductions; the forwarder's top-k scratch before that
+  __shared__ double s_rt[F_WAVES * FB_MAXB];
+  __shared__ int s_mark[64 * F_NV];
+  __shared__ int s_urank[FB_SLOTS];
+  __shared__ int s_wcnt[2];
+  __shared__ int s_nu;
+  __shared__ int s_uexp[FB_SLOTS];
+  __shared__ uint32_t s_umask[FB_SLOTS];
+  __shared__ int s_sidx[FB_SLOTS];
+  __shared__ int s_suid[FB_SLOTS];  // unique index of each slot's expert
+  __shared__ float s_sgate[FB_SLOTS];
+  __shared__ float s_ug[FB_SLOTS * FB_MAXB];  // gate of unique expert j for token t
+  __shared__ uint32_t s_touch[F_NW];          // tokens each workgroup's partials cover
+  __shared__ __align__(16) uint16_t s_hb[FB_MAXB * 32];
+  __shared__ float s_hbs[FB_MAXB];
+  const int H = L.H, I = L.I, B = G.B;
+  const int b = blockIdx.x, tid = threadIdx.x, rank = start_rank(b);
+  const uint32_t tag = ld_u32(my_counter(ws.sync)) + 1u;
+  uint64_t* tl = reinterpret_cast<uint64_t*>(ws.logits);  // [B][E][2]
+  uint64_t* res = ws.res_words + (size_t)(b % F_NX) * FB_RES_STRIDE;
+  uint64_t* part = ws.part_words;  // [256][B][H]
+  uint64_t* xsw = ws.xsum_words;   // [8][B][H]
+  uint64_t* pdone = ws.res_words + (size_t)F_NX * FB_RES_STRIDE;  // [256]: a workgroup's partials are in its XCD's L2
+  const uint32_t allm = (1u << B) - 1u;
+  const bool is_router = b < G.nR;
+  const bool is_shared = b >= F_NX && b < F_NX + G.nSG;
+  // the batch (B H / 8 16-byte pieces, two per thread) and the router rows
+  // are loaded together, unconditionally (clamped)
+  const int n8 = (B * H) >> 3;
+  const uint4 v0 = reinterpret_cast<const uint4*>(x)[min(tid, n8 - 1)];
+  const uint4 v1 = reinterpret_cast<const uint4*>(x)[min(tid + F_THREADS, n8 - 1)];
+  RouterRegs rrg;
+  router_issue(L, is_router, b, G.rr, rrg);
+#pragma unroll
+  for (int h = 0; h < 2; h++) {
+    const int i = tid + F_THREADS * h;
+    const uint4 v = h ? v1 : v0;
+    if (i < n8) reinterpret_cast<uint4*>(s_x)[i] = v;
+    // 32-element block sums: pieces 4b'..4b'+3 are lanes of one quad
+    float sm = ((bf16_lo(v.x) + bf16_hi(v.x)) + (bf16_lo(v.y) + bf16_hi(v.y))) +
+               ((bf16_lo(v.z) + bf16_hi(v.z)) + (bf16_lo(v.w) + bf16_hi(v.w)));
+    sm += dpp_f32<DPP_XOR1>(sm);
+    sm += dpp_f32<DPP_XOR2>(sm);
+    if (i < n8 && (i & 3) == 0) s_xsum[i >> 2] = sm;
+  }
+  __syncthreads();
+  if (is_router) router_finish_b(L, s_x, B, rrg, b, G.rr, tl, s_rt, tag);
+  float pacc[MAXB][F_RPT];
+#pragma unroll
+  for (int t = 0; t < MAXB; t++)
+#pragma unroll
+    for (int n = 0; n < F_RPT; n++) pacc[t][n] = 0.0f;
+  if (is_shared) {
+    // shared unit su: intermediates 8su .. 8su+7, every token
+    constexpr int SW = (SWT == MOE_W_F32) ? MOE_W_F32 : MOE_W_BF16;
+    const int su = b - F_NX, q = su >> 1, hf = su & 1;
+    DownPre<SW> spre;
+    gate_up_hb<SW, 16, MAXB>(L.sgu, nullptr, H, 2 * I, q, hf, s_x, nullptr, B, allm, s_red, s_hb,
+                       [&] { down_prefetch<SW, 8>(L.sdn, nullptr, H, 16 * q + 8 * hf, spre); });
+    constexpr int KCS = kchunk<SW>();
+#pragma unroll
+    for (int n = 0; n < F_RPT; n++) {
+      const int row = tid + F_THREADS * n;
+#pragma unroll
+      for (int t = 0; t < MAXB; t++) {
+        if (t < B) {
+          float v = 0.0f;
+          if constexpr (DownPlan<SW, 8>::PRE) {
+            v = ddot<SW>(spre.r[n], s_hb + 32 * t, 0.0f);
+          } else {
+#pragma unroll
+            for (int c = 0; c < 8 / KCS; c++)
+              v = ddot<SW>(load_chunk<SW>(L.sdn, (size_t)((16 * q + 8 * hf) / KCS + c) * H + min(row, H - 1)),
+                           s_hb + 32 * t + KCS * c, v);
+          }
+          pacc[t][n] += v;
+        }
+      }
+    }
+    __syncthreads();  // s_hb is reused
+  }
+  // the routing
+  if (b < F_NX) {
+    fwd_routing_b(L, tl, B, tag, ws.sync, G.wait_ticks, reinterpret_cast<uint8_t*>(s_red), s_mark, s_urank, s_wcnt,
+                  &s_nu, s_uexp, s_umask, s_sidx, s_suid, s_sgate, res, idx_out, gate_out);
+  } else {
+    wait_routing_b(L, res, B, tag, ws.sync, G.wait_ticks, &s_nu, s_uexp, s_umask, s_sidx, s_suid, s_sgate);
+  }
+  const int nu = s_nu, nunits = nu * G.gpe;
+  // gate of unique expert j for token t (0 where the token did not choose it)
+  for (int i = tid; i < FB_SLOTS * FB_MAXB; i += F_THREADS) s_ug[i] = 0.0f;
+  __syncthreads();
+  if (tid < B * L.k) s_ug[s_suid[tid] * FB_MAXB + tid / L.k] = s_sgate[tid];
+  for (int bb = tid; bb < F_NW; bb += F_THREADS) {
+    uint32_t m = (bb >= F_NX && bb < F_NX + G.nSG) ? allm : 0u;
+    for (int u = (bb - G.uoff + F_NW) % F_NW; u < nunits; u += F_NW) m |= s_umask[u / G.gpe];
+    s_touch[bb] = m & allm;
+  }
+  __syncthreads();
+  // routed units of this workgroup, u0, u0 + 256, ...: unit u + 256's loads
+  // are issued as soon as unit u's registers are free (gate/up after its dot
+  // products, down after its down products), so they are in flight while
+  // unit u is finished. The last unit issues its own loads once more (the
+  // lines are in the L2; a load under a branch would make the compiler wait
+  // for it at once).
+  const int u0 = (b - G.uoff + F_NW) % F_NW;
+  if (u0 < nunits) {
+    uint32_t magic = BF16_MAGIC2;
+    asm volatile("" : "+v"(magic));
+    GuRegs<WT> gr;
+    DownPre<WT> pre;
+    {
+      const int j = u0 / G.gpe, q = u0 - j * G.gpe, e = s_uexp[j];
+      gu_issue64<WT>(L.gu + (size_t)e * L.gu_stride, L.gu_s + (size_t)e * L.gu_s_stride, H, 2 * I, q, gr);
+      down_prefetch<WT, 32>(L.dn + (size_t)e * L.dn_stride, L.dn_s + (size_t)e * L.dn_s_stride, H, 32 * q, pre);
+    }
+    for (int u = u0; u < nunits; u += F_NW) {
+      const int j = u / G.gpe;
+      const uint32_t mask = s_umask[j] & allm;
+      const int un = (u + F_NW < nunits) ? u + F_NW : u;
+      const int jn = un / G.gpe, qn = un - jn * G.gpe, en = s_uexp[jn];
+      float acc[MAXB];
+#pragma unroll
+      for (int t = 0; t < MAXB; t++) acc[t] = 0.0f;
+      gu_dots64<WT, MAXB>(gr, H, s_x, s_xsum, B, mask, acc, magic);
+      gu_issue64<WT>(L.gu + (size_t)en * L.gu_stride, L.gu_s + (size_t)en * L.gu_s_stride, H, 2 * I, qn, gr);
+      gu_swiglu64<MAXB>(acc, B, mask, s_red, s_hb);
+      // each token's block sum of its 32 h values (32 lanes, fixed order)
+      {
+        // lanes of one 32-lane half: sum16 over each row of 16, then the two rows
+        const int t = tid >> 5;
+        const bool act = tid < 32 * MAXB && t < B && ((mask >> t) & 1u);
+        float v = act ? bf16_to_f32(s_hb[min(tid, 32 * MAXB - 1)]) : 0.0f;
+        v = sum16_f32(v);
+        v += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x401F));  // lane ^ 16 (bit-mode swizzle)
+        if (act && (tid & 31) == 0) s_hbs[t] = v;
+      }
+      __syncthreads();
+#pragma unroll
+      for (int n = 0; n < F_RPT; n++) {
+        uint32_t pr[16];
+        qunpack32_m<WT>(pre.r[n], pr, magic);
+        const float sc = f16_to_f32(pre.s[n]);
+#pragma unroll
+        for (int t = 0; t < MAXB; t++)
+          if (t < B && ((mask >> t) & 1u))
+            pacc[t][n] = __builtin_fmaf(sc * qdot32_p<WT>(pr, s_hb + 32 * t, s_hbs[t]), s_ug[j * FB_MAXB + t], pacc[t][n]);
+      }
+      down_prefetch<WT, 32>(L.dn + (size_t)en * L.dn_stride, L.dn_s + (size_t)en * L.dn_s_stride, H, 32 * qn, pre);
+      __syncthreads();  // s_red, s_hb and s_hbs are reused by the next unit
+    }
+  }
+  // this workgroup's partials of the tokens it touched, into its XCD's L2
+  {
+    const uint32_t mine = s_touch[b];
+#pragma unroll
+    for (int t = 0; t < MAXB; t++) {
+      if (t < B && ((mine >> t) & 1u)) {
+#pragma unroll
+        for (int n = 0; n < F_RPT; n++) {
+          const int row = tid + F_THREADS * n;
+          if (row < H) st_word_xcd(part + ((size_t)b * B + t) * H + row, __float_as_uint(pacc[t][n]), tag);
+        }
+      }
+    }
+    __syncthreads();  // every partial word has reached the L2 before the done word
+    if (tid == 0) st_word_xcd(pdone + b, 0u, tag);
+  }
+  // XCD-level sums: workgroup jx of XCD x sums rows r0 .. r0 + H/32 - 1 of
+  // every token over the producers of its XCD (workgroups x + 8 j', j' in
+  // order) that touched the token
+  {
+    const int xx = b % F_NX, jx = b / F_NX;
+    const int nrow = H / F_PX, r0 = jx * nrow;
+    const int rr = tid & 63, g = tid >> 6;
+    const int row = r0 + min(rr, nrow - 1);
+    const int pb0 = xx + F_NX * g, pb1 = xx + F_NX * (g + 16);
+    const uint32_t tm0 = s_touch[pb0], tm1 = s_touch[pb1];
+    // the producers' done words (one wave, lane l: workgroup xx + 8 l), then
+    // the partials once: polling the partial words themselves (up to 16 per
+    // thread and round) flooded the XCD's L2 while slower producers still ran
+    if (tid < 64) {
+      const uint64_t* dw = pdone + xx + F_NX * (tid & 31);
+      uint64_t d = ld_word_coherent(dw);
+      if (__builtin_amdgcn_ballot_w64(!tag_ok(d, tag)) != 0) {
+        const uint64_t c0 = wall_clock64();
+        int it = 0;
+        while (true) {
+          __builtin_amdgcn_s_sleep(2);
+          const uint64_t nd = ld_word_coherent(dw);
+          d = tag_ok(d, tag) ? d : nd;
+          if (__builtin_amdgcn_ballot_w64(!tag_ok(d, tag)) == 0) break;
+          if ((++it & 15) == 0 && wall_clock64() - c0 > G.wait_ticks) {
+            if (tid == 0) flag_error(ws.sync, 4u);
+            break;
+          }
+        }
+      }
+    }
+    __syncthreads();
+    uint64_t w0[MAXB], w1[MAXB];
+#pragma unroll
+    for (int t = 0; t < MAXB; t++) {
+      const int tt = min(t, B - 1);
+      w0[t] = ld_word_coherent(part + ((size_t)pb0 * B + tt) * H + row);  // unconditional, clamped
+      w1[t] = ld_word_coherent(part + ((size_t)pb1 * B + tt) * H + row);
+    }
+    auto need0 = [&](int t) { return t < B && ((tm0 >> t) & 1u); };
+    auto need1 = [&](int t) { return t < B && ((tm1 >> t) & 1u); };
+    bool stale = false;
+#pragma unroll
+    for (int t = 0; t < MAXB; t++) stale |= (need0(t) && !tag_ok(w0[t], tag)) || (need1(t) && !tag_ok(w1[t], tag));
+    if (__builtin_amdgcn_ballot_w64(stale) != 0) {
+      const uint64_t c0 = wall_clock64();
+      int it = 0;
+      while (true) {
+        __builtin_amdgcn_s_sleep(1);
+        uint64_t n0[MAXB], n1[MAXB];
+#pragma unroll
+        for (int t = 0; t < MAXB; t++) {
+          const int tt = min(t, B - 1);
+          n0[t] = ld_word_coherent(part + ((size_t)pb0 * B + tt) * H + row);
+          n1[t] = ld_word_coherent(part + ((size_t)pb1 * B + tt) * H + row);
+        }
+        stale = false;
+#pragma unroll
+        for (int t = 0; t < MAXB; t++) {
+          w0[t] = tag_ok(w0[t], tag) ? w0[t] : n0[t];
+          w1[t] = tag_ok(w1[t], tag) ? w1[t] : n1[t];
+          stale |= (need0(t) && !tag_ok(w0[t], tag)) || (need1(t) && !tag_ok(w1[t], tag));
+        }
+        if (__builtin_amdgcn_ballot_w64(stale) == 0) break;
+        if ((++it & 15) == 0 && wall_clock64() - c0 > G.wait_ticks) {
+          if ((tid & 63) == 0) flag_error(ws.sync, 4u);
+          break;
+        }
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < MAXB; t++) {
+      if (t < B) {
+        float a = need0(t) ? __uint_as_float((uint32_t)w0[t]) : 0.0f;
+        a += need1(t) ? __uint_as_float((uint32_t)w1[t]) : 0.0f;
+        s_red[(t * F_WAVES + g) * 64 + rr] = a;
+      }
+    }
+    __syncthreads();
+    if (tid < 64 * B) {
+      const int t = tid >> 6, r2 = tid & 63;
+      if (r2 < nrow) {
+        float sm = 0.0f;
+#pragma unroll
+        for (int q = 0; q < F_WAVES; q++) sm += s_red[(t * F_WAVES + q) * 64 + r2];
+        st_word(xsw + ((size_t)xx * B + t) * H + r0 + r2, __float_as_uint(sm), tag);
+      }
+    }
+  }
+  // final: rows row0 .. row0 + nr - 1 of every token; wave t takes token t,
+  // lane l row l % 8 and XCD l / 8, the XCDs added in order
+  {
+    const int row0 = rank * H / F_NW, nr = (rank + 1) * H / F_NW - row0;
+    const int wave = tid >> 6, lane = tid & 63;
+    if (wave < B && nr > 0) {
+      const int r = lane & 7, qx = lane >> 3;
+      const bool use = r < nr;
+      const uint64_t* pw = xsw + ((size_t)qx * B + wave) * H + row0 + min(r, nr - 1);
+      uint64_t w = ld_word_coherent(pw);
+      if (__builtin_amdgcn_ballot_w64(use && !tag_ok(w, tag)) != 0) {
+        const uint64_t c0 = wall_clock64();
+        int it = 0;
+        while (true) {
+          __builtin_amdgcn_s_sleep(1);
+          const uint64_t nw = ld_word_coherent(pw);
+          w = tag_ok(w, tag) ? w : nw;
+          if (__builtin_amdgcn_ballot_w64(use && !tag_ok(w, tag)) == 0) break;
+          if ((++it & 15) == 0 && wall_clock64() - c0 > G.wait_ticks) {
+            if (lane == 0) flag_error(ws.sync, 8u);
+            break;
+          }
+        }
+      }
+      const float v = use ? __uint_as_float((uint32_t)w) : 0.0f;
+      float t = v;
+#pragma unroll
+      for (int qq = 1; qq < F_NX; qq++) t += __shfl(v, r + 8 * qq, 64);
+      if (lane < nr) y[(size_t)wave * H + row0 + lane] = f32_to_bf16(t);
+    }
+  }
+  finish(ws.sync, tag);
+}
+
+size_t decode1b_part_words(int H, int B) { return (size_t)F_NW * B * H; }
+size_t decode1b_xsum_words(int H, int B) { return (size_t)F_NX * B * H; }
+size_t decode1b_res_words() { return (size_t)F_NX * FB_RES_STRIDE + F_NW; }  // routing words, then done words
+
+bool decode1b_fits(int wt, int E, int H, int I, int k, bool has_shared, int B) {
+  // quantised routed experts; the batch-1 limits on E, H, I and k; B k <= 128
+  // slots; the shared units and the forwarders within the grid
+  const int nSG = has_shared ? I / 8 : 0;
+  return (wt == MOE_W_Q4 || wt == MOE_W_Q3) && B >= 2 && B <= FB_MAXB && B * H <= FB_XMAX &&
+         E <= 64 * F_NV && E <= F_NW * F_RRMAX && H <= F_HMAX && H % 32 == 0 && I <= 1024 && k <= 16 &&
+         F_NX + nSG <= F_NW && F_NW <= decode1_capacity();
+}
+
+template <int WT, int SWT, int MAXB>
+static hipError_t launch_fused_bt(const LayerDev& L, const uint16_t* x, int B, uint16_t* y, int32_t* idx_out,
+                                  float* gate_out, const DecodeWs& ws, hipStream_t st) {
+  BatchGeo G;
+  G.B = B;
+  G.rr = L.E > F_NW ? 2 : 1;
+  G.nR = (L.E + G.rr - 1) / G.rr;
+  G.nSG = (SWT == MOE_W_NONE) ? 0 : L.I / 8;
+  G.gpe = L.I / 32;
+  G.uoff = F_NX + G.nSG;
+  G.wait_ticks = g_wait_ticks;
+  return launch_k(KC_DEC_FUSED, k_decode1b<WT, SWT, MAXB>, dim3(F_NW), dim3(F_THREADS), 0, st, L, x, y, idx_out,
+                  gate_out, ws, G);
+}
+
+template <int WT>
+static hipError_t launch_fused_bw(const LayerDev& L, const uint16_t* x, int B, uint16_t* y, int32_t* io, float* go,
+                                  const DecodeWs& ws, hipStream_t st) {
+  if (B <= 4) {
+    if (L.swt == MOE_W_NONE) return launch_fused_bt<WT, MOE_W_NONE, 4>(L, x, B, y, io, go, ws, st);
+    if (L.swt == MOE_W_F32) return launch_fused_bt<WT, MOE_W_F32, 4>(L, x, B, y, io, go, ws, st);
+    return launch_fused_bt<WT, MOE_W_BF16, 4>(L, x, B, y, io, go, ws, st);
+  }
+  if (L.swt == MOE_W_NONE) return launch_fused_bt<WT, MOE_W_NONE, 8>(L, x, B, y, io, go, ws, st);
+  if (L.swt == MOE_W_F32) return launch_fused_bt<WT, MOE_W_F32, 8>(L, x, B, y, io, go, ws, st);
+  return launch_fused_bt<WT, MOE_W_BF16, 8>(L, x, B, y, io, go, ws, st);
+}
+
+hipError_t launch_decode_fused_b(const LayerDev& L, const uint16_t* x, int B, uint16_t* y, int32_t* idx_out,
+                                 float* gate_out, const DecodeWs& ws, hipStream_t st) {
+  if (L.wt == MOE_W_Q4) return launch_fused_bw<MOE_W_Q4>(L, x, B, y, idx_out, gate_out, ws, st);
+  return launch_fused_bw<MOE_W_Q3>(L, x, B, y, idx_out, gate_out, ws, st);
+}
+
 }  // namespace moe

@@ -59,6 +59,7 @@ struct DecodeWs {
   uint64_t* part_words;  // one-kernel path: [producers][H] tagged partial down products (fp32 bits), read within each XCD
   uint64_t* xsum_words;  // one-kernel path: [8][H] tagged per-XCD sums of the partials
   uint32_t* ctr;         // one-kernel path: router counters, rotating slots x XCD groups, one 128-byte line each
+  uint64_t* res_words;   // batched one-kernel path: [8][512] tagged routing words per XCD
   int32_t* route;        // four-kernel path: the batch's routing (count, idx, gates, unique experts, masks)
   uint16_t* zb;          // [B][H] bf16: z of a stack layer taken as separate kernels
   uint16_t* yb;          // [B][H] bf16: its y
@@ -93,6 +94,11 @@ size_t decode1_part_words(int H, int I, int k, bool has_shared);
 size_t decode1_xsum_words(int H);
 size_t decode1_counter_words();
 bool decode1_fits(int E, int H, int I, int k, bool has_shared);  // shape handled by the one-kernel path
+// batched one-kernel path (B = 2..8): [256][B][H] partials, [8][B][H] XCD sums, [8][512] routing words
+bool decode1b_fits(int wt, int E, int H, int I, int k, bool has_shared, int B);
+size_t decode1b_part_words(int H, int B);
+size_t decode1b_xsum_words(int H, int B);
+size_t decode1b_res_words();
 void decode1_set_wait_ticks(uint64_t ticks);  // bound of the one-kernel path's waits (0: the default)
 // One layer of a pre-norm residual stack, in place on the residual stream h:
 // z = RMSNorm(h), y = MoE(z), h = bf16(h + y); z_out / y_out optional copies.
@@ -104,6 +110,8 @@ struct StackIo {
 };
 hipError_t launch_decode_fused(const LayerDev& L, const uint16_t* x, uint16_t* y, int32_t* idx_out,
                                float* gate_out, const DecodeWs& ws, hipStream_t st, const StackIo* stack = nullptr);
+hipError_t launch_decode_fused_b(const LayerDev& L, const uint16_t* x, int B, uint16_t* y, int32_t* idx_out,
+                                 float* gate_out, const DecodeWs& ws, hipStream_t st);
 hipError_t launch_decode(const LayerDev& L, const uint16_t* x, int B, uint16_t* y, int32_t* idx_out,
                          float* gate_out, const DecodeWs& ws, hipStream_t st);
 hipError_t launch_stack_decode(const LayerDev& L, uint16_t* h, int B, float eps, uint16_t* z_out, uint16_t* y_out,
