@@ -961,6 +961,25 @@ static int decode1_capacity() {
   return cap[dev];
 }
 
+// The kernel's workgroups wait for each other, so all of them must be
+// resident at once: a build that spills to scratch memory is not used (the
+// scratch a wave needs is handed out as waves launch and can hold some of
+// them back until others have finished).
+template <typename K>
+static bool no_scratch(K kernel) {
+  hipFuncAttributes a;
+  return hipFuncGetAttributes(&a, reinterpret_cast<const void*>(kernel)) == hipSuccess && a.localSizeBytes == 0;
+}
+static bool decode1_no_scratch() {
+  static const bool ok = no_scratch(k_decode1<MOE_W_Q4, MOE_W_NONE>) && no_scratch(k_decode1<MOE_W_Q4, MOE_W_F32>) &&
+                         no_scratch(k_decode1<MOE_W_Q4, MOE_W_BF16>) && no_scratch(k_decode1<MOE_W_Q3, MOE_W_NONE>) &&
+                         no_scratch(k_decode1<MOE_W_Q3, MOE_W_F32>) && no_scratch(k_decode1<MOE_W_Q3, MOE_W_BF16>) &&
+                         no_scratch(k_decode1<MOE_W_BF16, MOE_W_NONE>) && no_scratch(k_decode1<MOE_W_BF16, MOE_W_F32>) &&
+                         no_scratch(k_decode1<MOE_W_BF16, MOE_W_BF16>) && no_scratch(k_decode1<MOE_W_F32, MOE_W_NONE>) &&
+                         no_scratch(k_decode1<MOE_W_F32, MOE_W_F32>) && no_scratch(k_decode1<MOE_W_F32, MOE_W_BF16>);
+  return ok;
+}
+
 bool decode1_fits(int E, int H, int I, int k, bool has_shared) {
   // F_NV logits per lane in the top-k, F_RPT down rows per thread (the LDS
   // arrays are sized for H <= F_HMAX), at most one shared or routed unit per
@@ -968,7 +987,7 @@ bool decode1_fits(int E, int H, int I, int k, bool has_shared) {
   const int nSG = has_shared ? I / 8 : 0, nRG = k * (I / 32);
   const int sg0 = (nRG + F_NX - 1) / F_NX * F_NX;
   return E <= 64 * F_NV && E <= F_NW * F_RRMAX && H <= F_HMAX && I <= 1024 && sg0 + nSG <= F_NW &&
-         F_NW <= decode1_capacity();
+         F_NW <= decode1_capacity() && decode1_no_scratch();
 }
 
 template <int WT, int SWT>
@@ -1607,22 +1626,18 @@ __global__ __launch_bounds__(F_THREADS, 4) void k_decode1b(LayerDev L, const uin
 #pragma unroll
     for (int t = 0; t < MAXB; t++) stale |= (need0(t) && !tag_ok(w0[t], tag)) || (need1(t) && !tag_ok(w1[t], tag));
     if (__builtin_amdgcn_ballot_w64(stale) != 0) {
+      // not expected once the done words are current: stale words one at a
+      // time (few registers; this is the rare path)
       const uint64_t c0 = wall_clock64();
       int it = 0;
       while (true) {
         __builtin_amdgcn_s_sleep(1);
-        uint64_t n0[MAXB], n1[MAXB];
-#pragma unroll
-        for (int t = 0; t < MAXB; t++) {
-          const int tt = min(t, B - 1);
-          n0[t] = ld_word_coherent(part + ((size_t)pb0 * B + tt) * H + row);
-          n1[t] = ld_word_coherent(part + ((size_t)pb1 * B + tt) * H + row);
-        }
         stale = false;
 #pragma unroll
         for (int t = 0; t < MAXB; t++) {
-          w0[t] = tag_ok(w0[t], tag) ? w0[t] : n0[t];
-          w1[t] = tag_ok(w1[t], tag) ? w1[t] : n1[t];
+          const int tt = min(t, B - 1);
+          if (need0(t) && !tag_ok(w0[t], tag)) w0[t] = ld_word_coherent(part + ((size_t)pb0 * B + tt) * H + row);
+          if (need1(t) && !tag_ok(w1[t], tag)) w1[t] = ld_word_coherent(part + ((size_t)pb1 * B + tt) * H + row);
           stale |= (need0(t) && !tag_ok(w0[t], tag)) || (need1(t) && !tag_ok(w1[t], tag));
         }
         if (__builtin_amdgcn_ballot_w64(stale) == 0) break;
@@ -1689,13 +1704,24 @@ size_t decode1b_part_words(int H, int B) { return (size_t)F_NW * B * H; }
 size_t decode1b_xsum_words(int H, int B) { return (size_t)F_NX * B * H; }
 size_t decode1b_res_words() { return (size_t)F_NX * FB_RES_STRIDE + F_NW; }  // routing words, then done words
 
+static bool decode1b_no_scratch() {
+  static const bool ok =
+      no_scratch(k_decode1b<MOE_W_Q4, MOE_W_NONE, 4>) && no_scratch(k_decode1b<MOE_W_Q4, MOE_W_F32, 4>) &&
+      no_scratch(k_decode1b<MOE_W_Q4, MOE_W_BF16, 4>) && no_scratch(k_decode1b<MOE_W_Q3, MOE_W_NONE, 4>) &&
+      no_scratch(k_decode1b<MOE_W_Q3, MOE_W_F32, 4>) && no_scratch(k_decode1b<MOE_W_Q3, MOE_W_BF16, 4>) &&
+      no_scratch(k_decode1b<MOE_W_Q4, MOE_W_NONE, 8>) && no_scratch(k_decode1b<MOE_W_Q4, MOE_W_F32, 8>) &&
+      no_scratch(k_decode1b<MOE_W_Q4, MOE_W_BF16, 8>) && no_scratch(k_decode1b<MOE_W_Q3, MOE_W_NONE, 8>) &&
+      no_scratch(k_decode1b<MOE_W_Q3, MOE_W_F32, 8>) && no_scratch(k_decode1b<MOE_W_Q3, MOE_W_BF16, 8>);
+  return ok;
+}
+
 bool decode1b_fits(int wt, int E, int H, int I, int k, bool has_shared, int B) {
   // quantised routed experts; the batch-1 limits on E, H, I and k; B k <= 128
   // slots; the shared units and the forwarders within the grid
   const int nSG = has_shared ? I / 8 : 0;
   return (wt == MOE_W_Q4 || wt == MOE_W_Q3) && B >= 2 && B <= FB_MAXB && B * H <= FB_XMAX &&
          E <= 64 * F_NV && E <= F_NW * F_RRMAX && H <= F_HMAX && H % 32 == 0 && I <= 1024 && k <= 16 &&
-         F_NX + nSG <= F_NW && F_NW <= decode1_capacity();
+         F_NX + nSG <= F_NW && F_NW <= decode1_capacity() && decode1b_no_scratch();
 }
 
 template <int WT, int SWT, int MAXB>
