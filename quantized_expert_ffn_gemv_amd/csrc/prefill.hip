@@ -81,6 +81,7 @@ __global__ __launch_bounds__(256) void k_pf_rsplit(const float* __restrict__ W, 
 // rows load together), each exact logit summed across the wave in a fixed
 // order (DPP rows, then the four row sums).
 constexpr int RS_NV = 16;
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 template <int NXH>
 __global__ __launch_bounds__(256) void k_pf_rselect(const float* __restrict__ W, const float* __restrict__ bias,
                                                     const uint16_t* __restrict__ x, const float* __restrict__ approx,
@@ -91,6 +92,7 @@ __global__ __launch_bounds__(256) void k_pf_rselect(const float* __restrict__ W,
   __shared__ uint32_t s_key[4][64];       // lane maxima of the lower ends (sortable keys)
   __shared__ double s_ov[4][16];          // winners in order
   __shared__ int s_oe[4][16];
+  __shared__ double s_cv[4][64 * RS_NV];  // exact logits of the candidates, in candidate order
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int t = blockIdx.x * 4 + wave;
   if (t >= T) return;  // whole wave; no workgroup barrier below
@@ -102,8 +104,8 @@ __global__ __launch_bounds__(256) void k_pf_rselect(const float* __restrict__ W,
   constexpr bool XR = NXH <= 4;
   auto x_chunk = [&](int j) {
     const int h = 512 * j + 8 * lane;
-    const uint4 v = *reinterpret_cast<const uint4*>(xt + min(h, H - 8));
-    return (h < H) ? v : make_uint4(0u, 0u, 0u, 0u);
+    const u32x4_t vv = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(xt + min(h, H - 8)));
+    return (h < H) ? make_uint4(vv.x, vv.y, vv.z, vv.w) : make_uint4(0u, 0u, 0u, 0u);
   };
   uint4 xr[XR ? NXH : 1];
   double xs = 0.0;
@@ -128,7 +130,10 @@ __global__ __launch_bounds__(256) void k_pf_rselect(const float* __restrict__ W,
     const int e = lane + 64 * i;
     const int ec = min(e, E - 1);
     const float bv = bias ? bias[ec] : 0.0f;
-    const double a = (double)((approx[(size_t)t * 2 * E + ec] + approx[(size_t)t * 2 * E + E + ec]) + bv);
+    // (the approximate logits and x are read once: non-temporal, so that
+    // they do not push the router rows out of the L2)
+    const double a = (double)((__builtin_nontemporal_load(approx + (size_t)t * 2 * E + ec) +
+                               __builtin_nontemporal_load(approx + (size_t)t * 2 * E + E + ec)) + bv);
     const double B = C * wnorm[ec] * xn + 0x1p-22 * (__builtin_fabs(a) + __builtin_fabs((double)bv)) + 0x1p-110 * xn + 0x1p-100;
     lo[i] = (e < E) ? a - B : -__builtin_inf();
     up[i] = (e < E) ? a + B : -__builtin_inf();
@@ -167,10 +172,8 @@ __global__ __launch_bounds__(256) void k_pf_rselect(const float* __restrict__ W,
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  // exact logits, four candidates per pass
-  double cv[RS_NV];
-#pragma unroll
-  for (int i = 0; i < RS_NV; i++) cv[i] = -__builtin_inf();
+  // exact logits, four candidates per pass (each written to LDS by one lane)
+  double* cvl = s_cv[wave];
   for (int c0 = 0; c0 < nc; c0 += 4) {
     int e[4];
     double acc[4];
@@ -215,15 +218,19 @@ __global__ __launch_bounds__(256) void k_pf_rselect(const float* __restrict__ W,
 #pragma unroll
     for (int q = 0; q < 4; q++) {
       const double l = wave_total_f64(acc[q]) + (bias ? (double)bias[e[q]] : 0.0);
-      const int c = c0 + q;  // uniform: lane c % 64 keeps it in slot c / 64
-#pragma unroll
-      for (int i = 0; i < RS_NV; i++)
-        if (c < nc && c == lane + 64 * i) cv[i] = l;
+      if (lane == q && c0 + q < nc) cvl[c0 + q] = l;
     }
   }
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  // candidate c in lane c % 64, slot c / 64
+  double cv[RS_NV];
+#pragma unroll
+  for (int i = 0; i < RS_NV; i++) {
+    const int c = lane + 64 * i;
+    cv[i] = (c < nc) ? cvl[min(c, 64 * RS_NV - 1)] : -__builtin_inf();
+  }
   // ordered top-k among the candidates (value, then lower expert index)
   if (nc <= 64) {
     // rank of candidate c (lane c) by counting the candidates before it
@@ -544,9 +551,13 @@ __device__ __forceinline__ bf16x8_t frag_b(const BRaw<WT>& r, int t) {
 // ---------------------------------------------------------------------------
 // Grouped GEMM. Tile = (M tile of one expert's rows, 256 weight rows).
 // Workgroups go round-robin over the 8 XCDs; a contiguous range of logical
-// tiles runs on each XCD. Routed: the tiles of one expert are consecutive
-// (N tile outer, M tile inner), so the expert's weights and gathered rows
-// stay in that XCD's L2 while they run. Shared expert: N tile outer.
+// tiles runs on each XCD. Routed: the tiles of one expert are consecutive,
+// so the expert's weights and gathered rows stay in that XCD's L2 while they
+// run; gate/up takes them M tile outer (an M tile's 4 KB rows are read once
+// from memory for all its N tiles, the expert's 1 MB of weights stays in L2),
+// down N tile outer (its rows are short, 1 KB; each weight tile is read
+// once). One matrix for all tokens (shared expert, router): M tile outer,
+// so the x rows are read from memory once rather than once per N tile.
 //
 // Pipeline, per 128-wide K stage: A (bf16 rows, gathered) goes straight from
 // memory to LDS (global_load_lds, 16 B per lane) into a 2-slot ring; the
@@ -604,8 +615,9 @@ __global__ __launch_bounds__(G_THREADS, 2) void k_pf_gemm(GemmArgs g) {
     M = min(PF_BM, ti[4] - m0);
     pos0 = ti[3] + m0;
   } else {
-    nt = logical / mt_total;
-    m0 = (logical - nt * mt_total) * PF_BM;
+    const int mt = logical / NT;
+    nt = logical - mt * NT;
+    m0 = mt * PF_BM;
     M = min(PF_BM, g.M_total - m0);
     pos0 = m0;
   }
@@ -1025,13 +1037,20 @@ __global__ __launch_bounds__(G_THREADS, 2) void k_pf_gemm_q(GemmArgs g) {
     e = ti[0];
     const int ntiles = ti[2];
     const int pos = logical - NT * ti[1];
-    nt = pos / ntiles;
-    m0 = (pos - nt * ntiles) * PF_BM;
+    if (KIND == GK_GATE_UP) {
+      const int mt = pos / NT;
+      nt = pos - mt * NT;
+      m0 = mt * PF_BM;
+    } else {
+      nt = pos / ntiles;
+      m0 = (pos - nt * ntiles) * PF_BM;
+    }
     M = min(PF_BM, ti[4] - m0);
     pos0 = ti[3] + m0;
   } else {
-    nt = logical / mt_total;
-    m0 = (logical - nt * mt_total) * PF_BM;
+    const int mt = logical / NT;
+    nt = logical - mt * NT;
+    m0 = mt * PF_BM;
     M = min(PF_BM, g.M_total - m0);
     pos0 = m0;
   }
@@ -1045,31 +1064,50 @@ __global__ __launch_bounds__(G_THREADS, 2) void k_pf_gemm_q(GemmArgs g) {
 // ---------------------------------------------------------------------------
 // Combine: y[t] = sum_j g[t][j] Y[inv[t*k+j]] + Ys[t]
 // ---------------------------------------------------------------------------
+constexpr int PF_KMAX = 16;  // slots per token the combine takes (k <= 16)
 __global__ __launch_bounds__(256) void k_pf_combine(const uint16_t* __restrict__ Y, const uint16_t* __restrict__ Ys,
                                                      const int32_t* __restrict__ inv, const float* __restrict__ gates,
                                                      int T, int H, int k, uint16_t* __restrict__ y) {
+  // One workgroup per token. The token's k slot positions and gates first
+  // (one load each, clamped and unconditional), then the k rows' 16-byte
+  // pieces of every column group all in flight together: one memory round
+  // trip for the indices and one for the rows, not two per slot.
   const int t = blockIdx.x;
+  int pos[PF_KMAX];
+  float gv[PF_KMAX];
+#pragma unroll
+  for (int j = 0; j < PF_KMAX; j++) {
+    const size_t sj = (size_t)t * k + min(j, k - 1);
+    pos[j] = inv[sj];
+    gv[j] = (j < k) ? gates[sj] : 0.0f;
+  }
   for (int c = threadIdx.x * 8; c < H; c += 256 * 8) {
+    uint4 v[PF_KMAX];
+#pragma unroll
+    for (int j = 0; j < PF_KMAX; j++) v[j] = *reinterpret_cast<const uint4*>(Y + (size_t)pos[j] * H + c);
+    uint4 vs = make_uint4(0u, 0u, 0u, 0u);
+    if (Ys) vs = *reinterpret_cast<const uint4*>(Ys + (size_t)t * H + c);
     float acc[8];
 #pragma unroll
     for (int i = 0; i < 8; i++) acc[i] = 0.0f;
-    for (int j = 0; j < k; j++) {
-      const float gj = gates[(size_t)t * k + j];
-      const uint4 v = *reinterpret_cast<const uint4*>(Y + (size_t)inv[(size_t)t * k + j] * H + c);
-      const uint32_t vv[4] = {v.x, v.y, v.z, v.w};
+    // fixed slot order j = 0 .. k-1; slots past k (a repeat of slot k - 1)
+    // are zeroed, so they add exactly 0 whatever that row holds
+#pragma unroll
+    for (int j = 0; j < PF_KMAX; j++) {
+      const uint32_t m = (j < k) ? 0xFFFFFFFFu : 0u;
+      const uint32_t vv[4] = {v[j].x & m, v[j].y & m, v[j].z & m, v[j].w & m};
 #pragma unroll
       for (int i = 0; i < 4; i++) {
-        acc[2 * i] = __builtin_fmaf(gj, bf16_lo(vv[i]), acc[2 * i]);
-        acc[2 * i + 1] = __builtin_fmaf(gj, bf16_hi(vv[i]), acc[2 * i + 1]);
+        acc[2 * i] = __builtin_fmaf(gv[j], bf16_lo(vv[i]), acc[2 * i]);
+        acc[2 * i + 1] = __builtin_fmaf(gv[j], bf16_hi(vv[i]), acc[2 * i + 1]);
       }
     }
     if (Ys) {
-      const uint4 v = *reinterpret_cast<const uint4*>(Ys + (size_t)t * H + c);
-      const uint32_t vv[4] = {v.x, v.y, v.z, v.w};
+      const uint32_t ss[4] = {vs.x, vs.y, vs.z, vs.w};
 #pragma unroll
       for (int i = 0; i < 4; i++) {
-        acc[2 * i] += bf16_lo(vv[i]);
-        acc[2 * i + 1] += bf16_hi(vv[i]);
+        acc[2 * i] += bf16_lo(ss[i]);
+        acc[2 * i + 1] += bf16_hi(ss[i]);
       }
     }
     uint4 o;
