@@ -120,14 +120,16 @@ __device__ __forceinline__ float wave_total_f32(float v) {
 //      leading mantissa bits of the fp64 logit) with the low 6 bits replaced
 //      by 63 - lane, so the 64 keys are distinct and never contradict value
 //      order at the 26 bits they keep;
-//   2. rank of every lane key by counting (keys exchanged through LDS); tau
-//      = the key of rank k-1, and tv = the smallest fp64 value whose key
-//      truncates to tau's. Any value below tv is beaten by k lane bests, so
-//      it cannot be in the top-k;
+//   2. the larger key of each lane pair (32 keys); rank of every pair key
+//      by counting (keys exchanged through LDS); tau = the key of rank k-1,
+//      and tv = the smallest fp64 value whose key truncates to tau's. Any
+//      value below tv is beaten by the bests of k pairs, so it cannot be in
+//      the top-k;
 //   3. candidates = values >= tv, compacted to LDS (candidate lanes write);
 //   4. exact rank of each candidate among the candidates (fp64 value, then
-//      index; each candidate broadcast through scalar registers) picks and
-//      orders the k winners.
+//      index): four lanes per candidate up to 16 candidates (the usual
+//      case), else one lane each, the others broadcast through scalar
+//      registers; picks and orders the k winners.
 // Only massively tied logits (more than TOPK_CMAX candidates) take the slow
 // path: k rounds of a wave arg-max. Order: larger logit first, lower expert
 // index on ties. Lane r < k ends with expert r and its renormalised gate,
@@ -178,25 +180,27 @@ __device__ __forceinline__ void wave_topk_order(const double (&v)[NV], int E, in
   for (int i = 0; i < NV; i++)
     if (i < nv) bv = (v[i] > bv) ? v[i] : bv;
   const uint32_t key = (sort_key_hi(bv) & ~63u) | (uint32_t)(63 - lane);
-  S_key[lane] = key;
+  // the larger key of each lane pair: 32 distinct keys, each the maximum of
+  // 2 NV values (k <= 16 <= 32)
+  const uint32_t pk = max(key, (uint32_t)dpp_i32<DPP_XOR1>((int)key));
+  if ((lane & 1) == 0) S_key[lane >> 1] = pk;
   wave_lds_sync();
-  // 2. rank of this lane's key among the 64, and the threshold
-  int r0 = 0, r1 = 0, r2 = 0, r3 = 0;
+  // 2. rank of pair (lane & 31)'s key among the 32 (lanes < 32), and the
+  //    threshold: the k-th largest pair key; k pairs hold a value >= it, so
+  //    every top-k value is >= it (half the compares of ranking 64 lane keys)
+  const uint32_t mine = S_key[lane & 31];
+  int r0 = 0, r1 = 0;
   const uint4* kv = reinterpret_cast<const uint4*>(S_key);
 #pragma unroll
-  for (int j = 0; j < 16; j++) {
-    const uint4 q = kv[j];
-    r0 += q.x > key;
-    r1 += q.y > key;
-    r2 += q.z > key;
-    r3 += q.w > key;
+  for (int j = 0; j < 8; j += 2) {
+    const uint4 q = kv[j], q2 = kv[j + 1];
+    r0 += (int)(q.x > mine) + (int)(q.y > mine) + (int)(q.z > mine) + (int)(q.w > mine);
+    r1 += (int)(q2.x > mine) + (int)(q2.y > mine) + (int)(q2.z > mine) + (int)(q2.w > mine);
   }
-  const int rank = (r0 + r1) + (r2 + r3);
-  const uint64_t sel = __ballot(rank == k - 1);
-  const uint32_t tau = (uint32_t)__builtin_amdgcn_readlane((int)key, __ffsll((long long)sel) - 1) & ~63u;
+  const uint64_t sel = __ballot((lane < 32) & (r0 + r1 == k - 1));
+  const uint32_t tau = (uint32_t)__builtin_amdgcn_readlane((int)mine, __ffsll((long long)sel) - 1) & ~63u;
   const double tv = key_floor_value(tau);
-  // 3. candidates, compacted in (slot, lane) order; only candidate lanes
-  //    write (a few per slot)
+  // 3. candidates, compacted in (slot, lane) order
   int base = 0;
 #pragma unroll
   for (int i = 0; i < NV; i++) {
@@ -205,16 +209,37 @@ __device__ __forceinline__ void wave_topk_order(const double (&v)[NV], int E, in
       const bool cand = (e < E) & (v[i] >= tv);
       const uint64_t bal = __ballot(cand);
       const int pos = base + __popcll(bal & ((1ull << lane) - 1ull));
-      if (cand & (pos < TOPK_CMAX)) {
-        S_c[pos].v = v[i];
-        S_c[pos].i = e;
-      }
+      // every lane writes (no branch): non-candidates to their own slot past
+      // the candidate area
+      const int wp = (cand & (pos < TOPK_CMAX)) ? pos : TOPK_CMAX + lane;
+      S_c[wp].v = v[i];
+      S_c[wp].i = e;
       base += __popcll(bal);
     }
   }
   const int nc = base;
   wave_lds_sync();
-  if (nc <= 64) {
+  if (nc <= 16) {
+    // 4'. the usual case (about 11 candidates): four lanes per candidate,
+    //     each comparing it with every fourth candidate (broadcast LDS
+    //     reads), the four counts summed across the quad; a loop of scalar
+    //     broadcasts over the candidates costs ~3x as much
+    const int c = lane >> 2, g = lane & 3;
+    const TopkSlot me = S_c[c < nc ? c : 0];
+    int rk = 0;
+#pragma unroll
+    for (int jj = 0; jj < 4; jj++) {
+      const int j = g + 4 * jj;
+      const TopkSlot o = S_c[j < nc ? j : 0];
+      rk += (int)((j < nc) & topk_before(o.v, o.i, me.v, me.i));
+    }
+    rk += dpp_i32<DPP_XOR1>(rk);
+    rk += dpp_i32<DPP_XOR2>(rk);
+    if ((g == 0) & (c < nc) & (rk < k)) {
+      S_o[rk].v = me.v;
+      S_o[rk].i = me.i;
+    }
+  } else if (nc <= 64) {
     // 4. exact ranks: candidate c sits in lane c; each candidate in turn is
     //    broadcast through scalar registers and every lane compares
     const double cvv = (lane < nc) ? S_c[lane < nc ? lane : 0].v : -__builtin_inf();
