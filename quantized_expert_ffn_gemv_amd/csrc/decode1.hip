@@ -1112,11 +1112,17 @@ __device__ __forceinline__ void router_finish_b(const LayerDev& L, const uint16_
 // call, so the readers can check every tag).
 __device__ __forceinline__ void fwd_routing_b(const LayerDev& L, const uint64_t* logits, int B, uint32_t tag,
                                               uint32_t* sync, uint64_t ticks, uint8_t* scratch, int* s_mark,
-                                              int* s_urank, int* s_wcnt, int* s_nu, int* s_uexp, uint32_t* s_umask,
+                                              int* s_nu, int* s_uexp, uint32_t* s_umask,
                                               int* s_sidx, int* s_suid, float* s_sgate, uint64_t* res,
                                               int32_t* idx_out, float* gate_out) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, t0 = threadIdx.x;
   const int E = L.E, k = L.k, nslot = B * k;
+  if (wave >= B) {
+    // the waves without a token clear the union's arrays meanwhile
+    const int ct = t0 - 64 * B, nct = F_THREADS - 64 * B;
+    for (int e = ct; e < E; e += nct) s_mark[e] = 0x7FFFFFFF;
+    if (ct < FB_SLOTS) s_umask[ct] = 0u;
+  }
   if (wave < B) {
     const uint64_t* lg = logits + (size_t)wave * 2 * E;
     uint64_t wl[F_NV], wh[F_NV];
@@ -1168,26 +1174,27 @@ __device__ __forceinline__ void fwd_routing_b(const LayerDev& L, const uint64_t*
       s_sgate[wave * k + lane] = mg;
     }
   }
-  // unique experts in slot order of first appearance, and their token masks
-  for (int e = t0; e < E; e += F_THREADS) s_mark[e] = 0x7FFFFFFF;
+  // unique experts in slot order of first appearance, and their token masks:
+  // the first slot of each expert (LDS atomicMin), then every wave forms the
+  // first-appearance masks of all B k <= 128 slots itself (two ballots), so
+  // each slot finds its expert's unique index with two popcounts and no
+  // further exchange (three barriers in all)
   __syncthreads();
   if (t0 < nslot) atomicMin(&s_mark[s_sidx[t0]], t0);
   __syncthreads();
-  const bool first = t0 < nslot && s_mark[s_sidx[t0]] == t0;
-  const uint64_t bal = __builtin_amdgcn_ballot_w64(first);
-  if (lane == 0 && wave < 2) s_wcnt[wave] = __popcll(bal);
-  if (t0 < FB_SLOTS) s_umask[t0] = 0u;
-  __syncthreads();
-  const int rank = (wave == 1 ? s_wcnt[0] : 0) + __popcll(bal & ((1ull << lane) - 1ull));
-  if (first) {
-    s_urank[t0] = rank;
-    s_uexp[rank] = s_sidx[t0];
+  const int j0 = min(lane, nslot - 1), j1 = min(64 + lane, nslot - 1);
+  const uint64_t m0 = __builtin_amdgcn_ballot_w64((lane < nslot) & (s_mark[s_sidx[j0]] == lane));
+  const uint64_t m1 = __builtin_amdgcn_ballot_w64((64 + lane < nslot) & (s_mark[s_sidx[j1]] == 64 + lane));
+  const int n0 = __popcll(m0), nu = n0 + __popcll(m1);
+  if (t0 < nslot) {
+    const int f = s_mark[s_sidx[t0]];  // first slot of this slot's expert (<= t0)
+    const int u = f < 64 ? __popcll(m0 & ((1ull << f) - 1ull)) : n0 + __popcll(m1 & ((1ull << (f - 64)) - 1ull));
+    if (f == t0) s_uexp[u] = s_sidx[t0];
+    atomicOr(&s_umask[u], 1u << (t0 / k));
+    s_suid[t0] = u;
   }
+  if (t0 == 0) *s_nu = nu;
   __syncthreads();
-  if (t0 < nslot) atomicOr(&s_umask[s_urank[s_mark[s_sidx[t0]]]], 1u << (t0 / k));
-  if (t0 == 0) *s_nu = s_wcnt[0] + s_wcnt[1];
-  __syncthreads();
-  const int nu = *s_nu;
   if (t0 < FB_NRES) {
     uint32_t pl = 0u;
     if (t0 == 0) {
@@ -1197,7 +1204,7 @@ __device__ __forceinline__ void fwd_routing_b(const LayerDev& L, const uint64_t*
       pl = j < nu ? ((uint32_t)s_uexp[j] | (s_umask[j] << 16)) : 0u;
     } else if (t0 < FB_RES_G) {
       const int sl = t0 - FB_RES_I;
-      pl = sl < nslot ? ((uint32_t)s_sidx[sl] | ((uint32_t)s_urank[s_mark[s_sidx[sl]]] << 16)) : 0u;
+      pl = sl < nslot ? ((uint32_t)s_sidx[sl] | ((uint32_t)s_suid[sl] << 16)) : 0u;
     } else {
       const int sl = t0 - FB_RES_G;
       pl = sl < nslot ? __float_as_uint(s_sgate[sl]) : 0u;
@@ -1206,7 +1213,6 @@ __device__ __forceinline__ void fwd_routing_b(const LayerDev& L, const uint64_t*
   }
   if (idx_out && t0 < nslot) idx_out[t0] = s_sidx[t0];
   if (gate_out && t0 < nslot) gate_out[t0] = s_sgate[t0];
-  if (t0 < nslot) s_suid[t0] = s_urank[s_mark[s_sidx[t0]]];
 }
 
 // The other workgroups: the XCD's routing words (bounded poll), into LDS.
@@ -1416,8 +1422,6 @@ __global__ __launch_bounds__(F_THREADS, 4) void k_decode1b(LayerDev L, const uin
   __shared__ __align__(16) float s_red[FB_RED];  // reductions; the forwarder's top-k scratch before that
   __shared__ double s_rt[F_WAVES * FB_MAXB];
   __shared__ int s_mark[64 * F_NV];
-  __shared__ int s_urank[FB_SLOTS];
-  __shared__ int s_wcnt[2];
   __shared__ int s_nu;
   __shared__ int s_uexp[FB_SLOTS];
   __shared__ uint32_t s_umask[FB_SLOTS];
@@ -1496,8 +1500,8 @@ __global__ __launch_bounds__(F_THREADS, 4) void k_decode1b(LayerDev L, const uin
   }
   // the routing
   if (b < F_NX) {
-    fwd_routing_b(L, tl, B, tag, ws.sync, G.wait_ticks, reinterpret_cast<uint8_t*>(s_red), s_mark, s_urank, s_wcnt,
-                  &s_nu, s_uexp, s_umask, s_sidx, s_suid, s_sgate, res, idx_out, gate_out);
+    fwd_routing_b(L, tl, B, tag, ws.sync, G.wait_ticks, reinterpret_cast<uint8_t*>(s_red), s_mark, &s_nu, s_uexp,
+                  s_umask, s_sidx, s_suid, s_sgate, res, idx_out, gate_out);
   } else {
     wait_routing_b(L, res, B, tag, ws.sync, G.wait_ticks, &s_nu, s_uexp, s_umask, s_sidx, s_suid, s_sgate);
   }
