@@ -1072,6 +1072,7 @@ struct BatchGeo {
 // Router rows dotted with all B tokens: the parts of a row are summed in
 // part order by the row's first wave, per token (lanes 2t, 2t + 1 store
 // token t's low and high words).
+template <int MAXB>
 __device__ __forceinline__ void router_finish_b(const LayerDev& L, const uint16_t* xs, int B, const RouterRegs& R,
                                                 int rw, int rr, uint64_t* logits, double* s_rt, uint32_t tag) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -1086,23 +1087,38 @@ __device__ __forceinline__ void router_finish_b(const LayerDev& L, const uint16_
   float bias = R.bias;
   asm volatile("" : "+v"(bias));
   if (!in) w = make_float4(0.f, 0.f, 0.f, 0.f);
+  // all MAXB tokens at once (tokens past B repeat the last one and are not
+  // stored), so that their dependent DPP sums interleave instead of running
+  // one token after another; each 16-lane row sum goes to LDS and the
+  // row-0 wave of the row adds them as ((r0 + r1) + (r2 + r3)), part by
+  // part: the association of the batch-1 router
+  double v[MAXB];
 #pragma unroll
-  for (int t = 0; t < FB_MAXB; t++) {
-    if (t < B) {
-      const uint2 xx = reinterpret_cast<const uint2*>(xs + (size_t)t * L.H)[in ? c : 0];
-      const double a0 = __builtin_fma((double)w.z, (double)bf16_lo(xx.y), (double)w.x * (double)bf16_lo(xx.x));
-      const double a1 = __builtin_fma((double)w.w, (double)bf16_hi(xx.y), (double)w.y * (double)bf16_hi(xx.x));
-      const double part = wave_total_f64(a0 + a1);
-      if (lane == 0) s_rt[wave * FB_MAXB + t] = part;
-    }
+  for (int t = 0; t < MAXB; t++) {
+    const int tt = min(t, B - 1);
+    const uint2 xx = reinterpret_cast<const uint2*>(xs + (size_t)tt * L.H)[in ? c : 0];
+    const double a0 = __builtin_fma((double)w.z, (double)bf16_lo(xx.y), (double)w.x * (double)bf16_lo(xx.x));
+    const double a1 = __builtin_fma((double)w.w, (double)bf16_hi(xx.y), (double)w.y * (double)bf16_hi(xx.x));
+    v[t] = a0 + a1;
+  }
+#pragma unroll
+  for (int t = 0; t < MAXB; t++) v[t] = sum16_f64(v[t]);
+  if ((lane & 15) == 0) {
+#pragma unroll
+    for (int t = 0; t < MAXB; t++)
+      if (t < B) s_rt[((size_t)wave * MAXB + t) * 4 + (lane >> 4)] = v[t];
   }
   __syncthreads();
   if (p == 0 && valid && lane < 2 * B) {
     const int t = lane >> 1;
-    double tot = s_rt[wave * FB_MAXB + t];
-    for (int q = 1; q < P; q++) tot += s_rt[(wave + q) * FB_MAXB + t];
-    const uint64_t v = (uint64_t)__double_as_longlong(tot + (L.router_b ? (double)bias : 0.0));
-    st_word(logits + (size_t)t * 2 * L.E + 2 * e + (lane & 1), (lane & 1) ? (uint32_t)(v >> 32) : (uint32_t)v, tag);
+    double tot = 0.0;
+    for (int q = 0; q < P; q++) {
+      const double* r4 = s_rt + ((size_t)(wave + q) * MAXB + t) * 4;
+      const double part = (r4[0] + r4[1]) + (r4[2] + r4[3]);
+      tot = q ? tot + part : part;
+    }
+    const uint64_t bits = (uint64_t)__double_as_longlong(tot + (L.router_b ? (double)bias : 0.0));
+    st_word(logits + (size_t)t * 2 * L.E + 2 * e + (lane & 1), (lane & 1) ? (uint32_t)(bits >> 32) : (uint32_t)bits, tag);
   }
 }
 
@@ -1420,7 +1436,7 @@ __global__ __launch_bounds__(F_THREADS, 4) void k_decode1b(LayerDev L, const uin
   __shared__ __align__(16) uint16_t s_x[FB_XMAX];
   __shared__ __align__(16) float s_xsum[FB_XMAX / 32];
   __shared__ __align__(16) float s_red[FB_RED];  // reductions; the forwarder's top-k scratch before that
-  __shared__ double s_rt[F_WAVES * FB_MAXB];
+  __shared__ double s_rt[F_WAVES * MAXB * 4];  // router row sums: [wave][token][16-lane row]
   __shared__ int s_mark[64 * F_NV];
   __shared__ int s_nu;
   __shared__ int s_uexp[FB_SLOTS];
@@ -1463,7 +1479,7 @@ __global__ __launch_bounds__(F_THREADS, 4) void k_decode1b(LayerDev L, const uin
     if (i < n8 && (i & 3) == 0) s_xsum[i >> 2] = sm;
   }
   __syncthreads();
-  if (is_router) router_finish_b(L, s_x, B, rrg, b, G.rr, tl, s_rt, tag);
+  if (is_router) router_finish_b<MAXB>(L, s_x, B, rrg, b, G.rr, tl, s_rt, tag);
   float pacc[MAXB][F_RPT];
 #pragma unroll
   for (int t = 0; t < MAXB; t++)
