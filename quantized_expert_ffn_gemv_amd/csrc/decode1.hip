@@ -1611,33 +1611,54 @@ __global__ __launch_bounds__(F_THREADS, 4) void k_decode1b(LayerDev L, const uin
     const int row = r0 + min(rr, nrow - 1);
     const int pb0 = xx + F_NX * g, pb1 = xx + F_NX * (g + 16);
     const uint32_t tm0 = s_touch[pb0], tm1 = s_touch[pb1];
-    // the producers' done words (one wave, lane l: workgroup xx + 8 l), then
-    // the partials once: polling the partial words themselves (up to 16 per
-    // thread and round) flooded the XCD's L2 while slower producers still ran
-    if (tid < 64) {
-      const uint64_t* dw = pdone + xx + F_NX * (tid & 31);
-      uint64_t d = ld_word_coherent(dw);
-      if (__builtin_amdgcn_ballot_w64(!tag_ok(d, tag)) != 0) {
-        const uint64_t c0 = wall_clock64();
-        int it = 0;
-        while (true) {
-          __builtin_amdgcn_s_sleep(2);
-          const uint64_t nd = ld_word_coherent(dw);
-          d = tag_ok(d, tag) ? d : nd;
-          if (__builtin_amdgcn_ballot_w64(!tag_ok(d, tag)) == 0) break;
-          if ((++it & 15) == 0 && wall_clock64() - c0 > G.wait_ticks) {
-            if (tid == 0) flag_error(ws.sync, 4u);
-            break;
-          }
+    // each wave waits for its own two producers' done words (wave g:
+    // workgroups xx + 8 g and xx + 8 (g + 16)) and loads a producer's
+    // partials as soon as that producer is done, while the XCD's later
+    // producers still run: the early partials are read while they are still
+    // in the L2 (waiting for all 32 first left them to be read back from
+    // memory at the end, up to 4 MB per XCD at B = 8)
+    // (both done words are loaded up front: when both producers are already
+    // done, both producers' partials are requested back to back)
+    const uint64_t* dw0 = pdone + pb0;
+    const uint64_t* dw1 = pdone + pb1;
+    uint64_t d0 = ld_word_coherent(dw0), d1 = ld_word_coherent(dw1);
+    const bool nd0 = (tm0 & allm) != 0u, nd1 = (tm1 & allm) != 0u;  // wave-uniform
+    const uint64_t c0 = wall_clock64();
+    if (__builtin_amdgcn_ballot_w64(nd0 && !tag_ok(d0, tag)) != 0) {
+      int it = 0;
+      while (true) {
+        __builtin_amdgcn_s_sleep(2);
+        const uint64_t n0 = ld_word_coherent(dw0), n1 = ld_word_coherent(dw1);
+        d0 = tag_ok(d0, tag) ? d0 : n0;
+        d1 = tag_ok(d1, tag) ? d1 : n1;
+        if (__builtin_amdgcn_ballot_w64(!tag_ok(d0, tag)) == 0) break;
+        if ((++it & 15) == 0 && wall_clock64() - c0 > G.wait_ticks) {
+          if ((tid & 63) == 0) flag_error(ws.sync, 4u);
+          break;
         }
       }
     }
-    __syncthreads();
     uint64_t w0[MAXB], w1[MAXB];
 #pragma unroll
     for (int t = 0; t < MAXB; t++) {
       const int tt = min(t, B - 1);
       w0[t] = ld_word_coherent(part + ((size_t)pb0 * B + tt) * H + row);  // unconditional, clamped
+    }
+    if (__builtin_amdgcn_ballot_w64(nd1 && !tag_ok(d1, tag)) != 0) {
+      int it = 0;
+      while (true) {
+        __builtin_amdgcn_s_sleep(2);
+        d1 = ld_word_coherent(dw1);
+        if (__builtin_amdgcn_ballot_w64(!tag_ok(d1, tag)) == 0) break;
+        if ((++it & 15) == 0 && wall_clock64() - c0 > G.wait_ticks) {
+          if ((tid & 63) == 0) flag_error(ws.sync, 4u);
+          break;
+        }
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < MAXB; t++) {
+      const int tt = min(t, B - 1);
       w1[t] = ld_word_coherent(part + ((size_t)pb1 * B + tt) * H + row);
     }
     auto need0 = [&](int t) { return t < B && ((tm0 >> t) & 1u); };
