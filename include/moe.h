@@ -79,13 +79,13 @@ typedef enum {
  *         w0..w3; word j holds elements 8j..8j+7 as unsigned (code + 8):
  *         element 8j+2s   at bits [4s, 4s+4),
  *         element 8j+2s+1 at bits [16+4s, 16+4s+4),   s = 0..3
- *   Q3  : kc = 32 elements, cb = 12 bytes = words L0, L1, HB holding the
- *         unsigned (code + 4) in [0,7]:
- *         low two bits: element 2i (i=0..7) at L0 bits [2i, 2i+2) and
- *         element 2i+1 at L0 bits [16+2i, 16+2i+2); elements 16..31 the
- *         same in L1 with i-8;
- *         bit two: element 2i at HB bit i, element 2i+1 at HB bit 16+i
- *         (i = 0..15).
+ *   Q3  : kc = 32 elements, cb = 12 bytes = three little-endian 32-bit
+ *         words w0, w1, w2 holding the unsigned (code + 4) in [0,7]:
+ *         for i = 0..14, with m = i / 5 and s = i % 5, element 2i at
+ *         bits [3s, 3s+3) of word m and element 2i+1 at bits
+ *         [16+3s, 16+3s+3) of word m;
+ *         elements 30 and 31: bit b (b = 0..2) of element 30 at bit 15 of
+ *         word b, bit b of element 31 at bit 31 of word b.
  *   F32 and BF16 matrices have no scales.
  *
  * An expert's gate and up projections (each [I][H]) are fused into one

@@ -494,18 +494,18 @@ static moe_status pack_rows(int32_t wt, int32_t rows, int32_t K, const void* con
             memcpy(dst + 4 * j, &w, 4);
           }
         } else {
-          uint32_t l0 = 0, l1 = 0, hb = 0;
-          for (int i = 0; i < 16; i++) {
-            uint32_t& lw = (i < 8) ? l0 : l1;
-            const int s = i & 7;
-            lw |= (u[2 * i] & 3u) << (2 * s);
-            lw |= (u[2 * i + 1] & 3u) << (16 + 2 * s);
-            hb |= (u[2 * i] >> 2) << i;
-            hb |= (u[2 * i + 1] >> 2) << (16 + i);
+          // pairs 0..14: word i / 5, fields at 3 (i % 5) and 16 + 3 (i % 5);
+          // pair 15: bit b of elements 30 and 31 at bits 15 and 31 of word b
+          uint32_t w[3] = {0, 0, 0};
+          for (int i = 0; i < 15; i++) {
+            w[i / 5] |= u[2 * i] << (3 * (i % 5));
+            w[i / 5] |= u[2 * i + 1] << (16 + 3 * (i % 5));
           }
-          memcpy(dst, &l0, 4);
-          memcpy(dst + 4, &l1, 4);
-          memcpy(dst + 8, &hb, 4);
+          for (int b = 0; b < 3; b++) {
+            w[b] |= ((u[30] >> b) & 1u) << 15;
+            w[b] |= ((u[31] >> b) & 1u) << 31;
+          }
+          memcpy(dst, w, 12);
         }
         if (out_scales) out_scales[(size_t)c * rows + r] = rscale[r][c];
       }

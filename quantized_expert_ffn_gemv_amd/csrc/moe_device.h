@@ -65,35 +65,34 @@ __device__ __forceinline__ void q4_word_pairs(uint32_t wd, uint32_t (&p)[4]) {
   for (int s = 0; s < 4; s++) p[s] = ((wd >> (4 * s)) & 0x000F000Fu) | MAGIC2;
 }
 
+// Q3 chunk: three words W0, W1, W2. Pair i < 15 sits in word i / 5 as two
+// 3-bit fields at bits 3 (i % 5) (element 2i) and 16 + 3 (i % 5) (element
+// 2i + 1), so it is one shift and one and-or, like a Q4 pair; pair 15 takes
+// the spare bits 15 (element 30) and 31 (element 31) of the three words, bit
+// b of its codes from word b.
 template <uint32_t MAGIC2>
-__device__ __forceinline__ uint32_t q3_pair(uint32_t lw, uint32_t hb, int i) {
-  // i in 0..15 (compile-time after unrolling); lw is L0 for i<8, L1 otherwise
-  const int s = i & 7;
-  uint32_t p = ((lw >> (2 * s)) & 0x00030003u) | MAGIC2;
-  uint32_t h = (i >= 2) ? (hb >> (i - 2)) : (hb << (2 - i));
-  return p | (h & 0x00040004u);
+__device__ __forceinline__ uint32_t q3_pair(uint32_t w0, uint32_t w1, uint32_t w2, int i) {
+  // i in 0..15 (compile-time after unrolling)
+  if (i == 15) {
+    uint32_t p = ((w0 >> 15) & 0x00010001u) | MAGIC2;
+    p |= (w1 >> 14) & 0x00020002u;
+    return p | ((w2 >> 13) & 0x00040004u);
+  }
+  const uint32_t w = (i < 5) ? w0 : (i < 10) ? w1 : w2;
+  return ((w >> (3 * (i % 5))) & 0x00070007u) | MAGIC2;
 }
 
 template <uint32_t MAGIC2>
-__device__ __forceinline__ void q3_pairs(uint32_t l0, uint32_t l1, uint32_t hb, uint32_t (&p)[16]) {
+__device__ __forceinline__ void q3_pairs(uint32_t w0, uint32_t w1, uint32_t w2, uint32_t (&p)[16]) {
 #pragma unroll
-  for (int i = 0; i < 16; i++) p[i] = q3_pair<MAGIC2>(i < 8 ? l0 : l1, hb, i);
+  for (int i = 0; i < 16; i++) p[i] = q3_pair<MAGIC2>(w0, w1, w2, i);
 }
 
 // Pairs 4g..4g+3 of a Q3 chunk (elements 8g..8g+7).
 template <uint32_t MAGIC2>
-__device__ __forceinline__ void q3_group_pairs(uint32_t l0, uint32_t l1, uint32_t hb, int g,
-                                               uint32_t (&p)[4]) {
-  const uint32_t lw = (g < 2) ? l0 : l1;
-  const uint32_t lsh = lw >> (8 * (g & 1));           // pairs 4(g&1)..: bits 8*(g&1)
-  // high bits of pairs 4g+s sit at HB bits 4g+s (low half) and 16+4g+s
-  const uint32_t hsh = hb >> (4 * g);
+__device__ __forceinline__ void q3_group_pairs(uint32_t w0, uint32_t w1, uint32_t w2, int g, uint32_t (&p)[4]) {
 #pragma unroll
-  for (int s = 0; s < 4; s++) {
-    uint32_t v = ((lsh >> (2 * s)) & 0x00030003u) | MAGIC2;
-    uint32_t h = (s >= 2) ? (hsh >> (s - 2)) : (hsh << (2 - s));
-    p[s] = v | (h & 0x00040004u);
-  }
+  for (int s = 0; s < 4; s++) p[s] = q3_pair<MAGIC2>(w0, w1, w2, 4 * g + s);
 }
 
 static constexpr uint32_t BF16_MAGIC2 = 0x43004300u;  // bf16(128) in both halves

@@ -482,7 +482,7 @@ struct GemmArgs {
 // ---------------------------------------------------------------------------
 template <int WT> struct BRaw;
 template <> struct BRaw<MOE_W_Q4> { uint4 w; uint32_t s; };          // s: fp16 scale bits, 0 when out of range
-template <> struct BRaw<MOE_W_Q3> { uint32_t l0, l1, hb, s; };
+template <> struct BRaw<MOE_W_Q3> { uint32_t w0, w1, w2, s; };
 template <> struct BRaw<MOE_W_BF16> { uint4 w[4]; uint32_t ok; };
 template <> struct BRaw<MOE_W_F32> { uint4 w[8]; uint32_t ok; };
 
@@ -499,9 +499,9 @@ __device__ __forceinline__ void load_b(const uint8_t* __restrict__ w, const uint
     r.s = ws[cell] & (ok ? 0xFFFFu : 0u);
   } else if constexpr (WT == MOE_W_Q3) {
     const uint32_t* p = reinterpret_cast<const uint32_t*>(w + cell * 12u);
-    r.l0 = p[0];
-    r.l1 = p[1];
-    r.hb = p[2];
+    r.w0 = p[0];
+    r.w1 = p[1];
+    r.w2 = p[2];
     r.s = ws[cell] & (ok ? 0xFFFFu : 0u);
   } else {
     // dense: the block is NCH consecutive 16-byte chunks of chunk columns NCH*blk .. ; cell -> (blk, n)
@@ -525,7 +525,7 @@ __device__ __forceinline__ bf16x8_t frag_b(const BRaw<WT>& r, int t) {
       const uint32_t wd = (t == 0) ? r.w.x : (t == 1) ? r.w.y : (t == 2) ? r.w.z : r.w.w;
       q4_word_pairs<F16_MAGIC2>(wd, p);
     } else {
-      q3_group_pairs<F16_MAGIC2>(r.l0, r.l1, r.hb, t, p);
+      q3_group_pairs<F16_MAGIC2>(r.w0, r.w1, r.w2, t, p);
     }
     const float sc = f16_to_f32((uint16_t)r.s);
     const float negbase = -(1024.0f + (float)QOff<WT>::v) * sc;
@@ -928,9 +928,9 @@ __device__ __forceinline__ void gemm_q_tile(const GemmArgs& g, uint4* sA0, uint4
 #pragma unroll
       for (int sub = 0; sub < NSW; sub++) {
         const uint32_t* p = reinterpret_cast<const uint32_t*>(sb + (wave * NSW + sub) * GQ_REGION) + lane;
-        r[sub].l0 = p[0];
-        r[sub].l1 = p[64];
-        r[sub].hb = p[128];
+        r[sub].w0 = p[0];
+        r[sub].w1 = p[64];
+        r[sub].w2 = p[128];
         r[sub].s = sc[sub] & ((okbits >> sub) & 1u ? 0xFFFFu : 0u);
       }
 #pragma unroll

@@ -132,18 +132,19 @@ def _unpack_doc(wt, rows, K, packed, scales=None):
         codes = out - 8
     elif wt == moe.W_Q3:
         words = packed.view(np.uint32).reshape(K // 32, rows, 3)
-        L0, L1, HB = words[:, :, 0], words[:, :, 1], words[:, :, 2]
         out = np.empty((rows, K), np.int64)
         base = np.arange(K // 32) * 32
-        for i in range(16):
-            lw = L0 if i < 8 else L1
-            s = i % 8
-            lo_e = (lw >> (2 * s)) & 3
-            lo_o = (lw >> (16 + 2 * s)) & 3
-            hi_e = (HB >> i) & 1
-            hi_o = (HB >> (16 + i)) & 1
-            out[:, base + 2 * i] = (lo_e | (hi_e << 2)).T
-            out[:, base + 2 * i + 1] = (lo_o | (hi_o << 2)).T
+        for i in range(15):
+            w = words[:, :, i // 5]
+            out[:, base + 2 * i] = ((w >> (3 * (i % 5))) & 7).T
+            out[:, base + 2 * i + 1] = ((w >> (16 + 3 * (i % 5))) & 7).T
+        e30 = np.zeros_like(words[:, :, 0])
+        e31 = np.zeros_like(words[:, :, 0])
+        for b in range(3):
+            e30 |= ((words[:, :, b] >> 15) & 1) << b
+            e31 |= ((words[:, :, b] >> 31) & 1) << b
+        out[:, base + 30] = e30.T
+        out[:, base + 31] = e31.T
         codes = out - 4
     elif wt == moe.W_BF16:
         codes = packed.view(np.uint16).reshape(K // 8, rows, 8).transpose(1, 0, 2).reshape(rows, K)
