@@ -23,7 +23,8 @@
 //   sg0 <= b < sg0 + nSG   shared expert, 8 intermediates each: 16 gate/up
 //                          rows, SwiGLU -> h, then those 8 columns of the
 //                          shared down matrix times h: a partial y over all
-//                          H rows (sg0 = nRG rounded up to a multiple of 8).
+//                          H rows (sg0 = nRG rounded up to a multiple of 8);
+//                          started once the XCD's logits are forwarded.
 //
 // The down product is split along the intermediate dimension (split-K), so
 // h never leaves the workgroup that made it and the down weights stream in
@@ -65,7 +66,7 @@
 // for graph replay) without a memset.
 //
 // Progress: forwarders wait only for the routers (router rows never wait),
-// routed units for their forwarder, XCD sums for producers, final sums for
+// routed and shared units for their forwarder, XCD sums for producers, final sums for
 // XCD sums, so every value gets written once every workgroup is resident;
 // the path is taken only when the grid fits the chip at one workgroup per
 // CU.
@@ -863,7 +864,14 @@ __global__ __launch_bounds__(F_THREADS, 4) void k_decode1(LayerDev L, const uint
   __syncthreads();
   if (is_router) router_finish(L, s_x, rrg, b, G.rr, tl, s_rt, tag);
   if (is_shared) {
-    // shared expert, intermediates 8su .. 8su+7 (needed only by the sums)
+    // shared expert, intermediates 8su .. 8su+7 (needed only by the sums).
+    // Its 6 MB stream starts once the XCD's logits are forwarded: loads in
+    // flight slow the routers' logit words on their way across the XCDs,
+    // which are on the critical path (14.34 -> 14.22 us per token; with the
+    // routed experts' rows loaded ahead of the routing instead, a probe with
+    // the experts known in advance, 14.36 -> 15.05 us). Only when every XCD
+    // has a forwarder.
+    if (G.nRG >= F_NX) wait_ready(rdy, tag, ws.sync, G.wait_ticks);
     constexpr int SW = (SWT == MOE_W_F32) ? MOE_W_F32 : MOE_W_BF16;
     const int su = b - G.sg0;
     const int q = su >> 1, hf = su & 1;
@@ -1528,7 +1536,9 @@ __global__ __launch_bounds__(F_THREADS, 4) void k_decode1b(LayerDev L, const uin
 #pragma unroll
     for (int n = 0; n < F_RPT; n++) pacc[t][n] = 0.0f;
   if (is_shared) {
-    // shared unit su: intermediates 8su .. 8su+7, every token
+    // shared unit su: intermediates 8su .. 8su+7, every token (while the
+    // routing is made: after their routed units these workgroups were
+    // last to finish, B = 3..8 1.2 - 3.1 us per call slower)
     constexpr int SW = (SWT == MOE_W_F32) ? MOE_W_F32 : MOE_W_BF16;
     const int su = b - F_NX, q = su >> 1, hf = su & 1;
     DownPre<SW> spre;
