@@ -519,12 +519,18 @@ __device__ __forceinline__ void block_topk(const uint64_t* logits, int E, int k,
                                            uint64_t ticks, BlockTopk& S) {
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   // 1. one logit per thread: coherent loads (a line another call left in
-  //    this XCD's L2 is never used), clamped and unconditional
+  //    this XCD's L2 is never used), clamped; only the waves that hold
+  //    experts load (when every thread past E loaded the clamped last word,
+  //    the workgroups of an XCD sent ~300 requests for that one line to one
+  //    L2 channel, behind which the other words on that channel waited)
   const int e = min(t, E - 1);
-  uint64_t wl = ld_word_coherent(logits + 2 * e);
-  uint64_t wh = ld_word_coherent(logits + 2 * e + 1);
+  uint64_t wl = 0, wh = 0;
   if (t == 0) S.cnt = 0;
-  settle2(logits + 2 * e, logits + 2 * e + 1, wl, wh, tag, sync, ticks);  // the last router rows may be on their way
+  if (wave * 64 < E) {  // wave-uniform
+    wl = ld_word_coherent(logits + 2 * e);
+    wh = ld_word_coherent(logits + 2 * e + 1);
+    settle2(logits + 2 * e, logits + 2 * e + 1, wl, wh, tag, sync, ticks);  // the last router rows may be on their way
+  }
   const double v = (t < E) ? __longlong_as_double((long long)(((wh & 0xFFFFFFFFull) << 32) | (wl & 0xFFFFFFFFull)))
                            : -__builtin_inf();
   S.val[t] = v;
