@@ -1810,14 +1810,19 @@ size_t decode1b_part_words(int H, int B) { return (size_t)F_NW * B * H; }
 size_t decode1b_xsum_words(int H, int B) { return (size_t)F_NX * B * H; }
 size_t decode1b_res_words() { return (size_t)F_NX * FB_RES_STRIDE + F_NW; }  // routing words, then done words
 
+// Batch widths compiled (a call's batch is padded to the next one): every
+// token slot costs router sums, unit loops and partial loads whether the call
+// fills it or not. Q4: 2, 3, 4, 5, 8; Q3: 2, 3, 4, 8 (its width-5 build
+// spills to scratch).
+template <int WT, int MAXB>
+static bool no_scratch_b() {
+  return no_scratch(k_decode1b<WT, MOE_W_NONE, MAXB>) && no_scratch(k_decode1b<WT, MOE_W_F32, MAXB>) &&
+         no_scratch(k_decode1b<WT, MOE_W_BF16, MAXB>);
+}
 static bool decode1b_no_scratch() {
-  static const bool ok =
-      no_scratch(k_decode1b<MOE_W_Q4, MOE_W_NONE, 4>) && no_scratch(k_decode1b<MOE_W_Q4, MOE_W_F32, 4>) &&
-      no_scratch(k_decode1b<MOE_W_Q4, MOE_W_BF16, 4>) && no_scratch(k_decode1b<MOE_W_Q3, MOE_W_NONE, 4>) &&
-      no_scratch(k_decode1b<MOE_W_Q3, MOE_W_F32, 4>) && no_scratch(k_decode1b<MOE_W_Q3, MOE_W_BF16, 4>) &&
-      no_scratch(k_decode1b<MOE_W_Q4, MOE_W_NONE, 8>) && no_scratch(k_decode1b<MOE_W_Q4, MOE_W_F32, 8>) &&
-      no_scratch(k_decode1b<MOE_W_Q4, MOE_W_BF16, 8>) && no_scratch(k_decode1b<MOE_W_Q3, MOE_W_NONE, 8>) &&
-      no_scratch(k_decode1b<MOE_W_Q3, MOE_W_F32, 8>) && no_scratch(k_decode1b<MOE_W_Q3, MOE_W_BF16, 8>);
+  static const bool ok = no_scratch_b<MOE_W_Q4, 2>() && no_scratch_b<MOE_W_Q4, 3>() && no_scratch_b<MOE_W_Q4, 4>() &&
+                         no_scratch_b<MOE_W_Q4, 5>() && no_scratch_b<MOE_W_Q4, 8>() && no_scratch_b<MOE_W_Q3, 2>() &&
+                         no_scratch_b<MOE_W_Q3, 3>() && no_scratch_b<MOE_W_Q3, 4>() && no_scratch_b<MOE_W_Q3, 8>();
   return ok;
 }
 
@@ -1845,17 +1850,22 @@ static hipError_t launch_fused_bt(const LayerDev& L, const uint16_t* x, int B, u
                   gate_out, ws, G);
 }
 
+template <int WT, int MAXB>
+static hipError_t launch_fused_bs(const LayerDev& L, const uint16_t* x, int B, uint16_t* y, int32_t* io, float* go,
+                                  const DecodeWs& ws, hipStream_t st) {
+  if (L.swt == MOE_W_NONE) return launch_fused_bt<WT, MOE_W_NONE, MAXB>(L, x, B, y, io, go, ws, st);
+  if (L.swt == MOE_W_F32) return launch_fused_bt<WT, MOE_W_F32, MAXB>(L, x, B, y, io, go, ws, st);
+  return launch_fused_bt<WT, MOE_W_BF16, MAXB>(L, x, B, y, io, go, ws, st);
+}
 template <int WT>
 static hipError_t launch_fused_bw(const LayerDev& L, const uint16_t* x, int B, uint16_t* y, int32_t* io, float* go,
                                   const DecodeWs& ws, hipStream_t st) {
-  if (B <= 4) {
-    if (L.swt == MOE_W_NONE) return launch_fused_bt<WT, MOE_W_NONE, 4>(L, x, B, y, io, go, ws, st);
-    if (L.swt == MOE_W_F32) return launch_fused_bt<WT, MOE_W_F32, 4>(L, x, B, y, io, go, ws, st);
-    return launch_fused_bt<WT, MOE_W_BF16, 4>(L, x, B, y, io, go, ws, st);
-  }
-  if (L.swt == MOE_W_NONE) return launch_fused_bt<WT, MOE_W_NONE, 8>(L, x, B, y, io, go, ws, st);
-  if (L.swt == MOE_W_F32) return launch_fused_bt<WT, MOE_W_F32, 8>(L, x, B, y, io, go, ws, st);
-  return launch_fused_bt<WT, MOE_W_BF16, 8>(L, x, B, y, io, go, ws, st);
+  if (B == 2) return launch_fused_bs<WT, 2>(L, x, B, y, io, go, ws, st);
+  if (B == 3) return launch_fused_bs<WT, 3>(L, x, B, y, io, go, ws, st);
+  if (B == 4) return launch_fused_bs<WT, 4>(L, x, B, y, io, go, ws, st);
+  if constexpr (WT == MOE_W_Q4)
+    if (B == 5) return launch_fused_bs<WT, 5>(L, x, B, y, io, go, ws, st);
+  return launch_fused_bs<WT, 8>(L, x, B, y, io, go, ws, st);
 }
 
 hipError_t launch_decode_fused_b(const LayerDev& L, const uint16_t* x, int B, uint16_t* y, int32_t* idx_out,
