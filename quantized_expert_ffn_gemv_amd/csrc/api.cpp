@@ -113,7 +113,7 @@ size_t carve_decode(const moe_layer* L, int B, uint8_t* base, moe::DecodeWs* ws)
                                              : one_kernel_b ? (size_t)B * E * 16
                                                             : (size_t)E * 64));
   if (one_kernel_b) {
-    w.part_words = reinterpret_cast<uint64_t*>(take(8 * moe::decode1b_part_words(L->hidden, B)));
+    w.part = reinterpret_cast<float*>(take(4 * moe::decode1b_part_words(L->hidden, B)));
     w.xsum_words = reinterpret_cast<uint64_t*>(take(8 * moe::decode1b_xsum_words(L->hidden, B)));
     w.res_words = reinterpret_cast<uint64_t*>(take(8 * moe::decode1b_res_words()));
   } else if (one_kernel) {

@@ -143,6 +143,11 @@ __device__ __forceinline__ void st_word_xcd(uint64_t* p, uint32_t payload, uint3
 __device__ __forceinline__ uint32_t ld_u32(const uint32_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// an fp32 value another workgroup of this XCD stored (misses the L1)
+__device__ __forceinline__ float ld_f32_coherent(const float* p) {
+  return __uint_as_float(__hip_atomic_load(reinterpret_cast<const uint32_t*>(p), __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT));
+}
 __device__ __forceinline__ void flag_error(uint32_t* sync, uint32_t bit) {
   __hip_atomic_fetch_or(sync + SY_ERR, bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -1064,11 +1069,12 @@ hipError_t launch_decode_fused(const LayerDev& L, const uint16_t* x, uint16_t* y
 //     several tokens is streamed once and dotted with each of them;
 //   - every workgroup adds its units' down products into a partial y per
 //     token (2 rows per thread and token, registers), written once for the
-//     tokens it touched; the XCD-level and final sums are those of batch 1,
-//     per token.
+//     tokens it touched as plain fp32 (no tags: 4 bytes a value), then the
+//     workgroup's done word; the XCD-level and final sums are those of batch
+//     1, per token.
 // Waits: forwarders for the routers, the others for their forwarder's
-// routing words, XCD sums for the partials of the touched (workgroup,
-// token) pairs of their XCD, final sums for the XCD sums.
+// routing words, XCD sums for the done words of their XCD's producers
+// (then their partials), final sums for the XCD sums.
 constexpr int FB_MAXB = 8;
 constexpr int FB_XMAX = 16384;                         // B H: bf16 values of the staged batch
 constexpr int FB_SLOTS = FB_MAXB * 16;                 // B k <= 128
@@ -1516,7 +1522,9 @@ __global__ __launch_bounds__(F_THREADS, 4) void k_decode1b(LayerDev L, const uin
   const uint32_t tag = ld_u32(my_counter(ws.sync)) + 1u;
   uint64_t* tl = reinterpret_cast<uint64_t*>(ws.logits);  // [B][E][2]
   uint64_t* res = ws.res_words + (size_t)(b % F_NX) * FB_RES_STRIDE;
-  uint64_t* part = ws.part_words;  // [256][B][H]
+  // [256][B][H] fp32 partials (untagged: read only after their producer's
+  // done word)
+  float* part = ws.part;
   uint64_t* xsw = ws.xsum_words;   // [8][B][H]
   uint64_t* pdone = ws.res_words + (size_t)F_NX * FB_RES_STRIDE;  // [256]: a workgroup's partials are in its XCD's L2
   const uint32_t allm = (1u << B) - 1u;
@@ -1659,11 +1667,15 @@ __global__ __launch_bounds__(F_THREADS, 4) void k_decode1b(LayerDev L, const uin
 #pragma unroll
         for (int n = 0; n < F_RPT; n++) {
           const int row = tid + F_THREADS * n;
-          if (row < H) st_word_xcd(part + ((size_t)b * B + t) * H + row, __float_as_uint(pacc[t][n]), tag);
+          if (row < H) part[((size_t)b * B + t) * H + row] = pacc[t][n];
         }
       }
     }
-    __syncthreads();  // every partial word has reached the L2 before the done word
+    // every partial has reached the XCD's L2 (vmcnt counts stores until the
+    // L2 acknowledges them) before any wave passes the barrier, and so before
+    // the done word is stored: a reader that sees the done word finds them
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    __syncthreads();
     if (tid == 0) st_word_xcd(pdone + b, 0u, tag);
   }
   // XCD-level sums: workgroup jx of XCD x sums rows r0 .. r0 + H/32 - 1 of
@@ -1703,11 +1715,11 @@ __global__ __launch_bounds__(F_THREADS, 4) void k_decode1b(LayerDev L, const uin
         }
       }
     }
-    uint64_t w0[MAXB], w1[MAXB];
+    float w0[MAXB], w1[MAXB];
 #pragma unroll
     for (int t = 0; t < MAXB; t++) {
       const int tt = min(t, B - 1);
-      w0[t] = ld_word_coherent(part + ((size_t)pb0 * B + tt) * H + row);  // unconditional, clamped
+      w0[t] = ld_f32_coherent(part + ((size_t)pb0 * B + tt) * H + row);  // unconditional, clamped
     }
     if (__builtin_amdgcn_ballot_w64(nd1 && !tag_ok(d1, tag)) != 0) {
       int it = 0;
@@ -1724,40 +1736,15 @@ __global__ __launch_bounds__(F_THREADS, 4) void k_decode1b(LayerDev L, const uin
 #pragma unroll
     for (int t = 0; t < MAXB; t++) {
       const int tt = min(t, B - 1);
-      w1[t] = ld_word_coherent(part + ((size_t)pb1 * B + tt) * H + row);
+      w1[t] = ld_f32_coherent(part + ((size_t)pb1 * B + tt) * H + row);
     }
     auto need0 = [&](int t) { return t < B && ((tm0 >> t) & 1u); };
     auto need1 = [&](int t) { return t < B && ((tm1 >> t) & 1u); };
-    bool stale = false;
-#pragma unroll
-    for (int t = 0; t < MAXB; t++) stale |= (need0(t) && !tag_ok(w0[t], tag)) || (need1(t) && !tag_ok(w1[t], tag));
-    if (__builtin_amdgcn_ballot_w64(stale) != 0) {
-      // not expected once the done words are current: stale words one at a
-      // time (few registers; this is the rare path)
-      const uint64_t c0 = wall_clock64();
-      int it = 0;
-      while (true) {
-        __builtin_amdgcn_s_sleep(1);
-        stale = false;
-#pragma unroll
-        for (int t = 0; t < MAXB; t++) {
-          const int tt = min(t, B - 1);
-          if (need0(t) && !tag_ok(w0[t], tag)) w0[t] = ld_word_coherent(part + ((size_t)pb0 * B + tt) * H + row);
-          if (need1(t) && !tag_ok(w1[t], tag)) w1[t] = ld_word_coherent(part + ((size_t)pb1 * B + tt) * H + row);
-          stale |= (need0(t) && !tag_ok(w0[t], tag)) || (need1(t) && !tag_ok(w1[t], tag));
-        }
-        if (__builtin_amdgcn_ballot_w64(stale) == 0) break;
-        if ((++it & 15) == 0 && wall_clock64() - c0 > G.wait_ticks) {
-          if ((tid & 63) == 0) flag_error(ws.sync, 4u);
-          break;
-        }
-      }
-    }
 #pragma unroll
     for (int t = 0; t < MAXB; t++) {
       if (t < B) {
-        float a = need0(t) ? __uint_as_float((uint32_t)w0[t]) : 0.0f;
-        a += need1(t) ? __uint_as_float((uint32_t)w1[t]) : 0.0f;
+        float a = need0(t) ? w0[t] : 0.0f;
+        a += need1(t) ? w1[t] : 0.0f;
         s_red[(t * F_WAVES + g) * 64 + rr] = a;
       }
     }

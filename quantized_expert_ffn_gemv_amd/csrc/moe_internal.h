@@ -55,7 +55,8 @@ struct LayerDev {
 struct DecodeWs {
   uint32_t* sync;  // counts and epoch of the one-kernel path (counts zero between calls)
   double* logits;  // four-kernel path: [B][E] fp64; one-kernel path: rotating slots of [E][2] tagged words
-  float* part;     // four-kernel path: [B*k*(I/16) + B*(I/8)][H] partial down products
+  float* part;     // four-kernel path: [B*k*(I/16) + B*(I/8)][H] partial down products;
+                   // batched one-kernel path: [256][B][H] per-workgroup partials (untagged)
   uint64_t* part_words;  // one-kernel path: [producers][H] tagged partial down products (fp32 bits), read within each XCD
   uint64_t* xsum_words;  // one-kernel path: [8][H] tagged per-XCD sums of the partials
   uint32_t* ctr;         // one-kernel path: router counters, rotating slots x XCD groups, one 128-byte line each
@@ -94,7 +95,7 @@ size_t decode1_part_words(int H, int I, int k, bool has_shared);
 size_t decode1_xsum_words(int H);
 size_t decode1_counter_words();
 bool decode1_fits(int E, int H, int I, int k, bool has_shared);  // shape handled by the one-kernel path
-// batched one-kernel path (B = 2..8): [256][B][H] partials, [8][B][H] XCD sums, [8][512] routing words
+// batched one-kernel path (B = 2..8): [256][B][H] fp32 partials, [8][B][H] XCD sums, [8][512] routing words
 bool decode1b_fits(int wt, int E, int H, int I, int k, bool has_shared, int B);
 size_t decode1b_part_words(int H, int B);
 size_t decode1b_xsum_words(int H, int B);

@@ -54,13 +54,14 @@ def test_noalloc_matches_workspace_entry_point(moe, name):
 
 
 def test_noalloc_rejects_too_large_a_workspace(moe):
-    # a layer whose batch-8 workspace exceeds the 32 MiB scratch array
-    host = synth.random_layer(16, 16, 2048, 512, "q4", "bf16", seed=31, router_sd=0.05)
+    # a layer whose batch-4 workspace exceeds the 32 MiB scratch array (hidden
+    # 4096 takes the four-kernel path, whose partials are per slot and token)
+    host = synth.random_layer(16, 16, 4096, 512, "q4", "bf16", seed=31, router_sd=0.05)
     L = moe.DeviceLayer(host)
-    need = moe.moe_workspace_bytes(L, 8, 0)
+    need = moe.moe_workspace_bytes(L, 4, 0)
     assert need > 32 << 20
-    x = synth.normal_bf16(synth.key(31, 1, 1, 1, 1), (8, 2048), 1.0)
-    y = torch.empty((8, 2048), dtype=torch.int16, device="cuda")
+    x = synth.normal_bf16(synth.key(31, 1, 1, 1, 1), (4, 4096), 1.0)
+    y = torch.empty((4, 4096), dtype=torch.int16, device="cuda")
     with pytest.raises(moe.MoeError) as ei:
         moe.moe_forward_decode_noalloc(L, to_dev(x), y)
     assert ei.value.status == moe.MOE_ERR_WORKSPACE
