@@ -230,6 +230,40 @@ def test_decode_q4_verify_batches(moe, decode_q4, B):
             assert np.array_equal(y[c * B + i], y[c * B + j]), "identical tokens of one call must give identical outputs"
 
 
+@pytest.mark.parametrize("B", [4, 5])
+def test_batched_decode_replays_bit_identical(moe, decode_q4, B):
+    # the batched one-kernel path hands its per-workgroup partials over
+    # through done words (the partials themselves carry no tag): the 256
+    # tokens as calls of B, captured in a HIP graph and replayed with eager
+    # work between the replays, give the eager results bit for bit every time
+    _, L, x = decode_q4
+    T = (x.shape[0] // B) * B
+    x = x[:T]
+    log("batched decode B=%d: %d calls captured, 3 replays against eager" % (B, T // B))
+    y_eager, idx_eager, _ = _decode_calls(moe, L, x, B)
+    xd = to_dev(x)
+    yd = torch.zeros((T, L.H), dtype=torch.int16, device="cuda")
+    ws = moe.make_workspace(L, B, 0)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for t in range(0, T, B):
+            moe.moe_forward_decode(L, xd[t:t + B], yd[t:t + B], ws)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    gr = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gr):
+        for t in range(0, T, B):
+            moe.moe_forward_decode(L, xd[t:t + B], yd[t:t + B], ws)
+    for rep in range(3):
+        yd.zero_()
+        _decode_calls(moe, L, x[:2 * B], B)  # eager work between replays
+        gr.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(from_dev_bits(yd), y_eager), "replay %d differs from eager" % rep
+    moe.moe_workspace_check(ws)
+
+
 @pytest.mark.parametrize("B", [1, 3])
 def test_stack_decode_layer_matches_separate_calls(moe, decode_q4, B):
     # moe_stack_decode_layer (one kernel at batch 1: norm, MoE, residual)
