@@ -137,10 +137,11 @@ size_t moe_workspace_bytes(const moe_layer *layer, int32_t max_tokens, int32_t m
 /* Workspace contract (the library's own). A decode workspace must be all
  * zero before its first decode call: moe_workspace_init zero-fills all
  * ws_bytes (as would any zero fill). Its first 4096 bytes hold the counts and the call epoch of the
- * batch-1 decode kernel; the rest holds the tagged words through which its
- * workgroups hand data to each other (a word counts only when it carries the
- * current call's tag, so memory left by an earlier owner must not be reused
- * uninitialised). Every call leaves the counts zero and advances the epoch,
+ * one-kernel decode paths; the rest holds the words through which their
+ * workgroups hand data to each other: every flag, and every value not
+ * guarded by a flag, carries the call's tag (a word counts only when it
+ * carries the current call's tag, so memory left by an earlier owner must
+ * not be reused uninitialised). Every call leaves the counts zero and advances the epoch,
  * so the workspace can be reused call after call and inside captured HIP
  * graphs. Calls that share one workspace must be ordered (one stream);
  * concurrent calls on one workspace race. Prefill workspaces need no
