@@ -381,10 +381,10 @@ __device__ __forceinline__ float qdot32_reg(const Raw& r, const uint16_t* a, flo
 // ---------------------------------------------------------------------------
 constexpr int F_GU_NB = 4;  // chunks per thread and batch
 
-template <int WT, int RPW, typename After>
+template <int WT, int RPW, typename After, typename Before>
 __device__ __forceinline__ float gate_up_h(const uint8_t* __restrict__ gu, const uint16_t* __restrict__ gus, int H, int R,
                                            int q, int hf, const uint16_t* xs, const float* xsum, float* s_red,
-                                           uint16_t* s_h, After&& after_first_issue) {
+                                           uint16_t* s_h, After&& after_first_issue, Before&& before_reduce) {
   constexpr int KC = kchunk<WT>();
   constexpr int NKP = F_THREADS / RPW;  // k-parts
   constexpr int NB = F_GU_NB;
@@ -435,6 +435,7 @@ __device__ __forceinline__ float gate_up_h(const uint8_t* __restrict__ gu, const
   if constexpr (RPW == 16) acc += __shfl_xor(acc, 16, 64);
   if constexpr (RPW <= 32) acc += __shfl_xor(acc, 32, 64);
   if (lane < RPW) s_red[wave * RPW + rr] = acc;
+  before_reduce();  // work that needs neither h nor the barrier, done while the waves gather
   __syncthreads();
   float hv = 0.0f;
   if ((int)threadIdx.x < RPW / 2) {
@@ -705,6 +706,48 @@ __device__ __forceinline__ void down_store(const uint8_t* __restrict__ d, int H,
   }
 }
 
+// A routed unit's Q3 down chunks as bf16 pairs (128 + code), unpacked while
+// the workgroup gathers its gate/up sums, so that the VALU work left once h
+// is known is the dot products alone (a Q3 pair costs a few operations to
+// unpack: 13.58 -> 13.48 us per token; for Q4, one and-or per pair, the
+// earlier unpack measured 0.03 us slower and is not used), and their fp16
+// scales as fp32.
+struct DownPairs {
+  uint32_t p[F_RPT][16];
+  float s[F_RPT];
+};
+template <int WT>
+__device__ __forceinline__ void down_unpack(const DownPre<WT>& pre, DownPairs& d) {
+  static_assert(WT == MOE_W_Q3, "Q3 only");
+#pragma unroll
+  for (int n = 0; n < F_RPT; n++) {
+    q3_pairs<BF16_MAGIC2>(pre.r[n].w[0], pre.r[n].w[1], pre.r[n].w[2], d.p[n]);
+    d.s[n] = f16_to_f32(pre.s[n]);
+  }
+}
+// down_store for unpacked chunks: the same sums in the same order as
+// qdot32_regs, so the partials are bit for bit those of down_store
+template <int WT>
+__device__ __forceinline__ void down_store_pairs(const DownPairs& d, int H, const uint16_t* s_h, float hsum, float scale,
+                                                 uint64_t* part, uint32_t tag) {
+  const uint4* hp = reinterpret_cast<const uint4*>(s_h);
+  const uint4 hv[4] = {hp[0], hp[1], hp[2], hp[3]};
+#pragma unroll
+  for (int n = 0; n < F_RPT; n++) {
+    const int row = (int)threadIdx.x + F_THREADS * n;
+    float c0 = -(128.0f + (float)QOff<WT>::v) * hsum, c1 = 0.0f, c2 = 0.0f, c3 = 0.0f;
+#pragma unroll
+    for (int qq = 0; qq < 4; qq++) {
+      c0 = dot2_bf16(d.p[n][4 * qq + 0], hv[qq].x, c0);
+      c1 = dot2_bf16(d.p[n][4 * qq + 1], hv[qq].y, c1);
+      c2 = dot2_bf16(d.p[n][4 * qq + 2], hv[qq].z, c2);
+      c3 = dot2_bf16(d.p[n][4 * qq + 3], hv[qq].w, c3);
+    }
+    const float v = d.s[n] * ((c0 + c1) + (c2 + c3));
+    if (row < H) st_word_xcd(part + row, __float_as_uint(v * scale), tag);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // XCD-level sum. Workgroup j of XCD x sums rows r0 .. r0 + H/32 - 1 (r0 =
 // j * H/32) over the partials of the producers that run on XCD x (the
@@ -890,7 +933,7 @@ __global__ __launch_bounds__(F_THREADS, 4) void k_decode1(LayerDev L, const uint
     const int q = su >> 1, hf = su & 1;
     DownPre<SW> pre;
     gate_up_h<SW, 16>(L.sgu, nullptr, H, 2 * I, q, hf, s_x, nullptr, s_red, s_h,
-                      [&] { down_prefetch<SW, 8>(L.sdn, nullptr, H, 16 * q + 8 * hf, pre); });
+                      [&] { down_prefetch<SW, 8>(L.sdn, nullptr, H, 16 * q + 8 * hf, pre); }, [] {});
     __syncthreads();
     down_store<SW, 8>(L.sdn, H, 16 * q + 8 * hf, pre, s_h, 0.0f, 1.0f, part + (size_t)su * H, tag);
   }
@@ -916,15 +959,20 @@ __global__ __launch_bounds__(F_THREADS, 4) void k_decode1(LayerDev L, const uint
     const uint8_t* dn = L.dn + (size_t)e * L.dn_stride;
     const uint16_t* dns = is_q<WT>() ? L.dn_s + (size_t)e * L.dn_s_stride : nullptr;
     DownPre<WT> pre;
+    DownPairs dp;  // Q3: the down chunks as bf16 pairs, unpacked before h is known
     if constexpr (!is_q<WT>()) block_topk_gates(s_tk, L.E, L.k, s_idx, s_gate);
-    const float hv = gate_up_h<WT, 64>(L.gu + (size_t)e * L.gu_stride,
-                                       is_q<WT>() ? L.gu_s + (size_t)e * L.gu_s_stride : nullptr, H, 2 * I, q, 0, xs, xsum,
-                                       s_red, s_h, [&] {
-                                         down_prefetch<WT, 32>(dn, dns, H, 32 * q, pre);
-                                         // the gates, while the weights stream (read after gate_up_h's
-                                         // barrier); dense weights have no registers to spare there
-                                         if constexpr (is_q<WT>()) block_topk_gates(s_tk, L.E, L.k, s_idx, s_gate);
-                                       });
+    const float hv = gate_up_h<WT, 64>(
+        L.gu + (size_t)e * L.gu_stride, is_q<WT>() ? L.gu_s + (size_t)e * L.gu_s_stride : nullptr, H, 2 * I, q, 0, xs,
+        xsum, s_red, s_h,
+        [&] {
+          down_prefetch<WT, 32>(dn, dns, H, 32 * q, pre);
+          // the gates, while the weights stream (read after gate_up_h's
+          // barrier); dense weights have no registers to spare there
+          if constexpr (is_q<WT>()) block_topk_gates(s_tk, L.E, L.k, s_idx, s_gate);
+        },
+        [&] {
+          if constexpr (WT == MOE_W_Q3) down_unpack<WT>(pre, dp);
+        });
     if (ru == 0 && (int)threadIdx.x < L.k) {
       if (idx_out) idx_out[threadIdx.x] = s_idx[threadIdx.x];
       if (gate_out) gate_out[threadIdx.x] = s_gate[threadIdx.x];
@@ -939,8 +987,11 @@ __global__ __launch_bounds__(F_THREADS, 4) void k_decode1(LayerDev L, const uint
       }
     }
     __syncthreads();
-    down_store<WT, 32>(dn, H, 32 * q, pre, s_h, is_q<WT>() ? s_hsum : 0.0f, s_gate[u],
-                       part + (size_t)(G.nSG + ru) * H, tag);
+    if constexpr (WT == MOE_W_Q3)
+      down_store_pairs<WT>(dp, H, s_h, s_hsum, s_gate[u], part + (size_t)(G.nSG + ru) * H, tag);
+    else
+      down_store<WT, 32>(dn, H, 32 * q, pre, s_h, is_q<WT>() ? s_hsum : 0.0f, s_gate[u],
+                         part + (size_t)(G.nSG + ru) * H, tag);
   }
   // XCD sums (XCDs that hold producers), then the final rows
   if ((G.xmask >> (b % F_NX)) & 1) {
