@@ -151,8 +151,8 @@ moe_status moe_workspace_init(void *ws, size_t ws_bytes, hipStream_t stream);
 /* Synchronises `stream`, then reports whether a device-side wait of a
  * decode call on this workspace ran out of time since the last check
  * (MOE_ERR_DEVICE: results of those calls are invalid) and clears the
- * report. The one-kernel batch-1 decode needs all of its workgroups
- * resident at once (some wait for others); the library checks that the
+ * report. The one-kernel decode paths (batch 1 and 2..8) need all of their
+ * workgroups resident at once (some wait for others); the library checks that the
  * grid fits the device, but other work on the GPU (other streams, other
  * processes) can hold compute units long enough for a wait to reach its
  * bound (moe_debug_set_wait_limit; about 0.34 s by default). The bound
