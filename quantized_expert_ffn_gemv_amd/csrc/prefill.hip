@@ -82,9 +82,10 @@ __global__ __launch_bounds__(256) void k_pf_rsplit(const float* __restrict__ W, 
 // order (DPP rows, then the four row sums).
 constexpr int RS_NV = 16;
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
-template <int NXH>
+template <int NXH, bool SPLIT>
 __global__ __launch_bounds__(256) void k_pf_rselect(const float* __restrict__ W, const float* __restrict__ bias,
                                                     const uint16_t* __restrict__ x, const float* __restrict__ approx,
+                                                    const float* __restrict__ approx2,
                                                     const double* __restrict__ wnorm, int T, int E, int H, int k,
                                                     int32_t* __restrict__ idx, float* __restrict__ gates,
                                                     int32_t* idx_out, float* gate_out) {
@@ -132,8 +133,15 @@ __global__ __launch_bounds__(256) void k_pf_rselect(const float* __restrict__ W,
     const float bv = bias ? bias[ec] : 0.0f;
     // (the approximate logits and x are read once: non-temporal, so that
     // they do not push the router rows out of the L2)
-    const double a = (double)((__builtin_nontemporal_load(approx + (size_t)t * 2 * E + ec) +
-                               __builtin_nontemporal_load(approx + (size_t)t * 2 * E + E + ec)) + bv);
+    // (split K: each half's two parts added first; the bound below covers
+    // any summation order of the H products in fp32)
+    float ahi = __builtin_nontemporal_load(approx + (size_t)t * 2 * E + ec);
+    float alo = __builtin_nontemporal_load(approx + (size_t)t * 2 * E + E + ec);
+    if constexpr (SPLIT) {
+      ahi += __builtin_nontemporal_load(approx2 + (size_t)t * 2 * E + ec);
+      alo += __builtin_nontemporal_load(approx2 + (size_t)t * 2 * E + E + ec);
+    }
+    const double a = (double)((ahi + alo) + bv);
     const double B = C * wnorm[ec] * xn + 0x1p-22 * (__builtin_fabs(a) + __builtin_fabs((double)bv)) + 0x1p-110 * xn + 0x1p-100;
     lo[i] = (e < E) ? a - B : -__builtin_inf();
     up[i] = (e < E) ? a + B : -__builtin_inf();
@@ -473,6 +481,10 @@ struct GemmArgs {
   int M_total;            // rows when offsets == NULL
   uint16_t* out;          // gate/up: h [rows][N/2]; down: Y [rows][N]
   float* out_f32;         // GK_F32: [rows][N]
+  // GK_F32 over one matrix only: K split into ksplit equal parts, part p
+  // written to out_f32 + p * out_plane (the caller adds the parts)
+  int ksplit;
+  ptrdiff_t out_plane;
 };
 
 // ---------------------------------------------------------------------------
@@ -604,11 +616,17 @@ __global__ __launch_bounds__(G_THREADS, 2) void k_pf_gemm(GemmArgs g) {
   // ---- tile
   const int NT = (g.N + BN - 1) / BN;
   const int mt_total = g.offsets ? g.tile_start[g.E] : (g.M_total + PF_BM - 1) / PF_BM;
-  const int total = mt_total * NT;
+  const int nsplit = (KIND == GK_F32 && !g.offsets && g.ksplit > 1) ? g.ksplit : 1;
+  const int total = mt_total * NT * nsplit;
   const int per = (total + 7) >> 3;
   const int ix = blockIdx.x >> 3;
-  const int logical = (blockIdx.x & 7) * per + ix;
+  int logical = (blockIdx.x & 7) * per + ix;
   if (ix >= per || logical >= total) return;
+  // K part of this tile (split K: the parts of one output tile are adjacent
+  // in the list, so they run on one XCD and share its L2 copy of the rows)
+  const int ksp = logical % nsplit;
+  logical /= nsplit;
+  const int Kp = g.K / nsplit, kofs = ksp * Kp;
 
   int e = 0, m0 = 0, M = 0, pos0 = 0, nt = 0;
   if (g.offsets) {
@@ -647,7 +665,7 @@ __global__ __launch_bounds__(G_THREADS, 2) void k_pf_gemm(GemmArgs g) {
 #pragma unroll
     for (int j = 0; j < NSW; j++) acc[i][j] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 
-  const int nst = (g.K + G_BK - 1) / G_BK;
+  const int nst = (Kp + G_BK - 1) / G_BK;
   // A DMA: wave w, load i covers slot rows 4 (G_ALOADS w + i) .. +3; lane -> row + lane / 16, position
   // lane % 16 holding chunk (lane % 16) ^ (row % 16)
   // The issue helpers derive their per-lane offsets from an opaque copy of the
@@ -660,13 +678,13 @@ __global__ __launch_bounds__(G_THREADS, 2) void k_pf_gemm(GemmArgs g) {
     for (int i = 0; i < G_ALOADS; i++) {
       const int row = 4 * (G_ALOADS * wave + i) + (ln >> 4);
       const int k = s * G_BK + 8 * ((ln & 15) ^ (row & 15));
-      const uint16_t* src = g.a + (size_t)s_row[row] * g.K + (k < g.K ? k : 0);  // past K: a finite element (weight 0)
+      const uint16_t* src = g.a + (size_t)s_row[row] * g.K + kofs + (k < Kp ? k : 0);  // past K: a finite element (weight 0)
       __builtin_amdgcn_global_load_lds((gbl_void_t)src, (lds_void_t)(slot + 64 * (G_ALOADS * wave + i)), 16, 0, 0);
     }
   };
   // B: lane -> (row n = lane % 16 of each of the wave's 4 subtiles, K block j = lane / 16)
   const int bj = lane >> 4;
-  const int nblk = g.K >> 5;
+  const int nblk = Kp >> 5, blk0 = kofs >> 5;
   BRaw<WT> rb0[NSW];
   // lane's block of stage s: 4 s + bj; rows past N read row N - 1, blocks past K the stage's first block
   auto issue_b = [&](int s, BRaw<WT> (&r)[NSW]) {
@@ -674,7 +692,7 @@ __global__ __launch_bounds__(G_THREADS, 2) void k_pf_gemm(GemmArgs g) {
     asm volatile("" : "+v"(ln));
     const int j = ln >> 4;
     const bool okb = 4 * s + j < nblk;
-    const uint32_t blk = (uint32_t)(okb ? 4 * s + j : 4 * s);
+    const uint32_t blk = (uint32_t)(blk0 + (okb ? 4 * s + j : 4 * s));
 #pragma unroll
     for (int sub = 0; sub < NSW; sub++) {
       const int n = n0 + 16 * NSW * wave + (ln & 15) + 16 * sub;
@@ -764,7 +782,7 @@ __global__ __launch_bounds__(G_THREADS, 2) void k_pf_gemm(GemmArgs g) {
           for (int r = 0; r < 4; r++) {
             const int m = 16 * i + 4 * (lane >> 4) + r;
             if (m < M && col < g.N) {
-              if (KIND == GK_F32) g.out_f32[(size_t)(pos0 + m) * g.N + col] = acc[i][j][r];
+              if (KIND == GK_F32) g.out_f32[ksp * g.out_plane + (size_t)(pos0 + m) * g.N + col] = acc[i][j][r];
               else g.out[(size_t)(pos0 + m) * g.N + col] = f32_to_bf16(acc[i][j][r]);
             }
           }
@@ -1155,19 +1173,36 @@ static hipError_t route_steps(const LayerDev& L, const uint16_t* x, int T, int32
                               int32_t* counts_out, const PrefillWs& ws, hipStream_t st, bool permute) {
   const int E = L.E, k = L.k, H = L.H;
   float* approx = reinterpret_cast<float*>(ws.logits);  // [T][2E] fp32 in the [T][E] fp64 area
+  // Few tokens leave most of the GPU idle in the approximate-logit GEMM (a
+  // 4096-token call has 344 tiles for 768 workgroup slots, each tile a chain
+  // of 16 dependent K stages): K is then split in two, the second half's
+  // products going to a plane in the per-slot output area (free until the
+  // down GEMM), and the select adds the halves.
+  const int rtiles = (T + PF_BM - 1) / PF_BM * ((2 * E + g_bn<MOE_W_BF16>() - 1) / g_bn<MOE_W_BF16>());
+  const bool rsplit2 = 2 * rtiles <= 3 * 256 && H % (2 * G_BK) == 0 && (size_t)k * H >= (size_t)4 * E;
+  float* approx2 = reinterpret_cast<float*>(ws.Y);
   (void)launch_k(KC_PF_RSPLIT, k_pf_rsplit, dim3(E), dim3(256), 0, st, L.router_w, E, H, ws.rsplit, ws.wnorm);
   {
     GemmArgs g{};
     g.w = reinterpret_cast<const uint8_t*>(ws.rsplit); g.N = 2 * E; g.K = H; g.a = x; g.perm = nullptr; g.k = 1;
     g.offsets = nullptr; g.M_total = T; g.out_f32 = approx;
-    gemm_launch<MOE_W_BF16, GK_F32>(KC_PF_ROUTER, g, (T + PF_BM - 1) / PF_BM, st);
+    g.ksplit = rsplit2 ? 2 : 1;
+    g.out_plane = approx2 - approx;
+    gemm_launch<MOE_W_BF16, GK_F32>(KC_PF_ROUTER, g, g.ksplit * ((T + PF_BM - 1) / PF_BM), st);
   }
   {
     const int nxh = (H + 511) / 512;
-    auto sel = nxh <= 1 ? k_pf_rselect<1> : nxh <= 2 ? k_pf_rselect<2> : nxh <= 4 ? k_pf_rselect<4>
-             : nxh <= 8 ? k_pf_rselect<8> : k_pf_rselect<16>;
-    (void)launch_k(KC_PF_TOPK, sel, dim3((T + 3) / 4), dim3(256), 0, st, L.router_w, L.router_b, x, approx, ws.wnorm, T, E,
-                   H, k, ws.idx, ws.gates, idx_out, gate_out);
+    if (rsplit2) {
+      auto sel = nxh <= 1 ? k_pf_rselect<1, true> : nxh <= 2 ? k_pf_rselect<2, true> : nxh <= 4 ? k_pf_rselect<4, true>
+               : nxh <= 8 ? k_pf_rselect<8, true> : k_pf_rselect<16, true>;
+      (void)launch_k(KC_PF_TOPK, sel, dim3((T + 3) / 4), dim3(256), 0, st, L.router_w, L.router_b, x, approx, approx2,
+                     ws.wnorm, T, E, H, k, ws.idx, ws.gates, idx_out, gate_out);
+    } else {
+      auto sel = nxh <= 1 ? k_pf_rselect<1, false> : nxh <= 2 ? k_pf_rselect<2, false> : nxh <= 4 ? k_pf_rselect<4, false>
+               : nxh <= 8 ? k_pf_rselect<8, false> : k_pf_rselect<16, false>;
+      (void)launch_k(KC_PF_TOPK, sel, dim3((T + 3) / 4), dim3(256), 0, st, L.router_w, L.router_b, x, approx, approx,
+                     ws.wnorm, T, E, H, k, ws.idx, ws.gates, idx_out, gate_out);
+    }
   }
   if (!permute && !counts_out) return hipGetLastError();
   const int nblk = (T + PF_TOK_PER_BLK - 1) / PF_TOK_PER_BLK;
